@@ -1,0 +1,197 @@
+"""Seeded synthetic inputs for the hybrid attention forward.
+
+This module draws random numbers and rounds them to the I/O dtype; it holds
+none of the method's arithmetic. Both the HIP path (tests, bench) and the CPU
+oracle (tests only) take their inputs from here.
+
+Each tensor slice is drawn from ``numpy.random.default_rng([seed, tensor_id,
+b, h])`` so that a slice can be regenerated on its own. Tensor ids: q 0, k 1,
+v 2, gate 3, beta 4, alpha 5, text-k 6, text-v 7, text-beta 8, conv_k 9,
+conv_v 10.
+
+Distributions (the workloads of the hybrid attention on video-DiT latents):
+q, k, v, gate ~ N(0, 1); beta ~ U(0, 1) per (head, token); alpha ~ U(lo, hi)
+per (head, frame, key channel); conv taps ~ N(0, 1/4); RMSNorm weight = 1;
+text tokens k, v ~ N(0, 1), beta ~ U(0, 1). bf16 tensors are the fp32 draws
+rounded to nearest-even.
+"""
+
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+TID = dict(q=0, k=1, v=2, gate=3, beta=4, alpha=5, k_txt=6, v_txt=7,
+           beta_txt=8, conv_k=9, conv_v=10)
+
+# The five workload shapes. Token counts per frame follow 832x480 (52x30
+# latent grid) and 1024x1024 (64x64) canvases at 16x spatial compression.
+CONFIGS = {
+    0: dict(name="tiny-f32", batch=1, heads=1, head_dim=16, frames=10,
+            tokens_per_frame=16, dtype="f32", chunk=5, radius=1,
+            rules=("vdn_solve",), c=0.5, text_tokens=0, alpha=(0.8, 1.0),
+            seed=0),
+    1: dict(name="small-bf16-text", batch=1, heads=8, head_dim=64, frames=20,
+            tokens_per_frame=256, dtype="bf16", chunk=5, radius=1,
+            rules=("vdn_solve",), c=0.5, text_tokens=64, alpha=(0.8, 1.0),
+            seed=1),
+    2: dict(name="clip-832x480-31f", batch=1, heads=24, head_dim=128,
+            frames=31, tokens_per_frame=1560, dtype="bf16", chunk=5,
+            radius=1, rules=("vdn_solve",), c=0.5, text_tokens=256,
+            alpha=(0.9, 1.0), seed=2),
+    3: dict(name="long-clip-832x480-85f", batch=1, heads=24, head_dim=128,
+            frames=85, tokens_per_frame=1560, dtype="bf16", chunk=5,
+            radius=1, rules=("vdn_solve", "sana_scaled", "vdn_scaled"),
+            c=0.5, text_tokens=256, alpha=(0.9, 1.0), seed=3),
+    4: dict(name="canvas-1024x1024-64f", batch=1, heads=24, head_dim=128,
+            frames=64, tokens_per_frame=4096, dtype="bf16", chunk=5,
+            radius=1, rules=("vdn_solve",), c=0.5, text_tokens=256,
+            alpha=(0.95, 1.0), seed=4),
+}
+
+
+def tiny_config(frames=17, radius=1, text_tokens=16, rule="vdn_solve",
+                head_dim=16, tokens_per_frame=16, heads=1, dtype="f32",
+                seed=100, alpha=(0.8, 1.0), chunk=5, batch=1):
+    """Extra small cases: partial last chunk, text state on/off, radius 0."""
+    return dict(name=f"tiny-F{frames}-r{radius}-T{text_tokens}-{rule}",
+                batch=batch, heads=heads, head_dim=head_dim, frames=frames,
+                tokens_per_frame=tokens_per_frame, dtype=dtype, chunk=chunk,
+                radius=radius, rules=(rule,), c=0.5, text_tokens=text_tokens,
+                alpha=alpha, seed=seed)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Inputs:
+    """Host arrays of one workload. io tensors (q, k, v, gate, k_txt, v_txt)
+    are float32 for ``dtype == 'f32'`` and uint16 bf16 bits for 'bf16'."""
+    cfg: dict
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    gate: np.ndarray
+    beta: np.ndarray
+    alpha: np.ndarray
+    conv_k: np.ndarray
+    conv_v: np.ndarray
+    rms_weight: np.ndarray
+    k_txt: np.ndarray | None = None
+    v_txt: np.ndarray | None = None
+    beta_txt: np.ndarray | None = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def N(self) -> int:
+        return self.cfg["frames"] * self.cfg["tokens_per_frame"]
+
+    def f32(self, name: str, b=None, h=None) -> np.ndarray:
+        """float32 view of an io tensor (whole, or one (b, h) slice)."""
+        a = getattr(self, name)
+        if b is not None:
+            a = a[b, h]
+        if self.cfg["dtype"] == "bf16" and a.dtype == np.uint16:
+            return bf16_bits_to_f32(a)
+        return np.asarray(a, dtype=np.float32)
+
+    def f64(self, name: str, b=None, h=None) -> np.ndarray:
+        return self.f32(name, b, h).astype(np.float64)
+
+
+def _draw(seed, name, b, h, shape, kind, lo=0.0, hi=1.0, std=1.0):
+    rng = np.random.default_rng([seed, TID[name], b, h])
+    if kind == "normal":
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        return x
+    x = rng.random(shape, dtype=np.float32)
+    return (np.float32(lo) + np.float32(hi - lo) * x).astype(np.float32)
+
+
+def make(cfg, *, beta_zero=False, alpha_one=False, identity_conv=False,
+         workers=None) -> Inputs:
+    """Generate the inputs of a workload.
+
+    ``cfg`` is a key of :data:`CONFIGS` or a config dict. The switches replace
+    a tensor by a constant for the special cases the tests use: beta = 0,
+    alpha = 1, identity conv taps (1, 0, 0, 0).
+    """
+    if not isinstance(cfg, dict):
+        cfg = CONFIGS[int(cfg)]
+    cfg = dict(cfg)
+    B, H, d = cfg["batch"], cfg["heads"], cfg["head_dim"]
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+    N = F * S
+    T = cfg["text_tokens"]
+    seed = cfg["seed"]
+    bf16 = cfg["dtype"] == "bf16"
+    io_dtype = np.uint16 if bf16 else np.float32
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+
+    def io(x):
+        return f32_to_bf16_bits(x) if bf16 else x
+
+    q = np.empty((B, H, N, d), dtype=io_dtype)
+    k = np.empty_like(q)
+    v = np.empty_like(q)
+    gate = np.empty_like(q)
+    beta = np.empty((B, H, N), dtype=np.float32)
+    alpha = np.empty((B, H, F, d), dtype=np.float32)
+    if T > 0:
+        k_txt = np.empty((B, H, T, d), dtype=io_dtype)
+        v_txt = np.empty_like(k_txt)
+        beta_txt = np.empty((B, H, T), dtype=np.float32)
+    else:
+        k_txt = v_txt = beta_txt = None
+
+    def slice_job(bh):
+        b, h = bh
+        for name, arr in (("q", q), ("k", k), ("v", v), ("gate", gate)):
+            arr[b, h] = io(_draw(seed, name, b, h, (N, d), "normal"))
+        beta[b, h] = 0.0 if beta_zero else _draw(seed, "beta", b, h, (N,), "uniform")
+        a_lo, a_hi = cfg["alpha"]
+        alpha[b, h] = 1.0 if alpha_one else _draw(seed, "alpha", b, h, (F, d),
+                                                   "uniform", a_lo, a_hi)
+        if T > 0:
+            k_txt[b, h] = io(_draw(seed, "k_txt", b, h, (T, d), "normal"))
+            v_txt[b, h] = io(_draw(seed, "v_txt", b, h, (T, d), "normal"))
+            beta_txt[b, h] = _draw(seed, "beta_txt", b, h, (T,), "uniform")
+
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+    if workers > 1 and len(jobs) > 1:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(slice_job, jobs))
+    else:
+        for j in jobs:
+            slice_job(j)
+
+    conv_k = np.empty((H, d, 4), dtype=np.float32)
+    conv_v = np.empty_like(conv_k)
+    for h in range(H):
+        if identity_conv:
+            conv_k[h] = 0.0
+            conv_k[h, :, 0] = 1.0
+            conv_v[h] = conv_k[h]
+        else:
+            conv_k[h] = _draw(seed, "conv_k", 0, h, (d, 4), "normal", std=0.5)
+            conv_v[h] = _draw(seed, "conv_v", 0, h, (d, 4), "normal", std=0.5)
+    rms_weight = np.ones(d, dtype=np.float32)
+    return Inputs(cfg=cfg, q=q, k=k, v=v, gate=gate, beta=beta, alpha=alpha,
+                  conv_k=conv_k, conv_v=conv_v, rms_weight=rms_weight,
+                  k_txt=k_txt, v_txt=v_txt, beta_txt=beta_txt)

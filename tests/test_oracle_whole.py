@@ -1,0 +1,78 @@
+"""Whole-call pins of the oracle (CPU only).
+
+"Why video models are stuck on attention" (VDN-H3 article): the softmax branch
+covers the window, the linear branch everything outside it, and the outputs
+are summed.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from hybrid_window_softmax_amd import inputs
+
+
+def _run(inp, rule="vdn_solve", text=True, flip=False):
+    cfg = inp.cfg
+    B, H = cfg["batch"], cfg["heads"]
+    F, S, d = cfg["frames"], cfg["tokens_per_frame"], cfg["head_dim"]
+    outs = []
+    for b in range(B):
+        for h in range(H):
+            args = [inp.f64(n, b, h) for n in ("q", "k", "v")]
+            beta, alpha, gate = inp.beta[b, h].astype(np.float64), inp.alpha[b, h].astype(np.float64), inp.f64("gate", b, h)
+            st = None
+            if text and inp.k_txt is not None:
+                st = oracle.text_state(inp.f64("k_txt", b, h), inp.f64("v_txt", b, h), inp.beta_txt[b, h])
+            if flip:  # reverse the frame order, keep token order within frames
+                def fl(x, per_token=True):
+                    if per_token:
+                        return x.reshape(F, S, *x.shape[1:])[::-1].reshape(x.shape)
+                    return x[::-1]
+                args = [fl(a) for a in args]
+                beta, gate, alpha = fl(beta), fl(gate), fl(alpha, False)
+            r = oracle.hybrid_attn_head(*args, beta, alpha, gate, st, inp.conv_k[h], inp.conv_v[h],
+                                        inp.rms_weight, S, cfg["chunk"], cfg["radius"], rule,
+                                        cfg["c"], 0.5, 1e-6)
+            outs.append(r)
+    return outs
+
+
+def test_config0_has_no_far_field():
+    inp = inputs.make(0)
+    (out, o_sm, y, _), = _run(inp)
+    # F = 10 frames with chunk 5, radius 1: every window is [0, 9] and there is
+    # no text state, so the linear branch reads a zero state: y == 0 exactly
+    assert not np.any(y)
+    assert np.array_equal(out, o_sm)
+
+
+def test_beta0_no_text_is_pure_softmax():
+    cfg = inputs.tiny_config(frames=17, text_tokens=0)
+    inp = inputs.make(cfg, beta_zero=True)
+    (out, o_sm, y, _), = _run(inp)
+    assert not np.any(y)
+    assert np.array_equal(out, o_sm)
+
+
+@pytest.mark.parametrize("rule", oracle.RULES)
+def test_whole_frame_reversal_symmetry(rule):
+    # with F a multiple of chunk the window geometry is mirror-symmetric, so
+    # reversing the frames reverses the output (prefix and suffix swap roles)
+    cfg = inputs.tiny_config(frames=15, text_tokens=8, rule=rule)
+    inp = inputs.make(cfg)
+    (out, o_sm, y, _), = _run(inp, rule)
+    (outr, o_smr, yr, _), = _run(inp, rule, flip=True)
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+    back = lambda x: x.reshape(F, S, -1)[::-1].reshape(x.shape)  # noqa: E731
+    assert np.abs(back(o_smr) - o_sm).max() < 1e-12
+    assert np.abs(back(yr) - y).max() < 1e-9
+    assert np.any(y)
+
+
+def test_rel_frobenius_semantics():
+    a = np.ones((3, 4))
+    assert oracle.rel_frobenius(a, a) == 0.0
+    assert abs(oracle.rel_frobenius(1.5 * a, a) - 0.5) < 1e-15
+    assert oracle.rel_frobenius(np.zeros(3), np.zeros(3)) == 0.0
+    assert oracle.rel_frobenius(np.array([1e-30, 0, 0]), np.zeros(3)) == float("inf")
