@@ -1,0 +1,278 @@
+// C ABI of libhwa: argument validation, workspace layout and the launch
+// sequence of the hybrid attention forward. Declarations and semantics are
+// in include/hwa.h.
+
+#include <math.h>
+#include <string.h>
+
+#include "hwa_internal.h"
+
+using hwa::bf16_t;
+using hwa::Geom;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool head_dim_ok(int d, int dtype) {
+  if (dtype == HWA_BF16) return d == 64 || d == 128;
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+// Basic checks on the params struct shared by every entry point.
+hwa_status check_params(const hwa_params* p) {
+  if (!p || p->struct_size < sizeof(hwa_params)) return HWA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->heads < 1) return HWA_ERR_INVALID_ARG;
+  if (p->dtype != HWA_F32 && p->dtype != HWA_BF16) return HWA_ERR_INVALID_ARG;
+  if (p->head_dim < 1) return HWA_ERR_INVALID_ARG;
+  if (!head_dim_ok(p->head_dim, p->dtype)) return HWA_ERR_UNSUPPORTED;
+  return HWA_OK;
+}
+
+bool make_geom(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
+               int32_t radius, const hwa_params* p, Geom& g) {
+  if (frames < 1 || tokens_per_frame < 1 || chunk < 1 || radius < 0)
+    return false;
+  g.B = p->batch;
+  g.H = p->heads;
+  g.d = p->head_dim;
+  g.F = frames;
+  g.S = tokens_per_frame;
+  g.chunk = chunk;
+  g.radius = radius;
+  g.nch = (frames + chunk - 1) / chunk;
+  g.N = (long long)frames * tokens_per_frame;
+  // grid dimensions and 32-bit launch parameters stay in range
+  if (g.N > (1LL << 31) / 2 || (long long)g.B * g.H > 65535) return false;
+  return true;
+}
+
+hwa_workspace_layout compute_layout(const Geom& g, int dtype) {
+  hwa_workspace_layout L;
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t dd = (size_t)g.d * g.d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.lohi = take(2 * (size_t)g.F * sizeof(int32_t));
+  L.stat_a = take(bh * g.F * dd * sizeof(float));
+  L.stat_b = take(bh * g.F * dd * sizeof(float));
+  L.map_g = take(bh * g.F * dd * sizeof(float));
+  L.map_c = take(bh * g.F * dd * sizeof(float));
+  L.bank_p = take(bh * (g.nch + 1) * dd * sizeof(float));
+  L.bank_q = take(bh * (g.nch + 1) * dd * sizeof(float));
+  L.bank_e = take(2 * bh * (g.nch + 1) * g.d * sizeof(int32_t));
+  const size_t Np = (size_t)((g.N + 63) / 64 * 64);
+  L.v_t = take(dtype == HWA_BF16 ? bh * g.d * Np * sizeof(bf16_t) : 0);
+  L.total = off;
+  return L;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t x0 = (uintptr_t)a, x1 = x0 + na;
+  uintptr_t y0 = (uintptr_t)b, y1 = y0 + nb;
+  return x0 < y1 && y0 < x1;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hwa_status_string(hwa_status s) {
+  switch (s) {
+    case HWA_OK: return "HWA_OK: success";
+    case HWA_ERR_INVALID_ARG: return "HWA_ERR_INVALID_ARG: invalid argument";
+    case HWA_ERR_UNSUPPORTED: return "HWA_ERR_UNSUPPORTED: unsupported head_dim or dtype";
+    case HWA_ERR_WORKSPACE: return "HWA_ERR_WORKSPACE: workspace missing or too small";
+    case HWA_ERR_HIP: return "HWA_ERR_HIP: HIP launch error";
+  }
+  return "unknown hwa_status";
+}
+
+hwa_status hwa_window_bounds(int32_t frames, int32_t chunk, int32_t radius,
+                             int32_t* lo, int32_t* hi) {
+  if (frames < 1 || chunk < 1 || radius < 0 || !lo || !hi)
+    return HWA_ERR_INVALID_ARG;
+  for (int32_t t = 0; t < frames; ++t) {
+    const int64_t c = t / chunk;
+    const int64_t l = (c - radius) * (int64_t)chunk;
+    const int64_t h = (c + radius + 1) * (int64_t)chunk - 1;
+    lo[t] = (int32_t)(l < 0 ? 0 : l);
+    hi[t] = (int32_t)(h > frames - 1 ? frames - 1 : h);
+  }
+  return HWA_OK;
+}
+
+hwa_status hwa_get_workspace_layout(int32_t frames, int32_t tokens_per_frame,
+                                    int32_t chunk, const hwa_params* p,
+                                    hwa_workspace_layout* layout) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  Geom g;
+  if (!layout || !make_geom(frames, tokens_per_frame, chunk, 0, p, g))
+    return HWA_ERR_INVALID_ARG;
+  *layout = compute_layout(g, p->dtype);
+  return HWA_OK;
+}
+
+size_t hwa_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
+                           int32_t chunk, const hwa_params* p) {
+  hwa_workspace_layout L;
+  if (hwa_get_workspace_layout(frames, tokens_per_frame, chunk, p, &L) != HWA_OK)
+    return 0;
+  return L.total;
+}
+
+hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
+                           const float* beta, const float* alpha,
+                           const void* gate, const float* text_state,
+                           int32_t frames, int32_t tokens_per_frame,
+                           int32_t chunk, int32_t radius, int32_t rule,
+                           void* out, void* stream, const hwa_params* p) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, chunk, radius, p, g))
+    return HWA_ERR_INVALID_ARG;
+  if (rule < HWA_RULE_VDN_SOLVE || rule > HWA_RULE_VDN_SCALED)
+    return HWA_ERR_INVALID_ARG;
+  const uint32_t known = HWA_FLAG_SOFTMAX_ONLY | HWA_FLAG_LINEAR_ONLY |
+                         HWA_FLAG_KEEP_INTERMEDIATES;
+  if (p->flags & ~known) return HWA_ERR_INVALID_ARG;
+  const bool do_sm = !(p->flags & HWA_FLAG_LINEAR_ONLY);
+  const bool do_lin = !(p->flags & HWA_FLAG_SOFTMAX_ONLY);
+  if (!do_sm && !do_lin) return HWA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out) return HWA_ERR_INVALID_ARG;
+  if (do_lin && (!beta || !alpha || !gate || !p->conv_k || !p->conv_v))
+    return HWA_ERR_INVALID_ARG;
+  if (!isfinite(p->c) || !isfinite(p->text_scale) || !(p->rms_eps > 0.0f) ||
+      !isfinite(p->rms_eps))
+    return HWA_ERR_INVALID_ARG;
+
+  const size_t es = p->dtype == HWA_BF16 ? 2 : 4;
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t io_bytes = bh * (size_t)g.N * g.d * es;
+  const void* qs = p->q_rope ? p->q_rope : q;
+  const void* ks = p->k_rope ? p->k_rope : k;
+  const size_t va = p->dtype == HWA_BF16 ? 16 : 4;
+  if (!aligned(q, va) || !aligned(k, va) || !aligned(v, va) ||
+      !aligned(out, va) || !aligned(qs, va) || !aligned(ks, va) ||
+      (gate && !aligned(gate, va)) || (beta && !aligned(beta, 4)) ||
+      (alpha && !aligned(alpha, 4)) || (text_state && !aligned(text_state, 4)))
+    return HWA_ERR_INVALID_ARG;
+
+  const hwa_workspace_layout L = compute_layout(g, p->dtype);
+  if (!p->workspace || p->workspace_bytes < L.total ||
+      !aligned(p->workspace, kAlign))
+    return HWA_ERR_WORKSPACE;
+
+  // out must not alias any input or the workspace
+  const struct { const void* ptr; size_t n; } ins[] = {
+      {q, io_bytes},
+      {k, io_bytes},
+      {v, io_bytes},
+      {gate, io_bytes},
+      {p->q_rope, io_bytes},
+      {p->k_rope, io_bytes},
+      {beta, bh * (size_t)g.N * sizeof(float)},
+      {alpha, bh * (size_t)g.F * g.d * sizeof(float)},
+      {text_state, bh * (size_t)g.d * g.d * sizeof(float)},
+      {p->workspace, p->workspace_bytes},
+  };
+  for (const auto& in : ins)
+    if (overlaps(out, io_bytes, in.ptr, in.n)) return HWA_ERR_INVALID_ARG;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)p->workspace;
+  int32_t* lohi = (int32_t*)(ws + L.lohi);
+  float* A = (float*)(ws + L.stat_a);
+  float* Bm = (float*)(ws + L.stat_b);
+  float* G = (float*)(ws + L.map_g);
+  float* C = (float*)(ws + L.map_c);
+  float* bank_p = (float*)(ws + L.bank_p);
+  float* bank_q = (float*)(ws + L.bank_q);
+  int32_t* bank_e = (int32_t*)(ws + L.bank_e);
+  bf16_t* v_t = (bf16_t*)(ws + L.v_t);
+
+  if (hwa::launch_window_table(g, lohi, st) != hipSuccess) return HWA_ERR_HIP;
+  if (do_sm) {
+    if (p->dtype == HWA_BF16 &&
+        hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
+      return HWA_ERR_HIP;
+    if (hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out, st) !=
+        hipSuccess)
+      return HWA_ERR_HIP;
+  }
+  if (do_lin) {
+    if (hwa::launch_stats(g, p->dtype, k, v, beta, p->conv_k, p->conv_v, true,
+                          A, Bm, st) != hipSuccess)
+      return HWA_ERR_HIP;
+    if (hwa::launch_factor(g, rule, p->c, A, Bm, alpha, G, C, st) !=
+        hipSuccess)
+      return HWA_ERR_HIP;
+    if (hwa::launch_scan(g, G, C, text_state, p->text_scale, bank_p, bank_q,
+                         bank_e, st) != hipSuccess)
+      return HWA_ERR_HIP;
+    if (hwa::launch_readout(g, p->dtype, q, gate, alpha, lohi, bank_p, bank_q,
+                            bank_e, p->rms_weight, p->rms_eps, do_sm, out,
+                            st) != hipSuccess)
+      return HWA_ERR_HIP;
+  }
+  return HWA_OK;
+}
+
+size_t hwa_text_state_workspace_bytes(int32_t text_tokens,
+                                      const hwa_params* p) {
+  if (check_params(p) != HWA_OK || text_tokens < 1) return 0;
+  const size_t mat = (size_t)p->batch * p->heads * p->head_dim * p->head_dim *
+                     sizeof(float);
+  return 2 * align_up(mat);
+}
+
+hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
+                          const float* beta_txt, int32_t text_tokens,
+                          float* state_out, void* stream,
+                          const hwa_params* p) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  if (!k_txt || !v_txt || !beta_txt || !state_out || text_tokens < 1)
+    return HWA_ERR_INVALID_ARG;
+  Geom g;
+  if (!make_geom(1, text_tokens, 1, 0, p, g)) return HWA_ERR_INVALID_ARG;
+  const size_t need = hwa_text_state_workspace_bytes(text_tokens, p);
+  if (!p->workspace || p->workspace_bytes < need ||
+      !aligned(p->workspace, kAlign))
+    return HWA_ERR_WORKSPACE;
+  const size_t es = p->dtype == HWA_BF16 ? 2 : 4;
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t io_bytes = bh * (size_t)text_tokens * g.d * es;
+  const size_t st_bytes = bh * (size_t)g.d * g.d * sizeof(float);
+  if (overlaps(state_out, st_bytes, k_txt, io_bytes) ||
+      overlaps(state_out, st_bytes, v_txt, io_bytes) ||
+      overlaps(state_out, st_bytes, beta_txt, bh * text_tokens * sizeof(float)) ||
+      overlaps(state_out, st_bytes, p->workspace, p->workspace_bytes))
+    return HWA_ERR_INVALID_ARG;
+  const size_t va = p->dtype == HWA_BF16 ? 2 : 4;
+  if (!aligned(k_txt, va) || !aligned(v_txt, va) || !aligned(state_out, 16))
+    return HWA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  float* A = (float*)p->workspace;
+  float* Bm = (float*)((char*)p->workspace + need / 2);
+  if (hwa::launch_stats(g, p->dtype, k_txt, v_txt, beta_txt, nullptr, nullptr,
+                        false, A, Bm, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (hwa::launch_factor(g, HWA_RULE_VDN_SOLVE, 1.0f, A, Bm, nullptr, nullptr,
+                         state_out, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  return HWA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,390 @@
+// Windowed softmax branch (VDN-H3 article, "What the far field outside the
+// window is"): query frame t attends to all tokens of key frames
+// [lo_t, hi_t] with scale 1/sqrt(d), no mask inside the window.
+//
+// Because windows are chunk-aligned, every query of chunk c shares one key
+// range [lo_c * S, (hi_c + 1) * S). A workgroup takes 128 consecutive queries
+// of one chunk (a tile may span frames of the chunk, never two chunks) and
+// streams the chunk's key range through LDS in tiles of 64 keys.
+//
+// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16), per wave of 32 queries:
+//   S^T[key][query] = K . Q^T  with K rows from LDS as the A operand and the
+//                    wave's Q held in registers as the B operand;
+//   O^T[d][query] += V^T . P^T  with V^T rows from LDS as the A operand and P
+//                    (bf16) as the B operand straight from the S registers.
+// Both products leave one query per lane (column n = lane % 32), so the
+// online-softmax statistics and the O rescale are lane-local; the two lane
+// halves hold different keys of the same query and meet once per tile for
+// the running max and once at the end for the sum.
+// K rows are loaded into the S MFMA in a permuted order so that each lane
+// half ends up with 16 consecutive keys per 32-key block: the P registers are
+// then directly the PV B operand and each V^T read is one 16-byte LDS load.
+// V is read from a transposed copy V^T [B, H, d, Np] (Np = N rounded up to
+// 64, zero padded) made by vtranspose_kernel.
+
+#include "hwa_internal.h"
+
+namespace hwa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int SM_QT = 128;  // queries per workgroup (4 waves x 32)
+constexpr int SM_KT = 64;   // keys per LDS tile
+constexpr int SM_THREADS = 256;
+
+__host__ __device__ inline long long round_up64(long long n) {
+  return (n + 63) / 64 * 64;
+}
+
+// ---------------------------------------------------------------- window table
+__global__ void window_table_kernel(int F, int chunk, int radius,
+                                    int32_t* lohi) {
+  int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= F) return;
+  int lo, hi;
+  window_of(t, F, chunk, radius, lo, hi);
+  lohi[t] = lo;
+  lohi[F + t] = hi;
+}
+
+hipError_t launch_window_table(const Geom& g, int32_t* lohi, hipStream_t st) {
+  int threads = 256;
+  int blocks = (g.F + threads - 1) / threads;
+  hipLaunchKernelGGL(window_table_kernel, dim3(blocks), dim3(threads), 0, st,
+                     g.F, g.chunk, g.radius, lohi);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- V transpose
+// v [B,H,N,d] bf16 -> v_t [B,H,d,Np] bf16, keys >= N zero.
+template <int D>
+__global__ __launch_bounds__(256) void vtranspose_kernel(
+    const bf16_t* __restrict__ v, bf16_t* __restrict__ vt, long long N,
+    long long Np) {
+  __shared__ bf16_t tile[64][D + 8];
+  const int bh = blockIdx.y;
+  const long long n0 = (long long)blockIdx.x * 64;
+  const bf16_t* src = v + (long long)bh * N * D;
+  bf16_t* dst = vt + (long long)bh * D * Np;
+  constexpr int CH = 64 * D / 8;  // 16-byte chunks per tile
+  for (int c = threadIdx.x; c < CH; c += 256) {
+    int row = c / (D / 8), c8 = c % (D / 8);
+    long long n = n0 + row;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (n < N) val = *(const u32x4*)(src + n * D + c8 * 8);
+    *(u32x4*)(&tile[row][c8 * 8]) = val;
+  }
+  __syncthreads();
+  constexpr int OCH = D * 8;  // output chunks: D rows x 8 chunks of 8 keys
+  for (int c = threadIdx.x; c < OCH; c += 256) {
+    int dr = c / 8, k8 = c % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)tile[k8 * 8 + 2 * i][dr] |
+             ((uint32_t)tile[k8 * 8 + 2 * i + 1][dr] << 16);
+    u32x4 out = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(dst + (long long)dr * Np + n0 + k8 * 8) = out;
+  }
+}
+
+hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
+                             hipStream_t st) {
+  long long Np = round_up64(g.N);
+  dim3 grid((unsigned)(Np / 64), g.B * g.H);
+  if (g.d == 128)
+    hipLaunchKernelGGL(vtranspose_kernel<128>, grid, dim3(256), 0, st, v, v_t,
+                       g.N, Np);
+  else
+    hipLaunchKernelGGL(vtranspose_kernel<64>, grid, dim3(256), 0, st, v, v_t,
+                       g.N, Np);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- bf16 MFMA
+// Row of the 32-row MFMA block that lands on "16 consecutive keys per lane
+// half": MFMA output row m is held by lane half (m / 4) % 2 in register
+// 4 * (m / 8) + m % 4; loading tile key perm32(m) into row m makes register r
+// of half h hold key 16 * h + r.
+__device__ __forceinline__ int perm32(int m) {
+  return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ vt, const int32_t* __restrict__ lohi,
+    bf16_t* __restrict__ out, int F, int S, int chunk, long long N,
+    long long Np, int tiles_per_chunk, float scale_log2) {
+  constexpr int KP = D + 8;        // padded K row (bf16 elements)
+  constexpr int VP = SM_KT + 8;    // padded V^T row
+  __shared__ __attribute__((aligned(16))) bf16_t k_lds[SM_KT * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t v_lds[D * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int c = blockIdx.x / tiles_per_chunk;
+  const int tile = blockIdx.x % tiles_per_chunk;
+  const int bh = blockIdx.y;
+
+  const long long q_begin = (long long)c * chunk * S;
+  const int f_end = min(F, (c + 1) * chunk);
+  const long long q_end = (long long)f_end * S;
+  const long long q_tile0 = q_begin + (long long)tile * SM_QT;
+  if (q_tile0 >= q_end) return;  // partial last chunk: fewer tiles
+
+  const int lo = lohi[c * chunk];
+  const int hi = lohi[F + c * chunk];
+  const long long k_begin = (long long)lo * S;
+  const long long k_end = (long long)(hi + 1) * S;
+
+  const bf16_t* qb = q + (long long)bh * N * D;
+  const bf16_t* kb = k + (long long)bh * N * D;
+  const bf16_t* vb = vt + (long long)bh * D * Np;
+
+  // Q fragment: B operand of S^T = K Q^T, query = col, d = 16*kk + 8*half + i
+  const long long my_q = q_tile0 + wave * 32 + col;
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+    if (my_q < N) t = *(const u32x4*)(qb + my_q * D + kk * 16 + half * 8);
+    qreg[kk] = __builtin_bit_cast(bf16x8, t);
+  }
+
+  f32x16 acc_o[D / 32];
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[j][r] = 0.0f;
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  const long long kt_first = k_begin / SM_KT * SM_KT;
+  for (long long kt0 = kt_first; kt0 < k_end; kt0 += SM_KT) {
+    // ---- stage K [64][D] and V^T [D][64] tiles
+    constexpr int KCH = SM_KT * D / 8;
+#pragma unroll
+    for (int i = 0; i < KCH / SM_THREADS; ++i) {
+      int ch = tid + i * SM_THREADS;
+      int row = ch / (D / 8), c8 = ch % (D / 8);
+      long long n = kt0 + row;
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (n < N) t = *(const u32x4*)(kb + n * D + c8 * 8);
+      *(u32x4*)(&k_lds[row * KP + c8 * 8]) = t;
+    }
+    constexpr int VCH = D * SM_KT / 8;
+#pragma unroll
+    for (int i = 0; i < VCH / SM_THREADS; ++i) {
+      int ch = tid + i * SM_THREADS;
+      int dr = ch / (SM_KT / 8), k8 = ch % (SM_KT / 8);
+      u32x4 t = *(const u32x4*)(vb + (long long)dr * Np + kt0 + k8 * 8);
+      *(u32x4*)(&v_lds[dr * VP + k8 * 8]) = t;
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[blk][r] = 0.0f;
+      const bf16_t* krow = &k_lds[(blk * 32 + perm32(col)) * KP + half * 8];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        bf16x8 a = *(const bf16x8*)(krow + kk * 16);
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[blk],
+                                                         0, 0, 0);
+      }
+    }
+
+    // ---- mask keys outside [k_begin, k_end) (first and last tile only)
+    if (kt0 < k_begin || kt0 + SM_KT > k_end) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          long long key = kt0 + blk * 32 + half * 16 + r;
+          if (key < k_begin || key >= k_end) s[blk][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (base-2, scale folded into scale_log2)
+    float mx = s[0][0];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    m_run = m_new;
+    const float mb = m_new * scale_log2;
+    l_run *= corr;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[j][r] *= corr;
+
+    bf16x8 pb[4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(s[blk][r] * scale_log2 - mb);
+        l_run += p;
+        pb[blk * 2 + r / 8][r % 8] = (__bf16)p;
+      }
+
+    // ---- O^T += V^T P^T: P block j holds keys 32*(j/2) + 16*half + 8*(j%2) + i
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk) {
+      const bf16_t* vrow = &v_lds[(dblk * 32 + col) * VP + half * 16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 a = *(const bf16x8*)(vrow + (j / 2) * 32 + (j % 2) * 8);
+        acc_o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, pb[j], acc_o[dblk], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane holds d = 32*dblk + 8*(r/4) + 4*half + r%4
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (my_q < q_end) {
+    bf16_t* orow = out + (long long)bh * N * D + my_q * D;
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        int d0 = dblk * 32 + g4 * 8 + half * 4;
+        uint32_t w0 = (uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 0] * inv) |
+                      ((uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 1] * inv) << 16);
+        uint32_t w1 = (uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 2] * inv) |
+                      ((uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 3] * inv) << 16);
+        *(uint2*)(orow + d0) = make_uint2(w0, w1);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 VALU
+// One thread per query, keys staged in LDS 32 at a time. Used for the fp32
+// dtype (small exactness workloads); full fp32 products and accumulation.
+template <int D>
+__global__ __launch_bounds__(128) void softmax_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k,
+    const float* __restrict__ v, const int32_t* __restrict__ lohi,
+    float* __restrict__ out, int F, int S, int chunk, long long N,
+    int tiles_per_chunk, float scale_log2) {
+  constexpr int QT = 128, KT = 32;
+  __shared__ float k_lds[KT][D];
+  __shared__ float v_lds[KT][D];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x / tiles_per_chunk;
+  const int tile = blockIdx.x % tiles_per_chunk;
+  const int bh = blockIdx.y;
+  const long long q_begin = (long long)c * chunk * S;
+  const long long q_end = (long long)min(F, (c + 1) * chunk) * S;
+  const long long q0 = q_begin + (long long)tile * QT;
+  if (q0 >= q_end) return;
+  const long long k_begin = (long long)lohi[c * chunk] * S;
+  const long long k_end = (long long)(lohi[F + c * chunk] + 1) * S;
+  const float* qb = q + (long long)bh * N * D;
+  const float* kb = k + (long long)bh * N * D;
+  const float* vb = v + (long long)bh * N * D;
+  const long long my_q = q0 + tid;
+  const bool valid = my_q < q_end;
+
+  float qr[D], o[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    qr[i] = valid ? qb[my_q * D + i] : 0.0f;
+    o[i] = 0.0f;
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  for (long long kt0 = k_begin; kt0 < k_end; kt0 += KT) {
+    for (int e = tid; e < KT * D; e += QT) {
+      int r = e / D, cc = e % D;
+      long long n = kt0 + r;
+      bool in = n < k_end;
+      k_lds[r][cc] = in ? kb[n * D + cc] : 0.0f;
+      v_lds[r][cc] = in ? vb[n * D + cc] : 0.0f;
+    }
+    __syncthreads();
+    const int nk = (int)min((long long)KT, k_end - kt0);
+    float s[KT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) acc = fmaf(qr[i], k_lds[j][i], acc);
+      s[j] = j < nk ? acc : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    m_run = m_new;
+    l_run *= corr;
+#pragma unroll
+    for (int i = 0; i < D; ++i) o[i] *= corr;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      float p = __builtin_amdgcn_exp2f((s[j] - m_new) * scale_log2);
+      l_run += p;
+#pragma unroll
+      for (int i = 0; i < D; ++i) o[i] = fmaf(p, v_lds[j][i], o[i]);
+    }
+    __syncthreads();
+  }
+  if (valid) {
+    float inv = 1.0f / l_run;
+    float* orow = out + (long long)bh * N * D + my_q * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) orow[i] = o[i] * inv;
+  }
+}
+
+hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
+                          const void* k, const void* v, const bf16_t* v_t,
+                          const int32_t* lohi, void* out, hipStream_t st) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)g.d);
+  const int qpc = g.chunk * g.S;  // queries of a full chunk
+  if (dtype == HWA_BF16) {
+    const int tpc = (qpc + SM_QT - 1) / SM_QT;
+    dim3 grid(tpc * g.nch, g.B * g.H);
+    const long long Np = round_up64(g.N);
+#define SM_LAUNCH(DD)                                                        \
+  hipLaunchKernelGGL(softmax_bf16_kernel<DD>, grid, dim3(SM_THREADS), 0, st, \
+                     (const bf16_t*)q, (const bf16_t*)k, v_t, lohi,          \
+                     (bf16_t*)out, g.F, g.S, g.chunk, g.N, Np, tpc,          \
+                     scale_log2)
+    if (g.d == 128) SM_LAUNCH(128);
+    else SM_LAUNCH(64);
+#undef SM_LAUNCH
+  } else {
+    const int tpc = (qpc + 127) / 128;
+    dim3 grid(tpc * g.nch, g.B * g.H);
+#define SF_LAUNCH(DD)                                                          \
+  hipLaunchKernelGGL(softmax_f32_kernel<DD>, grid, dim3(128), 0, st,           \
+                     (const float*)q, (const float*)k, (const float*)v, lohi,  \
+                     (float*)out, g.F, g.S, g.chunk, g.N, tpc, scale_log2)
+    switch (g.d) {
+      case 16: SF_LAUNCH(16); break;
+      case 32: SF_LAUNCH(32); break;
+      case 64: SF_LAUNCH(64); break;
+      default: SF_LAUNCH(128); break;
+    }
+#undef SF_LAUNCH
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hwa

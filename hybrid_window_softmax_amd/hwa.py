@@ -1,0 +1,223 @@
+"""ctypes binding of libhwa.so (include/hwa.h).
+
+Argument marshalling only: every step of the hybrid attention runs in the HIP
+kernels behind the C ABI. PyTorch supplies device memory and the stream. The
+library must have been built (``python -m hybrid_window_softmax_amd.build``);
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhwa.so")
+_lib = None
+
+RULES = {"vdn_solve": 0, "sana_scaled": 1, "vdn_scaled": 2}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+FLAG_SOFTMAX_ONLY = 1
+FLAG_LINEAR_ONLY = 2
+FLAG_KEEP_INTERMEDIATES = 4
+
+HWA_OK = 0
+HWA_ERR_INVALID_ARG = 1
+HWA_ERR_UNSUPPORTED = 2
+HWA_ERR_WORKSPACE = 3
+HWA_ERR_HIP = 4
+
+EXPORTS = ("hybrid_attn_fwd", "hwa_workspace_bytes", "hwa_get_workspace_layout",
+           "hwa_window_bounds", "hwa_text_state", "hwa_text_state_workspace_bytes",
+           "hwa_status_string")
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("c", ctypes.c_float),
+        ("text_scale", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+        ("conv_k", ctypes.c_void_p),
+        ("conv_v", ctypes.c_void_p),
+        ("rms_weight", ctypes.c_void_p),
+        ("q_rope", ctypes.c_void_p),
+        ("k_rope", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("lohi", "stat_a", "stat_b", "map_g", "map_c", "bank_p", "bank_q",
+                 "bank_e", "v_t", "total")]
+
+
+class HwaError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(lib().hwa_status_string(code).decode())
+
+
+def lib():
+    """Load libhwa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m hybrid_window_softmax_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        PP = ctypes.POINTER(Params)
+        L.hybrid_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                      i32, vp, vp, PP]
+        L.hybrid_attn_fwd.restype = ctypes.c_int
+        L.hwa_workspace_bytes.argtypes = [i32, i32, i32, PP]
+        L.hwa_workspace_bytes.restype = sz
+        L.hwa_get_workspace_layout.argtypes = [i32, i32, i32, PP, ctypes.POINTER(Layout)]
+        L.hwa_get_workspace_layout.restype = ctypes.c_int
+        L.hwa_window_bounds.argtypes = [i32, i32, i32, ctypes.POINTER(i32),
+                                        ctypes.POINTER(i32)]
+        L.hwa_window_bounds.restype = ctypes.c_int
+        L.hwa_text_state.argtypes = [vp, vp, vp, i32, vp, vp, PP]
+        L.hwa_text_state.restype = ctypes.c_int
+        L.hwa_text_state_workspace_bytes.argtypes = [i32, PP]
+        L.hwa_text_state_workspace_bytes.restype = sz
+        L.hwa_status_string.argtypes = [ctypes.c_int]
+        L.hwa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_params(batch, heads, head_dim, dtype, c=0.5, text_scale=0.5,
+                rms_eps=1e-6, conv_k=None, conv_v=None, rms_weight=None,
+                q_rope=None, k_rope=None, workspace=None, flags=0) -> Params:
+    p = Params()
+    p.struct_size = ctypes.sizeof(Params)
+    p.batch, p.heads, p.head_dim = batch, heads, head_dim
+    p.dtype = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    p.c, p.text_scale, p.rms_eps = c, text_scale, rms_eps
+    for name, t in (("conv_k", conv_k), ("conv_v", conv_v), ("rms_weight", rms_weight),
+                    ("q_rope", q_rope), ("k_rope", k_rope)):
+        setattr(p, name, None if t is None else t.data_ptr())
+    if workspace is not None:
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    p.flags = flags
+    return p
+
+
+def window_bounds(frames: int, chunk: int, radius: int):
+    """Host window table from the library (int32 lists lo, hi)."""
+    lo = (ctypes.c_int32 * frames)()
+    hi = (ctypes.c_int32 * frames)()
+    code = lib().hwa_window_bounds(frames, chunk, radius, lo, hi)
+    if code != HWA_OK:
+        raise HwaError(code)
+    return list(lo), list(hi)
+
+
+def workspace_bytes(frames, tokens_per_frame, chunk, p: Params) -> int:
+    return int(lib().hwa_workspace_bytes(frames, tokens_per_frame, chunk, ctypes.byref(p)))
+
+
+def workspace_layout(frames, tokens_per_frame, chunk, p: Params) -> dict:
+    L = Layout()
+    code = lib().hwa_get_workspace_layout(frames, tokens_per_frame, chunk, ctypes.byref(p),
+                                          ctypes.byref(L))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return {n: getattr(L, n) for n, _ in Layout._fields_}
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
+                    frames: int, tokens_per_frame: int, chunk: int = 5,
+                    radius: int = 1, rule: str = "vdn_solve", c: float = 0.5,
+                    text_scale: float = 0.5, rms_eps: float = 1e-6,
+                    rms_weight=None, q_rope=None, k_rope=None, flags: int = 0,
+                    out=None, workspace=None, stream=None):
+    """out = windowed softmax + delta-rule linear branch (see include/hwa.h).
+
+    q, k, v, gate: [B, H, N, d] bf16 or fp32 CUDA tensors; beta [B, H, N],
+    alpha [B, H, F, d], text_state [B, H, d, d] (or None), conv_k/conv_v
+    [H, d, 4], rms_weight [d] (or None): fp32. Returns (out, workspace).
+    """
+    B, H, N, d = q.shape
+    dev = q.device
+    _check(q, "q", q.dtype, (B, H, N, d), dev)
+    for name, t in (("k", k), ("v", v), ("gate", gate), ("q_rope", q_rope),
+                    ("k_rope", k_rope)):
+        _check(t, name, q.dtype, (B, H, N, d), dev)
+    _check(beta, "beta", torch.float32, (B, H, N), dev)
+    _check(alpha, "alpha", torch.float32, (B, H, frames, d), dev)
+    _check(text_state, "text_state", torch.float32, (B, H, d, d), dev)
+    _check(conv_k, "conv_k", torch.float32, (H, d, 4), dev)
+    _check(conv_v, "conv_v", torch.float32, (H, d, 4), dev)
+    _check(rms_weight, "rms_weight", torch.float32, (d,), dev)
+    p = make_params(B, H, d, q.dtype, c, text_scale, rms_eps, conv_k, conv_v, rms_weight,
+                    q_rope, k_rope, None, flags)
+    need = workspace_bytes(frames, tokens_per_frame, chunk, p)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    st = _stream(dev) if stream is None else ctypes.c_void_p(stream)
+    code = lib().hybrid_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                                 _ptr(gate), _ptr(text_state), frames, tokens_per_frame,
+                                 chunk, radius, RULES[rule] if isinstance(rule, str) else rule,
+                                 _ptr(out), st, ctypes.byref(p))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return out, workspace
+
+
+def text_state(k_txt, v_txt, beta_txt, workspace=None, out=None):
+    """S_text [B, H, d, d] fp32 from text tokens (hwa_text_state)."""
+    B, H, T, d = k_txt.shape
+    dev = k_txt.device
+    _check(v_txt, "v_txt", k_txt.dtype, (B, H, T, d), dev)
+    _check(beta_txt, "beta_txt", torch.float32, (B, H, T), dev)
+    p = make_params(B, H, d, k_txt.dtype)
+    need = int(lib().hwa_text_state_workspace_bytes(T, ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    code = lib().hwa_text_state(_ptr(k_txt), _ptr(v_txt), _ptr(beta_txt), T, _ptr(out),
+                                _stream(dev), ctypes.byref(p))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return out

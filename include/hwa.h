@@ -1,0 +1,192 @@
+/*
+ * hwa.h -- C ABI of the MI355X (gfx950) hybrid window-softmax attention.
+ *
+ * The operation is the forward pass of the VDN-H3 hybrid attention as the
+ * VDN-H3 article ("VDN-Minimax-H3", icman.com.cn news 81972) defines it:
+ *
+ *   out = o_sm + y
+ *
+ * o_sm  windowed softmax attention: query frame t attends to every token of
+ *       key frames [lo_t, hi_t], a chunk-aligned window (article section
+ *       "What the far field outside the window is").
+ * y     bidirectional delta-rule linear branch for every frame outside the
+ *       window (article sections "Step 1" .. "Step 5" and "Text state"):
+ *         q^ = L2(SiLU(q)), k^ = L2(SiLU(conv_k(k))), v^ = conv_v(v)
+ *         A_f = sum_{n in f} beta_n k^_n k^_n^T,  B_f = sum beta_n v^_n k^_n^T
+ *         scans P_f = R(P_{f-1}), Q_f = R(Q_{f+1}) from text_scale * S_text
+ *         S_t = P_{lo_t-1} diag(prod_{lo_t..t} alpha) + Q_{hi_t+1} diag(prod_{t..hi_t} alpha)
+ *         y_n = RMSNorm(S_t q^_n) * w * sigmoid(gate_n)
+ *       with R one of the article's three update rules ("Step 3" table):
+ *         vdn_solve   (S D + B)(I + A)^-1
+ *         sana_scaled (S D)(I - c^2 A) + c B
+ *         vdn_scaled  (S D + c B)(I + c^2 A)^-1,   D = diag(alpha_f).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are device pointers to row-major contiguous memory; tokens are
+ *    frame-major (token n = t * tokens_per_frame + s). Shapes use B = batch,
+ *    H = heads, d = head_dim, F = frames, S = tokens_per_frame, N = F * S.
+ *  - The library never allocates or frees memory and keeps no pointer after
+ *    a call returns; the caller owns every buffer, including the workspace.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising. Faults during execution surface
+ *    at the caller's next synchronisation.
+ *  - Every argument check happens before the first enqueue: on an error the
+ *    call returns a status and writes nothing. No exception crosses the ABI
+ *    and nothing is printed. Non-finite inputs are not checked.
+ *  - Calls are stateless and thread-safe.
+ */
+#ifndef HWA_H
+#define HWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HWA_OK = 0,
+  HWA_ERR_INVALID_ARG = 1, /* NULL pointer, size <= 0, bad enum, aliasing  */
+  HWA_ERR_UNSUPPORTED = 2, /* head_dim or dtype the kernels do not handle  */
+  HWA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required      */
+  HWA_ERR_HIP = 4          /* a HIP launch error                           */
+} hwa_status;
+
+/* Update rule R of the scans (article "Step 3", rules table). */
+typedef enum {
+  HWA_RULE_VDN_SOLVE = 0,
+  HWA_RULE_SANA_SCALED = 1,
+  HWA_RULE_VDN_SCALED = 2
+} hwa_rule;
+
+/* Element type of q, k, v, gate, out (and of the text tokens). */
+typedef enum { HWA_F32 = 0, HWA_BF16 = 1 } hwa_dtype;
+
+enum {
+  HWA_FLAG_SOFTMAX_ONLY = 1,      /* out = o_sm (linear branch skipped)      */
+  HWA_FLAG_LINEAR_ONLY = 2,       /* out = y (softmax branch skipped)        */
+  HWA_FLAG_KEEP_INTERMEDIATES = 4 /* accepted for compatibility: the         */
+                                  /* intermediates are always left in the   */
+                                  /* workspace at hwa_workspace_layout's     */
+                                  /* offsets                                 */
+};
+
+typedef struct {
+  uint32_t struct_size;  /* = sizeof(hwa_params)                              */
+  int32_t batch;         /* B >= 1                                            */
+  int32_t heads;         /* H >= 1                                            */
+  int32_t head_dim;      /* d: 16, 32, 64 or 128 (bf16: 64 or 128)             */
+  int32_t dtype;         /* hwa_dtype                                          */
+  float c;               /* scale c of sana_scaled / vdn_scaled (ignored by    */
+                         /* vdn_solve)                                         */
+  float text_scale;      /* initial state of both scans = text_scale * S_text  */
+                         /* (0.5 in the article's "Text state")                */
+  float rms_eps;         /* RMSNorm epsilon (> 0)                              */
+  const float* conv_k;   /* [H, d, 4] fp32 causal taps; tap j multiplies the   */
+  const float* conv_v;   /*   token j places earlier in the same frame         */
+  const float* rms_weight; /* [d] fp32, NULL = ones                            */
+  const void* q_rope;    /* [B,H,N,d] softmax-branch q, NULL = use q           */
+  const void* k_rope;    /* [B,H,N,d] softmax-branch k, NULL = use k           */
+  void* workspace;       /* device scratch of >= hwa_workspace_bytes() bytes,  */
+  size_t workspace_bytes;/*   256-byte aligned; contents undefined afterwards  */
+  uint32_t flags;        /* HWA_FLAG_*                                         */
+} hwa_params;
+
+/*
+ * Byte offsets of the intermediates inside the workspace of one
+ * hybrid_attn_fwd call (all fp32 unless stated):
+ *   lohi     int32 [2, F]         window bounds lo then hi (inclusive frames)
+ *   stat_a   [B, H, F, d, d]      A_f
+ *   stat_b   [B, H, F, d, d]      B_f (d_v x d_k)
+ *   map_g    [B, H, F, d, d]      G_f: the update as S -> S G_f + C_f
+ *   map_c    [B, H, F, d, d]      C_f
+ *   bank_p   [B, H, n_ch+1, d, d] prefix states, slot m = P_{min(F, m*chunk)-1}
+ *   bank_q   [B, H, n_ch+1, d, d] suffix states, slot m = Q_{min(F, m*chunk)}
+ *   bank_e   int32 [2, B, H, n_ch+1, d] power-of-two exponent of every
+ *                                 state row: row i of the state = row i of the
+ *                                 bank * 2^e_i (prefix then suffix; e stays 0
+ *                                 unless a row exceeds 2^64, i.e. a diverging
+ *                                 sana_scaled scan)
+ *   v_t      bf16 [B, H, d, N]    v transposed (bf16 only, else unused)
+ * n_ch = ceil(F / chunk).
+ */
+typedef struct {
+  size_t lohi, stat_a, stat_b, map_g, map_c, bank_p, bank_q, bank_e, v_t;
+  size_t total;
+} hwa_workspace_layout;
+
+/*
+ * hybrid_attn_fwd -- out = windowed softmax + delta-rule linear branch.
+ *
+ *   q, k, v    [B, H, N, d]  dtype  raw (pre-RoPE) q/k and v, shared by both
+ *                                   branches (article: one QKV projection)
+ *   beta       [B, H, N]     fp32   per-token write strength
+ *   alpha      [B, H, F, d]  fp32   per-frame, per-key-channel forget gate
+ *   gate       [B, H, N, d]  dtype  output-gate pre-activation (sigmoid)
+ *   text_state [B, H, d, d]  fp32   S_text (d_v x d_k) or NULL (zero start)
+ *   frames, tokens_per_frame        F >= 1, S >= 1
+ *   chunk, radius                   chunk >= 1, radius >= 0
+ *   rule                            hwa_rule
+ *   out        [B, H, N, d]  dtype  written; must not alias any input
+ *   stream                          hipStream_t
+ *   p                               shapes, dtype, scalars, workspace, flags
+ *
+ * Returns HWA_OK, or an error status before anything is enqueued.
+ */
+hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
+                           const float* beta, const float* alpha,
+                           const void* gate, const float* text_state,
+                           int32_t frames, int32_t tokens_per_frame,
+                           int32_t chunk, int32_t radius, int32_t rule,
+                           void* out, void* stream, const hwa_params* p);
+
+/* Workspace bytes hybrid_attn_fwd needs for these sizes (0 on bad args). */
+size_t hwa_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
+                           int32_t chunk, const hwa_params* p);
+
+/* Offsets of the intermediates inside that workspace. */
+hwa_status hwa_get_workspace_layout(int32_t frames, int32_t tokens_per_frame,
+                                    int32_t chunk, const hwa_params* p,
+                                    hwa_workspace_layout* layout);
+
+/*
+ * hwa_window_bounds -- the window table on the host (article, "What the far
+ * field outside the window is"): frame t in chunk c = t / chunk sees key
+ * frames lo[t] = max(0, (c - radius) * chunk) .. hi[t] = min(F - 1,
+ * (c + radius + 1) * chunk - 1). lo and hi are host arrays of `frames`
+ * int32, written by the call.
+ */
+hwa_status hwa_window_bounds(int32_t frames, int32_t chunk, int32_t radius,
+                             int32_t* lo, int32_t* hi);
+
+/*
+ * hwa_text_state -- S_text of every (batch, head) from T text tokens.
+ *
+ * The article ("Text state") starts both scans from half a text state but
+ * does not say how the prompt becomes that state. This entry point builds it
+ * as one vdn_solve update from zero over one "frame" of text tokens, with the
+ * branch's feature map on k and no conv:
+ *   k^ = L2(SiLU(k_txt)),  A = sum beta k^ k^^T,  B = sum beta v k^^T,
+ *   S_text = B (I + A)^-1.
+ *   k_txt, v_txt [B, H, T, d] dtype;  beta_txt [B, H, T] fp32;
+ *   state_out    [B, H, d, d] fp32 (written).
+ * Uses p->batch, heads, head_dim, dtype, workspace (>= hwa_text_state_
+ * workspace_bytes) and ignores the other fields.
+ */
+hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
+                          const float* beta_txt, int32_t text_tokens,
+                          float* state_out, void* stream,
+                          const hwa_params* p);
+
+size_t hwa_text_state_workspace_bytes(int32_t text_tokens,
+                                      const hwa_params* p);
+
+/* Static English text of a status. */
+const char* hwa_status_string(hwa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HWA_H */

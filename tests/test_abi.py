@@ -1,0 +1,170 @@
+"""C-ABI contract of libhwa on the host (no GPU needed): the library loads,
+exports every entry point include/hwa.h declares, computes the window table
+bit-exactly, and rejects bad arguments with the documented status before
+anything is enqueued (none of these calls reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+from hybrid_window_softmax_amd import hwa, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "hwa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(hwa_[a-z_]+|hybrid_attn_fwd)\s*\(", src))
+
+
+def test_exports_every_declared_symbol():
+    L = hwa.lib()
+    names = _declared()
+    assert names == set(hwa.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in range(5):
+        assert hwa.lib().hwa_status_string(code).decode().startswith("HWA_")
+
+
+@pytest.mark.parametrize("F", range(1, 41))
+def test_window_bounds_bit_exact(F):
+    for chunk in range(1, 8):
+        for radius in range(0, 4):
+            lo, hi = hwa.window_bounds(F, chunk, radius)
+            olo, ohi = oracle.window_bounds(F, chunk, radius)
+            assert lo == olo.tolist() and hi == ohi.tolist()
+
+
+def test_window_bounds_configs():
+    for cfg in inputs.CONFIGS.values():
+        lo, hi = hwa.window_bounds(cfg["frames"], cfg["chunk"], cfg["radius"])
+        olo, ohi = oracle.window_bounds(cfg["frames"], cfg["chunk"], cfg["radius"])
+        assert lo == olo.tolist() and hi == ohi.tolist()
+
+
+def test_window_bounds_bad_args():
+    L = hwa.lib()
+    a = (ctypes.c_int32 * 4)()
+    assert L.hwa_window_bounds(0, 5, 1, a, a) == hwa.HWA_ERR_INVALID_ARG
+    assert L.hwa_window_bounds(4, 0, 1, a, a) == hwa.HWA_ERR_INVALID_ARG
+    assert L.hwa_window_bounds(4, 5, -1, a, a) == hwa.HWA_ERR_INVALID_ARG
+    assert L.hwa_window_bounds(4, 5, 1, None, a) == hwa.HWA_ERR_INVALID_ARG
+
+
+# Fake, never-dereferenced device addresses: every call below must fail
+# validation on the host. They are passed only where no GPU is visible, so a
+# validation bug can never turn one of them into a kernel launch.
+BASE = 1 << 40
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="fake device addresses are passed only without a GPU")
+
+
+def _params(**kw):
+    p = hwa.make_params(kw.pop("batch", 1), kw.pop("heads", 2), kw.pop("head_dim", 64),
+                        kw.pop("dtype", 1))
+    p.conv_k = BASE + (1 << 36)
+    p.conv_v = BASE + (2 << 36)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _call(p, F=10, S=16, chunk=5, radius=1, rule=0, **ptrs):
+    d = dict(q=BASE + (3 << 36), k=BASE + (4 << 36), v=BASE + (5 << 36),
+             beta=BASE + (6 << 36), alpha=BASE + (7 << 36), gate=BASE + (8 << 36),
+             text=None, out=BASE + (9 << 36))
+    d.update(ptrs)
+    vp = ctypes.c_void_p
+    return hwa.lib().hybrid_attn_fwd(vp(d["q"]), vp(d["k"]), vp(d["v"]), vp(d["beta"]),
+                                     vp(d["alpha"]), vp(d["gate"]), vp(d["text"]), F, S,
+                                     chunk, radius, rule, vp(d["out"]), None,
+                                     ctypes.byref(p))
+
+
+def _with_ws(p, F=10, S=16, chunk=5, extra=0):
+    n = hwa.workspace_bytes(F, S, chunk, p)
+    assert n > 0
+    p.workspace = BASE + (10 << 36)
+    p.workspace_bytes = n + extra
+    return p
+
+
+@no_gpu
+def test_argument_validation_codes():
+    E = hwa
+    p = _with_ws(_params())
+    assert _call(p, q=None) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, out=None) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, beta=None) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, F=0) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, S=0) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, chunk=0) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, radius=-1) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, rule=3) == E.HWA_ERR_INVALID_ARG
+    assert _call(p, q=BASE + 2) == E.HWA_ERR_INVALID_ARG          # misaligned
+    assert _call(p, out=BASE + (3 << 36)) == E.HWA_ERR_INVALID_ARG  # out aliases q
+    assert _call(p, out=p.workspace) == E.HWA_ERR_INVALID_ARG      # out aliases workspace
+    pf = _with_ws(_params(flags=hwa.FLAG_SOFTMAX_ONLY | hwa.FLAG_LINEAR_ONLY))
+    assert _call(pf) == E.HWA_ERR_INVALID_ARG
+    pf = _with_ws(_params(flags=64))
+    assert _call(pf) == E.HWA_ERR_INVALID_ARG
+    assert _call(_with_ws(_params(rms_eps=0.0))) == E.HWA_ERR_INVALID_ARG
+    assert _call(_with_ws(_params(c=float("nan")))) == E.HWA_ERR_INVALID_ARG
+    # softmax-only needs no linear-branch inputs but still a workspace
+    ps = _params(flags=hwa.FLAG_SOFTMAX_ONLY)
+    assert _call(ps, beta=None, alpha=None, gate=None) == E.HWA_ERR_WORKSPACE
+
+
+@no_gpu
+def test_unsupported_and_workspace_codes():
+    E = hwa
+    assert _call(_params(head_dim=48)) == E.HWA_ERR_UNSUPPORTED
+    assert _call(_params(head_dim=16, dtype=1)) == E.HWA_ERR_UNSUPPORTED
+    assert _call(_params(dtype=7)) == E.HWA_ERR_INVALID_ARG
+    assert _call(_params()) == E.HWA_ERR_WORKSPACE                  # no workspace
+    p = _with_ws(_params(), extra=-256)
+    assert _call(p) == E.HWA_ERR_WORKSPACE                          # too small
+    p = _with_ws(_params())
+    p.workspace += 16
+    assert _call(p) == E.HWA_ERR_WORKSPACE                          # misaligned
+    p = _params()
+    p.struct_size = 8
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+    assert hwa.lib().hybrid_attn_fwd(None, None, None, None, None, None, None, 10, 16, 5, 1,
+                                     0, None, None, None) == E.HWA_ERR_INVALID_ARG
+
+
+def test_workspace_layout_is_consistent():
+    for cfg in inputs.CONFIGS.values():
+        p = hwa.make_params(cfg["batch"], cfg["heads"], cfg["head_dim"],
+                            1 if cfg["dtype"] == "bf16" else 0)
+        L = hwa.workspace_layout(cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"], p)
+        offs = [L[k] for k in ("lohi", "stat_a", "stat_b", "map_g", "map_c", "bank_p",
+                               "bank_q", "bank_e", "v_t")]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert L["total"] == hwa.workspace_bytes(cfg["frames"], cfg["tokens_per_frame"],
+                                                 cfg["chunk"], p)
+        B, H, d, F = cfg["batch"], cfg["heads"], cfg["head_dim"], cfg["frames"]
+        assert L["stat_b"] - L["stat_a"] >= B * H * F * d * d * 4
+
+
+@no_gpu
+def test_text_state_validation():
+    E = hwa
+    vp = ctypes.c_void_p
+    p = _params()
+    L = hwa.lib()
+    assert L.hwa_text_state(vp(BASE), vp(BASE + (1 << 36)), vp(BASE + (2 << 36)), 0,
+                            vp(BASE + (3 << 36)), None, ctypes.byref(p)) == E.HWA_ERR_INVALID_ARG
+    assert L.hwa_text_state(vp(BASE), vp(BASE + (1 << 36)), vp(BASE + (2 << 36)), 16,
+                            vp(BASE + (3 << 36)), None, ctypes.byref(p)) == E.HWA_ERR_WORKSPACE
+    assert L.hwa_text_state_workspace_bytes(16, ctypes.byref(p)) > 0

@@ -1,0 +1,210 @@
+"""GPU parity of libhwa against the fp64 oracle (needs an MI355X).
+
+Each case runs the library through the C ABI three ways on the same seeded
+inputs: the whole call (out = o_sm + y), HWA_FLAG_SOFTMAX_ONLY (o_sm) and
+HWA_FLAG_LINEAR_ONLY (y), and compares every one with the oracle by the
+maximum over (batch, head) of the relative Frobenius error of the [N, d]
+slice. Tolerances: 1e-5 for fp32 workloads and 5e-3 for bf16 workloads
+(fp32 accumulation). The linear branch's output is 40-90x larger than the
+softmax branch's, so each branch is checked on its own as well as the sum.
+Window bounds are compared bit for bit.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hybrid_window_softmax_amd import hwa, inputs
+from harness import (TOL, GpuCase, oracle_head, oracle_linear_head, oracle_softmax_rows,
+                     oracle_text_state, out_f64, sample_rows, ws_view)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _worst(got, ref, heads):
+    return max(oracle.rel_frobenius(got[b, h], ref[b, h]) for b, h in heads)
+
+
+def _full_check(cfg, rule, text=True, check_intermediates=False):
+    """Whole-tensor parity for workloads the oracle finishes in seconds."""
+    _say(f"case {cfg['name']} rule={rule} text={text}")
+    inp = inputs.make(cfg)
+    case = GpuCase(inp)
+    B, H = cfg["batch"], cfg["heads"]
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    out, ws = case.run(rule, 0, text)
+    sm, _ = case.run(rule, hwa.FLAG_SOFTMAX_ONLY, text)
+    lin, ws_lin = case.run(rule, hwa.FLAG_LINEAR_ONLY, text)
+    torch.cuda.synchronize()
+    got = {"out": out_f64(out), "o_sm": out_f64(sm), "y": out_f64(lin)}
+    ref = {k: np.empty_like(got["out"]) for k in got}
+    inter = {}
+    for b, h in heads:
+        r = oracle_head(inp, b, h, rule, text, keep=check_intermediates)
+        ref["out"][b, h], ref["o_sm"][b, h], ref["y"][b, h] = r[0], r[1], r[2]
+        inter[(b, h)] = r[3]
+    tol = TOL[cfg["dtype"]]
+    for k in ("o_sm", "y", "out"):
+        err = _worst(got[k], ref[k], heads)
+        _say(f"  {k}: max rel Frobenius {err:.3e} (tol {tol:g})")
+        assert err <= tol, f"{cfg['name']} {rule} {k}: {err:.3e} > {tol:g}"
+    if check_intermediates:
+        _check_intermediates(case, ws_lin, inter, cfg, tol)
+    return got, ref
+
+
+def _check_intermediates(case, ws, inter, cfg, tol):
+    L = case.layout()
+    B, H, F, d = cfg["batch"], cfg["heads"], cfg["frames"], cfg["head_dim"]
+    nch = -(-F // cfg["chunk"])
+    lohi = ws_view(ws, L["lohi"], (2, F), torch.int32).cpu().numpy()
+    lo, hi = oracle.window_bounds(F, cfg["chunk"], cfg["radius"])
+    assert np.array_equal(lohi[0], lo) and np.array_equal(lohi[1], hi)
+    A = ws_view(ws, L["stat_a"], (B, H, F, d, d)).cpu().numpy()
+    Bm = ws_view(ws, L["stat_b"], (B, H, F, d, d)).cpu().numpy()
+    bp = ws_view(ws, L["bank_p"], (B, H, nch + 1, d, d)).cpu().numpy().astype(np.float64)
+    bq = ws_view(ws, L["bank_q"], (B, H, nch + 1, d, d)).cpu().numpy().astype(np.float64)
+    be = ws_view(ws, L["bank_e"], (2, B, H, nch + 1, d), torch.int32).cpu().numpy()
+    stat_tol = 1e-5 if cfg["dtype"] == "f32" else 1e-4
+    for (b, h), it in inter.items():
+        ea = oracle.rel_frobenius(A[b, h], it["A"])
+        eb = oracle.rel_frobenius(Bm[b, h], it["B"])
+        assert ea <= stat_tol and eb <= stat_tol, (ea, eb)
+        for m in range(nch + 1):
+            idx = min(F, m * cfg["chunk"])
+            P = bp[b, h, m] * np.exp2(be[0, b, h, m].astype(np.float64))[:, None]
+            Q = bq[b, h, m] * np.exp2(be[1, b, h, m].astype(np.float64))[:, None]
+            ep = oracle.rel_frobenius(P, it["prefix"][idx])
+            eq = oracle.rel_frobenius(Q, it["suffix"][idx])
+            assert ep <= max(tol, 1e-5) and eq <= max(tol, 1e-5), (m, ep, eq)
+
+
+def test_config0_tiny_fp32():
+    got, ref = _full_check(inputs.CONFIGS[0], "vdn_solve", check_intermediates=True)
+    # no far field and no text state: the linear branch is exactly zero
+    assert not np.any(got["y"])
+
+
+@pytest.mark.parametrize("rule", oracle.RULES)
+@pytest.mark.parametrize("text", [True, False])
+def test_tiny_partial_chunk(rule, text):
+    cfg = inputs.tiny_config(frames=17, text_tokens=16, rule=rule, heads=2)
+    _full_check(cfg, rule, text, check_intermediates=True)
+
+
+def test_tiny_radius0():
+    cfg = inputs.tiny_config(frames=20, radius=0, text_tokens=16, seed=101)
+    _full_check(cfg, "vdn_solve", check_intermediates=True)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_tiny_fp32_head_dims(d):
+    cfg = inputs.tiny_config(frames=11, text_tokens=8, head_dim=d, tokens_per_frame=24,
+                             seed=102 + d)
+    _full_check(cfg, "vdn_solve", check_intermediates=True)
+
+
+def test_sana_diverging_state_fp32():
+    # lambda_max(A) ~ 60 at 256 tokens per frame: |1 - c^2 lambda| ~ 14 per
+    # frame, so the states pass 2^64 and the exponent path is exercised
+    cfg = inputs.tiny_config(frames=40, text_tokens=16, tokens_per_frame=256,
+                             rule="sana_scaled", seed=103)
+    _full_check(cfg, "sana_scaled", check_intermediates=True)
+
+
+def test_beta_zero_no_text_is_softmax():
+    cfg = inputs.tiny_config(frames=17, text_tokens=0, seed=104)
+    inp = inputs.make(cfg, beta_zero=True)
+    case = GpuCase(inp)
+    out, _ = case.run()
+    sm, _ = case.run(flags=hwa.FLAG_SOFTMAX_ONLY)
+    torch.cuda.synchronize()
+    assert torch.equal(out, sm)
+
+
+def test_config1_small_bf16_text():
+    _full_check(inputs.CONFIGS[1], "vdn_solve", check_intermediates=True)
+
+
+@pytest.mark.parametrize("rule", oracle.RULES)
+def test_bf16_d128_ragged(rule):
+    # S = 100 tokens per frame: ragged query and key tiles; partial last chunk
+    cfg = inputs.tiny_config(frames=12, text_tokens=32, head_dim=128, tokens_per_frame=100,
+                             dtype="bf16", heads=2, rule=rule, seed=105)
+    _full_check(cfg, rule, check_intermediates=True)
+
+
+def test_bf16_d64_odd_tokens():
+    cfg = inputs.tiny_config(frames=7, text_tokens=8, head_dim=64, tokens_per_frame=33,
+                             dtype="bf16", heads=3, seed=106, chunk=3)
+    _full_check(cfg, "vdn_solve", check_intermediates=True)
+
+
+def test_text_state_entry_point():
+    for cfg in (inputs.CONFIGS[1], inputs.tiny_config(text_tokens=16)):
+        inp = inputs.make(cfg)
+        case = GpuCase(inp)
+        got = case.text_state.cpu().numpy()
+        for b in range(cfg["batch"]):
+            for h in range(cfg["heads"]):
+                err = oracle.rel_frobenius(got[b, h], oracle_text_state(inp, b, h))
+                assert err < 1e-5, err
+
+
+# ---------------------------------------------------------------- full sizes
+def _sampled_check(cfg_id, rules):
+    """Full-size workload in the launch configuration the benchmark times:
+    the softmax branch and the sum on sampled query rows of every head, the
+    linear branch on two whole heads."""
+    cfg = inputs.CONFIGS[cfg_id]
+    _say(f"case config{cfg_id} {cfg['name']}: generating inputs")
+    inp = inputs.make(cfg)
+    case = GpuCase(inp)
+    rows = sample_rows(cfg)
+    H = cfg["heads"]
+    tol = TOL[cfg["dtype"]]
+    heads_full = [0, H - 1]
+    for rule in rules:
+        _say(f"case config{cfg_id} rule={rule}")
+        out, ws = case.run(rule, 0)
+        sm, _ = case.run(rule, hwa.FLAG_SOFTMAX_ONLY, workspace=ws)
+        lin, _ = case.run(rule, hwa.FLAG_LINEAR_ONLY, workspace=ws)
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(rows).to(out.device)
+        o_rows = out[0].index_select(1, idx).float().cpu().numpy().astype(np.float64)
+        s_rows = sm[0].index_select(1, idx).float().cpu().numpy().astype(np.float64)
+        worst = {"o_sm": 0.0, "y": 0.0, "out": 0.0}
+        for h in range(H):
+            ref_sm = oracle_softmax_rows(inp, 0, h, rows)
+            worst["o_sm"] = max(worst["o_sm"], oracle.rel_frobenius(s_rows[h], ref_sm))
+            if h in heads_full:
+                y_ref, _ = oracle_linear_head(inp, 0, h, rule)
+                y_got = lin[0, h].float().cpu().numpy().astype(np.float64)
+                worst["y"] = max(worst["y"], oracle.rel_frobenius(y_got, y_ref))
+                worst["out"] = max(worst["out"],
+                                   oracle.rel_frobenius(o_rows[h], ref_sm + y_ref[rows]))
+        _say(f"  {rule}: " + ", ".join(f"{k} {v:.3e}" for k, v in worst.items()))
+        for k, v in worst.items():
+            assert v <= tol, f"config{cfg_id} {rule} {k}: {v:.3e} > {tol:g}"
+        del out, sm, lin, ws
+        torch.cuda.empty_cache()
+
+
+def test_config2_full_size_sampled():
+    _sampled_check(2, ("vdn_solve",))
+
+
+def test_config3_full_size_sampled_all_rules():
+    _sampled_check(3, oracle.RULES)
+
+
+def test_config4_full_size_sampled():
+    _sampled_check(4, ("vdn_solve",))
