@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid window-softmax attention forward on one MI355X.
+
+One step = one hybrid_attn_fwd call over the whole workload (window table,
+V transpose, windowed softmax, fused features + statistics, update maps,
+bidirectional scan, readout epilogue), inputs resident in HBM. Prints one
+JSON line: whole-job tokens/s, per-kernel times from hipEvents the library
+records at its kernel boundaries on the call's stream, the roofline of the
+dominant kernel (the windowed softmax, bf16 MFMA) and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--rule vdn_solve]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector, packed) / fp32 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_traffic.json")
+SOFTMAX_SRC = os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", "softmax.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def window_pairs(cfg):
+    """Query-key token pairs one head scores: sum_t S * S * (hi_t - lo_t + 1)."""
+    F, S, ch, r = cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"], cfg["radius"]
+    tot = 0
+    for t in range(F):
+        c = t // ch
+        lo, hi = max(0, (c - r) * ch), min(F - 1, (c + r + 1) * ch - 1)
+        tot += S * S * (hi - lo + 1)
+    return tot
+
+
+def algorithmic_work(cfg):
+    """Algorithmic bytes and flops of every kernel of one call (bf16 I/O)."""
+    B, H, d = cfg["batch"], cfg["heads"], cfg["head_dim"]
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+    N = F * S
+    nch = -(-F // cfg["chunk"])
+    io = 2 if cfg["dtype"] == "bf16" else 4
+    tok = B * H * N            # (token, head) units
+    mat = B * H * F * d * d * 4  # one fp32 [B,H,F,d,d] tensor
+    bank = B * H * (nch + 1) * d * d * 4
+    return {
+        "vtranspose": dict(bytes=2 * tok * d * io, flops=0),
+        "softmax": dict(bytes=4 * tok * d * io, flops=4 * d * window_pairs(cfg) * B * H),
+        "stats": dict(bytes=2 * tok * d * io + tok * 4 + 2 * mat, flops=4 * d * d * tok),
+        "maps": dict(bytes=4 * mat + B * H * F * d * 4, flops=0),
+        "scan": dict(bytes=4 * mat + 2 * bank, flops=2 * 2 * d * d * d * B * H * F),
+        "readout": dict(bytes=4 * tok * d * io + 2 * bank, flops=2 * d * d * tok),
+    }
+
+
+def softmax_traffic():
+    """HBM bytes per softmax launch from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(SOFTMAX_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, rule, heads_run=1):
+    """The fp64 oracle as it stands, on `heads_run` whole heads of the same
+    workload (softmax branch, linear branch and text state), scaled to the
+    whole job's tokens/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    cfg = inp.cfg
+    S = cfg["tokens_per_frame"]
+    t0 = time.perf_counter()
+    for h in range(heads_run):
+        st = None
+        if inp.k_txt is not None:
+            st = oracle.text_state(inp.f64("k_txt", 0, h), inp.f64("v_txt", 0, h),
+                                   inp.beta_txt[0, h].astype(np.float64))
+        oracle.hybrid_attn_head(inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h),
+                                inp.beta[0, h], inp.alpha[0, h], inp.f64("gate", 0, h), st,
+                                inp.conv_k[h], inp.conv_v[h], inp.rms_weight, S,
+                                cfg["chunk"], cfg["radius"], rule, cfg["c"], 0.5, 1e-6)
+    dt = time.perf_counter() - t0
+    N = cfg["frames"] * S
+    total_s = dt * cfg["heads"] * cfg["batch"] / heads_run
+    return {"value": N * cfg["batch"] / total_s, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads_run} of {cfg['heads']} heads (all {N} tokens of each), "
+                      f"{dt:.1f} s wall, scaled by heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--rule", default="vdn_solve")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the hot path shards by "
+              "heads with no exchange; see the sharding design). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hybrid_window_softmax_amd import hwa, inputs
+
+    cfg = inputs.CONFIGS[args.config]
+    log(f"bench: generating config {args.config} ({cfg['name']})")
+    inp = inputs.make(cfg)
+    dev = torch.device("cuda:0")
+    bf = cfg["dtype"] == "bf16"
+
+    def up(a):
+        if a is None:
+            return None
+        if bf and a.dtype.name == "uint16":
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
+                                          "conv_v", "rms_weight", "k_txt", "v_txt",
+                                          "beta_txt")}
+    text = None
+    if t["k_txt"] is not None:
+        text = hwa.text_state(t["k_txt"], t["v_txt"], t["beta_txt"])
+    out = torch.empty_like(t["q"])
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+
+    def call(events=None, ws=None):
+        return hwa.hybrid_attn_fwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"],
+                                   text, t["conv_k"], t["conv_v"], F, S, cfg["chunk"],
+                                   cfg["radius"], args.rule, cfg["c"], 0.5, 1e-6,
+                                   t["rms_weight"], out=out, workspace=ws,
+                                   stage_events=events)[1]
+
+    log("bench: warmup")
+    ws = call()
+    for _ in range(max(0, args.warmup - 1)):
+        call(ws=ws)
+    torch.cuda.synchronize()
+    timer = hwa.StageTimer(args.steps)
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(events=timer.sets[i], ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage = timer.stage_ms()
+    timer.close()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    tokens = cfg["batch"] * F * S
+    log("bench: stage ms " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()))
+
+    work = algorithmic_work(cfg)
+    kernels = {}
+    for name, w in work.items():
+        sec = stage[name] / 1000.0
+        if sec <= 0:
+            continue
+        rec = {"ms": round(stage[name], 4),
+               "hbm_GBs": round(w["bytes"] / sec / 1e9, 1),
+               "hbm_frac": round(w["bytes"] / sec / 1e9 / PEAK_HBM_GBS, 4)}
+        if w["flops"]:
+            rec["TFLOPs"] = round(w["flops"] / sec / 1e12, 2)
+        kernels[name] = rec
+    sm_flops = work["softmax"]["flops"]
+    achieved = sm_flops / (stage["softmax"] / 1000.0) / 1e12
+    roofline = {"kernel": "softmax_bf16_kernel", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": softmax_traffic(),
+                "algorithmic_flops_per_launch": sm_flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        del t, out, ws
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(inp, args.rule, args.cpu_heads)
+
+    rec = {
+        "metric": "hybrid-attn fwd tokens/s at 48k-262k tokens; % of MFMA / HBM roofline",
+        "value": round(tokens / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: B{cfg['batch']} H{cfg['heads']} "
+                               f"d{cfg['head_dim']} F{F} x S{S} = {F * S} tokens, "
+                               f"chunk {cfg['chunk']} radius {cfg['radius']}, "
+                               f"{args.rule}, text state from {cfg['text_tokens']} tokens",
+                   "tokens": F * S, "heads": cfg["heads"], "head_dim": cfg["head_dim"],
+                   "rule": args.rule},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -202,30 +202,38 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   int32_t* bank_e = (int32_t*)(ws + L.bank_e);
   bf16_t* v_t = (bf16_t*)(ws + L.v_t);
 
+  void* const* ev = p->stage_events;
+  auto mark = [&](int i) {
+    return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+  };
+  if (mark(0) != hipSuccess) return HWA_ERR_HIP;
   if (hwa::launch_window_table(g, lohi, st) != hipSuccess) return HWA_ERR_HIP;
-  if (do_sm) {
-    if (p->dtype == HWA_BF16 &&
-        hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
-      return HWA_ERR_HIP;
-    if (hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out, st) !=
-        hipSuccess)
-      return HWA_ERR_HIP;
-  }
-  if (do_lin) {
-    if (hwa::launch_stats(g, p->dtype, k, v, beta, p->conv_k, p->conv_v, true,
-                          A, Bm, st) != hipSuccess)
-      return HWA_ERR_HIP;
-    if (hwa::launch_factor(g, rule, p->c, A, Bm, alpha, G, C, st) !=
-        hipSuccess)
-      return HWA_ERR_HIP;
-    if (hwa::launch_scan(g, G, C, text_state, p->text_scale, bank_p, bank_q,
-                         bank_e, st) != hipSuccess)
-      return HWA_ERR_HIP;
-    if (hwa::launch_readout(g, p->dtype, q, gate, alpha, lohi, bank_p, bank_q,
-                            bank_e, p->rms_weight, p->rms_eps, do_sm, out,
-                            st) != hipSuccess)
-      return HWA_ERR_HIP;
-  }
+  if (mark(1) != hipSuccess) return HWA_ERR_HIP;
+  if (do_sm && p->dtype == HWA_BF16 &&
+      hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(2) != hipSuccess) return HWA_ERR_HIP;
+  if (do_sm && hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out,
+                                   st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(3) != hipSuccess) return HWA_ERR_HIP;
+  if (do_lin && hwa::launch_stats(g, p->dtype, k, v, beta, p->conv_k,
+                                  p->conv_v, true, A, Bm, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(4) != hipSuccess) return HWA_ERR_HIP;
+  if (do_lin && hwa::launch_factor(g, rule, p->c, A, Bm, alpha, G, C, st) !=
+                    hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(5) != hipSuccess) return HWA_ERR_HIP;
+  if (do_lin && hwa::launch_scan(g, G, C, text_state, p->text_scale, bank_p,
+                                 bank_q, bank_e, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(6) != hipSuccess) return HWA_ERR_HIP;
+  if (do_lin && hwa::launch_readout(g, p->dtype, q, gate, alpha, lohi, bank_p,
+                                    bank_q, bank_e, p->rms_weight, p->rms_eps,
+                                    do_sm, out, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(7) != hipSuccess) return HWA_ERR_HIP;
   return HWA_OK;
 }
 

@@ -21,6 +21,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 FLAG_SOFTMAX_ONLY = 1
 FLAG_LINEAR_ONLY = 2
 FLAG_KEEP_INTERMEDIATES = 4
+NUM_STAGE_EVENTS = 8
+STAGES = ("window", "vtranspose", "softmax", "stats", "maps", "scan", "readout")
 
 HWA_OK = 0
 HWA_ERR_INVALID_ARG = 1
@@ -51,6 +53,7 @@ class Params(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("flags", ctypes.c_uint32),
+        ("stage_events", ctypes.c_void_p),
     ]
 
 
@@ -164,12 +167,14 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
                     radius: int = 1, rule: str = "vdn_solve", c: float = 0.5,
                     text_scale: float = 0.5, rms_eps: float = 1e-6,
                     rms_weight=None, q_rope=None, k_rope=None, flags: int = 0,
-                    out=None, workspace=None, stream=None):
+                    out=None, workspace=None, stream=None, stage_events=None):
     """out = windowed softmax + delta-rule linear branch (see include/hwa.h).
 
     q, k, v, gate: [B, H, N, d] bf16 or fp32 CUDA tensors; beta [B, H, N],
     alpha [B, H, F, d], text_state [B, H, d, d] (or None), conv_k/conv_v
-    [H, d, 4], rms_weight [d] (or None): fp32. Returns (out, workspace).
+    [H, d, 4], rms_weight [d] (or None): fp32. ``stage_events``: optional
+    ctypes array of NUM_STAGE_EVENTS hipEvent_t (see :class:`StageTimer`).
+    Returns (out, workspace).
     """
     B, H, N, d = q.shape
     dev = q.device
@@ -190,6 +195,8 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
         workspace = alloc_workspace(need, dev)
     p.workspace = workspace.data_ptr()
     p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if stage_events is not None:
+        p.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
     if out is None:
         out = torch.empty_like(q)
     st = _stream(dev) if stream is None else ctypes.c_void_p(stream)
@@ -221,3 +228,42 @@ def text_state(k_txt, v_txt, beta_txt, workspace=None, out=None):
     if code != HWA_OK:
         raise HwaError(code)
     return out
+
+
+class StageTimer:
+    """hipEvents recorded by the library at its kernel boundaries on the
+    call's stream (hwa_params.stage_events); yields per-kernel durations."""
+
+    def __init__(self, steps: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.sets = []
+        for _ in range(steps):
+            arr = (ctypes.c_void_p * NUM_STAGE_EVENTS)()
+            for i in range(NUM_STAGE_EVENTS):
+                ev = ctypes.c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev
+            self.sets.append(arr)
+
+    def stage_ms(self) -> dict:
+        """Mean duration (ms) of every stage over the recorded steps; call
+        after the stream has been synchronised."""
+        tot = [0.0] * (NUM_STAGE_EVENTS - 1)
+        ms = ctypes.c_float()
+        for arr in self.sets:
+            for i in range(NUM_STAGE_EVENTS - 1):
+                if self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[i], arr[i + 1]) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                tot[i] += ms.value
+        return {s: t / len(self.sets) for s, t in zip(STAGES, tot)}
+
+    def close(self):
+        for arr in self.sets:
+            for i in range(NUM_STAGE_EVENTS):
+                self.hip.hipEventDestroy(arr[i])
+        self.sets = []

@@ -91,7 +91,16 @@ typedef struct {
   void* workspace;       /* device scratch of >= hwa_workspace_bytes() bytes,  */
   size_t workspace_bytes;/*   256-byte aligned; contents undefined afterwards  */
   uint32_t flags;        /* HWA_FLAG_*                                         */
+  void* const* stage_events; /* NULL, or HWA_NUM_STAGE_EVENTS caller-created  */
+                         /* hipEvent_t recorded on `stream` at the kernel     */
+                         /* boundaries of hybrid_attn_fwd, for per-kernel     */
+                         /* timing: [0] start, then after [1] window table,   */
+                         /* [2] V transpose, [3] softmax, [4] statistics,     */
+                         /* [5] update maps, [6] scan, [7] readout (a skipped */
+                         /* stage records its event with the previous one)   */
 } hwa_params;
+
+#define HWA_NUM_STAGE_EVENTS 8
 
 /*
  * Byte offsets of the intermediates inside the workspace of one
