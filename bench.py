@@ -61,8 +61,9 @@ def algorithmic_work(cfg):
         "vtranspose": dict(bytes=2 * tok * d * io, flops=0),
         "softmax": dict(bytes=4 * tok * d * io, flops=4 * d * window_pairs(cfg) * B * H),
         "stats": dict(bytes=2 * tok * d * io + tok * 4 + 2 * mat, flops=4 * d * d * tok),
-        "maps": dict(bytes=4 * mat + B * H * F * d * 4, flops=0),
-        "scan": dict(bytes=4 * mat + 2 * bank, flops=2 * 2 * d * d * d * B * H * F),
+        "inverse": dict(bytes=2 * mat, flops=2 * d * d * d * B * H * F),
+        "scan": dict(bytes=4 * mat + 2 * B * H * F * d * 4 + 2 * bank,
+                     flops=2 * 2 * d * d * d * B * H * F),
         "readout": dict(bytes=4 * tok * d * io + 2 * bank, flops=2 * d * d * tok),
     }
 

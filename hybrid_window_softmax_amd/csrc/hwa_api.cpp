@@ -62,8 +62,7 @@ hwa_workspace_layout compute_layout(const Geom& g, int dtype) {
   L.lohi = take(2 * (size_t)g.F * sizeof(int32_t));
   L.stat_a = take(bh * g.F * dd * sizeof(float));
   L.stat_b = take(bh * g.F * dd * sizeof(float));
-  L.map_g = take(bh * g.F * dd * sizeof(float));
-  L.map_c = take(bh * g.F * dd * sizeof(float));
+  L.map_m = take(bh * g.F * dd * sizeof(float));
   L.bank_p = take(bh * (g.nch + 1) * dd * sizeof(float));
   L.bank_q = take(bh * (g.nch + 1) * dd * sizeof(float));
   L.bank_e = take(2 * bh * (g.nch + 1) * g.d * sizeof(int32_t));
@@ -195,8 +194,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   int32_t* lohi = (int32_t*)(ws + L.lohi);
   float* A = (float*)(ws + L.stat_a);
   float* Bm = (float*)(ws + L.stat_b);
-  float* G = (float*)(ws + L.map_g);
-  float* C = (float*)(ws + L.map_c);
+  float* M = (float*)(ws + L.map_m);
   float* bank_p = (float*)(ws + L.bank_p);
   float* bank_q = (float*)(ws + L.bank_q);
   int32_t* bank_e = (int32_t*)(ws + L.bank_e);
@@ -221,12 +219,15 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                   p->conv_v, true, A, Bm, st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(4) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && hwa::launch_factor(g, rule, p->c, A, Bm, alpha, G, C, st) !=
-                    hipSuccess)
-    return HWA_ERR_HIP;
+  if (do_lin && rule != HWA_RULE_SANA_SCALED) {
+    const float cc = rule == HWA_RULE_VDN_SCALED ? p->c : 1.0f;
+    if (hwa::launch_inverse(g, cc * cc, A, M, st) != hipSuccess)
+      return HWA_ERR_HIP;
+  }
   if (mark(5) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && hwa::launch_scan(g, G, C, text_state, p->text_scale, bank_p,
-                                 bank_q, bank_e, st) != hipSuccess)
+  if (do_lin && hwa::launch_scan(g, rule, p->c, A, Bm, M, alpha, text_state,
+                                 p->text_scale, bank_p, bank_q, bank_e,
+                                 st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(6) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && hwa::launch_readout(g, p->dtype, q, gate, alpha, lohi, bank_p,
@@ -242,7 +243,7 @@ size_t hwa_text_state_workspace_bytes(int32_t text_tokens,
   if (check_params(p) != HWA_OK || text_tokens < 1) return 0;
   const size_t mat = (size_t)p->batch * p->heads * p->head_dim * p->head_dim *
                      sizeof(float);
-  return 2 * align_up(mat);
+  return 3 * align_up(mat);
 }
 
 hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
@@ -273,12 +274,13 @@ hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
     return HWA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   float* A = (float*)p->workspace;
-  float* Bm = (float*)((char*)p->workspace + need / 2);
+  float* Bm = (float*)((char*)p->workspace + need / 3);
+  float* M = (float*)((char*)p->workspace + 2 * (need / 3));
   if (hwa::launch_stats(g, p->dtype, k_txt, v_txt, beta_txt, nullptr, nullptr,
                         false, A, Bm, st) != hipSuccess)
     return HWA_ERR_HIP;
-  if (hwa::launch_factor(g, HWA_RULE_VDN_SOLVE, 1.0f, A, Bm, nullptr, nullptr,
-                         state_out, st) != hipSuccess)
+  if (hwa::launch_inverse(g, 1.0f, A, M, st) != hipSuccess) return HWA_ERR_HIP;
+  if (hwa::launch_matmul_bm(g, Bm, M, state_out, st) != hipSuccess)
     return HWA_ERR_HIP;
   return HWA_OK;
 }

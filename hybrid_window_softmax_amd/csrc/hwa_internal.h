@@ -84,13 +84,17 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
                         const float* conv_v, bool conv, float* A, float* Bm,
                         hipStream_t st);
 
-// G_f, C_f of the affine update S -> S G_f + C_f for every (b, h, f).
-// alpha == NULL means alpha = 1. G may be NULL (not written).
-hipError_t launch_factor(const Geom& g, int rule, float c, const float* A,
-                         const float* Bm, const float* alpha, float* G,
-                         float* C, hipStream_t st);
+// M_f = (I + c2 A_f)^-1 for every (b, h, f) (Gauss-Jordan sweep, fp32).
+hipError_t launch_inverse(const Geom& g, float c2, const float* A, float* M,
+                          hipStream_t st);
 
-hipError_t launch_scan(const Geom& g, const float* G, const float* C,
+// C = B M for every (b, h, f).
+hipError_t launch_matmul_bm(const Geom& g, const float* Bm, const float* M,
+                            float* C, hipStream_t st);
+
+// Prefix/suffix scans; writes the chunk-boundary state banks.
+hipError_t launch_scan(const Geom& g, int rule, float c, const float* A,
+                       const float* Bm, const float* M, const float* alpha,
                        const float* text_state, float text_scale,
                        float* bank_p, float* bank_q, int32_t* bank_e,
                        hipStream_t st);
@@ -101,5 +105,35 @@ hipError_t launch_readout(const Geom& g, int dtype, const void* q,
                           const float* bank_q, const int32_t* bank_e,
                           const float* rms_weight, float rms_eps,
                           bool accumulate, void* out, hipStream_t st);
+
+}  // namespace hwa
+
+namespace hwa {
+
+// ---------------------------------------------------------------- MFMA helpers
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// x ~= hi + lo with hi = bf16(x) and lo = bf16(x - hi): the split-bf16
+// ("bf16x3") products hi*hi + hi*lo + lo*hi keep ~16 mantissa bits.
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b,
+                                           f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// C += A*B with both operands given as (hi, lo) pairs: three MFMAs.
+__device__ __forceinline__ f32x16_t mfma32x3(bf16x8_t ah, bf16x8_t al,
+                                             bf16x8_t bh, bf16x8_t bl,
+                                             f32x16_t c) {
+  c = mfma32(al, bh, c);
+  c = mfma32(ah, bl, c);
+  return mfma32(ah, bh, c);
+}
 
 }  // namespace hwa

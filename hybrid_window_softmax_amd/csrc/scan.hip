@@ -1,20 +1,25 @@
 // Bidirectional frame scan of the linear branch (VDN-H3 article, "Step 4:
 // bidirectional scan + boundary gather" and "Text state"):
-//   prefix  P_{-1} = s0,  P_f = P_{f-1} G_f + C_f   for f = 0 .. F-1
-//   suffix  Q_F    = s0,  Q_f = Q_{f+1} G_f + C_f   for f = F-1 .. 0
-// with s0 = text_scale * S_text (zero without a text state) and (G_f, C_f)
-// the affine form of the update rule. Only the states a window can gather
-// are kept: bank slot m holds P_{min(F, m*chunk)-1} and Q_{min(F, m*chunk)}.
+//   prefix  P_{-1} = s0,  P_f = R_f(P_{f-1})   for f = 0 .. F-1
+//   suffix  Q_F    = s0,  Q_f = R_f(Q_{f+1})   for f = F-1 .. 0
+// with s0 = text_scale * S_text (zero without a text state). Every update
+// rule of the rules table is one step
+//   X = S diag(alpha_f) + c1 B_f,   R_f(S) = X M_f + c2 B_f
+//   vdn_solve    c1 = 1, c2 = 0, M_f = (I + A_f)^-1
+//   vdn_scaled   c1 = c, c2 = 0, M_f = (I + c^2 A_f)^-1
+//   sana_scaled  c1 = 0, c2 = c, M_f = I - c^2 A_f (formed here from A_f)
+// Only the states a window can gather are kept: bank slot m holds
+// P_{min(F, m*chunk)-1} and Q_{min(F, m*chunk)}.
 //
 // The update right-multiplies the state, so its rows evolve independently:
 // a workgroup owns 8 rows of one (b, h, direction) chain for the whole scan
-// and never exchanges data with the other row blocks. G_f is staged in LDS
-// once per step and shared by the workgroup's rows.
+// and never exchanges data with the other row blocks. M_f is staged in LDS
+// once per step and shared by the workgroup's rows (fp32 throughout).
 //
 // Every state row carries a power-of-two exponent e (row = stored * 2^e).
 // When a row's max |value| passes 2^64 it is rescaled by an exact power of
-// two; C_f is scaled by 2^-e before it is added. This keeps a diverging
-// sana_scaled scan finite in fp32 and is a no-op for the contracting rules.
+// two, and B_f enters scaled by 2^-e. This keeps a diverging sana_scaled scan
+// finite in fp32 and is a no-op for the contracting rules.
 
 #include "hwa_internal.h"
 
@@ -24,13 +29,14 @@ constexpr int SC_R = 8;  // state rows per workgroup
 
 template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(
-    const float* __restrict__ G, const float* __restrict__ C,
-    const float* __restrict__ text_state, float text_scale,
+    const float* __restrict__ Am, const float* __restrict__ Bm,
+    const float* __restrict__ Mi, const float* __restrict__ alpha, int rule,
+    float c, const float* __restrict__ text_state, float text_scale,
     float* __restrict__ bank_p, float* __restrict__ bank_q,
     int32_t* __restrict__ bank_e, int F, int chunk, int nch, int BH) {
   constexpr int TPR = D / 4;  // threads per state row (4 columns each)
   __shared__ __attribute__((aligned(16))) float g_lds[D * D];
-  __shared__ float s_lds[SC_R][D];
+  __shared__ float x_lds[SC_R][D];
 
   const int tid = threadIdx.x;
   const int rb = blockIdx.x;   // row block
@@ -40,6 +46,10 @@ __global__ __launch_bounds__(256) void scan_kernel(
   const int j0 = (tid % TPR) * 4;
   const bool active = r < SC_R;
   const int row = rb * SC_R + r;
+  const bool sana = rule == HWA_RULE_SANA_SCALED;
+  const float c1 = sana ? 0.0f : (rule == HWA_RULE_VDN_SCALED ? c : 1.0f);
+  const float c2 = sana ? c : 0.0f;
+  const float cs = c * c;
 
   float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int e = 0;
@@ -62,25 +72,42 @@ __global__ __launch_bounds__(256) void scan_kernel(
   for (int i = 0; i < F; ++i) {
     const int f = dir == 0 ? i : F - 1 - i;
     const long long mo = ((long long)bh * F + f) * D * D;
-    for (int x = tid; x < D * D / 4; x += 256)
-      *(float4*)&g_lds[x * 4] = *(const float4*)&G[mo + (long long)x * 4];
+    if (sana) {
+      for (int x = tid; x < D * D / 4; x += 256) {
+        const float4 a4 = *(const float4*)&Am[mo + (long long)x * 4];
+        const int kk = (x * 4) / D, jj = (x * 4) % D;
+        float4 g4 = make_float4(-cs * a4.x, -cs * a4.y, -cs * a4.z, -cs * a4.w);
+        if (kk >= jj && kk < jj + 4) (&g4.x)[kk - jj] += 1.0f;
+        *(float4*)&g_lds[x * 4] = g4;
+      }
+    } else {
+      for (int x = tid; x < D * D / 4; x += 256)
+        *(float4*)&g_lds[x * 4] = *(const float4*)&Mi[mo + (long long)x * 4];
+    }
+    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (active) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s_lds[r][j0 + q] = s[q];
+      const float4 b4 = *(const float4*)&Bm[mo + (long long)row * D + j0];
+      const float4 a4 = *(const float4*)&alpha[((long long)bh * F + f) * D + j0];
+      bv[0] = ldexpf(b4.x, -e);
+      bv[1] = ldexpf(b4.y, -e);
+      bv[2] = ldexpf(b4.z, -e);
+      bv[3] = ldexpf(b4.w, -e);
+      x_lds[r][j0 + 0] = fmaf(c1, bv[0], s[0] * a4.x);
+      x_lds[r][j0 + 1] = fmaf(c1, bv[1], s[1] * a4.y);
+      x_lds[r][j0 + 2] = fmaf(c1, bv[2], s[2] * a4.z);
+      x_lds[r][j0 + 3] = fmaf(c1, bv[3], s[3] * a4.w);
     }
     __syncthreads();
     if (active) {
-      float4 cv = *(const float4*)&C[mo + (long long)row * D + j0];
-      float acc[4] = {ldexpf(cv.x, -e), ldexpf(cv.y, -e), ldexpf(cv.z, -e),
-                      ldexpf(cv.w, -e)};
+      float acc[4] = {c2 * bv[0], c2 * bv[1], c2 * bv[2], c2 * bv[3]};
 #pragma unroll 8
       for (int kk = 0; kk < D; ++kk) {
-        const float sv = s_lds[r][kk];
+        const float xv = x_lds[r][kk];
         const float4 gv = *(const float4*)&g_lds[kk * D + j0];
-        acc[0] = fmaf(sv, gv.x, acc[0]);
-        acc[1] = fmaf(sv, gv.y, acc[1]);
-        acc[2] = fmaf(sv, gv.z, acc[2]);
-        acc[3] = fmaf(sv, gv.w, acc[3]);
+        acc[0] = fmaf(xv, gv.x, acc[0]);
+        acc[1] = fmaf(xv, gv.y, acc[1]);
+        acc[2] = fmaf(xv, gv.z, acc[2]);
+        acc[3] = fmaf(xv, gv.w, acc[3]);
       }
       float mx = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])),
                        fmaxf(fabsf(acc[2]), fabsf(acc[3])));
@@ -105,15 +132,16 @@ __global__ __launch_bounds__(256) void scan_kernel(
   }
 }
 
-hipError_t launch_scan(const Geom& g, const float* G, const float* C,
+hipError_t launch_scan(const Geom& g, int rule, float c, const float* A,
+                       const float* Bm, const float* M, const float* alpha,
                        const float* text_state, float text_scale,
                        float* bank_p, float* bank_q, int32_t* bank_e,
                        hipStream_t st) {
   dim3 grid(g.d / SC_R, 2, g.B * g.H);
-#define SCAN_LAUNCH(DD)                                                      \
-  hipLaunchKernelGGL(scan_kernel<DD>, grid, dim3(256), 0, st, G, C,          \
-                     text_state, text_scale, bank_p, bank_q, bank_e, g.F,    \
-                     g.chunk, g.nch, g.B * g.H)
+#define SCAN_LAUNCH(DD)                                                       \
+  hipLaunchKernelGGL(scan_kernel<DD>, grid, dim3(256), 0, st, A, Bm, M, alpha, \
+                     rule, c, text_state, text_scale, bank_p, bank_q, bank_e, \
+                     g.F, g.chunk, g.nch, g.B * g.H)
   switch (g.d) {
     case 16: SCAN_LAUNCH(16); break;
     case 32: SCAN_LAUNCH(32); break;

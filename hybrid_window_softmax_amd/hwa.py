@@ -22,7 +22,7 @@ FLAG_SOFTMAX_ONLY = 1
 FLAG_LINEAR_ONLY = 2
 FLAG_KEEP_INTERMEDIATES = 4
 NUM_STAGE_EVENTS = 8
-STAGES = ("window", "vtranspose", "softmax", "stats", "maps", "scan", "readout")
+STAGES = ("window", "vtranspose", "softmax", "stats", "inverse", "scan", "readout")
 
 HWA_OK = 0
 HWA_ERR_INVALID_ARG = 1
@@ -59,8 +59,8 @@ class Params(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("lohi", "stat_a", "stat_b", "map_g", "map_c", "bank_p", "bank_q",
-                 "bank_e", "v_t", "total")]
+                ("lohi", "stat_a", "stat_b", "map_m", "bank_p", "bank_q", "bank_e",
+                 "v_t", "total")]
 
 
 class HwaError(RuntimeError):

@@ -96,7 +96,7 @@ typedef struct {
                          /* boundaries of hybrid_attn_fwd, for per-kernel     */
                          /* timing: [0] start, then after [1] window table,   */
                          /* [2] V transpose, [3] softmax, [4] statistics,     */
-                         /* [5] update maps, [6] scan, [7] readout (a skipped */
+                         /* [5] inverses, [6] scan, [7] readout (a skipped    */
                          /* stage records its event with the previous one)   */
 } hwa_params;
 
@@ -108,8 +108,9 @@ typedef struct {
  *   lohi     int32 [2, F]         window bounds lo then hi (inclusive frames)
  *   stat_a   [B, H, F, d, d]      A_f
  *   stat_b   [B, H, F, d, d]      B_f (d_v x d_k)
- *   map_g    [B, H, F, d, d]      G_f: the update as S -> S G_f + C_f
- *   map_c    [B, H, F, d, d]      C_f
+ *   map_m    [B, H, F, d, d]      M_f = (I + c~^2 A_f)^-1 (c~ = 1 for vdn_solve,
+ *                                 c for vdn_scaled; not written for
+ *                                 sana_scaled)
  *   bank_p   [B, H, n_ch+1, d, d] prefix states, slot m = P_{min(F, m*chunk)-1}
  *   bank_q   [B, H, n_ch+1, d, d] suffix states, slot m = Q_{min(F, m*chunk)}
  *   bank_e   int32 [2, B, H, n_ch+1, d] power-of-two exponent of every
@@ -121,7 +122,7 @@ typedef struct {
  * n_ch = ceil(F / chunk).
  */
 typedef struct {
-  size_t lohi, stat_a, stat_b, map_g, map_c, bank_p, bank_q, bank_e, v_t;
+  size_t lohi, stat_a, stat_b, map_m, bank_p, bank_q, bank_e, v_t;
   size_t total;
 } hwa_workspace_layout;
 
