@@ -20,19 +20,40 @@ SOURCES = ["hwa_api.cpp", "softmax.hip", "stats.hip", "factor.hip",
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops off for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wno-unused-result",
 ]
+
+# Per-source extra flags. The softmax never produces NaN from finite inputs
+# (masked scores are -inf and exp2(-inf) = 0), so NaN-preserving max
+# canonicalisation is dropped there; infinities stay honoured.
+EXTRA = {"softmax.hip": ["-fno-honor-nans"]}
 
 
 def build(verbose: bool = False) -> str:
     """Compile every source into libhwa.so next to this file; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(objdir, src + ".o")
+        _run([HIPCC, *COMPILE_FLAGS, *EXTRA.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        return obj
+
+    with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,8 +65,6 @@ def build(verbose: bool = False) -> str:
         for line in (r.stdout + r.stderr).splitlines():
             if noise not in line:
                 print(line)
-    os.replace(tmp, LIB)
-    return LIB
 
 
 if __name__ == "__main__":

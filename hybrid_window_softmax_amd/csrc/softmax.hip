@@ -120,8 +120,12 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     long long Np, int tiles_per_chunk, float scale_log2) {
   constexpr int KP = D + 8;        // padded K row (bf16 elements)
   constexpr int VP = SM_KT + 8;    // padded V^T row
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[SM_KT * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t v_lds[D * VP];
+  constexpr int KCH = SM_KT * D / 8 / SM_THREADS;  // 16-byte K chunks per thread
+  constexpr int VCH = D * SM_KT / 8 / SM_THREADS;  // 16-byte V^T chunks per thread
+  // two stages: the next tile is fetched into registers while the current
+  // one is consumed, then written to the other stage (one barrier per tile)
+  __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][SM_KT * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][D * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -157,36 +161,67 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     qreg[kk] = __builtin_bit_cast(bf16x8, t);
   }
 
+  // tile loaders: chunk ch of K is row ch / (D/8), 8 channels at (ch % (D/8))*8;
+  // chunk ch of V^T is row ch / 8, 8 keys at (ch % 8)*8
+  u32x4 kr[KCH], vr[VCH];
+  auto fetch = [&](long long kt0) {
+    if (kt0 + SM_KT <= N) {  // every row exists (all tiles but the last)
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int ch = tid + i * SM_THREADS;
+        kr[i] = *(const u32x4*)(kb + (kt0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int ch = tid + i * SM_THREADS;
+        const long long n = kt0 + ch / (D / 8);
+        kr[i] = u32x4{0u, 0u, 0u, 0u};
+        if (n < N) kr[i] = *(const u32x4*)(kb + n * D + (ch % (D / 8)) * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int ch = tid + i * SM_THREADS;
+      vr[i] = *(const u32x4*)(vb + (long long)(ch / 8) * Np + kt0 + (ch % 8) * 8);
+    }
+  };
+  auto stash = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * SM_THREADS;
+      *(u32x4*)(&k_lds[st][(ch / (D / 8)) * KP + (ch % (D / 8)) * 8]) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int ch = tid + i * SM_THREADS;
+      *(u32x4*)(&v_lds[st][(ch / 8) * VP + (ch % 8) * 8]) = vr[i];
+    }
+  };
+
   f32x16 acc_o[D / 32];
 #pragma unroll
   for (int j = 0; j < D / 32; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[j][r] = 0.0f;
+  // m_run may lag the true running max by up to 2^8 in exp2 units: p <= 256
+  // stays exact in fp32/bf16 and the O rescale is only paid when it grows
+  const float lag = 8.0f / scale_log2;
   float m_run = -INFINITY;
   float l_run = 0.0f;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   const long long kt_first = k_begin / SM_KT * SM_KT;
-  for (long long kt0 = kt_first; kt0 < k_end; kt0 += SM_KT) {
-    // ---- stage K [64][D] and V^T [D][64] tiles
-    constexpr int KCH = SM_KT * D / 8;
-#pragma unroll
-    for (int i = 0; i < KCH / SM_THREADS; ++i) {
-      int ch = tid + i * SM_THREADS;
-      int row = ch / (D / 8), c8 = ch % (D / 8);
-      long long n = kt0 + row;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (n < N) t = *(const u32x4*)(kb + n * D + c8 * 8);
-      *(u32x4*)(&k_lds[row * KP + c8 * 8]) = t;
-    }
-    constexpr int VCH = D * SM_KT / 8;
-#pragma unroll
-    for (int i = 0; i < VCH / SM_THREADS; ++i) {
-      int ch = tid + i * SM_THREADS;
-      int dr = ch / (SM_KT / 8), k8 = ch % (SM_KT / 8);
-      u32x4 t = *(const u32x4*)(vb + (long long)dr * Np + kt0 + k8 * 8);
-      *(u32x4*)(&v_lds[dr * VP + k8 * 8]) = t;
-    }
-    __syncthreads();
+  const int ntiles = (int)((k_end - kt_first + SM_KT - 1) / SM_KT);
+  fetch(kt_first);
+  stash(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const long long kt0 = kt_first + (long long)it * SM_KT;
+    if (it + 1 < ntiles) fetch(kt0 + SM_KT);
 
     // ---- S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
@@ -194,7 +229,7 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[blk][r] = 0.0f;
-      const bf16_t* krow = &k_lds[(blk * 32 + perm32(col)) * KP + half * 8];
+      const bf16_t* krow = &k_lds[cur][(blk * 32 + perm32(col)) * KP + half * 8];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         bf16x8 a = *(const bf16x8*)(krow + kk * 16);
@@ -214,37 +249,43 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
         }
     }
 
-    // ---- online softmax (base-2, scale folded into scale_log2)
-    float mx = s[0][0];
+    // ---- online softmax (base 2, scale folded into scale_log2)
+    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    m_run = m_new;
-    const float mb = m_new * scale_log2;
-    l_run *= corr;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + lag) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      m_run = m_new;
+      l_run *= corr;
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j)
+      for (int j = 0; j < D / 32; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[j][r] *= corr;
+        for (int r = 0; r < 16; ++r) acc_o[j][r] *= corr;
+    }
+    const float mb = m_run * scale_log2;
 
+    // probabilities in bf16 pairs (one v_cvt_pk_bf16_f32 each); the row sum
+    // is taken over the same bf16 values the PV product uses
     bf16x8 pb[4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(s[blk][r] * scale_log2 - mb);
-        l_run += p;
-        pb[blk * 2 + r / 8][r % 8] = (__bf16)p;
+      for (int r = 0; r < 16; r += 2) {
+        const f32x2 e2 = {
+            __builtin_amdgcn_exp2f(fmaf(s[blk][r], scale_log2, -mb)),
+            __builtin_amdgcn_exp2f(fmaf(s[blk][r + 1], scale_log2, -mb))};
+        const bf16x2 p2 = __builtin_convertvector(e2, bf16x2);
+        pb[blk * 2 + r / 8][r % 8] = p2[0];
+        pb[blk * 2 + r / 8][r % 8 + 1] = p2[1];
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
       }
 
     // ---- O^T += V^T P^T: P block j holds keys 32*(j/2) + 16*half + 8*(j%2) + i
 #pragma unroll
     for (int dblk = 0; dblk < D / 32; ++dblk) {
-      const bf16_t* vrow = &v_lds[(dblk * 32 + col) * VP + half * 16];
+      const bf16_t* vrow = &v_lds[cur][(dblk * 32 + col) * VP + half * 16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8 a = *(const bf16x8*)(vrow + (j / 2) * 32 + (j % 2) * 8);
@@ -252,6 +293,7 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
             a, pb[j], acc_o[dblk], 0, 0, 0);
       }
     }
+    if (it + 1 < ntiles) stash(cur ^ 1);
     __syncthreads();
   }
 
