@@ -112,18 +112,36 @@ __device__ __forceinline__ int perm32(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 }
 
+// LDS rows are padded by one 16-byte slot (K: d + 8 bf16, V^T: 64 + 8 bf16)
+// so that the 32 rows one MFMA operand read touches fall in distinct banks.
+// Tiles are copied global -> LDS by the gfx950 direct load
+// (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
+// dst + 16 * l), one instruction per 64 slots of the padded tile; a pad slot
+// fetches a harmless duplicate.
+//
+// Software pipeline, per wave and key tile i (K runs one tile ahead of V):
+//   issue DMA K(i+2), V(i+1);  S(i+1) = K(i+1) Q^T  (MFMA);
+//   softmax of S(i) (VALU, overlapping those MFMAs);  O += V(i)^T P(i)^T;
+//   wait DMA; barrier.
+// Two K stages and two V stages (72 KB at d = 128) allow two workgroups per
+// CU; one barrier per tile.
 template <int D>
 __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ vt, const int32_t* __restrict__ lohi,
-    bf16_t* __restrict__ out, int F, int S, int chunk, long long N,
+    bf16_t* __restrict__ out, int F, int S, int chunk, int nch, long long N,
     long long Np, int tiles_per_chunk, float scale_log2) {
+  // the body uses device-only lambdas; the host pass needs only the stub
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KP = D + 8;        // padded K row (bf16 elements)
   constexpr int VP = SM_KT + 8;    // padded V^T row
-  constexpr int KCH = SM_KT * D / 8 / SM_THREADS;  // 16-byte K chunks per thread
-  constexpr int VCH = D * SM_KT / 8 / SM_THREADS;  // 16-byte V^T chunks per thread
-  // two stages: the next tile is fetched into registers while the current
-  // one is consumed, then written to the other stage (one barrier per tile)
+  constexpr int KSL = KP / 8;      // 16-byte slots per K row
+  constexpr int VSL = VP / 8;      // 16-byte slots per V^T row
+  constexpr int KINS = SM_KT * KSL / 64;  // DMA instructions per K tile
+  constexpr int VINS = D * VSL / 64;      // DMA instructions per V^T tile
+  constexpr int KPW = (KINS + 3) / 4;     // per wave (upper bound)
+  constexpr int VPW = (VINS + 3) / 4;
+  static_assert(SM_KT * KSL % 64 == 0 && D * VSL % 64 == 0, "whole DMA rows");
   __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][SM_KT * KP];
   __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][D * VP];
 
@@ -132,9 +150,17 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int c = blockIdx.x / tiles_per_chunk;
-  const int tile = blockIdx.x % tiles_per_chunk;
-  const int bh = blockIdx.y;
+  // XCD-aware order: workgroup p is dispatched to XCD p % 8; give each XCD a
+  // contiguous run of logical tiles so that the query tiles of one (head,
+  // chunk), which all stream the same key range, share that XCD's L2
+  const int G = gridDim.x;
+  const int p = blockIdx.x;
+  const int xq = G / 8, xr = G % 8, xcd = p % 8;
+  const int L = xcd * xq + min(xcd, xr) + p / 8;
+  const int per_bh = tiles_per_chunk * nch;
+  const int bh = L / per_bh;
+  const int c = (L % per_bh) / tiles_per_chunk;
+  const int tile = L % tiles_per_chunk;
 
   const long long q_begin = (long long)c * chunk * S;
   const int f_end = min(F, (c + 1) * chunk);
@@ -161,41 +187,40 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     qreg[kk] = __builtin_bit_cast(bf16x8, t);
   }
 
-  // tile loaders: chunk ch of K is row ch / (D/8), 8 channels at (ch % (D/8))*8;
-  // chunk ch of V^T is row ch / 8, 8 keys at (ch % 8)*8
-  u32x4 kr[KCH], vr[VCH];
-  auto fetch = [&](long long kt0) {
-    if (kt0 + SM_KT <= N) {  // every row exists (all tiles but the last)
+  // per-lane DMA sources inside a tile (fixed for the whole kernel):
+  // instruction w + 4*j of this wave fills padded slots 64*(w + 4*j) + lane
+  int k_row[KPW], k_col[KPW], v_off[VPW];
 #pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int ch = tid + i * SM_THREADS;
-        kr[i] = *(const u32x4*)(kb + (kt0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8);
+  for (int j = 0; j < KPW; ++j) {
+    const int slot = (wave + 4 * j) * 64 + lane;
+    const int r = slot / KSL, cs = slot % KSL;
+    k_row[j] = r;
+    k_col[j] = (cs < KSL - 1 ? cs : 0) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < VPW; ++j) {
+    const int slot = (wave + 4 * j) * 64 + lane;
+    const int r = slot / VSL, cs = slot % VSL;
+    v_off[j] = r * (int)Np + (cs < VSL - 1 ? cs : 0) * 8;
+  }
+  auto dma_k = [&] __device__(long long kt0, int st) {
+    const bool whole = kt0 + SM_KT <= N;
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      if (wave + 4 * j < KINS) {
+        long long n = kt0 + k_row[j];
+        if (!whole) n = n < N ? n : N - 1;  // rows past N: any valid row, masked
+        __builtin_amdgcn_global_load_lds(kb + n * D + k_col[j],
+                                         &k_lds[st][(wave + 4 * j) * 512], 16, 0, 0);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int ch = tid + i * SM_THREADS;
-        const long long n = kt0 + ch / (D / 8);
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        if (n < N) kr[i] = *(const u32x4*)(kb + n * D + (ch % (D / 8)) * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ch = tid + i * SM_THREADS;
-      vr[i] = *(const u32x4*)(vb + (long long)(ch / 8) * Np + kt0 + (ch % 8) * 8);
     }
   };
-  auto stash = [&](int st) {
+  auto dma_v = [&] __device__(long long kt0, int st) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * SM_THREADS;
-      *(u32x4*)(&k_lds[st][(ch / (D / 8)) * KP + (ch % (D / 8)) * 8]) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ch = tid + i * SM_THREADS;
-      *(u32x4*)(&v_lds[st][(ch / 8) * VP + (ch % 8) * 8]) = vr[i];
+    for (int j = 0; j < VPW; ++j) {
+      if (wave + 4 * j < VINS)
+        __builtin_amdgcn_global_load_lds(vb + kt0 + v_off[j],
+                                         &v_lds[st][(wave + 4 * j) * 512], 16, 0, 0);
     }
   };
 
@@ -213,75 +238,97 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  const long long kt_first = k_begin / SM_KT * SM_KT;
-  const int ntiles = (int)((k_end - kt_first + SM_KT - 1) / SM_KT);
-  fetch(kt_first);
-  stash(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const long long kt0 = kt_first + (long long)it * SM_KT;
-    if (it + 1 < ntiles) fetch(kt0 + SM_KT);
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
+  auto qk = [&] __device__(int st, f32x16 (&sv)[2]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[blk][r] = 0.0f;
-      const bf16_t* krow = &k_lds[cur][(blk * 32 + perm32(col)) * KP + half * 8];
+      for (int r = 0; r < 16; ++r) sv[blk][r] = 0.0f;
+      const bf16_t* krow = &k_lds[st][(blk * 32 + perm32(col)) * KP + half * 8];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         bf16x8 a = *(const bf16x8*)(krow + kk * 16);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[blk],
-                                                         0, 0, 0);
+        sv[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sv[blk],
+                                                          0, 0, 0);
       }
     }
+  };
 
+  const long long kt_first = k_begin / SM_KT * SM_KT;
+  const int ntiles = (int)((k_end - kt_first + SM_KT - 1) / SM_KT);
+
+  // one pipeline step: consumes scores sc of tile it, produces sn of tile it+1
+  auto step = [&] __device__(int it, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int cur = it & 1, nxt = cur ^ 1;
+    const long long kt0 = kt_first + (long long)it * SM_KT;
+    if (it + 2 < ntiles) dma_k(kt0 + 2 * SM_KT, cur);
+    if (it + 1 < ntiles) dma_v(kt0 + SM_KT, nxt);
     // ---- mask keys outside [k_begin, k_end) (first and last tile only)
     if (kt0 < k_begin || kt0 + SM_KT > k_end) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          long long key = kt0 + blk * 32 + half * 16 + r;
-          if (key < k_begin || key >= k_end) s[blk][r] = -INFINITY;
+          const long long key = kt0 + blk * 32 + half * 16 + r;
+          if (key < k_begin || key >= k_end) sc[blk][r] = -INFINITY;
         }
     }
-
-    // ---- online softmax (base 2, scale folded into scale_log2)
-    float mx = fmaxf(s[0][0], s[1][0]);
+    // ---- running max of S(i); m_run may lag the true one by up to 2^8 in
+    // exp2 units (p <= 256 stays exact) and moves only past that lag, so
+    // the O rescale below is rare
+    float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[1][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + lag) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      m_run = m_new;
-      l_run *= corr;
+    const float m_new = mx > m_run + lag ? fmaxf(m_run, mx) : m_run;
+    const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[j][r] *= corr;
     }
+    m_run = m_new;
+    l_run *= corr;
     const float mb = m_run * scale_log2;
 
-    // probabilities in bf16 pairs (one v_cvt_pk_bf16_f32 each); the row sum
-    // is taken over the same bf16 values the PV product uses
-    bf16x8 pb[4];
+    // ---- the MFMAs of S(i+1) (on the last tile they read a stale stage and
+    // are discarded) interleaved by hand with exp2 of S(i): group g issues
+    // the LDS read of the K operand of group g + 2, the MFMA of group g and
+    // one pair of probabilities (2 exp2, bf16 pack, row-sum dot2); the
+    // sched_barrier fences keep the compiler from regrouping them, so the
+    // VALU work fills the MFMA pipeline's issue gaps.
+    constexpr int NG = 2 * (D / 16);  // QK MFMAs per tile (16 at d = 128)
+    const bf16_t* krow0 = &k_lds[nxt][perm32(col) * KP + half * 8];
+    auto kop = [&] __device__(int g) {  // g: blk = g % 2, kk = g / 2
+      return *(const bf16x8*)(krow0 + (g % 2) * 32 * KP + (g / 2) * 16);
+    };
+    bf16x8 ka[3];
+    ka[0] = kop(0);
+    ka[1] = kop(1);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
+      for (int r = 0; r < 16; ++r) sn[blk][r] = 0.0f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g + 2 < NG) ka[(g + 2) % 3] = kop(g + 2);
+      sn[g % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g % 3], qreg[g / 2],
+                                                          sn[g % 2], 0, 0, 0);
+      // probability pair e = 2 * (g * 16 / NG) ... covers all 32 over the groups
+#pragma unroll
+      for (int e = g * 16 / NG; e < (g + 1) * 16 / NG; ++e) {
+        const int blk = e / 8, r = (e % 8) * 2;
         const f32x2 e2 = {
-            __builtin_amdgcn_exp2f(fmaf(s[blk][r], scale_log2, -mb)),
-            __builtin_amdgcn_exp2f(fmaf(s[blk][r + 1], scale_log2, -mb))};
+            __builtin_amdgcn_exp2f(fmaf(sc[blk][r], scale_log2, -mb)),
+            __builtin_amdgcn_exp2f(fmaf(sc[blk][r + 1], scale_log2, -mb))};
         const bf16x2 p2 = __builtin_convertvector(e2, bf16x2);
         pb[blk * 2 + r / 8][r % 8] = p2[0];
         pb[blk * 2 + r / 8][r % 8 + 1] = p2[1];
         l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
       }
-
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // ---- O^T += V^T P^T: P block j holds keys 32*(j/2) + 16*half + 8*(j%2) + i
 #pragma unroll
     for (int dblk = 0; dblk < D / 32; ++dblk) {
@@ -293,8 +340,23 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
             a, pb[j], acc_o[dblk], 0, 0, 0);
       }
     }
-    if (it + 1 < ntiles) stash(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  // prologue: K(0), V(0), K(1) in flight; S(0)
+  f32x16 sa[2], sb[2];
+  dma_k(kt_first, 0);
+  dma_v(kt_first, 0);
+  if (ntiles > 1) dma_k(kt_first + SM_KT, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(0, sa);
+  __syncthreads();  // K stage 0 is refilled in step 0
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, sa, sb);
+    if (it + 1 >= ntiles) break;
+    step(it + 1, sb, sa);
   }
 
   // ---- normalise and store: lane holds d = 32*dblk + 8*(r/4) + 4*half + r%4
@@ -306,14 +368,16 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        int d0 = dblk * 32 + g4 * 8 + half * 4;
-        uint32_t w0 = (uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 0] * inv) |
-                      ((uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 1] * inv) << 16);
-        uint32_t w1 = (uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 2] * inv) |
-                      ((uint32_t)f32_to_bf16(acc_o[dblk][g4 * 4 + 3] * inv) << 16);
-        *(uint2*)(orow + d0) = make_uint2(w0, w1);
+        const int d0 = dblk * 32 + g4 * 8 + half * 4;
+        const f32x2 a2 = {acc_o[dblk][g4 * 4 + 0] * inv, acc_o[dblk][g4 * 4 + 1] * inv};
+        const f32x2 b2 = {acc_o[dblk][g4 * 4 + 2] * inv, acc_o[dblk][g4 * 4 + 3] * inv};
+        const bf16x2 pa = __builtin_convertvector(a2, bf16x2);
+        const bf16x2 pb2 = __builtin_convertvector(b2, bf16x2);
+        *(uint2*)(orow + d0) = make_uint2(__builtin_bit_cast(uint32_t, pa),
+                                          __builtin_bit_cast(uint32_t, pb2));
       }
   }
+#endif
 }
 
 // ---------------------------------------------------------------- fp32 VALU
@@ -401,12 +465,12 @@ hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
   const int qpc = g.chunk * g.S;  // queries of a full chunk
   if (dtype == HWA_BF16) {
     const int tpc = (qpc + SM_QT - 1) / SM_QT;
-    dim3 grid(tpc * g.nch, g.B * g.H);
+    dim3 grid(tpc * g.nch * g.B * g.H);
     const long long Np = round_up64(g.N);
 #define SM_LAUNCH(DD)                                                        \
   hipLaunchKernelGGL(softmax_bf16_kernel<DD>, grid, dim3(SM_THREADS), 0, st, \
                      (const bf16_t*)q, (const bf16_t*)k, v_t, lohi,          \
-                     (bf16_t*)out, g.F, g.S, g.chunk, g.N, Np, tpc,          \
+                     (bf16_t*)out, g.F, g.S, g.chunk, g.nch, g.N, Np, tpc,   \
                      scale_log2)
     if (g.d == 128) SM_LAUNCH(128);
     else SM_LAUNCH(64);
