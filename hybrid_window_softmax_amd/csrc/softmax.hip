@@ -30,9 +30,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int SM_QT = 128;  // queries per workgroup (4 waves x 32)
+constexpr int SM_NW = 8;                // waves per workgroup
+constexpr int SM_QT = 32 * SM_NW;       // queries per workgroup
 constexpr int SM_KT = 64;   // keys per LDS tile
-constexpr int SM_THREADS = 256;
+constexpr int SM_THREADS = 64 * SM_NW;
 
 __host__ __device__ inline long long round_up64(long long n) {
   return (n + 63) / 64 * 64;
@@ -112,38 +113,53 @@ __device__ __forceinline__ int perm32(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 }
 
-// LDS rows are padded by one 16-byte slot (K: d + 8 bf16, V^T: 64 + 8 bf16)
-// so that the 32 rows one MFMA operand read touches fall in distinct banks.
-// Tiles are copied global -> LDS by the gfx950 direct load
-// (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
-// dst + 16 * l), one instruction per 64 slots of the padded tile; a pad slot
-// fetches a harmless duplicate.
+// LDS tiles are unpadded and XOR-swizzled by 16-byte chunk: K row r keeps
+// logical chunk c at chunk c ^ swz_k(r), V^T row r at c ^ swz_v(r). The
+// swizzles make the 16 lanes of every LDS pass of an MFMA operand read hit 16
+// distinct bank groups. Tiles are copied global -> LDS by the gfx950 direct
+// load (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
+// dst + 16 * l); each lane fetches the global chunk that belongs in its slot.
 //
 // Software pipeline, per wave and key tile i (K runs one tile ahead of V):
-//   issue DMA K(i+2), V(i+1);  S(i+1) = K(i+1) Q^T  (MFMA);
-//   softmax of S(i) (VALU, overlapping those MFMAs);  O += V(i)^T P(i)^T;
-//   wait DMA; barrier.
-// Two K stages and two V stages (72 KB at d = 128) allow two workgroups per
-// CU; one barrier per tile.
+//   issue DMA K(i+3), V(i+2);  S(i+1) = K(i+1) Q^T (MFMA) interleaved with
+//   the exp2 work of S(i);  O += V(i)^T P(i)^T;  wait for the DMA issued one
+//   step earlier; barrier.
+// Three K and three V stages (96 KB at d = 128): loads have a whole step to
+// land. Eight waves (256 queries) share every tile; one workgroup per CU.
+__device__ __forceinline__ int swz_k(int r, int chunks) {
+  return chunks == 16 ? ((r + 8 * (r >> 4)) & 15) : (((r >> 1) + 4 * (r >> 4)) & 7);
+}
+__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
+
+// s_waitcnt vmcnt(n) for a small run-time n (the immediate must be constant)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
+__global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ vt, const int32_t* __restrict__ lohi,
     bf16_t* __restrict__ out, int F, int S, int chunk, int nch, long long N,
     long long Np, int tiles_per_chunk, float scale_log2) {
   // the body uses device-only lambdas; the host pass needs only the stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int KP = D + 8;        // padded K row (bf16 elements)
-  constexpr int VP = SM_KT + 8;    // padded V^T row
-  constexpr int KSL = KP / 8;      // 16-byte slots per K row
-  constexpr int VSL = VP / 8;      // 16-byte slots per V^T row
-  constexpr int KINS = SM_KT * KSL / 64;  // DMA instructions per K tile
-  constexpr int VINS = D * VSL / 64;      // DMA instructions per V^T tile
-  constexpr int KPW = (KINS + 3) / 4;     // per wave (upper bound)
-  constexpr int VPW = (VINS + 3) / 4;
-  static_assert(SM_KT * KSL % 64 == 0 && D * VSL % 64 == 0, "whole DMA rows");
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][SM_KT * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][D * VP];
+  constexpr int KC = D / 8;          // 16-byte chunks per K row
+  constexpr int VC = SM_KT / 8;      // 16-byte chunks per V^T row
+  constexpr int KINS = SM_KT * KC / 64;  // DMA instructions per K tile
+  constexpr int VINS = D * VC / 64;      // DMA instructions per V^T tile
+  constexpr int KPW = KINS / SM_NW;      // per wave
+  constexpr int VPW = VINS / SM_NW;
+  constexpr int NST = 3;                 // pipeline stages
+  static_assert(KINS % SM_NW == 0 && VINS % SM_NW == 0, "uniform DMA per wave");
+  __shared__ __attribute__((aligned(16))) bf16_t k_lds[NST][SM_KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t v_lds[NST][D * SM_KT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -188,40 +204,36 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
   }
 
   // per-lane DMA sources inside a tile (fixed for the whole kernel):
-  // instruction w + 4*j of this wave fills padded slots 64*(w + 4*j) + lane
+  // instruction wave + SM_NW*j fills slots 64*(wave + SM_NW*j) + lane
   int k_row[KPW], k_col[KPW], v_off[VPW];
 #pragma unroll
   for (int j = 0; j < KPW; ++j) {
-    const int slot = (wave + 4 * j) * 64 + lane;
-    const int r = slot / KSL, cs = slot % KSL;
+    const int slot = (wave + SM_NW * j) * 64 + lane;
+    const int r = slot / KC, pc = slot % KC;
     k_row[j] = r;
-    k_col[j] = (cs < KSL - 1 ? cs : 0) * 8;
+    k_col[j] = (pc ^ swz_k(r, KC)) * 8;
   }
 #pragma unroll
   for (int j = 0; j < VPW; ++j) {
-    const int slot = (wave + 4 * j) * 64 + lane;
-    const int r = slot / VSL, cs = slot % VSL;
-    v_off[j] = r * (int)Np + (cs < VSL - 1 ? cs : 0) * 8;
+    const int slot = (wave + SM_NW * j) * 64 + lane;
+    const int r = slot / VC, pc = slot % VC;
+    v_off[j] = r * (int)Np + (pc ^ swz_v(r)) * 8;
   }
   auto dma_k = [&] __device__(long long kt0, int st) {
     const bool whole = kt0 + SM_KT <= N;
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
-      if (wave + 4 * j < KINS) {
-        long long n = kt0 + k_row[j];
-        if (!whole) n = n < N ? n : N - 1;  // rows past N: any valid row, masked
-        __builtin_amdgcn_global_load_lds(kb + n * D + k_col[j],
-                                         &k_lds[st][(wave + 4 * j) * 512], 16, 0, 0);
-      }
+      long long n = kt0 + k_row[j];
+      if (!whole) n = n < N ? n : N - 1;  // rows past N: any valid row, masked
+      __builtin_amdgcn_global_load_lds(kb + n * D + k_col[j],
+                                       &k_lds[st][(wave + SM_NW * j) * 512], 16, 0, 0);
     }
   };
   auto dma_v = [&] __device__(long long kt0, int st) {
 #pragma unroll
-    for (int j = 0; j < VPW; ++j) {
-      if (wave + 4 * j < VINS)
-        __builtin_amdgcn_global_load_lds(vb + kt0 + v_off[j],
-                                         &v_lds[st][(wave + 4 * j) * 512], 16, 0, 0);
-    }
+    for (int j = 0; j < VPW; ++j)
+      __builtin_amdgcn_global_load_lds(vb + kt0 + v_off[j],
+                                       &v_lds[st][(wave + SM_NW * j) * 512], 16, 0, 0);
   };
 
   f32x16 acc_o[D / 32];
@@ -238,18 +250,28 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // LDS operand reads: K row (blk*32 + perm32(col)), logical chunk 2*kk + half;
+  // V^T row (dblk*32 + col), logical chunk 2*half + 4*(j/2) + (j%2)
+  const int kr0 = perm32(col), kr1 = 32 + perm32(col);
+  const int ksw0 = swz_k(kr0, KC), ksw1 = swz_k(kr1, KC);
+  auto kop = [&] __device__(int st, int blk, int kk) {
+    const int r = blk ? kr1 : kr0, sw = blk ? ksw1 : ksw0;
+    return *(const bf16x8*)&k_lds[st][r * D + (((2 * kk + half) ^ sw) * 8)];
+  };
+  auto vop = [&] __device__(int st, int dblk, int j) {
+    const int r = dblk * 32 + col;
+    const int lc = 2 * half + 4 * (j / 2) + (j % 2);
+    return *(const bf16x8*)&v_lds[st][r * SM_KT + ((lc ^ swz_v(r)) * 8)];
+  };
   auto qk = [&] __device__(int st, f32x16 (&sv)[2]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[blk][r] = 0.0f;
-      const bf16_t* krow = &k_lds[st][(blk * 32 + perm32(col)) * KP + half * 8];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        bf16x8 a = *(const bf16x8*)(krow + kk * 16);
-        sv[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sv[blk],
-                                                          0, 0, 0);
-      }
+      for (int kk = 0; kk < D / 16; ++kk)
+        sv[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(st, blk, kk), qreg[kk],
+                                                          sv[blk], 0, 0, 0);
     }
   };
 
@@ -258,10 +280,12 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
 
   // one pipeline step: consumes scores sc of tile it, produces sn of tile it+1
   auto step = [&] __device__(int it, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    const int cur = it & 1, nxt = cur ^ 1;
+    const int sv = it % NST;            // V(it)
+    const int sk = (it + 1) % NST;      // K(it+1)
     const long long kt0 = kt_first + (long long)it * SM_KT;
-    if (it + 2 < ntiles) dma_k(kt0 + 2 * SM_KT, cur);
-    if (it + 1 < ntiles) dma_v(kt0 + SM_KT, nxt);
+    int issued = 0;
+    if (it + 3 < ntiles) { dma_k(kt0 + 3 * SM_KT, it % NST); issued += KPW; }
+    if (it + 2 < ntiles) { dma_v(kt0 + 2 * SM_KT, (it + 2) % NST); issued += VPW; }
     // ---- mask keys outside [k_begin, k_end) (first and last tile only)
     if (kt0 < k_begin || kt0 + SM_KT > k_end) {
 #pragma unroll
@@ -298,24 +322,19 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     // sched_barrier fences keep the compiler from regrouping them, so the
     // VALU work fills the MFMA pipeline's issue gaps.
     constexpr int NG = 2 * (D / 16);  // QK MFMAs per tile (16 at d = 128)
-    const bf16_t* krow0 = &k_lds[nxt][perm32(col) * KP + half * 8];
-    auto kop = [&] __device__(int g) {  // g: blk = g % 2, kk = g / 2
-      return *(const bf16x8*)(krow0 + (g % 2) * 32 * KP + (g / 2) * 16);
-    };
     bf16x8 ka[3];
-    ka[0] = kop(0);
-    ka[1] = kop(1);
+    ka[0] = kop(sk, 0, 0);
+    ka[1] = kop(sk, 1, 0);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[blk][r] = 0.0f;
     bf16x8 pb[4];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (g + 2 < NG) ka[(g + 2) % 3] = kop(g + 2);
+    for (int g = 0; g < NG; ++g) {  // g: blk = g % 2, kk = g / 2
+      if (g + 2 < NG) ka[(g + 2) % 3] = kop(sk, (g + 2) % 2, (g + 2) / 2);
       sn[g % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g % 3], qreg[g / 2],
                                                           sn[g % 2], 0, 0, 0);
-      // probability pair e = 2 * (g * 16 / NG) ... covers all 32 over the groups
 #pragma unroll
       for (int e = g * 16 / NG; e < (g + 1) * 16 / NG; ++e) {
         const int blk = e / 8, r = (e % 8) * 2;
@@ -331,25 +350,25 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     }
     // ---- O^T += V^T P^T: P block j holds keys 32*(j/2) + 16*half + 8*(j%2) + i
 #pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk) {
-      const bf16_t* vrow = &v_lds[cur][(dblk * 32 + col) * VP + half * 16];
+    for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 a = *(const bf16x8*)(vrow + (j / 2) * 32 + (j % 2) * 8);
+      for (int j = 0; j < 4; ++j)
         acc_o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, pb[j], acc_o[dblk], 0, 0, 0);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            vop(sv, dblk, j), pb[j], acc_o[dblk], 0, 0, 0);
+    // the loads issued one step earlier are needed by the next step
+    wait_vmcnt(issued);
     __syncthreads();
   };
 
-  // prologue: K(0), V(0), K(1) in flight; S(0)
+  // prologue: K(0), V(0), K(1) land first; K(2), V(1) stay in flight
   f32x16 sa[2], sb[2];
   dma_k(kt_first, 0);
   dma_v(kt_first, 0);
   if (ntiles > 1) dma_k(kt_first + SM_KT, 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int pend = 0;
+  if (ntiles > 2) { dma_k(kt_first + 2 * SM_KT, 2); pend += KPW; }
+  if (ntiles > 1) { dma_v(kt_first + SM_KT, 1); pend += VPW; }
+  wait_vmcnt(pend);
   __syncthreads();
   qk(0, sa);
   __syncthreads();  // K stage 0 is refilled in step 0
@@ -358,6 +377,7 @@ __global__ __launch_bounds__(SM_THREADS, 2) void softmax_bf16_kernel(
     if (it + 1 >= ntiles) break;
     step(it + 1, sb, sa);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- normalise and store: lane holds d = 32*dblk + 8*(r/4) + 4*half + r%4
   const float l_tot = l_run + __shfl_xor(l_run, 32);
