@@ -38,35 +38,42 @@ __global__ __launch_bounds__(256) void inverse_kernel(
       m[a][b] = (i == j ? 1.0f : 0.0f) + c2 * A[mo + (long long)i * D + j];
     }
 
-  for (int k = 0; k < D; ++k) {
-    const int buf = k & 1;
-    const int kb = k / BS, kr = k % BS;
-    if (ib == kb) {
+  // pivot k = kb * BS + kr; kr is unrolled so register indices are static
+  for (int kb = 0; kb < 16; ++kb) {
 #pragma unroll
-      for (int b = 0; b < BS; ++b) rowbuf[buf][jb * BS + b] = m[kr][b];
-    }
-    if (jb == kb) {
+    for (int kr = 0; kr < BS; ++kr) {
+      const int k = kb * BS + kr;
+      const int buf = k & 1;
+      if (ib == kb) {
 #pragma unroll
-      for (int a = 0; a < BS; ++a) colbuf[buf][ib * BS + a] = m[a][kr];
-    }
-    __syncthreads();
-    const float rp = 1.0f / rowbuf[buf][k];
-    float row[BS], colv[BS];
+        for (int b = 0; b < BS; ++b) rowbuf[buf][jb * BS + b] = m[kr][b];
+      }
+      if (jb == kb) {
 #pragma unroll
-    for (int b = 0; b < BS; ++b) row[b] = rowbuf[buf][jb * BS + b];
+        for (int a = 0; a < BS; ++a) colbuf[buf][ib * BS + a] = m[a][kr];
+      }
+      __syncthreads();
+      const float rp = 1.0f / rowbuf[buf][k];
+      float row[BS], colv[BS];
 #pragma unroll
-    for (int a = 0; a < BS; ++a) colv[a] = colbuf[buf][ib * BS + a];
+      for (int b = 0; b < BS; ++b) row[b] = rowbuf[buf][jb * BS + b];
 #pragma unroll
-    for (int a = 0; a < BS; ++a) {
-      const float fa = colv[a] * rp;
-      const bool rowk = ib * BS + a == k;
+      for (int a = 0; a < BS; ++a) colv[a] = colbuf[buf][ib * BS + a] * rp;
+      // every element: m[i][j] -= m[i][k] m[k][j] / p
 #pragma unroll
-      for (int b = 0; b < BS; ++b) {
-        const bool colk = jb * BS + b == k;
-        float nv = fmaf(-fa, row[b], m[a][b]);
-        if (colk) nv = -fa;
-        if (rowk) nv = colk ? rp : row[b] * rp;
-        m[a][b] = nv;
+      for (int a = 0; a < BS; ++a)
+#pragma unroll
+        for (int b = 0; b < BS; ++b) m[a][b] = fmaf(-colv[a], row[b], m[a][b]);
+      // pivot row m[k][j] = m[k][j] / p, column m[i][k] = -m[i][k] / p,
+      // pivot 1 / p
+      if (ib == kb) {
+#pragma unroll
+        for (int b = 0; b < BS; ++b) m[kr][b] = row[b] * rp;
+      }
+      if (jb == kb) {
+#pragma unroll
+        for (int a = 0; a < BS; ++a) m[a][kr] = -colv[a];
+        if (ib == kb) m[kr][kr] = rp;
       }
     }
   }

@@ -229,9 +229,9 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
       return HWA_ERR_HIP;
   }
   if (mark(5) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && hwa::launch_scan(g, rule, p->c, A, Bm, M, alpha, text_state,
-                                 p->text_scale, bank_p, bank_q, bank_e,
-                                 st) != hipSuccess)
+  if (do_lin && hwa::launch_scan(g, p->dtype, rule, p->c, A, Bm, M, alpha,
+                                 text_state, p->text_scale, bank_p, bank_q,
+                                 bank_e, st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(6) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && hwa::launch_readout(g, p->dtype, q, gate, alpha, lohi, bank_p,

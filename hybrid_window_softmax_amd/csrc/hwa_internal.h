@@ -93,11 +93,11 @@ hipError_t launch_matmul_bm(const Geom& g, const float* Bm, const float* M,
                             float* C, hipStream_t st);
 
 // Prefix/suffix scans; writes the chunk-boundary state banks.
-hipError_t launch_scan(const Geom& g, int rule, float c, const float* A,
-                       const float* Bm, const float* M, const float* alpha,
-                       const float* text_state, float text_scale,
-                       float* bank_p, float* bank_q, int32_t* bank_e,
-                       hipStream_t st);
+hipError_t launch_scan(const Geom& g, int dtype, int rule, float c,
+                       const float* A, const float* Bm, const float* M,
+                       const float* alpha, const float* text_state,
+                       float text_scale, float* bank_p, float* bank_q,
+                       int32_t* bank_e, hipStream_t st);
 
 hipError_t launch_readout(const Geom& g, int dtype, const void* q,
                           const void* gate, const float* alpha,

@@ -132,11 +132,181 @@ __global__ __launch_bounds__(256) void scan_kernel(
   }
 }
 
-hipError_t launch_scan(const Geom& g, int rule, float c, const float* A,
-                       const float* Bm, const float* M, const float* alpha,
-                       const float* text_state, float text_scale,
-                       float* bank_p, float* bank_q, int32_t* bank_e,
-                       hipStream_t st) {
+// ---------------------------------------------------------------- bf16 path
+// Same recurrence on MFMA (v_mfma_f32_32x32x16_bf16, split-bf16 operands:
+// hi*hi + hi*lo + lo*hi, about 16 mantissa bits per product; the state stays
+// fp32). A workgroup owns 32 state rows of one (b, h, direction) chain for
+// the whole scan; wave w owns the 32 x 32 output block of columns 32w..32w+31
+// and holds it in the MFMA accumulator layout (lane: column lane % 32, rows
+// 8*(r/4) + 4*(lane/32) + r%4). Per frame:
+//   X = S diag(alpha) + c1 2^-e B  -> split to bf16 (hi, lo) in LDS (double
+//   buffered, one barrier per frame);
+//   S = X M (+ c2 2^-e B): A operand = rows of X from LDS, B operand = rows
+//   of M (M is symmetric, so row n is the needed column n), read from global
+//   memory one frame ahead into registers.
+// Row exponents (diverging sana_scaled only, SANA = true): the row max over
+// all d columns is combined across waves through LDS.
+template <int D, bool SANA>
+__global__ __launch_bounds__(2 * D) void scan_mfma_kernel(
+    const float* __restrict__ Msrc, const float* __restrict__ Bm,
+    const float* __restrict__ alpha, float c1, float c2, float cs,
+    const float* __restrict__ text_state, float text_scale,
+    float* __restrict__ bank_p, float* __restrict__ bank_q,
+    int32_t* __restrict__ bank_e, int F, int chunk, int nch, int BH) {
+  constexpr int XP = D + 8;  // padded X row (bf16)
+  __shared__ __attribute__((aligned(16))) bf16_t x_hi[2][32 * XP];
+  __shared__ __attribute__((aligned(16))) bf16_t x_lo[2][32 * XP];
+  __shared__ unsigned rmax[2][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int rb = blockIdx.x;   // 32-row block
+  const int dir = blockIdx.y;  // 0 prefix, 1 suffix
+  const int bh = blockIdx.z;
+  const int n = wave * 32 + col;  // this lane's state column
+  // rows of accumulator register r: 8*(r/4) + 4*half + r%4 (within the block)
+  auto rowof = [&](int r) { return 8 * (r / 4) + 4 * half + (r % 4); };
+
+  float sv[16];
+  int e[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = rb * 32 + rowof(r);
+    sv[r] = text_state ? text_scale * text_state[((long long)bh * D + row) * D + n] : 0.0f;
+    e[r] = 0;
+  }
+  if (tid < 32) rmax[0][tid] = rmax[1][tid] = 0u;  // published by the first barrier
+  float* bank = dir == 0 ? bank_p : bank_q;
+  int32_t* be = bank_e + (long long)dir * BH * (nch + 1) * D;
+  auto store = [&](int slot) {
+    float* dst = bank + ((long long)bh * (nch + 1) + slot) * D * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[(long long)(rb * 32 + rowof(r)) * D + n] = sv[r];
+    if (wave == 0 && col == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        be[((long long)bh * (nch + 1) + slot) * D + rb * 32 + rowof(r)] = e[r];
+    }
+  };
+  store(dir == 0 ? 0 : nch);
+
+  // prefetch of the next frame: M rows n (k = 16*kk + 8*half .. +7), B, alpha
+  float mraw[D / 16][8], braw[16], anext;
+  auto fetch = [&](int f) {
+    const long long mo = ((long long)bh * F + f) * D * D;
+    const float* mrow = Msrc + mo + (long long)n * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const float4 a = *(const float4*)(mrow + kk * 16);
+      const float4 b = *(const float4*)(mrow + kk * 16 + 4);
+      mraw[kk][0] = a.x; mraw[kk][1] = a.y; mraw[kk][2] = a.z; mraw[kk][3] = a.w;
+      mraw[kk][4] = b.x; mraw[kk][5] = b.y; mraw[kk][6] = b.z; mraw[kk][7] = b.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) braw[r] = Bm[mo + (long long)(rb * 32 + rowof(r)) * D + n];
+    anext = alpha[((long long)bh * F + f) * D + n];
+  };
+  fetch(dir == 0 ? 0 : F - 1);
+
+  for (int i = 0; i < F; ++i) {
+    const int f = dir == 0 ? i : F - 1 - i;
+    const int buf = i & 1;
+    // ---- X = S diag(alpha) + c1 2^-e B (own block) -> LDS (hi, lo)
+    float bcur[16];
+    const float acur = anext;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      bcur[r] = ldexpf(braw[r], -e[r]);
+      const float x = fmaf(c1, bcur[r], sv[r] * acur);
+      __bf16 h, l;
+      split_bf16(x, h, l);
+      x_hi[buf][rowof(r) * XP + n] = __builtin_bit_cast(bf16_t, h);
+      x_lo[buf][rowof(r) * XP + n] = __builtin_bit_cast(bf16_t, l);
+    }
+    // ---- this frame's M operand (hi, lo); then start fetching the next one
+    bf16x8_t mh[D / 16], ml[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float mv = SANA ? ((16 * kk + 8 * half + u == n ? 1.0f : 0.0f) -
+                                 cs * mraw[kk][u])
+                              : mraw[kk][u];
+        __bf16 h, l;
+        split_bf16(mv, h, l);
+        mh[kk][u] = h;
+        ml[kk][u] = l;
+      }
+    if (i + 1 < F) fetch(dir == 0 ? f + 1 : f - 1);
+    __syncthreads();
+    // ---- S = X M (+ c2 2^-e B)
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = c2 * bcur[r];
+    const bf16_t* xh = &x_hi[buf][col * XP + half * 8];
+    const bf16_t* xl = &x_lo[buf][col * XP + half * 8];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8_t ah = *(const bf16x8_t*)(xh + kk * 16);
+      const bf16x8_t al = *(const bf16x8_t*)(xl + kk * 16);
+      acc = mfma32x3(ah, al, mh[kk], ml[kk], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = acc[r];
+    if (SANA) {
+      // row max |S| over all columns: 32 lanes of a half, then the waves
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float m = fabsf(sv[r]);
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (col == 0) atomicMax(&rmax[buf][rowof(r)], __float_as_uint(m));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float m = __uint_as_float(rmax[buf][rowof(r)]);
+        if (m > 0x1p64f) {
+          int ex;
+          frexpf(m, &ex);
+          sv[r] = ldexpf(sv[r], -ex);
+          e[r] += ex;
+        }
+      }
+      if (tid < 32) rmax[buf ^ 1][tid] = 0u;  // cleared for the next frame
+    }
+    if (dir == 0) {
+      if ((f + 1) % chunk == 0 || f + 1 == F) store((f + chunk) / chunk);
+    } else {
+      if (f % chunk == 0) store(f / chunk);
+    }
+  }
+}
+
+hipError_t launch_scan(const Geom& g, int dtype, int rule, float c,
+                       const float* A, const float* Bm, const float* M,
+                       const float* alpha, const float* text_state,
+                       float text_scale, float* bank_p, float* bank_q,
+                       int32_t* bank_e, hipStream_t st) {
+  if (dtype == HWA_BF16) {
+    const bool sana = rule == HWA_RULE_SANA_SCALED;
+    const float c1 = sana ? 0.0f : (rule == HWA_RULE_VDN_SCALED ? c : 1.0f);
+    const float c2 = sana ? c : 0.0f;
+    const float* msrc = sana ? A : M;
+    dim3 grid(g.d / 32, 2, g.B * g.H);
+#define SM_SCAN(DD, SN)                                                         \
+  hipLaunchKernelGGL((scan_mfma_kernel<DD, SN>), grid, dim3(2 * DD), 0, st,    \
+                     msrc, Bm, alpha, c1, c2, c * c, text_state, text_scale,   \
+                     bank_p, bank_q, bank_e, g.F, g.chunk, g.nch, g.B * g.H)
+    if (g.d == 128) {
+      if (sana) SM_SCAN(128, true); else SM_SCAN(128, false);
+    } else {
+      if (sana) SM_SCAN(64, true); else SM_SCAN(64, false);
+    }
+#undef SM_SCAN
+    return hipGetLastError();
+  }
   dim3 grid(g.d / SC_R, 2, g.B * g.H);
 #define SCAN_LAUNCH(DD)                                                       \
   hipLaunchKernelGGL(scan_kernel<DD>, grid, dim3(256), 0, st, A, Bm, M, alpha, \
