@@ -69,6 +69,7 @@ hwa_workspace_layout compute_layout(const Geom& g, int dtype) {
   L.map_m = take(bh * g.F * dd * sizeof(float));
   L.bank_p = take(bh * (g.nch + 1) * dd * sizeof(float));
   L.bank_q = take(bh * (g.nch + 1) * dd * sizeof(float));
+  L.decay = take(bh * g.F * 2 * g.d * sizeof(float));
   L.bank_e = take(2 * bh * (g.nch + 1) * g.d * sizeof(int32_t));
   const size_t Np = (size_t)((g.N + 63) / 64 * 64);
   L.v_t = take(dtype == HWA_BF16 ? bh * g.d * Np * sizeof(bf16_t) : 0);
@@ -202,6 +203,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   float* bank_p = (float*)(ws + L.bank_p);
   float* bank_q = (float*)(ws + L.bank_q);
   int32_t* bank_e = (int32_t*)(ws + L.bank_e);
+  float* decay = (float*)(ws + L.decay);
   bf16_t* v_t = (bf16_t*)(ws + L.v_t);
 
   void* const* ev = p->stage_events;
@@ -234,9 +236,10 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                  bank_e, st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(6) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && hwa::launch_readout(g, p->dtype, q, gate, alpha, lohi, bank_p,
-                                    bank_q, bank_e, p->rms_weight, p->rms_eps,
-                                    do_sm, out, st) != hipSuccess)
+  if (do_lin && (hwa::launch_decay(g, alpha, lohi, decay, st) != hipSuccess ||
+                 hwa::launch_readout(g, p->dtype, q, gate, decay, lohi, bank_p,
+                                     bank_q, bank_e, p->rms_weight, p->rms_eps,
+                                     do_sm, out, st) != hipSuccess))
     return HWA_ERR_HIP;
   if (mark(7) != hipSuccess) return HWA_ERR_HIP;
   return HWA_OK;

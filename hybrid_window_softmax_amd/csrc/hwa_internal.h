@@ -49,12 +49,23 @@ __device__ __forceinline__ void st_io<bf16_t>(bf16_t* p, long long i, float x) {
   p[i] = f32_to_bf16(x);
 }
 
+// Hardware reciprocal / reciprocal square root / exp2 (about 1 ulp each);
+// the IEEE-exact division and sqrt sequences are not needed anywhere here.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// x * sigmoid(x) = x / (1 + e^-x)
 __device__ __forceinline__ float silu_f(float x) {
-  return x / (1.0f + __expf(-x));
+  return x * fast_rcp(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
 __device__ __forceinline__ float sigmoid_f(float x) {
-  return 1.0f / (1.0f + __expf(-x));
+  return fast_rcp(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+// 1 / max(||x||, 1e-12) from the squared norm
+__device__ __forceinline__ float inv_l2(float ss) {
+  return fast_rsq(fmaxf(ss, 1e-24f));
 }
 
 // Window of query frame t (article: chunk-aligned, radius chunks each side).
@@ -99,8 +110,12 @@ hipError_t launch_scan(const Geom& g, int dtype, int rule, float c,
                        float text_scale, float* bank_p, float* bank_q,
                        int32_t* bank_e, hipStream_t st);
 
+// Bridge decays of every (b, h, t): prod_{j=lo..t} alpha_j, prod_{j=t..hi}.
+hipError_t launch_decay(const Geom& g, const float* alpha, const int32_t* lohi,
+                        float* decay, hipStream_t st);
+
 hipError_t launch_readout(const Geom& g, int dtype, const void* q,
-                          const void* gate, const float* alpha,
+                          const void* gate, const float* decay,
                           const int32_t* lohi, const float* bank_p,
                           const float* bank_q, const int32_t* bank_e,
                           const float* rms_weight, float rms_eps,

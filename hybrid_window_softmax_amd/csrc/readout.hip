@@ -20,7 +20,7 @@ constexpr int RO_TT = 16;    // tokens per inner tile
 template <typename T, int D>
 __global__ __launch_bounds__(256) void readout_kernel(
     const T* __restrict__ q, const T* __restrict__ gate,
-    const float* __restrict__ alpha, const int32_t* __restrict__ lohi,
+    const float* __restrict__ decay, const int32_t* __restrict__ lohi,
     const float* __restrict__ bank_p, const float* __restrict__ bank_q,
     const int32_t* __restrict__ bank_e, const float* __restrict__ rms_w,
     float eps, int accumulate, T* __restrict__ out, int F, int S, int chunk,
@@ -39,22 +39,18 @@ __global__ __launch_bounds__(256) void readout_kernel(
   const int bh = blockIdx.z;
   const int tok0 = blockIdx.x * RO_TOK;
   if (tok0 >= S) return;
-  const int lo = lohi[t], hi = lohi[F + t];
   const int c = t / chunk;
   const int slot_p = max(0, c - radius);
   const int slot_q = min(nch, c + radius + 1);
 
   // decays a_t, b_t and row exponents
-  const float* al = alpha + (long long)bh * F * D;
+  const float* dct = decay + ((long long)bh * F + t) * 2 * D;
   const int32_t* ep = bank_e + ((long long)bh * (nch + 1) + slot_p) * D;
   const int32_t* eq = bank_e + (long long)BH * (nch + 1) * D +
                       ((long long)bh * (nch + 1) + slot_q) * D;
   for (int j = tid; j < D; j += 256) {
-    float a = 1.0f, b = 1.0f;
-    for (int x = lo; x <= t; ++x) a *= al[(long long)x * D + j];
-    for (int x = t; x <= hi; ++x) b *= al[(long long)x * D + j];
-    dec[0][j] = a;
-    dec[1][j] = b;
+    dec[0][j] = dct[j];
+    dec[1][j] = dct[D + j];
     rowexp[0][j] = ep[j];
     rowexp[1][j] = eq[j];
   }
@@ -94,7 +90,7 @@ __global__ __launch_bounds__(256) void readout_kernel(
     }
 #pragma unroll
     for (int off = 1; off < TPT; off <<= 1) ss += __shfl_xor(ss, off);
-    const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    const float inv = inv_l2(ss);
 #pragma unroll
     for (int a = 0; a < RPT; ++a) qh_lds[tt][i0 + a] = qv[a] * inv;
     __syncthreads();
@@ -111,7 +107,7 @@ __global__ __launch_bounds__(256) void readout_kernel(
     for (int a = 0; a < RPT; ++a) sq = fmaf(o[a], o[a], sq);
 #pragma unroll
     for (int off = 1; off < TPT; off <<= 1) sq += __shfl_xor(sq, off);
-    const float rn = 1.0f / sqrtf(sq / (float)D + eps_s);
+    const float rn = fast_rsq(sq / (float)D + eps_s);
     if (valid) {
 #pragma unroll
       for (int a = 0; a < RPT; ++a) {
@@ -136,7 +132,7 @@ __global__ __launch_bounds__(256) void readout_kernel(
 template <int D>
 __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ gate,
-    const float* __restrict__ alpha, const int32_t* __restrict__ lohi,
+    const float* __restrict__ decay, const int32_t* __restrict__ lohi,
     const float* __restrict__ bank_p, const float* __restrict__ bank_q,
     const int32_t* __restrict__ bank_e, const float* __restrict__ rms_w,
     float eps, int accumulate, bf16_t* __restrict__ out, int F, int S,
@@ -153,21 +149,17 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
   const int t = blockIdx.y;
   const int bh = blockIdx.z;
   const int tok0 = blockIdx.x * tok_per_wg;
-  const int lo = lohi[t], hi = lohi[F + t];
   const int c = t / chunk;
   const int slot_p = max(0, c - radius);
   const int slot_q = min(nch, c + radius + 1);
 
-  const float* al = alpha + (long long)bh * F * D;
+  const float* dct = decay + ((long long)bh * F + t) * 2 * D;
   const int32_t* ep = bank_e + ((long long)bh * (nch + 1) + slot_p) * D;
   const int32_t* eq = bank_e + (long long)BH * (nch + 1) * D +
                       ((long long)bh * (nch + 1) + slot_q) * D;
   for (int j = tid; j < D; j += 256) {
-    float a = 1.0f, b = 1.0f;
-    for (int x = lo; x <= t; ++x) a *= al[(long long)x * D + j];
-    for (int x = t; x <= hi; ++x) b *= al[(long long)x * D + j];
-    dec[0][j] = a;
-    dec[1][j] = b;
+    dec[0][j] = dct[j];
+    dec[1][j] = dct[D + j];
     rowexp[0][j] = ep[j];
     rowexp[1][j] = eq[j];
     w_lds[j] = rms_w ? rms_w[j] : 1.0f;
@@ -206,17 +198,28 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
   const bf16_t* qb = q + (long long)bh * N * D;
   const bf16_t* gb = gate + (long long)bh * N * D;
   bf16_t* ob = out + (long long)bh * N * D;
+  // q of this lane's token (channels 16*kk + 8*half + 0..7), one tile ahead
+  u32x4_t qraw[D / 16];
+  auto load_q = [&](int s0) {
+    const int s = s0 + col;
+    const long long n = (long long)t * S + s;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qraw[kk] = u32x4_t{0u, 0u, 0u, 0u};
+      if (s < tok_end) qraw[kk] = *(const u32x4_t*)(qb + n * D + kk * 16 + half * 8);
+    }
+  };
+  load_q(tok0 + wave * 32);
   for (int s0 = tok0 + wave * 32; s0 < tok_end; s0 += 128) {
     const int s = s0 + col;
     const bool valid = s < tok_end;
     const long long n = (long long)t * S + s;
-    // q^ = L2(SiLU(q)) of this lane's token, channels 16*kk + 8*half + 0..7
+    // q^ = L2(SiLU(q))
     float qv[D / 16][8];
     float ss = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (valid) raw = *(const u32x4_t*)(qb + n * D + kk * 16 + half * 8);
+      const u32x4_t raw = qraw[kk];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float x0 = __uint_as_float(raw[u] << 16);
@@ -227,8 +230,9 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) ss = fmaf(qv[kk][u], qv[kk][u], ss);
     }
+    if (s0 + 128 < tok_end) load_q(s0 + 128);
     ss += __shfl_xor(ss, 32);
-    const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    const float inv = inv_l2(ss);
     f32x16_t acc[D / 32];
 #pragma unroll
     for (int ib = 0; ib < D / 32; ++ib)
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) sq = fmaf(acc[ib][r], acc[ib][r], sq);
     sq += __shfl_xor(sq, 32);
-    const float rn = 1.0f / sqrtf(sq / (float)D + eps_s);
+    const float rn = fast_rsq(sq / (float)D + eps_s);
     if (valid) {
 #pragma unroll
       for (int ib = 0; ib < D / 32; ++ib)
@@ -293,8 +297,34 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------- decays
+// a_t = prod_{j=lo_t..t} alpha_j and b_t = prod_{j=t..hi_t} alpha_j for every
+// (b, h, t) and channel, in parallel (the readout then reads 2*d floats).
+__global__ void decay_kernel(const float* __restrict__ alpha,
+                             const int32_t* __restrict__ lohi,
+                             float* __restrict__ decay, int F, int D) {
+  const int t = blockIdx.x, bh = blockIdx.y;
+  const int lo = lohi[t], hi = lohi[F + t];
+  const float* al = alpha + (long long)bh * F * D;
+  float* dst = decay + ((long long)bh * F + t) * 2 * D;
+  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+    float a = 1.0f, b = 1.0f;
+    for (int x = lo; x <= t; ++x) a *= al[(long long)x * D + j];
+    for (int x = t; x <= hi; ++x) b *= al[(long long)x * D + j];
+    dst[j] = a;
+    dst[D + j] = b;
+  }
+}
+
+hipError_t launch_decay(const Geom& g, const float* alpha, const int32_t* lohi,
+                        float* decay, hipStream_t st) {
+  hipLaunchKernelGGL(decay_kernel, dim3(g.F, g.B * g.H), dim3(g.d), 0, st,
+                     alpha, lohi, decay, g.F, g.d);
+  return hipGetLastError();
+}
+
 hipError_t launch_readout(const Geom& g, int dtype, const void* q,
-                          const void* gate, const float* alpha,
+                          const void* gate, const float* decay,
                           const int32_t* lohi, const float* bank_p,
                           const float* bank_q, const int32_t* bank_e,
                           const float* rms_weight, float rms_eps,
@@ -306,7 +336,7 @@ hipError_t launch_readout(const Geom& g, int dtype, const void* q,
     dim3 grid((g.S + per - 1) / per, g.F, g.B * g.H);
 #define RM_LAUNCH(DD)                                                         \
   hipLaunchKernelGGL(readout_mfma_kernel<DD>, grid, dim3(256), 0, st,         \
-                     (const bf16_t*)q, (const bf16_t*)gate, alpha, lohi,      \
+                     (const bf16_t*)q, (const bf16_t*)gate, decay, lohi,      \
                      bank_p, bank_q, bank_e, rms_weight, rms_eps,             \
                      (int)accumulate, (bf16_t*)out, g.F, g.S, g.chunk,        \
                      g.radius, g.nch, g.B * g.H, g.N, per)
@@ -318,7 +348,7 @@ hipError_t launch_readout(const Geom& g, int dtype, const void* q,
   dim3 grid((g.S + RO_TOK - 1) / RO_TOK, g.F, g.B * g.H);
 #define RO_LAUNCH(TT, DD)                                                     \
   hipLaunchKernelGGL((readout_kernel<TT, DD>), grid, dim3(256), 0, st,        \
-                     (const TT*)q, (const TT*)gate, alpha, lohi, bank_p,      \
+                     (const TT*)q, (const TT*)gate, decay, lohi, bank_p,      \
                      bank_q, bank_e, rms_weight, rms_eps, (int)accumulate,    \
                      (TT*)out, g.F, g.S, g.chunk, g.radius, g.nch, g.B * g.H, \
                      g.N)

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void stats_kernel(
     // L2 norm over the token's d channels: TPT consecutive lanes
 #pragma unroll
     for (int off = 1; off < TPT; off <<= 1) ss += __shfl_xor(ss, off);
-    const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    const float inv = inv_l2(ss);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       float kh = kc[i] * inv;
@@ -184,19 +184,31 @@ __global__ __launch_bounds__(4 * D) void stats_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
 
-  // causal width-4 conv of TPG tokens x 4 channels from raw rows sb-3 .. sb+TPG-1
-  auto conv4 = [&](const bf16_t* src, const float (&w)[4][4], int sb,
+  // raw rows sb-3 .. sb+TPG-1 (4 channels each) of k and v for one tile;
+  // fetched one tile ahead so the loads overlap the previous tile's MFMAs
+  uint2 kraw[TPG + 3], vraw[TPG + 3];
+  auto fetch = [&](int s0) {
+    const int sb = s0 + tg * TPG;
+#pragma unroll
+    for (int x = 0; x < TPG + 3; ++x) {
+      const int s = sb - 3 + x;
+      kraw[x] = vraw[x] = make_uint2(0u, 0u);
+      if (s >= 0 && s < S) {
+        kraw[x] = *(const uint2*)(kp + (n0 + s) * D + c0);
+        vraw[x] = *(const uint2*)(vp + (n0 + s) * D + c0);
+      }
+    }
+  };
+  // causal width-4 conv of TPG tokens x 4 channels
+  auto conv4 = [&](const uint2 (&raw)[TPG + 3], const float (&w)[4][4],
                    float (&o)[TPG][4]) {
     float r[TPG + 3][4];
 #pragma unroll
     for (int x = 0; x < TPG + 3; ++x) {
-      const int s = sb - 3 + x;
-      uint2 raw = make_uint2(0u, 0u);
-      if (s >= 0 && s < S) raw = *(const uint2*)(src + (n0 + s) * D + c0);
-      r[x][0] = __uint_as_float(raw.x << 16);
-      r[x][1] = __uint_as_float(raw.x & 0xffff0000u);
-      r[x][2] = __uint_as_float(raw.y << 16);
-      r[x][3] = __uint_as_float(raw.y & 0xffff0000u);
+      r[x][0] = __uint_as_float(raw[x].x << 16);
+      r[x][1] = __uint_as_float(raw[x].x & 0xffff0000u);
+      r[x][2] = __uint_as_float(raw[x].y << 16);
+      r[x][3] = __uint_as_float(raw[x].y & 0xffff0000u);
     }
 #pragma unroll
     for (int u = 0; u < TPG; ++u)
@@ -217,14 +229,18 @@ __global__ __launch_bounds__(4 * D) void stats_mfma_kernel(
     *(bf16x4_t*)&ls[o] = bf16x4_t{lv[0], lv[1], lv[2], lv[3]};
   };
 
+  fetch(0);
   for (int s0 = 0; s0 < S; s0 += SX_TT) {
     const int sb = s0 + tg * TPG;
     float sqb[TPG];
 #pragma unroll
-    for (int u = 0; u < TPG; ++u) sqb[u] = sb + u < S ? sqrtf(bp[n0 + sb + u]) : 0.0f;
+    for (int u = 0; u < TPG; ++u) sqb[u] = sb + u < S ? __builtin_amdgcn_sqrtf(bp[n0 + sb + u]) : 0.0f;
+    float vf[TPG][4];
+    conv4(vraw, wv, vf);
     {  // k' = sqrt(beta) L2(SiLU(conv_k(k)))
       float kf[TPG][4], ss[TPG];
-      conv4(kp, wk, sb, kf);
+      conv4(kraw, wk, kf);
+      if (s0 + SX_TT < S) fetch(s0 + SX_TT);
 #pragma unroll
       for (int u = 0; u < TPG; ++u) {
         ss[u] = 0.0f;
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(4 * D) void stats_mfma_kernel(
 #pragma unroll
         for (int u = 0; u < TPG; ++u) ss[u] += __shfl_xor(ss[u], off);
 #pragma unroll
-      for (int u = 0; u < TPG; ++u) ss[u] = sqb[u] / fmaxf(sqrtf(ss[u]), 1e-12f);
+      for (int u = 0; u < TPG; ++u) ss[u] = sqb[u] * inv_l2(ss[u]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x[TPG];
@@ -249,8 +265,6 @@ __global__ __launch_bounds__(4 * D) void stats_mfma_kernel(
       }
     }
     {  // v' = sqrt(beta) conv_v(v)
-      float vf[TPG][4];
-      conv4(vp, wv, sb, vf);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x[TPG];

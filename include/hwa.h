@@ -113,6 +113,7 @@ typedef struct {
  *                                 sana_scaled)
  *   bank_p   [B, H, n_ch+1, d, d] prefix states, slot m = P_{min(F, m*chunk)-1}
  *   bank_q   [B, H, n_ch+1, d, d] suffix states, slot m = Q_{min(F, m*chunk)}
+ *   decay    [B, H, F, 2, d]      bridge decays prod_{lo..t} alpha, prod_{t..hi} alpha
  *   bank_e   int32 [2, B, H, n_ch+1, d] power-of-two exponent of every
  *                                 state row: row i of the state = row i of the
  *                                 bank * 2^e_i (prefix then suffix; e stays 0
@@ -122,7 +123,7 @@ typedef struct {
  * n_ch = ceil(F / chunk).
  */
 typedef struct {
-  size_t lohi, stat_a, stat_b, map_m, bank_p, bank_q, bank_e, v_t;
+  size_t lohi, stat_a, stat_b, map_m, bank_p, bank_q, decay, bank_e, v_t;
   size_t total;
 } hwa_workspace_layout;
 
