@@ -22,6 +22,8 @@
 // V is read from a transposed copy V^T [B, H, d, Np] (Np = N rounded up to
 // 64, zero padded) made by vtranspose_kernel.
 
+#include <type_traits>
+
 #include "hwa_internal.h"
 
 namespace hwa {
@@ -34,6 +36,9 @@ constexpr int SM_NW = 8;                // waves per workgroup
 constexpr int SM_QT = 32 * SM_NW;       // queries per workgroup
 constexpr int SM_KT = 64;   // keys per LDS tile
 constexpr int SM_THREADS = 64 * SM_NW;
+#ifndef SM_PREFETCH
+#define SM_PREFETCH 3
+#endif
 
 __host__ __device__ inline long long round_up64(long long n) {
   return (n + 63) / 64 * 64;
@@ -113,33 +118,28 @@ __device__ __forceinline__ int perm32(int m) {
   return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 }
 
-// LDS tiles are unpadded and XOR-swizzled by 16-byte chunk: K row r keeps
-// logical chunk c at chunk c ^ swz_k(r), V^T row r at c ^ swz_v(r). The
-// swizzles make the 16 lanes of every LDS pass of an MFMA operand read hit 16
-// distinct bank groups. Tiles are copied global -> LDS by the gfx950 direct
-// load (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
+// LDS tiles are unpadded rows of 128 bytes (8 chunks of 16 bytes): V^T as
+// [d][64 keys], K as [d / 64][64 rows][64 d] where LDS row m of the key tile
+// holds key 32 * (m / 32) + perm32(m % 32). Row m keeps logical chunk c at
+// chunk c ^ swz(m). For an MFMA operand read, lane (col, half) of step j takes
+// row 32 * blk + col, chunk op_chunk(j, half); with this swizzle a wave's
+// ds_read_b128 completes in the minimum four LDS cycles on gfx950 (measured:
+// a 1 KB contiguous wave read, or the 256-byte-row layout, takes eight). The
+// contraction index d is read in the same permuted chunk order for K and Q.
+// Tiles are copied global -> LDS by the gfx950 direct load
+// (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
 // dst + 16 * l); each lane fetches the global chunk that belongs in its slot.
 //
-// Software pipeline, per wave and key tile i (K runs one tile ahead of V):
-//   issue DMA K(i+3), V(i+2);  S(i+1) = K(i+1) Q^T (MFMA) interleaved with
-//   the exp2 work of S(i);  O += V(i)^T P(i)^T;  wait for the DMA issued one
-//   step earlier; barrier.
-// Three K and three V stages (96 KB at d = 128): loads have a whole step to
-// land. Eight waves (256 queries) share every tile; one workgroup per CU.
-__device__ __forceinline__ int swz_k(int r, int chunks) {
-  return chunks == 16 ? ((r + 8 * (r >> 4)) & 15) : (((r >> 1) + 4 * (r >> 4)) & 7);
-}
-__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
-
-// s_waitcnt vmcnt(n) for a small run-time n (the immediate must be constant)
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-  }
+// Software pipeline, per key tile i (K runs two tiles ahead of V): one
+// stream of D/4 MFMA groups, S(i+1) = K(i+1) Q^T then O += V(i-1)^T P(i-1)^T,
+// carrying the exp2 work of S(i), the lane max of S(i+1) and the direct loads
+// K(i+2), V(i); then the running-max update, wait for the loads, barrier.
+// Two K and two V stages (64 KB at d = 128); the loop is unrolled by two so
+// that stage indices are compile-time. Eight waves (256 queries) share every
+// tile; one workgroup per CU (two waves per SIMD).
+__device__ __forceinline__ int swz(int m) { return (m >> 1) & 7; }
+__device__ __forceinline__ int op_chunk(int j, int half) {
+  return 2 * half + 4 * (j / 2) + (j % 2);
 }
 
 template <int D>
@@ -150,20 +150,20 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     long long Np, int tiles_per_chunk, float scale_log2) {
   // the body uses device-only lambdas; the host pass needs only the stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int KC = D / 8;          // 16-byte chunks per K row
+  constexpr int KC = D / 8;          // 16-byte chunks per key
   constexpr int VC = SM_KT / 8;      // 16-byte chunks per V^T row
   constexpr int KINS = SM_KT * KC / 64;  // DMA instructions per K tile
   constexpr int VINS = D * VC / 64;      // DMA instructions per V^T tile
   constexpr int KPW = KINS / SM_NW;      // per wave
   constexpr int VPW = VINS / SM_NW;
-  constexpr int NST = 3;                 // pipeline stages
+  constexpr int NST = 2;                 // pipeline stages
   static_assert(KINS % SM_NW == 0 && VINS % SM_NW == 0, "uniform DMA per wave");
   __shared__ __attribute__((aligned(16))) bf16_t k_lds[NST][SM_KT * D];
   __shared__ __attribute__((aligned(16))) bf16_t v_lds[NST][D * SM_KT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5;
   const int col = lane & 31;
   // XCD-aware order: workgroup p is dispatched to XCD p % 8; give each XCD a
@@ -193,47 +193,54 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   const bf16_t* kb = k + (long long)bh * N * D;
   const bf16_t* vb = vt + (long long)bh * D * Np;
 
-  // Q fragment: B operand of S^T = K Q^T, query = col, d = 16*kk + 8*half + i
+  // Q fragment: B operand of S^T = K Q^T, query = col; step kk takes the d
+  // chunk 8 * (kk / 4) + op_chunk(kk % 4, half), as the K operand does
   const long long my_q = q_tile0 + wave * 32 + col;
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 t = {0u, 0u, 0u, 0u};
-    if (my_q < N) t = *(const u32x4*)(qb + my_q * D + kk * 16 + half * 8);
+    const int dc = 8 * (kk / 4) + op_chunk(kk % 4, half);
+    if (my_q < N) t = *(const u32x4*)(qb + my_q * D + dc * 8);
     qreg[kk] = __builtin_bit_cast(bf16x8, t);
   }
 
   // per-lane DMA sources inside a tile (fixed for the whole kernel):
   // instruction wave + SM_NW*j fills slots 64*(wave + SM_NW*j) + lane
+  // per-lane element offsets inside a tile (fixed for the kernel): slot
+  // (wave + SM_NW * j) * 64 + lane holds K row k_row, column k_col, resp. V^T
+  // element v_off of the tile
   int k_row[KPW], k_col[KPW], v_off[VPW];
 #pragma unroll
   for (int j = 0; j < KPW; ++j) {
     const int slot = (wave + SM_NW * j) * 64 + lane;
-    const int r = slot / KC, pc = slot % KC;
-    k_row[j] = r;
-    k_col[j] = (pc ^ swz_k(r, KC)) * 8;
+    const int sub = slot / 512, m = (slot / 8) % 64, pc = slot % 8;
+    k_row[j] = 32 * (m / 32) + perm32(m % 32);
+    k_col[j] = (8 * sub + (pc ^ swz(m))) * 8;
   }
 #pragma unroll
   for (int j = 0; j < VPW; ++j) {
     const int slot = (wave + SM_NW * j) * 64 + lane;
     const int r = slot / VC, pc = slot % VC;
-    v_off[j] = r * (int)Np + (pc ^ swz_v(r)) * 8;
+    v_off[j] = r * (int)Np + (pc ^ swz(r)) * 8;
   }
-  auto dma_k = [&] __device__(long long kt0, int st) {
-    const bool whole = kt0 + SM_KT <= N;
+  // direct loads of the K (resp. V^T) tile at key kt0 into stage st; K rows
+  // past N (last tile of the last chunk) are clamped to N - 1: they are
+  // masked or never read
+  auto dma_k = [&] __device__(long long kt0, int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
       long long n = kt0 + k_row[j];
-      if (!whole) n = n < N ? n : N - 1;  // rows past N: any valid row, masked
-      __builtin_amdgcn_global_load_lds(kb + n * D + k_col[j],
-                                       &k_lds[st][(wave + SM_NW * j) * 512], 16, 0, 0);
+      n = n < N ? n : N - 1;
+      __builtin_amdgcn_global_load_lds(kb + n * D + k_col[j], &k_lds[st][(wave + SM_NW * j) * 512],
+                                       16, 0, 0);
     }
   };
-  auto dma_v = [&] __device__(long long kt0, int st) {
+  auto dma_v = [&] __device__(long long kt0, int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < VPW; ++j)
-      __builtin_amdgcn_global_load_lds(vb + kt0 + v_off[j],
-                                       &v_lds[st][(wave + SM_NW * j) * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + kt0 + v_off[j], &v_lds[st][(wave + SM_NW * j) * 512],
+                                       16, 0, 0);
   };
 
   f32x16 acc_o[D / 32];
@@ -250,132 +257,209 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // LDS operand reads: K row (blk*32 + perm32(col)), logical chunk 2*kk + half;
-  // V^T row (dblk*32 + col), logical chunk 2*half + 4*(j/2) + (j%2)
-  const int kr0 = perm32(col), kr1 = 32 + perm32(col);
-  const int ksw0 = swz_k(kr0, KC), ksw1 = swz_k(kr1, KC);
-  auto kop = [&] __device__(int st, int blk, int kk) {
-    const int r = blk ? kr1 : kr0, sw = blk ? ksw1 : ksw0;
-    return *(const bf16x8*)&k_lds[st][r * D + (((2 * kk + half) ^ sw) * 8)];
+  // LDS operand offsets (elements): step j of lane (col, half) reads row col,
+  // chunk op_chunk(j, half) ^ swz(col) of a 32-row block of 128-byte rows;
+  // K block blk, part kk / 4 and V^T block dblk add constant offsets, so each
+  // operand read is one ds_read_b128 with a per-lane address and an immediate
+  // offset (stage bases are compile-time: the loop is unrolled over stages)
+  int voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) voff[j] = col * 64 + ((op_chunk(j, half) ^ swz(col)) * 8);
+  auto k_op = [&] __device__(const bf16_t* ks, int blk, int kk) __attribute__((always_inline)) {
+    return *(const bf16x8*)(ks + (kk / 4) * (SM_KT * 64) + blk * (32 * 64) + voff[kk % 4]);
   };
-  auto vop = [&] __device__(int st, int dblk, int j) {
-    const int r = dblk * 32 + col;
-    const int lc = 2 * half + 4 * (j / 2) + (j % 2);
-    return *(const bf16x8*)&v_lds[st][r * SM_KT + ((lc ^ swz_v(r)) * 8)];
+  auto v_op = [&] __device__(const bf16_t* vs, int dblk, int j) __attribute__((always_inline)) {
+    return *(const bf16x8*)(vs + dblk * (32 * SM_KT) + voff[j]);
   };
-  auto qk = [&] __device__(int st, f32x16 (&sv)[2]) {
+  auto qk_full = [&] __device__(const bf16_t* ks, f32x16 (&sv)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[blk][r] = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk)
-        sv[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop(st, blk, kk), qreg[kk],
-                                                          sv[blk], 0, 0, 0);
+        sv[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            k_op(ks, blk, kk), qreg[kk], sv[blk], 0, 0, 0);
     }
   };
 
   const long long kt_first = k_begin / SM_KT * SM_KT;
   const int ntiles = (int)((k_end - kt_first + SM_KT - 1) / SM_KT);
 
-  // one pipeline step: consumes scores sc of tile it, produces sn of tile it+1
-  auto step = [&] __device__(int it, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    const int sv = it % NST;            // V(it)
-    const int sk = (it + 1) % NST;      // K(it+1)
-    const long long kt0 = kt_first + (long long)it * SM_KT;
-    int issued = 0;
-    if (it + 3 < ntiles) { dma_k(kt0 + 3 * SM_KT, it % NST); issued += KPW; }
-    if (it + 2 < ntiles) { dma_v(kt0 + 2 * SM_KT, (it + 2) % NST); issued += VPW; }
-    // ---- mask keys outside [k_begin, k_end) (first and last tile only)
-    if (kt0 < k_begin || kt0 + SM_KT > k_end) {
+  // keys of tile `it` outside [k_begin, k_end) score -inf (first and last
+  // tile only); returns whether the tile needed it
+  auto mask = [&] __device__(int it, f32x16 (&sv)[2]) __attribute__((always_inline)) {
+    const int lo_rel = (int)(k_begin - kt_first) - it * SM_KT;  // keys before lo_rel and
+    const int hi_rel = (int)(k_end - kt_first) - it * SM_KT;    // from hi_rel on are out
+    if (lo_rel <= 0 && hi_rel >= SM_KT) return false;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const long long key = kt0 + blk * 32 + half * 16 + r;
-          if (key < k_begin || key >= k_end) sc[blk][r] = -INFINITY;
-        }
-    }
-    // ---- running max of S(i); m_run may lag the true one by up to 2^8 in
-    // exp2 units (p <= 256 stays exact) and moves only past that lag, so
-    // the O rescale below is rare
-    float mx = fmaxf(sc[0][0], sc[1][0]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = blk * 32 + half * 16 + r;
+        if (key < lo_rel || key >= hi_rel) sv[blk][r] = -INFINITY;
+      }
+    return true;
+  };
+  auto lane_max = [&] __device__(const f32x16 (&sv)[2]) __attribute__((always_inline)) {
+    float mx = fmaxf(sv[0][0], sv[0][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sc[0][r]), sc[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int e = 1; e < 16; ++e) mx = fmaxf(fmaxf(mx, sv[e / 8][(2 * e) % 16]), sv[e / 8][(2 * e) % 16 + 1]);
+    return mx;
+  };
+  // running max from a lane's partial max over its 32 scores of a tile (the
+  // lane pair l, l ^ 32 shares the query): m_run moves only when the tile max
+  // passes it by more than the lag; corr rescales l_run now and O after the
+  // next PV, when `moved`
+  float corr = 1.0f;
+  bool moved = false;
+  auto update_max = [&] __device__(float mx) __attribute__((always_inline)) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float m_new = mx > m_run + lag ? fmaxf(m_run, mx) : m_run;
-    const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+    corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    moved = m_new != m_run;
+    m_run = m_new;
+    l_run *= corr;
+  };
+
+  // One pipeline step i (stage indices are compile-time: SI = i % 2), one
+  // stream of D/4 MFMA groups: S(i+1) = K(i+1) Q^T (D/8 groups), then
+  // O += V(i-1)^T P(i-1)^T (D/8 groups, consecutive ones on different
+  // accumulators). Riding on the groups: the 16 probability pairs of S(i)
+  // (exp2, bf16 P(i), row sums), the direct loads K(i+2) -> K[i%2] and
+  // V(i) -> V[i%2] (needed in step i+1), and the lane max of S(i+1) once its
+  // MFMAs are done. Then: the pending O rescale (after PV(i-1)), the running
+  // max update for S(i+1), wait for this step's loads, barrier.
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  constexpr int NQK = D / 8, NG = D / 4, EVERY = NG / 16;
+  static_assert(NG % 16 == 0, "16 probability pairs over the MFMA groups");
+  constexpr int G_MAX = NQK + 2;  // first group that reads the finished S(i+1)
+  constexpr int PF = SM_PREFETCH;
+  auto step = [&] __device__(auto si_tag, int it, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                             bf16x8 (&pp)[4], bf16x8 (&pc)[4])
+                   __attribute__((always_inline)) {
+    constexpr int SI = decltype(si_tag)::value;
+    constexpr int SO = SI ^ 1;  // K(i+1) and V(i-1)
+    const long long kt0 = kt_first + (long long)it * SM_KT;
+    const bf16_t* ks = &k_lds[SO][0];
+    const bf16_t* vs = &v_lds[SO][0];
+    const float mb = m_run * scale_log2;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[blk][r] = 0.0f;
+    float mx = -INFINITY;
+    // operands are read PF groups ahead of their MFMA
+    bf16x8 opa[PF + 1];
+    auto op_read = [&] __device__(int gn) __attribute__((always_inline)) {
+      if (gn < NQK) return k_op(ks, gn % 2, gn / 2);
+      return v_op(vs, (gn - NQK) % (D / 32), (gn - NQK) / (D / 32));
+    };
+#pragma unroll
+    for (int g = 0; g < PF; ++g) opa[g] = op_read(g);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      // operand read for group g + PF (QK groups 0..NQK-1, PV groups after)
+      if (g + PF < NG) opa[(g + PF) % (PF + 1)] = op_read(g + PF);
+      // this step's direct loads: waves 0..3 issue theirs with group 0, waves
+      // 4..7 at mid-step, so the eight waves' loads do not queue up at once
+      // (K(i+2) past the last tile loads rows that nothing reads)
+      if (g == 0 || g == NG / 2) {
+        if ((wave < SM_NW / 2) == (g == 0)) {
+          dma_k(kt0 + 2 * SM_KT, SI);
+          dma_v(kt0, SI);
+        }
+      }
+      if (g < NQK) {
+        sn[g % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[g % (PF + 1)], qreg[g / 2],
+                                                            sn[g % 2], 0, 0, 0);
+      } else {  // PV(i-1); in step 0 it multiplies P = 0 by a zeroed stage
+        const int dblk = (g - NQK) % (D / 32), j = (g - NQK) / (D / 32);
+        acc_o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[g % (PF + 1)], pp[j],
+                                                              acc_o[dblk], 0, 0, 0);
+      }
+      if (g % EVERY == EVERY - 1) {
+        const int e = g / EVERY, blk = e / 8, r = (e % 8) * 2;
+        // the empty volatile asm statements pin this pair between the MFMAs of
+        // its group: instruction selection may otherwise move pure arithmetic
+        // across the (memory-ordered) scheduling barriers
+        float s0 = sc[blk][r], s1 = sc[blk][r + 1];
+        asm volatile("" : "+v"(s0), "+v"(s1));
+        const f32x2 e2 = {__builtin_amdgcn_exp2f(fmaf(s0, scale_log2, -mb)),
+                          __builtin_amdgcn_exp2f(fmaf(s1, scale_log2, -mb))};
+        bf16x2_t p2 = __builtin_convertvector(e2, bf16x2_t);
+        asm volatile("" : "+v"(p2));
+        pc[blk * 2 + r / 8][r % 8] = p2[0];
+        pc[blk * 2 + r / 8][r % 8 + 1] = p2[1];
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
+      }
+      if (g >= G_MAX) {  // lane max of S(i+1): 16 pairs over groups G_MAX..NG-1
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (G_MAX + (e * (NG - G_MAX)) / 16 == g)
+            mx = fmaxf(fmaxf(mx, sn[e / 8][(2 * e) % 16]), sn[e / 8][(2 * e) % 16 + 1]);
+        asm volatile("" : "+v"(mx));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- rare: rescale O (which now includes PV(i-1)) when the max moved
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[j][r] *= corr;
     }
-    m_run = m_new;
-    l_run *= corr;
-    const float mb = m_run * scale_log2;
-
-    // ---- the MFMAs of S(i+1) (on the last tile they read a stale stage and
-    // are discarded) interleaved by hand with exp2 of S(i): group g issues
-    // the LDS read of the K operand of group g + 2, the MFMA of group g and
-    // one pair of probabilities (2 exp2, bf16 pack, row-sum dot2); the
-    // sched_barrier fences keep the compiler from regrouping them, so the
-    // VALU work fills the MFMA pipeline's issue gaps.
-    constexpr int NG = 2 * (D / 16);  // QK MFMAs per tile (16 at d = 128)
-    bf16x8 ka[3];
-    ka[0] = kop(sk, 0, 0);
-    ka[1] = kop(sk, 1, 0);
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sn[blk][r] = 0.0f;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {  // g: blk = g % 2, kk = g / 2
-      if (g + 2 < NG) ka[(g + 2) % 3] = kop(sk, (g + 2) % 2, (g + 2) / 2);
-      sn[g % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g % 3], qreg[g / 2],
-                                                          sn[g % 2], 0, 0, 0);
-#pragma unroll
-      for (int e = g * 16 / NG; e < (g + 1) * 16 / NG; ++e) {
-        const int blk = e / 8, r = (e % 8) * 2;
-        const f32x2 e2 = {
-            __builtin_amdgcn_exp2f(fmaf(sc[blk][r], scale_log2, -mb)),
-            __builtin_amdgcn_exp2f(fmaf(sc[blk][r + 1], scale_log2, -mb))};
-        const bf16x2 p2 = __builtin_convertvector(e2, bf16x2);
-        pb[blk * 2 + r / 8][r % 8] = p2[0];
-        pb[blk * 2 + r / 8][r % 8 + 1] = p2[1];
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < ntiles) {
+      if (mask(it + 1, sn)) mx = lane_max(sn);  // first or last tile only
+      update_max(mx);
     }
-    // ---- O^T += V^T P^T: P block j holds keys 32*(j/2) + 16*half + 8*(j%2) + i
-#pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc_o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            vop(sv, dblk, j), pb[j], acc_o[dblk], 0, 0, 0);
-    // the loads issued one step earlier are needed by the next step
-    wait_vmcnt(issued);
+    // this step's loads are needed by the next step
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
-  // prologue: K(0), V(0), K(1) land first; K(2), V(1) stay in flight
+  // prologue: K(0), K(1) land; S(0) and its max
   f32x16 sa[2], sb[2];
+  bf16x8 pa[4], pb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pb[j][u] = (__bf16)0.0f;  // P(-1)
+  // V stage 1 is read (times P = 0) by step 0's PV: make it finite
+  for (int x = tid; x < D * SM_KT / 8; x += SM_THREADS)
+    *(u32x4*)&v_lds[1][x * 8] = u32x4{0u, 0u, 0u, 0u};
   dma_k(kt_first, 0);
-  dma_v(kt_first, 0);
   if (ntiles > 1) dma_k(kt_first + SM_KT, 1);
-  int pend = 0;
-  if (ntiles > 2) { dma_k(kt_first + 2 * SM_KT, 2); pend += KPW; }
-  if (ntiles > 1) { dma_v(kt_first + SM_KT, 1); pend += VPW; }
-  wait_vmcnt(pend);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  qk(0, sa);
+  qk_full(&k_lds[0][0], sa);
   __syncthreads();  // K stage 0 is refilled in step 0
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, sa, sb);
-    if (it + 1 >= ntiles) break;
-    step(it + 1, sb, sa);
+  mask(0, sa);
+  update_max(lane_max(sa));
+  typedef std::integral_constant<int, 0> S0;
+  typedef std::integral_constant<int, 1> S1;
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(S0{}, it, sa, sb, pb, pa);
+    step(S1{}, it + 1, sb, sa, pa, pb);
+  }
+  if (it < ntiles) step(S0{}, it, sa, sb, pb, pa);
+  // drain: O += V(last)^T P(last)^T (P of even tiles is in pa, odd in pb)
+  {
+    const int last = ntiles - 1;
+    const bf16_t* vs = &v_lds[last % NST][0];
+    auto drain = [&] __device__(const bf16x8(&pl)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc_o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_op(vs, dblk, j), pl[j],
+                                                                acc_o[dblk], 0, 0, 0);
+    };
+    if (last % 2 == 0) drain(pa);
+    else drain(pb);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
