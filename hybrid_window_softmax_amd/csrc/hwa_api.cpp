@@ -46,6 +46,8 @@ bool make_geom(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
   g.N = (long long)frames * tokens_per_frame;
   // grid dimensions and 32-bit launch parameters stay in range
   if (g.N > (1LL << 31) / 2 || (long long)g.B * g.H > 65535) return false;
+  // bf16 softmax tiles are fetched with 32-bit byte offsets inside one head
+  if (p->dtype == HWA_BF16 && ((g.N + 63) / 64 * 64) * g.d * 2 > (1LL << 31) - 1) return false;
   // one-dimensional softmax grid: query tiles x chunks x heads x batch
   if ((long long)((g.chunk * (long long)g.S + 127) / 128) * g.nch * g.B * g.H >
       (1LL << 31) - 1)

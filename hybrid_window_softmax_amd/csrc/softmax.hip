@@ -26,6 +26,17 @@
 
 #include "hwa_internal.h"
 
+// MUBUF direct load global -> LDS (buffer_load_dword* ... lds): lane l of a
+// wave writes its bytes at the LDS address in M0 + 16 * l (dwordx4); lanes
+// whose offset lies past the descriptor's num_records read zeros. Unlike the
+// FLAT-encoded global_load_lds, it is not counted as an LDS access by the
+// compiler's wait-count tracking, so waits for ds_read results stay counted.
+typedef int hwa_i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void hwa_raw_buffer_load_lds(hwa_i32x4 rsrc,
+                                                   __attribute__((address_space(3))) void* lds,
+                                                   int size, int voffset, int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 namespace hwa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -207,40 +218,53 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
 
   // per-lane DMA sources inside a tile (fixed for the whole kernel):
   // instruction wave + SM_NW*j fills slots 64*(wave + SM_NW*j) + lane
-  // per-lane element offsets inside a tile (fixed for the kernel): slot
-  // (wave + SM_NW * j) * 64 + lane holds K row k_row, column k_col, resp. V^T
-  // element v_off of the tile
-  int k_row[KPW], k_col[KPW], v_off[VPW];
+  // per-lane byte offsets inside a tile (fixed for the kernel): slot
+  // (wave + SM_NW * j) * 64 + lane holds K row k_row, column k_col, resp. the
+  // V^T element at row r, column chunk c of the tile
+  int k_off[KPW], v_off[VPW];
 #pragma unroll
   for (int j = 0; j < KPW; ++j) {
     const int slot = (wave + SM_NW * j) * 64 + lane;
     const int sub = slot / 512, m = (slot / 8) % 64, pc = slot % 8;
-    k_row[j] = 32 * (m / 32) + perm32(m % 32);
-    k_col[j] = (8 * sub + (pc ^ swz(m))) * 8;
+    const int k_row = 32 * (m / 32) + perm32(m % 32);
+    const int k_col = (8 * sub + (pc ^ swz(m))) * 8;
+    k_off[j] = (k_row * D + k_col) * 2;
   }
 #pragma unroll
   for (int j = 0; j < VPW; ++j) {
     const int slot = (wave + SM_NW * j) * 64 + lane;
     const int r = slot / VC, pc = slot % VC;
-    v_off[j] = r * (int)Np + (pc ^ swz(r)) * 8;
+    v_off[j] = (r * (int)Np + (pc ^ swz(r)) * 8) * 2;
   }
-  // direct loads of the K (resp. V^T) tile at key kt0 into stage st; K rows
-  // past N (last tile of the last chunk) are clamped to N - 1: they are
-  // masked or never read
+  // buffer descriptor of a tile: base at the tile's first byte, num_records =
+  // bytes left in this head (clamped to 32 bits), so K rows past N read zeros
+  // (they are masked or never read); all fields wave-uniform
+  auto tile_rsrc = [&] __device__(const bf16_t* head, long long head_elems, long long first)
+                       __attribute__((always_inline)) {
+    const unsigned long long base = (unsigned long long)(head + first);
+    const long long left = (head_elems - first) * 2;
+    hwa_i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)(base & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(base >> 32));  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane(
+        (int)(unsigned)(left <= 0 ? 0 : (left > 0xfffffff0LL ? 0xfffffff0LL : left)));
+    r[3] = 0x00020000;  // raw buffer, 32-bit data format
+    return r;
+  };
+  // direct loads of the K (resp. V^T) tile at key kt0 into stage st
   auto dma_k = [&] __device__(long long kt0, int st) __attribute__((always_inline)) {
+    const hwa_i32x4 rs = tile_rsrc(kb, N * D, kt0 * D);
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      long long n = kt0 + k_row[j];
-      n = n < N ? n : N - 1;
-      __builtin_amdgcn_global_load_lds(kb + n * D + k_col[j], &k_lds[st][(wave + SM_NW * j) * 512],
-                                       16, 0, 0);
-    }
+    for (int j = 0; j < KPW; ++j)
+      hwa_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&k_lds[st][(wave + SM_NW * j) * 512],
+                              16, k_off[j], 0, 0, 0);
   };
   auto dma_v = [&] __device__(long long kt0, int st) __attribute__((always_inline)) {
+    const hwa_i32x4 rs = tile_rsrc(vb, (long long)D * Np, kt0);
 #pragma unroll
     for (int j = 0; j < VPW; ++j)
-      __builtin_amdgcn_global_load_lds(vb + kt0 + v_off[j], &v_lds[st][(wave + SM_NW * j) * 512],
-                                       16, 0, 0);
+      hwa_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&v_lds[st][(wave + SM_NW * j) * 512],
+                              16, v_off[j], 0, 0, 0);
   };
 
   f32x16 acc_o[D / 32];

@@ -29,6 +29,8 @@ HWA_ERR_INVALID_ARG = 1
 HWA_ERR_UNSUPPORTED = 2
 HWA_ERR_WORKSPACE = 3
 HWA_ERR_HIP = 4
+HWA_F32 = 0
+HWA_BF16 = 1
 
 EXPORTS = ("hybrid_attn_fwd", "hwa_workspace_bytes", "hwa_get_workspace_layout",
            "hwa_window_bounds", "hwa_text_state", "hwa_text_state_workspace_bytes",

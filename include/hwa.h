@@ -136,7 +136,8 @@ typedef struct {
  *   alpha      [B, H, F, d]  fp32   per-frame, per-key-channel forget gate
  *   gate       [B, H, N, d]  dtype  output-gate pre-activation (sigmoid)
  *   text_state [B, H, d, d]  fp32   S_text (d_v x d_k) or NULL (zero start)
- *   frames, tokens_per_frame        F >= 1, S >= 1
+ *   frames, tokens_per_frame        F >= 1, S >= 1, N = F * S <= 2^30; with
+ *                                   bf16, roundup(N, 64) * d * 2 < 2^31 too
  *   chunk, radius                   chunk >= 1, radius >= 0
  *   rule                            hwa_rule
  *   out        [B, H, N, d]  dtype  written; must not alias any input

@@ -119,6 +119,10 @@ def test_argument_validation_codes():
     assert _call(pf) == E.HWA_ERR_INVALID_ARG
     assert _call(_with_ws(_params(rms_eps=0.0))) == E.HWA_ERR_INVALID_ARG
     assert _call(_with_ws(_params(c=float("nan")))) == E.HWA_ERR_INVALID_ARG
+    # bf16 tiles use 32-bit byte offsets within a head: roundup(N, 64) * d * 2 < 2^31
+    pb = _with_ws(_params(head_dim=128, dtype=hwa.HWA_BF16))
+    assert _call(pb, F=2048, S=4096) == E.HWA_ERR_INVALID_ARG     # 2^23 tokens
+    assert _call(pb, F=2048, S=4095) == E.HWA_ERR_WORKSPACE       # in range, small workspace
     # softmax-only needs no linear-branch inputs but still a workspace
     ps = _params(flags=hwa.FLAG_SOFTMAX_ONLY)
     assert _call(ps, beta=None, alpha=None, gate=None) == E.HWA_ERR_WORKSPACE
