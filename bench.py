@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--rule", default="vdn_solve")
     ap.add_argument("--cpu-heads", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (three times), the "
+                         "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -134,6 +137,16 @@ def main():
 
     import torch
     from hybrid_window_softmax_amd import hwa, inputs
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
+        return
 
     cfg = inputs.CONFIGS[args.config]
     log(f"bench: generating config {args.config} ({cfg['name']})")
