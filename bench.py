@@ -64,7 +64,12 @@ def algorithmic_work(cfg):
         "inverse": dict(bytes=2 * mat, flops=2 * d * d * d * B * H * F),
         "scan": dict(bytes=4 * mat + 2 * B * H * F * d * 4 + 2 * bank,
                      flops=2 * 2 * d * d * d * B * H * F),
+        "decay": dict(bytes=B * H * F * d * 4 * 3, flops=0),
         "readout": dict(bytes=4 * tok * d * io + 2 * bank, flops=2 * d * d * tok),
+        # bf16 calls fuse the readout into the softmax kernel's epilogue: q and
+        # out are not re-read, the gate and the banks are
+        "softmax+readout": dict(bytes=4 * tok * d * io + tok * d * io + 2 * bank,
+                                flops=4 * d * window_pairs(cfg) * B * H + 2 * d * d * tok),
     }
 
 
@@ -197,6 +202,12 @@ def main():
     log("bench: stage ms " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()))
 
     work = algorithmic_work(cfg)
+    fused = bf  # the library fuses the readout into the softmax on bf16 (no q_rope)
+    if fused:
+        work["softmax"] = work.pop("softmax+readout")
+        work.pop("readout")
+    else:
+        work.pop("softmax+readout")
     kernels = {}
     for name, w in work.items():
         sec = stage[name] / 1000.0
@@ -210,7 +221,8 @@ def main():
         kernels[name] = rec
     sm_flops = work["softmax"]["flops"]
     achieved = sm_flops / (stage["softmax"] / 1000.0) / 1e12
-    roofline = {"kernel": "softmax_bf16_kernel", "bound": "mfma",
+    roofline = {"kernel": "softmax_bf16_kernel" + (" (readout fused)" if fused else ""),
+                "bound": "mfma",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": softmax_traffic(),

@@ -212,38 +212,47 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   auto mark = [&](int i) {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
   };
+  // the linear branch first, so that on bf16 the softmax kernel can add its
+  // readout in the epilogue (raw q only: no RoPE'd q on that path)
+  const bool fuse = do_sm && do_lin && p->dtype == HWA_BF16 && qs == q;
   if (mark(0) != hipSuccess) return HWA_ERR_HIP;
   if (hwa::launch_window_table(g, lohi, st) != hipSuccess) return HWA_ERR_HIP;
   if (mark(1) != hipSuccess) return HWA_ERR_HIP;
-  if (do_sm && p->dtype == HWA_BF16 &&
-      hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
-    return HWA_ERR_HIP;
-  if (mark(2) != hipSuccess) return HWA_ERR_HIP;
-  if (do_sm && hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out,
-                                   st) != hipSuccess)
-    return HWA_ERR_HIP;
-  if (mark(3) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && hwa::launch_stats(g, p->dtype, k, v, beta, p->conv_k,
                                   p->conv_v, true, A, Bm, st) != hipSuccess)
     return HWA_ERR_HIP;
-  if (mark(4) != hipSuccess) return HWA_ERR_HIP;
+  if (mark(2) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && rule != HWA_RULE_SANA_SCALED) {
     const float cc = rule == HWA_RULE_VDN_SCALED ? p->c : 1.0f;
     if (hwa::launch_inverse(g, cc * cc, A, M, st) != hipSuccess)
       return HWA_ERR_HIP;
   }
-  if (mark(5) != hipSuccess) return HWA_ERR_HIP;
+  if (mark(3) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && hwa::launch_scan(g, p->dtype, rule, p->c, A, Bm, M, alpha,
                                  text_state, p->text_scale, bank_p, bank_q,
                                  bank_e, st) != hipSuccess)
     return HWA_ERR_HIP;
+  if (mark(4) != hipSuccess) return HWA_ERR_HIP;
+  if (do_lin && hwa::launch_decay(g, alpha, lohi, decay, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(5) != hipSuccess) return HWA_ERR_HIP;
+  if (do_sm && p->dtype == HWA_BF16 &&
+      hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
+    return HWA_ERR_HIP;
   if (mark(6) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && (hwa::launch_decay(g, alpha, lohi, decay, st) != hipSuccess ||
-                 hwa::launch_readout(g, p->dtype, q, gate, decay, lohi, bank_p,
-                                     bank_q, bank_e, p->rms_weight, p->rms_eps,
-                                     do_sm, out, st) != hipSuccess))
+  const hwa::ReadoutArgs ra{(const bf16_t*)gate, decay, bank_p, bank_q, bank_e,
+                            p->rms_weight, p->rms_eps, g.F, g.chunk, g.radius,
+                            g.nch, g.B * g.H};
+  if (do_sm && hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out, st,
+                                   fuse ? &ra : nullptr) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(7) != hipSuccess) return HWA_ERR_HIP;
+  if (do_lin && !fuse &&
+      hwa::launch_readout(g, p->dtype, q, gate, decay, lohi, bank_p, bank_q,
+                          bank_e, p->rms_weight, p->rms_eps, do_sm, out,
+                          st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(8) != hipSuccess) return HWA_ERR_HIP;
   return HWA_OK;
 }
 

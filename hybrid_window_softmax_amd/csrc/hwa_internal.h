@@ -82,9 +82,26 @@ __device__ __forceinline__ void window_of(int t, int F, int chunk, int radius,
 // Each returns hipGetLastError() after its launch(es).
 hipError_t launch_window_table(const Geom& g, int32_t* lohi, hipStream_t st);
 
+// Per-call inputs of the linear-branch readout (device pointers; bank_e holds
+// the power-of-two exponents of the prefix bank rows, then the suffix's)
+struct ReadoutArgs {
+  const bf16_t* gate;
+  const float* decay;  // [B*H, F, 2, d]: a_t then b_t
+  const float* bank_p;
+  const float* bank_q;
+  const int32_t* bank_e;
+  const float* rms_w;  // [d] or null (ones)
+  float eps;
+  int F, chunk, radius, nch, BH;
+};
+
+// fuse != null (bf16 only): the softmax kernel also adds the linear-branch
+// readout y = RMSNorm(S_t q^) * sigmoid(gate) of its queries (q must then be
+// the raw q) before it writes out.
 hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
-                          const int32_t* lohi, void* out, hipStream_t st);
+                          const int32_t* lohi, void* out, hipStream_t st,
+                          const ReadoutArgs* fuse = nullptr);
 
 hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
                              hipStream_t st);

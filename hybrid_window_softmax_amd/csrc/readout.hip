@@ -11,6 +11,7 @@
 // and eps scaled by 2^-2E), then streams its tokens 16 at a time.
 
 #include "hwa_internal.h"
+#include "readout_core.h"
 
 namespace hwa {
 
@@ -123,81 +124,29 @@ __global__ __launch_bounds__(256) void readout_kernel(
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
-// bf16 I/O: o = S_t q^ as a split-bf16 MFMA product (v_mfma_f32_32x32x16_bf16,
-// hi*hi + hi*lo + lo*hi). S_t (hi, lo) sits in LDS as the A operand (rows =
-// output channels); every lane forms q^ of one token in registers as the B
-// operand (token = lane % 32, the two lane halves hold alternate 8-channel
-// groups). The output block then holds one token per lane, so RMSNorm needs
-// one exchange between the lane halves.
+// A workgroup takes up to 1024 tokens of one frame: it forms S_t once in LDS,
+// then each wave streams 32 tokens at a time, q of its next tokens loaded
+// while the current ones go through the MFMAs (readout_core.h).
 template <int D>
 __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ gate,
-    const float* __restrict__ decay, const int32_t* __restrict__ lohi,
-    const float* __restrict__ bank_p, const float* __restrict__ bank_q,
-    const int32_t* __restrict__ bank_e, const float* __restrict__ rms_w,
-    float eps, int accumulate, bf16_t* __restrict__ out, int F, int S,
-    int chunk, int radius, int nch, int BH, long long N, int tok_per_wg) {
-  constexpr int SP = D + 8;  // padded LDS row (bf16)
-  __shared__ __attribute__((aligned(16))) bf16_t st_hi[D * SP];
-  __shared__ __attribute__((aligned(16))) bf16_t st_lo[D * SP];
-  __shared__ float dec[2][D];
-  __shared__ int rowexp[2][D];
-  __shared__ float w_lds[D];
-  __shared__ int emax_s;
-
+    const bf16_t* __restrict__ q, ReadoutArgs a, int accumulate, bf16_t* __restrict__ out,
+    int S, long long N, int tok_per_wg) {
+  __shared__ ReadoutLds<D> L;
   const int tid = threadIdx.x;
   const int t = blockIdx.y;
   const int bh = blockIdx.z;
   const int tok0 = blockIdx.x * tok_per_wg;
-  const int c = t / chunk;
-  const int slot_p = max(0, c - radius);
-  const int slot_q = min(nch, c + radius + 1);
-
-  const float* dct = decay + ((long long)bh * F + t) * 2 * D;
-  const int32_t* ep = bank_e + ((long long)bh * (nch + 1) + slot_p) * D;
-  const int32_t* eq = bank_e + (long long)BH * (nch + 1) * D +
-                      ((long long)bh * (nch + 1) + slot_q) * D;
-  for (int j = tid; j < D; j += 256) {
-    dec[0][j] = dct[j];
-    dec[1][j] = dct[D + j];
-    rowexp[0][j] = ep[j];
-    rowexp[1][j] = eq[j];
-    w_lds[j] = rms_w ? rms_w[j] : 1.0f;
-  }
-  if (tid == 0) emax_s = INT32_MIN;
-  __syncthreads();
-  if (tid < D) atomicMax(&emax_s, max(rowexp[0][tid], rowexp[1][tid]));
-  __syncthreads();
-  const int E = emax_s;
-  const float* Pm = bank_p + ((long long)bh * (nch + 1) + slot_p) * D * D;
-  const float* Qm = bank_q + ((long long)bh * (nch + 1) + slot_q) * D * D;
-  for (int x = tid * 4; x < D * D; x += 256 * 4) {
-    const int i = x / D, j = x % D;
-    const float4 pv = *(const float4*)&Pm[x];
-    const float4 qv = *(const float4*)&Qm[x];
-    const int sp = rowexp[0][i] - E, sq = rowexp[1][i] - E;
-    const float v4[4] = {
-        ldexpf(pv.x, sp) * dec[0][j] + ldexpf(qv.x, sq) * dec[1][j],
-        ldexpf(pv.y, sp) * dec[0][j + 1] + ldexpf(qv.y, sq) * dec[1][j + 1],
-        ldexpf(pv.z, sp) * dec[0][j + 2] + ldexpf(qv.z, sq) * dec[1][j + 2],
-        ldexpf(pv.w, sp) * dec[0][j + 3] + ldexpf(qv.w, sq) * dec[1][j + 3]};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      __bf16 h, l;
-      split_bf16(v4[u], h, l);
-      st_hi[i * SP + j + u] = __builtin_bit_cast(bf16_t, h);
-      st_lo[i * SP + j + u] = __builtin_bit_cast(bf16_t, l);
-    }
-  }
-  const float eps_s = ldexpf(eps, -2 * E);
-  __syncthreads();
+  const float eps_s = build_st<D, 256>(L, a, bh, t, tid);
 
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int tok_end = min(S, tok0 + tok_per_wg);
   const bf16_t* qb = q + (long long)bh * N * D;
-  const bf16_t* gb = gate + (long long)bh * N * D;
+  const bf16_t* gb = a.gate + (long long)bh * N * D;
   bf16_t* ob = out + (long long)bh * N * D;
+  int qcol[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) qcol[kk] = kk * 16 + half * 8;
   // q of this lane's token (channels 16*kk + 8*half + 0..7), one tile ahead
   u32x4_t qraw[D / 16];
   auto load_q = [&](int s0) {
@@ -206,94 +155,23 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       qraw[kk] = u32x4_t{0u, 0u, 0u, 0u};
-      if (s < tok_end) qraw[kk] = *(const u32x4_t*)(qb + n * D + kk * 16 + half * 8);
+      if (s < tok_end) qraw[kk] = *(const u32x4_t*)(qb + n * D + qcol[kk]);
     }
   };
   load_q(tok0 + wave * 32);
   for (int s0 = tok0 + wave * 32; s0 < tok_end; s0 += 128) {
     const int s = s0 + col;
-    const bool valid = s < tok_end;
     const long long n = (long long)t * S + s;
-    // q^ = L2(SiLU(q))
-    float qv[D / 16][8];
-    float ss = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const u32x4_t raw = qraw[kk];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float x0 = __uint_as_float(raw[u] << 16);
-        const float x1 = __uint_as_float(raw[u] & 0xffff0000u);
-        qv[kk][2 * u] = silu_f(x0);
-        qv[kk][2 * u + 1] = silu_f(x1);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) ss = fmaf(qv[kk][u], qv[kk][u], ss);
-    }
-    if (s0 + 128 < tok_end) load_q(s0 + 128);
-    ss += __shfl_xor(ss, 32);
-    const float inv = inv_l2(ss);
-    f32x16_t acc[D / 32];
-#pragma unroll
-    for (int ib = 0; ib < D / 32; ++ib)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[ib][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      bf16x8_t qh, ql;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        __bf16 h, l;
-        split_bf16(qv[kk][u] * inv, h, l);
-        qh[u] = h;
-        ql[u] = l;
-      }
-#pragma unroll
-      for (int ib = 0; ib < D / 32; ++ib) {
-        int ro = (ib * 32 + col) * SP + half * 8 + kk * 16;
-        // S_t is loop-invariant; keep its operands in LDS instead of letting
-        // the compiler hoist all of them into registers
-        asm volatile("" : "+v"(ro));
-        const bf16x8_t ah = *(const bf16x8_t*)&st_hi[ro];
-        const bf16x8_t alo = *(const bf16x8_t*)&st_lo[ro];
-        acc[ib] = mfma32x3(ah, alo, qh, ql, acc[ib]);
-      }
-    }
-    float sq = 0.0f;
-#pragma unroll
-    for (int ib = 0; ib < D / 32; ++ib)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sq = fmaf(acc[ib][r], acc[ib][r], sq);
-    sq += __shfl_xor(sq, 32);
-    const float rn = fast_rsq(sq / (float)D + eps_s);
-    if (valid) {
-#pragma unroll
-      for (int ib = 0; ib < D / 32; ++ib)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int i0 = ib * 32 + g4 * 8 + half * 4;
-          const long long idx = n * D + i0;
-          const uint2 graw = *(const uint2*)(gb + idx);
-          uint2 oraw = make_uint2(0u, 0u);
-          if (accumulate) oraw = *(const uint2*)(ob + idx);
-          const uint32_t gw[2] = {graw.x, graw.y};
-          const uint32_t ow[2] = {oraw.x, oraw.y};
-          uint32_t res[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float y2[2];
-#pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-              const int r = g4 * 4 + u * 2 + e2;
-              const float gv = __uint_as_float(e2 ? (gw[u] & 0xffff0000u) : (gw[u] << 16));
-              const float ov = __uint_as_float(e2 ? (ow[u] & 0xffff0000u) : (ow[u] << 16));
-              y2[e2] = acc[ib][r] * rn * w_lds[i0 + u * 2 + e2] * sigmoid_f(gv) + ov;
-            }
-            res[u] = (uint32_t)f32_to_bf16(y2[0]) | ((uint32_t)f32_to_bf16(y2[1]) << 16);
-          }
-          *(uint2*)(ob + idx) = make_uint2(res[0], res[1]);
-        }
-    }
+    bf16_t* orow = ob + n * D;
+    readout_token<D>(
+        L, eps_s, qraw, qcol, s < tok_end, gb + n * D, orow,
+        [&]() {
+          if (s0 + 128 < tok_end) load_q(s0 + 128);
+        },
+        [&](int ib, int g4) {
+          return accumulate ? *(const uint2*)(orow + ib * 32 + g4 * 8 + half * 4)
+                            : make_uint2(0u, 0u);
+        });
   }
 }
 
@@ -334,12 +212,12 @@ hipError_t launch_readout(const Geom& g, int dtype, const void* q,
     const int pieces = (g.S + 1023) / 1024;
     const int per = ((g.S + pieces - 1) / pieces + 127) / 128 * 128;
     dim3 grid((g.S + per - 1) / per, g.F, g.B * g.H);
-#define RM_LAUNCH(DD)                                                         \
-  hipLaunchKernelGGL(readout_mfma_kernel<DD>, grid, dim3(256), 0, st,         \
-                     (const bf16_t*)q, (const bf16_t*)gate, decay, lohi,      \
-                     bank_p, bank_q, bank_e, rms_weight, rms_eps,             \
-                     (int)accumulate, (bf16_t*)out, g.F, g.S, g.chunk,        \
-                     g.radius, g.nch, g.B * g.H, g.N, per)
+    const ReadoutArgs ra{(const bf16_t*)gate, decay, bank_p, bank_q, bank_e, rms_weight,
+                         rms_eps, g.F, g.chunk, g.radius, g.nch, g.B * g.H};
+#define RM_LAUNCH(DD)                                                        \
+  hipLaunchKernelGGL(readout_mfma_kernel<DD>, grid, dim3(256), 0, st,        \
+                     (const bf16_t*)q, ra, (int)accumulate, (bf16_t*)out, g.S, \
+                     g.N, per)
     if (g.d == 128) RM_LAUNCH(128);
     else RM_LAUNCH(64);
 #undef RM_LAUNCH

@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "hwa_internal.h"
+#include "readout_core.h"
 
 // MUBUF direct load global -> LDS (buffer_load_dword* ... lds): lane l of a
 // wave writes its bytes at the LDS address in M0 + 16 * l (dwordx4); lanes
@@ -48,7 +49,7 @@ constexpr int SM_QT = 32 * SM_NW;       // queries per workgroup
 constexpr int SM_KT = 64;   // keys per LDS tile
 constexpr int SM_THREADS = 64 * SM_NW;
 #ifndef SM_PREFETCH
-#define SM_PREFETCH 3
+#define SM_PREFETCH 2
 #endif
 
 __host__ __device__ inline long long round_up64(long long n) {
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ vt, const int32_t* __restrict__ lohi,
     bf16_t* __restrict__ out, int F, int S, int chunk, int nch, long long N,
-    long long Np, int tiles_per_chunk, float scale_log2) {
+    long long Np, int tiles_per_chunk, float scale_log2, ReadoutArgs ra, int fuse) {
   // the body uses device-only lambdas; the host pass needs only the stub
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KC = D / 8;          // 16-byte chunks per key
@@ -487,23 +488,54 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- normalise and store: lane holds d = 32*dblk + 8*(r/4) + 4*half + r%4
+  // ---- normalise: lane holds d = 32*dblk + 8*(r/4) + 4*half + r%4, as bf16
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
-  if (my_q < q_end) {
-    bf16_t* orow = out + (long long)bh * N * D + my_q * D;
+  uint2 osm[D / 32][4];
 #pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk)
+  for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = dblk * 32 + g4 * 8 + half * 4;
-        const f32x2 a2 = {acc_o[dblk][g4 * 4 + 0] * inv, acc_o[dblk][g4 * 4 + 1] * inv};
-        const f32x2 b2 = {acc_o[dblk][g4 * 4 + 2] * inv, acc_o[dblk][g4 * 4 + 3] * inv};
-        const bf16x2 pa = __builtin_convertvector(a2, bf16x2);
-        const bf16x2 pb2 = __builtin_convertvector(b2, bf16x2);
-        *(uint2*)(orow + d0) = make_uint2(__builtin_bit_cast(uint32_t, pa),
-                                          __builtin_bit_cast(uint32_t, pb2));
-      }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x2 a2 = {acc_o[dblk][g4 * 4 + 0] * inv, acc_o[dblk][g4 * 4 + 1] * inv};
+      const f32x2 b2 = {acc_o[dblk][g4 * 4 + 2] * inv, acc_o[dblk][g4 * 4 + 3] * inv};
+      osm[dblk][g4] = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(a2, bf16x2)),
+                                 __builtin_bit_cast(uint32_t, __builtin_convertvector(b2, bf16x2)));
+    }
+  bf16_t* orow = out + (long long)bh * N * D + my_q * D;
+  if (!fuse) {
+    if (my_q < q_end) {
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(uint2*)(orow + dblk * 32 + g4 * 8 + half * 4) = osm[dblk][g4];
+    }
+    return;
+  }
+
+  // ---- fused linear-branch readout: out = o_sm + y, frame by frame (a tile
+  // of SM_QT queries spans at most two frames when S >= SM_QT; in general
+  // every frame from the first query's to the last's). qreg holds raw q
+  // (no RoPE on this path) in the chunk order of the QK operand; S_t's
+  // columns are read in the same order.
+  __shared__ ReadoutLds<D> rl;
+  int qcol[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) qcol[kk] = (8 * (kk / 4) + op_chunk(kk % 4, half)) * 8;
+  u32x4 qraw[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) qraw[kk] = __builtin_bit_cast(u32x4, qreg[kk]);
+  const long long q_last = min(q_tile0 + SM_QT, q_end) - 1;
+  const int t_first = (int)(q_tile0 / S), t_last = (int)(q_last / S);
+  const int my_t = my_q < q_end ? (int)(my_q / S) : -1;
+  const bf16_t* grow = ra.gate + (long long)bh * N * D + my_q * D;
+  for (int t = t_first; t <= t_last; ++t) {
+    const float eps_s = build_st<D, SM_THREADS>(rl, ra, bh, t, tid);
+    const bool mine = my_t == t;
+    if (__builtin_amdgcn_ballot_w64(mine) != 0)
+      readout_token<D>(rl, eps_s, qraw, qcol, mine, grow, orow, [&]() {},
+                       [&](int ib, int g4) { return osm[ib][g4]; });
+    __syncthreads();  // S_t of the next frame overwrites rl
   }
 #endif
 }
@@ -588,18 +620,20 @@ __global__ __launch_bounds__(128) void softmax_f32_kernel(
 
 hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
-                          const int32_t* lohi, void* out, hipStream_t st) {
+                          const int32_t* lohi, void* out, hipStream_t st,
+                          const ReadoutArgs* fuse) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)g.d);
   const int qpc = g.chunk * g.S;  // queries of a full chunk
   if (dtype == HWA_BF16) {
     const int tpc = (qpc + SM_QT - 1) / SM_QT;
     dim3 grid(tpc * g.nch * g.B * g.H);
     const long long Np = round_up64(g.N);
+    const ReadoutArgs ra = fuse ? *fuse : ReadoutArgs{};
 #define SM_LAUNCH(DD)                                                        \
   hipLaunchKernelGGL(softmax_bf16_kernel<DD>, grid, dim3(SM_THREADS), 0, st, \
                      (const bf16_t*)q, (const bf16_t*)k, v_t, lohi,          \
                      (bf16_t*)out, g.F, g.S, g.chunk, g.nch, g.N, Np, tpc,   \
-                     scale_log2)
+                     scale_log2, ra, fuse ? 1 : 0)
     if (g.d == 128) SM_LAUNCH(128);
     else SM_LAUNCH(64);
 #undef SM_LAUNCH

@@ -21,8 +21,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 FLAG_SOFTMAX_ONLY = 1
 FLAG_LINEAR_ONLY = 2
 FLAG_KEEP_INTERMEDIATES = 4
-NUM_STAGE_EVENTS = 8
-STAGES = ("window", "vtranspose", "softmax", "stats", "inverse", "scan", "readout")
+NUM_STAGE_EVENTS = 9
+STAGES = ("window", "stats", "inverse", "scan", "decay", "vtranspose", "softmax", "readout")
 
 HWA_OK = 0
 HWA_ERR_INVALID_ARG = 1

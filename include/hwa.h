@@ -95,12 +95,15 @@ typedef struct {
                          /* hipEvent_t recorded on `stream` at the kernel     */
                          /* boundaries of hybrid_attn_fwd, for per-kernel     */
                          /* timing: [0] start, then after [1] window table,   */
-                         /* [2] V transpose, [3] softmax, [4] statistics,     */
-                         /* [5] inverses, [6] scan, [7] readout (a skipped    */
-                         /* stage records its event with the previous one)   */
+                         /* [2] statistics, [3] inverses, [4] scan, [5] decay */
+                         /* products, [6] V transpose, [7] softmax (with the  */
+                         /* linear-branch readout fused in, on bf16 calls     */
+                         /* without q_rope that run both branches), [8]       */
+                         /* separate readout (a skipped stage records its     */
+                         /* event with the previous one)                      */
 } hwa_params;
 
-#define HWA_NUM_STAGE_EVENTS 8
+#define HWA_NUM_STAGE_EVENTS 9
 
 /*
  * Byte offsets of the intermediates inside the workspace of one
