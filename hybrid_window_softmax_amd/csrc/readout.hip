@@ -163,11 +163,13 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
     const int s = s0 + col;
     const long long n = (long long)t * S + s;
     bf16_t* orow = ob + n * D;
+    const bf16_t* grow = gb + n * D;
     readout_token<D>(
-        L, eps_s, qraw, qcol, s < tok_end, gb + n * D, orow,
+        L, eps_s, qraw, qcol, s < tok_end, orow,
         [&]() {
           if (s0 + 128 < tok_end) load_q(s0 + 128);
         },
+        [&](int ib, int g4) { return *(const uint2*)(grow + ib * 32 + g4 * 8 + half * 4); },
         [&](int ib, int g4) {
           return accumulate ? *(const uint2*)(orow + ib * 32 + g4 * 8 + half * 4)
                             : make_uint2(0u, 0u);

@@ -58,6 +58,8 @@ __device__ __forceinline__ float build_st(ReadoutLds<D>& L, const ReadoutArgs& a
   const float* Pm = a.bank_p + ((long long)bh * (a.nch + 1) + slot_p) * D * D;
   const float* Qm = a.bank_q + ((long long)bh * (a.nch + 1) + slot_q) * D * D;
   // eight consecutive columns per step: two 16-byte LDS stores
+  static_assert(D * D % (NT * 8) == 0, "whole steps");
+#pragma unroll 1
   for (int x = tid * 8; x < D * D; x += NT * 8) {
     const int i = x / D, j = x % D;
     const float4 p0 = *(const float4*)&Pm[x], p1 = *(const float4*)&Pm[x + 4];
@@ -87,13 +89,14 @@ __device__ __forceinline__ float build_st(ReadoutLds<D>& L, const ReadoutArgs& a
 // alike). after_features() runs once q^ is in registers (the caller may then
 // overwrite qraw, e.g. with the next token's q). When `valid`, writes
 // out[i] = addend(ib, g4) + y[i] for the lane's channels i = 32 ib + 8 g4 +
-// 4 half + 0..3, addend as four packed bf16.
-template <int D, typename AfterF, typename Addend>
+// 4 half + 0..3, with the gate pre-activations gate_at(ib, g4) and addend as
+// four packed bf16 each.
+template <int D, typename AfterF, typename GateAt, typename Addend>
 __device__ __forceinline__ void readout_token(const ReadoutLds<D>& L, float eps_s,
                                               const u32x4_t (&qraw)[D / 16],
                                               const int (&qcol)[D / 16], bool valid,
-                                              const bf16_t* grow, bf16_t* orow,
-                                              AfterF after_features, Addend addend) {
+                                              bf16_t* orow, AfterF after_features,
+                                              GateAt gate_at, Addend addend) {
   constexpr int SP = ReadoutLds<D>::SP;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -152,7 +155,7 @@ __device__ __forceinline__ void readout_token(const ReadoutLds<D>& L, float eps_
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int i0 = ib * 32 + g4 * 8 + half * 4;
-      const uint2 graw = *(const uint2*)(grow + i0);
+      const uint2 graw = gate_at(ib, g4);
       const uint2 oraw = addend(ib, g4);
       const uint32_t gw[2] = {graw.x, graw.y};
       const uint32_t ow[2] = {oraw.x, oraw.y};

@@ -528,12 +528,44 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   const long long q_last = min(q_tile0 + SM_QT, q_end) - 1;
   const int t_first = (int)(q_tile0 / S), t_last = (int)(q_last / S);
   const int my_t = my_q < q_end ? (int)(my_q / S) : -1;
-  const bf16_t* grow = ra.gate + (long long)bh * N * D + my_q * D;
+  // the gate rows of the tile's queries go to the K/V stage LDS (free after
+  // the drain) by direct loads, so their latency hides behind the S_t build:
+  // 16-byte chunk c of row r sits at slot r*CH + (c ^ (r % CH)); rows past
+  // the head's end read zeros (never used)
+  constexpr int CH = D / 8;                     // 16-byte chunks per row
+  constexpr int KSLOTS = NST * SM_KT * D / 8;   // 16-byte slots in k_lds
+  constexpr int GPW = SM_QT * CH / 64 / SM_NW;  // load instructions per wave
+  static_assert(SM_QT * CH == 2 * KSLOTS, "the gate tile fills the K and V stages");
+  __syncthreads();  // every wave is done reading the K/V stages
+  {
+    const hwa_i32x4 rs = tile_rsrc(ra.gate + (long long)bh * N * D, N * D, q_tile0 * D);
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+      const int s0 = (wave + SM_NW * j) * 64;  // first slot of this instruction
+      const int slot = s0 + lane;
+      const int r = slot / CH, c = (slot % CH) ^ (r % CH);
+      bf16_t* dst = s0 < KSLOTS ? &k_lds[0][0] + s0 * 8 : &v_lds[0][0] + (s0 - KSLOTS) * 8;
+      hwa_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16,
+                              (r * D + c * 8) * 2, 0, 0, 0);
+    }
+  }
+  auto gate_at = [&] __device__(int ib, int g4) __attribute__((always_inline)) {
+    const int r = wave * 32 + col, c = ib * 4 + g4;
+    const int slot = r * CH + (c ^ (r % CH));
+    const bf16_t* src = slot < KSLOTS ? &k_lds[0][0] + slot * 8 : &v_lds[0][0] + (slot - KSLOTS) * 8;
+    return *(const uint2*)(src + half * 4);
+  };
+  bool gate_ready = false;
   for (int t = t_first; t <= t_last; ++t) {
     const float eps_s = build_st<D, SM_THREADS>(rl, ra, bh, t, tid);
+    if (!gate_ready) {  // every wave's gate loads have landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      gate_ready = true;
+    }
     const bool mine = my_t == t;
     if (__builtin_amdgcn_ballot_w64(mine) != 0)
-      readout_token<D>(rl, eps_s, qraw, qcol, mine, grow, orow, [&]() {},
+      readout_token<D>(rl, eps_s, qraw, qcol, mine, orow, [&]() {}, gate_at,
                        [&](int ib, int g4) { return osm[ib][g4]; });
     __syncthreads();  // S_t of the next frame overwrites rl
   }
