@@ -144,9 +144,10 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
   const bf16_t* qb = q + (long long)bh * N * D;
   const bf16_t* gb = a.gate + (long long)bh * N * D;
   bf16_t* ob = out + (long long)bh * N * D;
-  int qcol[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) qcol[kk] = kk * 16 + half * 8;
+  struct KOff {
+    static constexpr int at(int kk) { return kk * 16; }
+  };
+  const int qlane = half * 8;  // chunk kk of the lane half: channels 16 kk + 8 half + 0..7
   // q of this lane's token (channels 16*kk + 8*half + 0..7), one tile ahead
   u32x4_t qraw[D / 16];
   auto load_q = [&](int s0) {
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       qraw[kk] = u32x4_t{0u, 0u, 0u, 0u};
-      if (s < tok_end) qraw[kk] = *(const u32x4_t*)(qb + n * D + qcol[kk]);
+      if (s < tok_end) qraw[kk] = *(const u32x4_t*)(qb + n * D + qlane + KOff::at(kk));
     }
   };
   load_q(tok0 + wave * 32);
@@ -164,8 +165,8 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
     const long long n = (long long)t * S + s;
     bf16_t* orow = ob + n * D;
     const bf16_t* grow = gb + n * D;
-    readout_token<D>(
-        L, eps_s, qraw, qcol, s < tok_end, orow,
+    readout_token<D, KOff>(
+        L, eps_s, qraw, qlane, s < tok_end, orow,
         [&]() {
           if (s0 + 128 < tok_end) load_q(s0 + 128);
         },

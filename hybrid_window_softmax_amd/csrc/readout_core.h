@@ -84,36 +84,37 @@ __device__ __forceinline__ float build_st(ReadoutLds<D>& L, const ReadoutArgs& a
 }
 
 // y of this lane's token (lane % 32 of the calling wave; the wave must be
-// converged): chunk kk of the lane half holds raw q channels qcol[kk] ..
-// qcol[kk] + 7 (any permutation of the channels, applied to S_t's columns
-// alike). after_features() runs once q^ is in registers (the caller may then
-// overwrite qraw, e.g. with the next token's q). When `valid`, writes
+// converged): qraw[kk] holds raw q channels qlane + KOff::at(kk) + 0..7 (any
+// permutation of the channels, applied to S_t's columns alike; qlane is the
+// lane-dependent part, KOff::at a compile-time one). after_features() runs once qraw has been read for the last time
+// (the caller may then overwrite it, e.g. with the next token's q). When
+// `valid`, writes
 // out[i] = addend(ib, g4) + y[i] for the lane's channels i = 32 ib + 8 g4 +
 // 4 half + 0..3, with the gate pre-activations gate_at(ib, g4) and addend as
 // four packed bf16 each.
-template <int D, typename AfterF, typename GateAt, typename Addend>
+template <int D, typename KOff, typename AfterF, typename GateAt, typename Addend>
 __device__ __forceinline__ void readout_token(const ReadoutLds<D>& L, float eps_s,
-                                              const u32x4_t (&qraw)[D / 16],
-                                              const int (&qcol)[D / 16], bool valid,
-                                              bf16_t* orow, AfterF after_features,
+                                              const u32x4_t (&qraw)[D / 16], int qlane,
+                                              bool valid, bf16_t* orow, AfterF after_features,
                                               GateAt gate_at, Addend addend) {
   constexpr int SP = ReadoutLds<D>::SP;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
-  float qv[D / 16][8];
+  // q^ = L2(SiLU(q)): the squared norm first, then SiLU again per MFMA step
+  // (recomputing it is cheaper than holding d floats per lane)
+  auto silu_pair = [&](uint32_t w, float& a, float& b) __attribute__((always_inline)) {
+    a = silu_f(__uint_as_float(w << 16));
+    b = silu_f(__uint_as_float(w & 0xffff0000u));
+  };
   float ss = 0.0f;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const u32x4_t raw = qraw[kk];
+  for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      qv[kk][2 * u] = silu_f(__uint_as_float(raw[u] << 16));
-      qv[kk][2 * u + 1] = silu_f(__uint_as_float(raw[u] & 0xffff0000u));
+      float a, b;
+      silu_pair(qraw[kk][u], a, b);
+      ss = fmaf(a, a, fmaf(b, b, ss));
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) ss = fmaf(qv[kk][u], qv[kk][u], ss);
-  }
-  after_features();
   ss += __shfl_xor(ss, 32);
   const float inv = inv_l2(ss);
   f32x16_t acc[D / 32];
@@ -121,22 +122,29 @@ __device__ __forceinline__ void readout_token(const ReadoutLds<D>& L, float eps_
   for (int ib = 0; ib < D / 32; ++ib)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[ib][r] = 0.0f;
+  // S_t does not change across tokens: keep its operands in LDS (one lane
+  // base, immediate offsets) rather than letting the compiler hoist them
+  int ro_base = col * SP + qlane;
+  asm volatile("" : "+v"(ro_base));
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     bf16x8_t qh, ql;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
+      float a, b;
+      silu_pair(qraw[kk][u], a, b);
       __bf16 h, l;
-      split_bf16(qv[kk][u] * inv, h, l);
-      qh[u] = h;
-      ql[u] = l;
+      split_bf16(a * inv, h, l);
+      qh[2 * u] = h;
+      ql[2 * u] = l;
+      split_bf16(b * inv, h, l);
+      qh[2 * u + 1] = h;
+      ql[2 * u + 1] = l;
     }
+    if (kk == D / 16 - 1) after_features();
 #pragma unroll
     for (int ib = 0; ib < D / 32; ++ib) {
-      int ro = (ib * 32 + col) * SP + qcol[kk];
-      // S_t does not change across tokens: keep its operands in LDS rather
-      // than letting the compiler hoist them all into registers
-      asm volatile("" : "+v"(ro));
+      const int ro = ro_base + ib * 32 * SP + KOff::at(kk);
       const bf16x8_t ah = *(const bf16x8_t*)&L.hi[ro];
       const bf16x8_t alo = *(const bf16x8_t*)&L.lo[ro];
       acc[ib] = mfma32x3(ah, alo, qh, ql, acc[ib]);

@@ -519,9 +519,12 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   // (no RoPE on this path) in the chunk order of the QK operand; S_t's
   // columns are read in the same order.
   __shared__ ReadoutLds<D> rl;
-  int qcol[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) qcol[kk] = (8 * (kk / 4) + op_chunk(kk % 4, half)) * 8;
+  // chunk kk of the lane half: channels 8 * (8 * (kk / 4) + op_chunk(kk % 4, half)),
+  // a lane part 16 * half plus a compile-time part
+  struct KOff {
+    static constexpr int at(int kk) { return 64 * (kk / 4) + 32 * ((kk % 4) / 2) + 8 * (kk % 2); }
+  };
+  const int qlane = 16 * half;
   u32x4 qraw[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) qraw[kk] = __builtin_bit_cast(u32x4, qreg[kk]);
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     }
     const bool mine = my_t == t;
     if (__builtin_amdgcn_ballot_w64(mine) != 0)
-      readout_token<D>(rl, eps_s, qraw, qcol, mine, orow, [&]() {}, gate_at,
+      readout_token<D, KOff>(rl, eps_s, qraw, qlane, mine, orow, [&]() {}, gate_at,
                        [&](int ib, int g4) { return osm[ib][g4]; });
     __syncthreads();  // S_t of the next frame overwrites rl
   }
