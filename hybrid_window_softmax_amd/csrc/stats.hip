@@ -128,119 +128,140 @@ __global__ __launch_bounds__(256) void stats_kernel(
 // bf16 I/O: the two contractions over a frame's tokens run on MFMA
 // (v_mfma_f32_32x32x16_bf16) as split-bf16 products. With
 // k' = sqrt(beta) k^ and v' = sqrt(beta) v^:  A = K'^T K',  B = V'^T K'.
-// A tile of 64 tokens is turned into features in registers (thread = 4
-// consecutive tokens x 4 channels; the L2 norm is reduced over the d/4 lanes
-// that share the tokens) and written to LDS channel-major, so that every MFMA
-// operand lane (one channel, 8 consecutive tokens) is one 16-byte read.
-// 4*d threads; each wave owns 4 (d = 128) or 2 (d = 64) of the output blocks
-// of 32 x 32 (the A blocks, then the B blocks).
+// Eight waves per (b, h, frame) in two roles, one of each per SIMD, so that
+// the feature VALU work and the MFMAs overlap:
+//  - waves 0..3 turn 64-token tiles into features (thread = SX_TPG
+//    consecutive tokens x 4 channels; the conv reads raw rows held in
+//    registers, fetched one tile ahead; the L2 norm is reduced with DPP over
+//    the d/4 lanes that share the tokens) and store them channel-major
+//    (hi, lo) to one of two LDS buffers;
+//  - waves 4..7 run the MFMAs of the previous tile from the other buffer;
+//    each owns a quarter of the 32 x 32 output blocks (A blocks, then B).
+// One barrier per tile; both roles pass the same number of barriers.
 constexpr int SX_TT = 64;  // tokens per tile
 
+// sum over the 32 (W = 32) or 16 (W = 16) consecutive lanes of a row group,
+// in every lane of it: DPP quad / half-mirror / mirror within each 16-lane
+// row, then one exchange between the two rows of a 32-lane group
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, false));
+}
+template <int W>
+__device__ __forceinline__ float row_group_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  if constexpr (W == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(4 * D) void stats_mfma_kernel(
+__global__ __launch_bounds__(512) void stats_mfma_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ conv_k,
     const float* __restrict__ conv_v, int conv, float* __restrict__ A,
     float* __restrict__ Bm, int F, int S, int H, long long N) {
-  constexpr int NT = 4 * D;          // threads
+  constexpr int NP = 256;            // producer threads
   constexpr int CG = D / 4;          // channel groups of 4
-  constexpr int TG = NT / CG;        // token groups (16)
-  constexpr int TPG = SX_TT / TG;    // tokens per group (4)
+  constexpr int TG = NP / CG;        // token groups
+  constexpr int TPG = SX_TT / TG;    // tokens per producer thread (8 or 4)
   constexpr int TP = SX_TT + 8;      // padded LDS row (tokens)
   constexpr int NB = D / 32;         // 32-wide blocks per dimension
-  constexpr int BPW = 2 * NB * NB / (NT / 64);  // output blocks per wave
-  static_assert(TPG == 4, "token group");
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) bf16_t kh_s[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16_t kl_s[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16_t vh_s[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16_t vl_s[D * TP];
+  constexpr int BPW = 2 * NB * NB / 4;  // output blocks per consumer wave
+  static_assert(TPG == 8 || TPG == 4, "token group");
+  static_assert(CG == 32 || CG == 16, "channel groups span a 32- or 16-lane group");
+  typedef __bf16 bf16xT_t __attribute__((ext_vector_type(TPG)));
+  // [stage][k hi, k lo, v hi, v lo][channel][token]
+  __shared__ __attribute__((aligned(16))) bf16_t buf[2][4][D * TP];
 
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int f = blockIdx.x;
   const int bh = blockIdx.y;
   const int h = bh % H;
-  const bf16_t* kp = k + (long long)bh * N * D;
-  const bf16_t* vp = v + (long long)bh * N * D;
-  const float* bp = beta + (long long)bh * N;
   const long long n0 = (long long)f * S;
+  const int ntiles = (S + SX_TT - 1) / SX_TT;
 
-  const int tg = tid / CG, cg = tid % CG;
-  const int c0 = cg * 4;
-  float wk[4][4], wv[4][4];
+  if (wave < 4) {
+    // ------------------------------------------------ producers: features
+    const bf16_t* kp = k + (long long)bh * N * D;
+    const bf16_t* vp = v + (long long)bh * N * D;
+    const float* bp = beta + (long long)bh * N;
+    const int tg = tid / CG, cg = tid % CG;
+    const int c0 = cg * 4;
+    float wk[4][4], wv[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wk[i][j] = conv ? conv_k[((long long)h * D + c0 + i) * 4 + j] : (j == 0 ? 1.0f : 0.0f);
-      wv[i][j] = conv ? conv_v[((long long)h * D + c0 + i) * 4 + j] : (j == 0 ? 1.0f : 0.0f);
-    }
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, col = lane & 31;
-  f32x16_t acc[BPW];
-#pragma unroll
-  for (int b = 0; b < BPW; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
-
-  // raw rows sb-3 .. sb+TPG-1 (4 channels each) of k and v for one tile;
-  // fetched one tile ahead so the loads overlap the previous tile's MFMAs
-  uint2 kraw[TPG + 3], vraw[TPG + 3];
-  auto fetch = [&](int s0) {
-    const int sb = s0 + tg * TPG;
-#pragma unroll
-    for (int x = 0; x < TPG + 3; ++x) {
-      const int s = sb - 3 + x;
-      kraw[x] = vraw[x] = make_uint2(0u, 0u);
-      if (s >= 0 && s < S) {
-        kraw[x] = *(const uint2*)(kp + (n0 + s) * D + c0);
-        vraw[x] = *(const uint2*)(vp + (n0 + s) * D + c0);
+      for (int j = 0; j < 4; ++j) {
+        wk[i][j] = conv ? conv_k[((long long)h * D + c0 + i) * 4 + j] : (j == 0 ? 1.0f : 0.0f);
+        wv[i][j] = conv ? conv_v[((long long)h * D + c0 + i) * 4 + j] : (j == 0 ? 1.0f : 0.0f);
       }
-    }
-  };
-  // causal width-4 conv of TPG tokens x 4 channels
-  auto conv4 = [&](const uint2 (&raw)[TPG + 3], const float (&w)[4][4],
-                   float (&o)[TPG][4]) {
-    float r[TPG + 3][4];
+    // raw rows sb-3 .. sb+TPG-1 (4 channels each) of k and v for one tile,
+    // fetched one tile ahead so the loads overlap the feature work
+    uint2 kraw[TPG + 3], vraw[TPG + 3];
+    auto fetch = [&](int s0) {
+      const int sb = s0 + tg * TPG;
 #pragma unroll
-    for (int x = 0; x < TPG + 3; ++x) {
-      r[x][0] = __uint_as_float(raw[x].x << 16);
-      r[x][1] = __uint_as_float(raw[x].x & 0xffff0000u);
-      r[x][2] = __uint_as_float(raw[x].y << 16);
-      r[x][3] = __uint_as_float(raw[x].y & 0xffff0000u);
-    }
-#pragma unroll
-    for (int u = 0; u < TPG; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float a = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a = fmaf(w[i][j], r[u + 3 - j][i], a);
-        o[u][i] = a;
+      for (int x = 0; x < TPG + 3; ++x) {
+        const int s = sb - 3 + x;
+        kraw[x] = vraw[x] = make_uint2(0u, 0u);
+        if (s >= 0 && s < S) {
+          kraw[x] = *(const uint2*)(kp + (n0 + s) * D + c0);
+          vraw[x] = *(const uint2*)(vp + (n0 + s) * D + c0);
+        }
       }
-  };
-  auto store4 = [&](bf16_t* hs, bf16_t* ls, int i, const float (&x)[TPG]) {
-    __bf16 hv[4], lv[4];
+    };
+    // causal width-4 conv of TPG tokens x 4 channels
+    auto conv4 = [&](const uint2 (&raw)[TPG + 3], const float (&w)[4][4], float (&o)[TPG][4]) {
+      float r[TPG + 3][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) split_bf16(x[u], hv[u], lv[u]);
-    const int o = (c0 + i) * TP + tg * TPG;
-    *(bf16x4_t*)&hs[o] = bf16x4_t{hv[0], hv[1], hv[2], hv[3]};
-    *(bf16x4_t*)&ls[o] = bf16x4_t{lv[0], lv[1], lv[2], lv[3]};
-  };
-
-  fetch(0);
-  for (int s0 = 0; s0 < S; s0 += SX_TT) {
-    const int sb = s0 + tg * TPG;
-    float sqb[TPG];
+      for (int x = 0; x < TPG + 3; ++x) {
+        r[x][0] = __uint_as_float(raw[x].x << 16);
+        r[x][1] = __uint_as_float(raw[x].x & 0xffff0000u);
+        r[x][2] = __uint_as_float(raw[x].y << 16);
+        r[x][3] = __uint_as_float(raw[x].y & 0xffff0000u);
+      }
 #pragma unroll
-    for (int u = 0; u < TPG; ++u) sqb[u] = sb + u < S ? __builtin_amdgcn_sqrtf(bp[n0 + sb + u]) : 0.0f;
-    float vf[TPG][4];
-    conv4(vraw, wv, vf);
-    {  // k' = sqrt(beta) L2(SiLU(conv_k(k)))
-      float kf[TPG][4], ss[TPG];
+      for (int u = 0; u < TPG; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a = fmaf(w[i][j], r[u + 3 - j][i], a);
+          o[u][i] = a;
+        }
+    };
+    auto store = [&](int st, int arr, int i, const float (&x)[TPG]) {
+      bf16xT_t hv, lv;
+#pragma unroll
+      for (int u = 0; u < TPG; ++u) {
+        __bf16 hb, lb;
+        split_bf16(x[u], hb, lb);
+        hv[u] = hb;
+        lv[u] = lb;
+      }
+      const int o = (c0 + i) * TP + tg * TPG;
+      *(bf16xT_t*)&buf[st][arr][o] = hv;
+      *(bf16xT_t*)&buf[st][arr + 1][o] = lv;
+    };
+    // features of the tile at token s0 -> LDS stage st; prefetches the next
+    auto make = [&](int s0, int st) {
+      const int sb = s0 + tg * TPG;
+      float sqb[TPG];
+#pragma unroll
+      for (int u = 0; u < TPG; ++u)
+        sqb[u] = sb + u < S ? __builtin_amdgcn_sqrtf(bp[n0 + sb + u]) : 0.0f;
+      float kf[TPG][4], vf[TPG][4];
       conv4(kraw, wk, kf);
+      conv4(vraw, wv, vf);
       if (s0 + SX_TT < S) fetch(s0 + SX_TT);
+      // k' = sqrt(beta) L2(SiLU(conv_k(k)))
+      float ss[TPG];
 #pragma unroll
       for (int u = 0; u < TPG; ++u) {
         ss[u] = 0.0f;
@@ -249,65 +270,71 @@ __global__ __launch_bounds__(4 * D) void stats_mfma_kernel(
           kf[u][i] = silu_f(kf[u][i]);
           ss[u] = fmaf(kf[u][i], kf[u][i], ss[u]);
         }
+        ss[u] = sqb[u] * inv_l2(row_group_sum<CG>(ss[u]));
       }
-#pragma unroll
-      for (int off = 1; off < CG; off <<= 1)
-#pragma unroll
-        for (int u = 0; u < TPG; ++u) ss[u] += __shfl_xor(ss[u], off);
-#pragma unroll
-      for (int u = 0; u < TPG; ++u) ss[u] = sqb[u] * inv_l2(ss[u]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float x[TPG];
+        float x[TPG], y[TPG];
 #pragma unroll
-        for (int u = 0; u < TPG; ++u) x[u] = kf[u][i] * ss[u];
-        store4(kh_s, kl_s, i, x);
+        for (int u = 0; u < TPG; ++u) {
+          x[u] = kf[u][i] * ss[u];
+          y[u] = vf[u][i] * sqb[u];  // v' = sqrt(beta) conv_v(v)
+        }
+        store(st, 0, i, x);
+        store(st, 2, i, y);
       }
+    };
+    fetch(0);
+    make(0, 0);
+    __syncthreads();  // tile 0 is in stage 0
+    for (int i = 0; i < ntiles; ++i) {
+      if (i + 1 < ntiles) make((i + 1) * SX_TT, (i + 1) & 1);
+      __syncthreads();
     }
-    {  // v' = sqrt(beta) conv_v(v)
+  } else {
+    // ------------------------------------------------ consumers: MFMAs
+    const int cw = wave - 4;
+    const int half = lane >> 5, col = lane & 31;
+    f32x16_t acc[BPW];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x[TPG];
+    for (int b = 0; b < BPW; ++b)
 #pragma unroll
-        for (int u = 0; u < TPG; ++u) x[u] = vf[u][i] * sqb[u];
-        store4(vh_s, vl_s, i, x);
+      for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+    __syncthreads();  // tile 0 is in stage 0
+    for (int i = 0; i < ntiles; ++i) {
+      const int st = i & 1;
+#pragma unroll
+      for (int kk = 0; kk < SX_TT / 16; ++kk) {
+        const int to = kk * 16 + half * 8;
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+          const int blk = cw * BPW + b;
+          const int isB = blk / (NB * NB);
+          const int ib = (blk / NB) % NB, jb = blk % NB;
+          const int ra = (ib * 32 + col) * TP + to;
+          const int rb = (jb * 32 + col) * TP + to;
+          const bf16x8_t ah = *(const bf16x8_t*)&buf[st][isB ? 2 : 0][ra];
+          const bf16x8_t al = *(const bf16x8_t*)&buf[st][isB ? 3 : 1][ra];
+          const bf16x8_t bh8 = *(const bf16x8_t*)&buf[st][0][rb];
+          const bf16x8_t bl8 = *(const bf16x8_t*)&buf[st][1][rb];
+          acc[b] = mfma32x3(ah, al, bh8, bl8, acc[b]);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
-
-    // ---- MFMA over the tile's 64 tokens (4 k-steps of 16)
+    // write: lane holds rows 8*(r/4) + 4*half + r%4, column col
+    const long long mo = ((long long)bh * F + f) * D * D;
 #pragma unroll
-    for (int kk = 0; kk < SX_TT / 16; ++kk) {
-      const int to = kk * 16 + half * 8;
+    for (int b = 0; b < BPW; ++b) {
+      const int blk = cw * BPW + b;
+      const int isB = blk / (NB * NB);
+      const int ib = (blk / NB) % NB, jb = blk % NB;
+      float* dst = (isB ? Bm : A) + mo;
 #pragma unroll
-      for (int b = 0; b < BPW; ++b) {
-        const int blk = wave * BPW + b;
-        const int isB = blk / (NB * NB);
-        const int ib = (blk / NB) % NB, jb = blk % NB;
-        const int ra = (ib * 32 + col) * TP + to;
-        const int rb = (jb * 32 + col) * TP + to;
-        const bf16x8_t ah = *(const bf16x8_t*)(isB ? &vh_s[ra] : &kh_s[ra]);
-        const bf16x8_t al = *(const bf16x8_t*)(isB ? &vl_s[ra] : &kl_s[ra]);
-        const bf16x8_t bh8 = *(const bf16x8_t*)&kh_s[rb];
-        const bf16x8_t bl8 = *(const bf16x8_t*)&kl_s[rb];
-        acc[b] = mfma32x3(ah, al, bh8, bl8, acc[b]);
+      for (int r = 0; r < 16; ++r) {
+        const int i = ib * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+        dst[(long long)i * D + jb * 32 + col] = acc[b][r];
       }
-    }
-    __syncthreads();
-  }
-
-  // ---- write: lane holds rows 8*(r/4) + 4*half + r%4, column col
-  const long long mo = ((long long)bh * F + f) * D * D;
-#pragma unroll
-  for (int b = 0; b < BPW; ++b) {
-    const int blk = wave * BPW + b;
-    const int isB = blk / (NB * NB);
-    const int ib = (blk / NB) % NB, jb = blk % NB;
-    float* dst = (isB ? Bm : A) + mo;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = ib * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-      dst[(long long)i * D + jb * 32 + col] = acc[b][r];
     }
   }
 }
@@ -330,7 +357,7 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
   }
   if (dtype == HWA_BF16) {
 #define SX_LAUNCH(DD)                                                        \
-  hipLaunchKernelGGL(stats_mfma_kernel<DD>, grid, dim3(4 * DD), 0, st,       \
+  hipLaunchKernelGGL(stats_mfma_kernel<DD>, grid, dim3(512), 0, st,          \
                      (const bf16_t*)k, (const bf16_t*)v, beta, conv_k,       \
                      conv_v, (int)conv, A, Bm, g.F, g.S, g.H, g.N)
     if (g.d == 128) SX_LAUNCH(128);
