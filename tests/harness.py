@@ -37,14 +37,19 @@ class GpuCase:
             self.text_state = hwa.text_state(self.t["k_txt"], self.t["v_txt"],
                                              self.t["beta_txt"])
 
-    def run(self, rule="vdn_solve", flags=0, text=True, out=None, workspace=None):
+    def run(self, rule="vdn_solve", flags=0, text=True, out=None, workspace=None, rope=None):
+        """rope: optional (q_rope, k_rope) host arrays for the softmax branch."""
         c = self.cfg
         t = self.t
+        qr = kr = None
+        if rope is not None:
+            qr, kr = (to_dev(a, self.bf16) for a in rope)
         return hwa.hybrid_attn_fwd(
             t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"],
             self.text_state if text else None, t["conv_k"], t["conv_v"],
             c["frames"], c["tokens_per_frame"], c["chunk"], c["radius"], rule, c["c"],
-            0.5, 1e-6, t["rms_weight"], flags=flags, out=out, workspace=workspace)
+            0.5, 1e-6, t["rms_weight"], q_rope=qr, k_rope=kr, flags=flags, out=out,
+            workspace=workspace)
 
     def layout(self):
         c = self.cfg
@@ -70,16 +75,18 @@ def oracle_text_state(inp, b, h):
                              inp.beta_txt[b, h].astype(np.float64))
 
 
-def oracle_head(inp, b, h, rule="vdn_solve", text=True, keep=False):
-    """(out, o_sm, y, intermediates) of one (b, h) in fp64."""
+def oracle_head(inp, b, h, rule="vdn_solve", text=True, keep=False, rope=None):
+    """(out, o_sm, y, intermediates) of one (b, h) in fp64; rope: optional
+    (q_rope, k_rope) fp64 [N, d] slices for the softmax branch."""
     c = inp.cfg
     st = oracle_text_state(inp, b, h) if text else None
+    qr, kr = rope if rope is not None else (None, None)
     return oracle.hybrid_attn_head(
         inp.f64("q", b, h), inp.f64("k", b, h), inp.f64("v", b, h),
         inp.beta[b, h].astype(np.float64), inp.alpha[b, h].astype(np.float64),
         inp.f64("gate", b, h), st, inp.conv_k[h], inp.conv_v[h], inp.rms_weight,
         c["tokens_per_frame"], c["chunk"], c["radius"], rule, c["c"], 0.5, 1e-6,
-        keep=keep)
+        q_rope=qr, k_rope=kr, keep=keep)
 
 
 def oracle_linear_head(inp, b, h, rule="vdn_solve", text=True, keep=False):

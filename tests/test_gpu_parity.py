@@ -142,6 +142,30 @@ def test_bf16_d128_ragged(rule):
     _full_check(cfg, rule, check_intermediates=True)
 
 
+def test_bf16_separate_rope_inputs():
+    # q_rope / k_rope feed the softmax branch only; the linear branch keeps
+    # raw q, k (the library then runs its readout as a separate kernel)
+    cfg = inputs.tiny_config(frames=8, text_tokens=16, head_dim=128, tokens_per_frame=100,
+                             dtype="bf16", heads=2, seed=107, chunk=3)
+    _say(f"case {cfg['name']} with q_rope/k_rope")
+    inp = inputs.make(cfg)
+    other = inputs.make({**cfg, "seed": 207})  # independent draws stand in for RoPE'd q, k
+    case = GpuCase(inp)
+    rope_bits = (other.q, other.k)
+    out, _ = case.run("vdn_solve", 0, True, rope=rope_bits)
+    sm, _ = case.run("vdn_solve", hwa.FLAG_SOFTMAX_ONLY, True, rope=rope_bits)
+    torch.cuda.synchronize()
+    got = {"out": out_f64(out), "o_sm": out_f64(sm)}
+    for b in range(cfg["batch"]):
+        for h in range(cfg["heads"]):
+            r = oracle_head(inp, b, h, "vdn_solve", True,
+                            rope=(other.f64("q", b, h), other.f64("k", b, h)))
+            for key, ref in (("out", r[0]), ("o_sm", r[1])):
+                err = oracle.rel_frobenius(got[key][b, h], ref)
+                _say(f"  ({b},{h}) {key}: {err:.3e}")
+                assert err <= TOL["bf16"], (key, b, h, err)
+
+
 def test_bf16_d64_odd_tokens():
     cfg = inputs.tiny_config(frames=7, text_tokens=8, head_dim=64, tokens_per_frame=33,
                              dtype="bf16", heads=3, seed=106, chunk=3)
