@@ -128,17 +128,19 @@ __global__ __launch_bounds__(256) void stats_kernel(
 // bf16 I/O: the two contractions over a frame's tokens run on MFMA
 // (v_mfma_f32_32x32x16_bf16) as split-bf16 products. With
 // k' = sqrt(beta) k^ and v' = sqrt(beta) v^:  A = K'^T K',  B = V'^T K'.
-// Eight waves per (b, h, frame) in two roles, one of each per SIMD, so that
-// the feature VALU work and the MFMAs overlap:
-//  - waves 0..3 turn 64-token tiles into features (thread = SX_TPG
+// Waves in two roles per (b, h, frame), so that the feature VALU work and
+// the MFMAs overlap:
+//  - SX_PW(d) producer waves turn 64-token tiles into features (thread = 4
 //    consecutive tokens x 4 channels; the conv reads raw rows held in
 //    registers, fetched one tile ahead; the L2 norm is reduced with DPP over
 //    the d/4 lanes that share the tokens) and store them channel-major
 //    (hi, lo) to one of two LDS buffers;
-//  - waves 4..7 run the MFMAs of the previous tile from the other buffer;
-//    each owns a quarter of the 32 x 32 output blocks (A blocks, then B).
+//  - four consumer waves run the MFMAs of the previous tile from the other
+//    buffer; each owns a quarter of the 32 x 32 output blocks (A, then B).
 // One barrier per tile; both roles pass the same number of barriers.
 constexpr int SX_TT = 64;  // tokens per tile
+// producer waves: d / 16 (4 channels x 4 tokens per thread over a 64-token tile)
+__host__ __device__ constexpr int sx_pw(int d) { return d / 16; }
 
 // sum over the 32 (W = 32) or 16 (W = 16) consecutive lanes of a row group,
 // in every lane of it: DPP quad / half-mirror / mirror within each 16-lane
@@ -159,19 +161,20 @@ __device__ __forceinline__ float row_group_sum(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(512) void stats_mfma_kernel(
+__global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ conv_k,
     const float* __restrict__ conv_v, int conv, float* __restrict__ A,
     float* __restrict__ Bm, int F, int S, int H, long long N) {
-  constexpr int NP = 256;            // producer threads
+  constexpr int NPW = sx_pw(D);      // producer waves
+  constexpr int NP = 64 * NPW;       // producer threads
   constexpr int CG = D / 4;          // channel groups of 4
   constexpr int TG = NP / CG;        // token groups
   constexpr int TPG = SX_TT / TG;    // tokens per producer thread (8 or 4)
   constexpr int TP = SX_TT + 8;      // padded LDS row (tokens)
   constexpr int NB = D / 32;         // 32-wide blocks per dimension
   constexpr int BPW = 2 * NB * NB / 4;  // output blocks per consumer wave
-  static_assert(TPG == 8 || TPG == 4, "token group");
+  static_assert(TPG == 4, "token group");
   static_assert(CG == 32 || CG == 16, "channel groups span a 32- or 16-lane group");
   typedef __bf16 bf16xT_t __attribute__((ext_vector_type(TPG)));
   // [stage][k hi, k lo, v hi, v lo][channel][token]
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(512) void stats_mfma_kernel(
   const long long n0 = (long long)f * S;
   const int ntiles = (S + SX_TT - 1) / SX_TT;
 
-  if (wave < 4) {
+  if (wave < NPW) {
     // ------------------------------------------------ producers: features
     const bf16_t* kp = k + (long long)bh * N * D;
     const bf16_t* vp = v + (long long)bh * N * D;
@@ -201,11 +204,15 @@ __global__ __launch_bounds__(512) void stats_mfma_kernel(
         wk[i][j] = conv ? conv_k[((long long)h * D + c0 + i) * 4 + j] : (j == 0 ? 1.0f : 0.0f);
         wv[i][j] = conv ? conv_v[((long long)h * D + c0 + i) * 4 + j] : (j == 0 ? 1.0f : 0.0f);
       }
-    // raw rows sb-3 .. sb+TPG-1 (4 channels each) of k and v for one tile,
-    // fetched one tile ahead so the loads overlap the feature work
+    // raw rows sb-3 .. sb+TPG-1 (4 channels each) of k and v, and beta of
+    // rows sb .. sb+TPG-1, for one tile, fetched one tile ahead so the loads
+    // overlap the feature work
     uint2 kraw[TPG + 3], vraw[TPG + 3];
+    float braw[TPG];
     auto fetch = [&](int s0) {
       const int sb = s0 + tg * TPG;
+#pragma unroll
+      for (int u = 0; u < TPG; ++u) braw[u] = sb + u < S ? bp[n0 + sb + u] : 0.0f;
 #pragma unroll
       for (int x = 0; x < TPG + 3; ++x) {
         const int s = sb - 3 + x;
@@ -251,11 +258,9 @@ __global__ __launch_bounds__(512) void stats_mfma_kernel(
     };
     // features of the tile at token s0 -> LDS stage st; prefetches the next
     auto make = [&](int s0, int st) {
-      const int sb = s0 + tg * TPG;
       float sqb[TPG];
 #pragma unroll
-      for (int u = 0; u < TPG; ++u)
-        sqb[u] = sb + u < S ? __builtin_amdgcn_sqrtf(bp[n0 + sb + u]) : 0.0f;
+      for (int u = 0; u < TPG; ++u) sqb[u] = __builtin_amdgcn_sqrtf(braw[u]);  // 0 past S
       float kf[TPG][4], vf[TPG][4];
       conv4(kraw, wk, kf);
       conv4(vraw, wv, vf);
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(512) void stats_mfma_kernel(
     }
   } else {
     // ------------------------------------------------ consumers: MFMAs
-    const int cw = wave - 4;
+    const int cw = wave - NPW;
     const int half = lane >> 5, col = lane & 31;
     f32x16_t acc[BPW];
 #pragma unroll
@@ -357,7 +362,7 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
   }
   if (dtype == HWA_BF16) {
 #define SX_LAUNCH(DD)                                                        \
-  hipLaunchKernelGGL(stats_mfma_kernel<DD>, grid, dim3(512), 0, st,          \
+  hipLaunchKernelGGL(stats_mfma_kernel<DD>, grid, dim3(64 * (sx_pw(DD) + 4)), 0, st, \
                      (const bf16_t*)k, (const bf16_t*)v, beta, conv_k,       \
                      conv_v, (int)conv, A, Bm, g.F, g.S, g.H, g.N)
     if (g.d == 128) SX_LAUNCH(128);
