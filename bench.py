@@ -132,6 +132,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (three times), the "
                          "reference kernel for scaling HBM byte counters")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time the vendor library's square bf16 GEMMs (torch.matmul on "
+                         "hipBLASLt), the practical MFMA rate this GPU sustains, for context")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -151,6 +154,26 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
+        return
+    if args.gemm_ceiling:
+        torch.manual_seed(0)
+        for n, reps in ((8192, 20), (16384, 5)):
+            a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+            b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+            for _ in range(3):
+                c = a @ b
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            print(json.dumps({"gemm": f"bf16 {n}x{n}x{n}", "ms": round(ms, 4),
+                              "TFLOP/s": round(2 * n ** 3 / ms / 1e9, 1)}), flush=True)
+            del a, b, c
         return
 
     cfg = inputs.CONFIGS[args.config]
