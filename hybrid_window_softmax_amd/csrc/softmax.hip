@@ -139,7 +139,7 @@ __device__ __forceinline__ int perm32(int m) {
 // a 1 KB contiguous wave read, or the 256-byte-row layout, takes eight). The
 // contraction index d is read in the same permuted chunk order for K and Q.
 // Tiles are copied global -> LDS by the gfx950 direct load
-// (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
+// (buffer_load_dwordx4 ... lds: lane l of a wave writes its 16 bytes at
 // dst + 16 * l); each lane fetches the global chunk that belongs in its slot.
 //
 // Software pipeline, per key tile i (K runs two tiles ahead of V): one

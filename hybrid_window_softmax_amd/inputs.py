@@ -7,7 +7,7 @@ oracle (tests only) take their inputs from here.
 Each tensor slice is drawn from ``numpy.random.default_rng([seed, tensor_id,
 b, h])`` so that a slice can be regenerated on its own. Tensor ids: q 0, k 1,
 v 2, gate 3, beta 4, alpha 5, text-k 6, text-v 7, text-beta 8, conv_k 9,
-conv_v 10.
+conv_v 10, RMSNorm weight 11 (drawn only when asked for).
 
 Distributions (the workloads of the hybrid attention on video-DiT latents):
 q, k, v, gate ~ N(0, 1); beta ~ U(0, 1) per (head, token); alpha ~ U(lo, hi)
@@ -25,7 +25,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TID = dict(q=0, k=1, v=2, gate=3, beta=4, alpha=5, k_txt=6, v_txt=7,
-           beta_txt=8, conv_k=9, conv_v=10)
+           beta_txt=8, conv_k=9, conv_v=10, rms_weight=11)
 
 # The five workload shapes. Token counts per frame follow 832x480 (52x30
 # latent grid) and 1024x1024 (64x64) canvases at 16x spatial compression.
@@ -124,12 +124,13 @@ def _draw(seed, name, b, h, shape, kind, lo=0.0, hi=1.0, std=1.0):
 
 
 def make(cfg, *, beta_zero=False, alpha_one=False, identity_conv=False,
-         workers=None) -> Inputs:
+         random_rms_weight=False, workers=None) -> Inputs:
     """Generate the inputs of a workload.
 
     ``cfg`` is a key of :data:`CONFIGS` or a config dict. The switches replace
     a tensor by a constant for the special cases the tests use: beta = 0,
-    alpha = 1, identity conv taps (1, 0, 0, 0).
+    alpha = 1, identity conv taps (1, 0, 0, 0); ``random_rms_weight`` draws
+    the RMSNorm weight from U(0.5, 1.5) instead of ones.
     """
     if not isinstance(cfg, dict):
         cfg = CONFIGS[int(cfg)]
@@ -191,7 +192,8 @@ def make(cfg, *, beta_zero=False, alpha_one=False, identity_conv=False,
         else:
             conv_k[h] = _draw(seed, "conv_k", 0, h, (d, 4), "normal", std=0.5)
             conv_v[h] = _draw(seed, "conv_v", 0, h, (d, 4), "normal", std=0.5)
-    rms_weight = np.ones(d, dtype=np.float32)
+    rms_weight = (_draw(seed, "rms_weight", 0, 0, (d,), "uniform", 0.5, 1.5)
+                  if random_rms_weight else np.ones(d, dtype=np.float32))
     return Inputs(cfg=cfg, q=q, k=k, v=v, gate=gate, beta=beta, alpha=alpha,
                   conv_k=conv_k, conv_v=conv_v, rms_weight=rms_weight,
                   k_txt=k_txt, v_txt=v_txt, beta_txt=beta_txt)

@@ -33,10 +33,12 @@ def _worst(got, ref, heads):
     return max(oracle.rel_frobenius(got[b, h], ref[b, h]) for b, h in heads)
 
 
-def _full_check(cfg, rule, text=True, check_intermediates=False):
-    """Whole-tensor parity for workloads the oracle finishes in seconds."""
-    _say(f"case {cfg['name']} rule={rule} text={text}")
-    inp = inputs.make(cfg)
+def _full_check(cfg, rule, text=True, check_intermediates=False, **make_kw):
+    """Whole-tensor parity for workloads the oracle finishes in seconds
+    (``make_kw`` goes to inputs.make)."""
+    _say(f"case {cfg['name']} B={cfg['batch']} H={cfg['heads']} d={cfg['head_dim']} "
+         f"S={cfg['tokens_per_frame']} {cfg['dtype']} rule={rule} text={text} {make_kw}")
+    inp = inputs.make(cfg, **make_kw)
     case = GpuCase(inp)
     B, H = cfg["batch"], cfg["heads"]
     heads = [(b, h) for b in range(B) for h in range(H)]
@@ -170,6 +172,53 @@ def test_bf16_d64_odd_tokens():
     cfg = inputs.tiny_config(frames=7, text_tokens=8, head_dim=64, tokens_per_frame=33,
                              dtype="bf16", heads=3, seed=106, chunk=3)
     _full_check(cfg, "vdn_solve", check_intermediates=True)
+
+
+# ---- degenerate shapes of the method
+
+@pytest.mark.parametrize("dtype,d,S", [("f32", 16, 16), ("bf16", 64, 70)])
+def test_edge_single_frame(dtype, d, S):
+    # F = 1: one chunk, the window is the frame, both scans are one step and
+    # the readout gathers only the text state (P_{-1}, Q_F)
+    cfg = inputs.tiny_config(frames=1, text_tokens=16, head_dim=d, tokens_per_frame=S,
+                             dtype=dtype, heads=2, seed=110)
+    _full_check(cfg, "vdn_solve", check_intermediates=True)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 128)])
+def test_edge_one_token_per_frame(dtype, d):
+    # S = 1: the conv sees no earlier token, a window holds 10 or 15 keys (one
+    # key tile, mostly masked), every key tile spans many frames
+    cfg = inputs.tiny_config(frames=23, text_tokens=8, head_dim=d, tokens_per_frame=1,
+                             dtype=dtype, heads=2, seed=111)
+    _full_check(cfg, "vdn_scaled", check_intermediates=True)
+
+
+@pytest.mark.parametrize("text", [True, False])
+def test_edge_window_covers_everything(text):
+    # radius past the last chunk: no frame is outside any window, so y comes
+    # from the text state alone, and is exactly zero without one
+    cfg = inputs.tiny_config(frames=10, chunk=4, radius=5, text_tokens=16, head_dim=128,
+                             tokens_per_frame=40, dtype="bf16", heads=2, seed=112)
+    got, _ = _full_check(cfg, "vdn_solve", text=text)
+    if not text:
+        assert not np.any(got["y"]), "y must be exactly zero with no far field and no text"
+
+
+def test_edge_chunk_one():
+    # chunk = 1, radius 2: five-frame windows, a bank slot per frame
+    cfg = inputs.tiny_config(frames=9, chunk=1, radius=2, text_tokens=8, tokens_per_frame=16,
+                             seed=113)
+    _full_check(cfg, "vdn_scaled", check_intermediates=True)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_batch2_rms_weight(dtype, d):
+    # B = 2 (batch-major (b, h) indexing in every kernel) and a non-unit
+    # RMSNorm weight
+    cfg = inputs.tiny_config(frames=11, text_tokens=16, head_dim=d, tokens_per_frame=50,
+                             dtype=dtype, heads=2, batch=2, seed=114)
+    _full_check(cfg, "vdn_solve", check_intermediates=True, random_rms_weight=True)
 
 
 def test_text_state_entry_point():
