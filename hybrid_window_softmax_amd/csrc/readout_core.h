@@ -4,11 +4,14 @@
 //   S_t = P_{lo-1} diag(a_t) + Q_{hi+1} diag(b_t)
 //   o_n = S_t q^_n,  q^_n = L2(SiLU(q_n))
 //   y_n = o_n / sqrt(mean(o_n^2) + eps) * w * sigmoid(g_n),  out_n = addend_n + y_n
-// o = S_t q^ runs as a split-bf16 MFMA product (v_mfma_f32_32x32x16_bf16,
-// hi*hi + hi*lo + lo*hi): S_t (hi, lo) sits in LDS as the A operand (rows =
-// output channels), each lane forms q^ of one token in registers as the B
-// operand. The output block then holds one token per lane, so the RMSNorm
-// needs one exchange between the lane halves.
+// o = S_t q^ runs as one fp16 MFMA product per step (v_mfma_f32_32x32x16_f16,
+// fp32 accumulation). S_t sits in LDS as the A operand (rows = output
+// channels), scaled by an exact power of two 2^-k that puts its largest entry
+// in [2^14, 2^15): fp16 then holds every entry down to 2^-28 of the largest
+// with 11 significant bits, and the RMSNorm is unchanged when eps is scaled
+// by 2^-2k as well. Each lane forms q^ of one token in registers as the B
+// operand (|q^| <= 1, so fp16 needs no scaling). The output block holds one
+// token per lane, so the RMSNorm needs one exchange between the lane halves.
 
 #pragma once
 
@@ -16,26 +19,30 @@
 
 namespace hwa {
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
 // LDS working set of one S_t
 template <int D>
 struct ReadoutLds {
-  static constexpr int SP = D + 8;  // padded row (bf16): 16-byte aligned rows
-  bf16_t hi[D * SP];
-  bf16_t lo[D * SP];
+  static constexpr int SP = D + 8;  // padded row (fp16): 16-byte aligned rows
+  _Float16 st[D * SP];
   float dec[2][D];
   int rowexp[2][D];
   float w[D];
   int emax;
+  unsigned vmax;  // bits of the largest |entry| (a non-negative float)
 };
 
 // Forms S_t of frame t of head bh in L (every thread of the NT-thread
 // workgroup calls it; it synchronises the workgroup). The two gathered
-// states' rows are brought to one power-of-two scale 2^E; returns eps
-// scaled by 2^-2E to match.
+// states' rows are brought to one power-of-two scale 2^E, then the whole
+// matrix to 2^-k; returns eps scaled by 2^-2(E+k) to match.
 template <int D, int NT>
 __device__ __forceinline__ float build_st(ReadoutLds<D>& L, const ReadoutArgs& a, int bh,
                                           int t, int tid) {
   constexpr int SP = ReadoutLds<D>::SP;
+  constexpr int NX = D * D / (NT * 8);  // groups of eight columns per thread
+  static_assert(D * D % (NT * 8) == 0, "whole groups");
   const int c = t / a.chunk;
   const int slot_p = max(0, c - a.radius);
   const int slot_q = min(a.nch, c + a.radius + 1);
@@ -50,45 +57,65 @@ __device__ __forceinline__ float build_st(ReadoutLds<D>& L, const ReadoutArgs& a
     L.rowexp[1][j] = eq[j];
     L.w[j] = a.rms_w ? a.rms_w[j] : 1.0f;
   }
-  if (tid == 0) L.emax = INT32_MIN;
+  if (tid == 0) {
+    L.emax = INT32_MIN;
+    L.vmax = 0u;
+  }
   __syncthreads();
   if (tid < D) atomicMax(&L.emax, max(L.rowexp[0][tid], L.rowexp[1][tid]));
   __syncthreads();
   const int E = L.emax;
   const float* Pm = a.bank_p + ((long long)bh * (a.nch + 1) + slot_p) * D * D;
   const float* Qm = a.bank_q + ((long long)bh * (a.nch + 1) + slot_q) * D * D;
-  // eight consecutive columns per step: two 16-byte LDS stores
-  static_assert(D * D % (NT * 8) == 0, "whole steps");
-#pragma unroll 1
-  for (int x = tid * 8; x < D * D; x += NT * 8) {
+  // entries in registers (eight consecutive columns per group) and their max
+  float v[NX][8];
+  float vm = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NX; ++s) {
+    const int x = (tid + s * NT) * 8;
     const int i = x / D, j = x % D;
     const float4 p0 = *(const float4*)&Pm[x], p1 = *(const float4*)&Pm[x + 4];
     const float4 q0 = *(const float4*)&Qm[x], q1 = *(const float4*)&Qm[x + 4];
     const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     const int sp = L.rowexp[0][i] - E, sq = L.rowexp[1][i] - E;
-    bf16x8_t h8, l8;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float v = ldexpf(pv[u], sp) * L.dec[0][j + u] + ldexpf(qv[u], sq) * L.dec[1][j + u];
-      __bf16 h, l;
-      split_bf16(v, h, l);
-      h8[u] = h;
-      l8[u] = l;
+      v[s][u] = ldexpf(pv[u], sp) * L.dec[0][j + u] + ldexpf(qv[u], sq) * L.dec[1][j + u];
+      vm = fmaxf(vm, fabsf(v[s][u]));
     }
-    *(bf16x8_t*)&L.hi[i * SP + j] = h8;
-    *(bf16x8_t*)&L.lo[i * SP + j] = l8;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) vm = fmaxf(vm, __shfl_xor(vm, off));
+  if ((tid & 63) == 0) atomicMax(&L.vmax, __float_as_uint(vm));
+  __syncthreads();
+  // largest entry -> [2^14, 2^15); the scale-up is capped at 2^40 so that the
+  // scaled eps stays finite (an all-zero S_t keeps k = 0)
+  const float m = __uint_as_float(L.vmax);
+  int k = 0;
+  if (m > 0.0f) {
+    int ex;
+    frexpf(m, &ex);
+    k = max(ex - 15, -40);
+  }
+#pragma unroll
+  for (int s = 0; s < NX; ++s) {
+    const int x = (tid + s * NT) * 8;
+    f16x8_t h8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) h8[u] = (_Float16)ldexpf(v[s][u], -k);
+    *(f16x8_t*)&L.st[(x / D) * SP + x % D] = h8;
   }
   __syncthreads();
-  return ldexpf(a.eps, -2 * E);
+  return ldexpf(a.eps, -2 * (E + k));
 }
 
 // y of this lane's token (lane % 32 of the calling wave; the wave must be
 // converged): qraw[kk] holds raw q channels qlane + KOff::at(kk) + 0..7 (any
 // permutation of the channels, applied to S_t's columns alike; qlane is the
-// lane-dependent part, KOff::at a compile-time one). after_features() runs once qraw has been read for the last time
-// (the caller may then overwrite it, e.g. with the next token's q). When
-// `valid`, writes
+// lane-dependent part, KOff::at a compile-time one). after_features() runs
+// once qraw has been read for the last time (the caller may then overwrite
+// it, e.g. with the next token's q). When `valid`, writes
 // out[i] = addend(ib, g4) + y[i] for the lane's channels i = 32 ib + 8 g4 +
 // 4 half + 0..3, with the gate pre-activations gate_at(ib, g4) and addend as
 // four packed bf16 each.
@@ -100,21 +127,20 @@ __device__ __forceinline__ void readout_token(const ReadoutLds<D>& L, float eps_
   constexpr int SP = ReadoutLds<D>::SP;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
-  // q^ = L2(SiLU(q)): the squared norm first, then SiLU again per MFMA step
-  // (recomputing it is cheaper than holding d floats per lane)
-  auto silu_pair = [&](uint32_t w, float& a, float& b) __attribute__((always_inline)) {
-    a = silu_f(__uint_as_float(w << 16));
-    b = silu_f(__uint_as_float(w & 0xffff0000u));
-  };
+  // q^ = L2(SiLU(q)): SiLU once into fp32 registers, the norm, then fp16 per
+  // MFMA step
+  float fq[D / 16][8];
   float ss = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float a, b;
-      silu_pair(qraw[kk][u], a, b);
-      ss = fmaf(a, a, fmaf(b, b, ss));
+      const uint32_t w = qraw[kk][u];
+      fq[kk][2 * u] = silu_f(__uint_as_float(w << 16));
+      fq[kk][2 * u + 1] = silu_f(__uint_as_float(w & 0xffff0000u));
+      ss = fmaf(fq[kk][2 * u], fq[kk][2 * u], fmaf(fq[kk][2 * u + 1], fq[kk][2 * u + 1], ss));
     }
+  after_features();
   ss += __shfl_xor(ss, 32);
   const float inv = inv_l2(ss);
   f32x16_t acc[D / 32];
@@ -128,26 +154,13 @@ __device__ __forceinline__ void readout_token(const ReadoutLds<D>& L, float eps_
   asm volatile("" : "+v"(ro_base));
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    bf16x8_t qh, ql;
+    f16x8_t qh;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float a, b;
-      silu_pair(qraw[kk][u], a, b);
-      __bf16 h, l;
-      split_bf16(a * inv, h, l);
-      qh[2 * u] = h;
-      ql[2 * u] = l;
-      split_bf16(b * inv, h, l);
-      qh[2 * u + 1] = h;
-      ql[2 * u + 1] = l;
-    }
-    if (kk == D / 16 - 1) after_features();
+    for (int u = 0; u < 8; ++u) qh[u] = (_Float16)(fq[kk][u] * inv);
 #pragma unroll
     for (int ib = 0; ib < D / 32; ++ib) {
-      const int ro = ro_base + ib * 32 * SP + KOff::at(kk);
-      const bf16x8_t ah = *(const bf16x8_t*)&L.hi[ro];
-      const bf16x8_t alo = *(const bf16x8_t*)&L.lo[ro];
-      acc[ib] = mfma32x3(ah, alo, qh, ql, acc[ib]);
+      const f16x8_t as = *(const f16x8_t*)&L.st[ro_base + ib * 32 * SP + KOff::at(kk)];
+      acc[ib] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, qh, acc[ib], 0, 0, 0);
     }
   }
   float sq = 0.0f;

@@ -3,9 +3,10 @@
 // [lo_t, hi_t] with scale 1/sqrt(d), no mask inside the window.
 //
 // Because windows are chunk-aligned, every query of chunk c shares one key
-// range [lo_c * S, (hi_c + 1) * S). A workgroup takes 128 consecutive queries
-// of one chunk (a tile may span frames of the chunk, never two chunks) and
-// streams the chunk's key range through LDS in tiles of 64 keys.
+// range [lo_c * S, (hi_c + 1) * S). A bf16 workgroup takes 256 consecutive
+// queries of one chunk (the fp32 one 128; a tile may span frames of the
+// chunk, never two chunks) and streams the chunk's key range through LDS in
+// tiles of 64 keys (fp32: 32).
 //
 // bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16), per wave of 32 queries:
 //   S^T[key][query] = K . Q^T  with K rows from LDS as the A operand and the
