@@ -140,10 +140,16 @@ __global__ __launch_bounds__(256) void scan_kernel(
 // and holds it in the MFMA accumulator layout (lane: column lane % 32, rows
 // 8*(r/4) + 4*(lane/32) + r%4). Per frame:
 //   X = S diag(alpha) + c1 2^-e B  -> split to bf16 (hi, lo) in LDS (double
-//   buffered, one barrier per frame);
-//   S = X M (+ c2 2^-e B): A operand = rows of X from LDS, B operand = rows
-//   of M (M is symmetric, so row n is the needed column n), read from global
-//   memory one frame ahead into registers.
+//   buffered);
+//   M_f -> split to bf16 (hi, lo) in LDS: every thread splits the part it
+//   read, one frame ahead, with loads where each instruction covers 1 KB of
+//   consecutive memory (a per-lane row read touched 64 cache lines per
+//   instruction and left the step waiting on the vector memory pipeline);
+//   S = X M (+ c2 2^-e B): A operand = rows of X, B operand = rows of M (M is
+//   symmetric, so row n is the needed column n), both from LDS; the three
+//   partial products accumulate separately so the MFMAs do not wait on each
+//   other.
+// Two barriers per frame: X and M visible; everyone done reading M.
 // Row exponents (diverging sana_scaled only, SANA = true): the row max over
 // all d columns is combined across waves through LDS.
 template <int D, bool SANA>
@@ -153,9 +159,13 @@ __global__ __launch_bounds__(2 * D) void scan_mfma_kernel(
     const float* __restrict__ text_state, float text_scale,
     float* __restrict__ bank_p, float* __restrict__ bank_q,
     int32_t* __restrict__ bank_e, int F, int chunk, int nch, int BH) {
-  constexpr int XP = D + 8;  // padded X row (bf16)
+  constexpr int NT = 2 * D;    // threads
+  constexpr int XP = D + 8;    // padded X / M row (bf16)
+  constexpr int MV = D * D / 4 / NT;  // float4 of M per thread and frame
   __shared__ __attribute__((aligned(16))) bf16_t x_hi[2][32 * XP];
   __shared__ __attribute__((aligned(16))) bf16_t x_lo[2][32 * XP];
+  __shared__ __attribute__((aligned(16))) bf16_t m_hi[D * XP];
+  __shared__ __attribute__((aligned(16))) bf16_t m_lo[D * XP];
   __shared__ unsigned rmax[2][32];
 
   const int tid = threadIdx.x;
@@ -191,21 +201,39 @@ __global__ __launch_bounds__(2 * D) void scan_mfma_kernel(
   };
   store(dir == 0 ? 0 : nch);
 
-  // prefetch of the next frame: M rows n (k = 16*kk + 8*half .. +7), B, alpha
-  float mraw[D / 16][8], braw[16], anext;
+  // the next frame, read ahead: M_f in consecutive float4 (element 4*(j*NT +
+  // tid) .. +3 in mraw[j]), this block's B rows, alpha
+  float4 mraw[MV];
+  float braw[16], anext;
   auto fetch = [&](int f) {
     const long long mo = ((long long)bh * F + f) * D * D;
-    const float* mrow = Msrc + mo + (long long)n * D + half * 8;
+    const float4* m4 = (const float4*)(Msrc + mo);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const float4 a = *(const float4*)(mrow + kk * 16);
-      const float4 b = *(const float4*)(mrow + kk * 16 + 4);
-      mraw[kk][0] = a.x; mraw[kk][1] = a.y; mraw[kk][2] = a.z; mraw[kk][3] = a.w;
-      mraw[kk][4] = b.x; mraw[kk][5] = b.y; mraw[kk][6] = b.z; mraw[kk][7] = b.w;
-    }
+    for (int j = 0; j < MV; ++j) mraw[j] = m4[j * NT + tid];
 #pragma unroll
     for (int r = 0; r < 16; ++r) braw[r] = Bm[mo + (long long)(rb * 32 + rowof(r)) * D + n];
     anext = alpha[((long long)bh * F + f) * D + n];
+  };
+  // this thread's part of the M operand (hi, lo) -> LDS
+  auto put_m = [&]() {
+#pragma unroll
+    for (int j = 0; j < MV; ++j) {
+      const int el = 4 * (j * NT + tid);
+      const int r = el / D, c = el % D;
+      const float mv[4] = {mraw[j].x, mraw[j].y, mraw[j].z, mraw[j].w};
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t h4, l4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float m = SANA ? ((r == c + u ? 1.0f : 0.0f) - cs * mv[u]) : mv[u];
+        __bf16 h, l;
+        split_bf16(m, h, l);
+        h4[u] = h;
+        l4[u] = l;
+      }
+      *(bf16x4_t*)&m_hi[r * XP + c] = h4;
+      *(bf16x4_t*)&m_lo[r * XP + c] = l4;
+    }
   };
   fetch(dir == 0 ? 0 : F - 1);
 
@@ -224,36 +252,37 @@ __global__ __launch_bounds__(2 * D) void scan_mfma_kernel(
       x_hi[buf][rowof(r) * XP + n] = __builtin_bit_cast(bf16_t, h);
       x_lo[buf][rowof(r) * XP + n] = __builtin_bit_cast(bf16_t, l);
     }
-    // ---- this frame's M operand (hi, lo); then start fetching the next one
-    bf16x8_t mh[D / 16], ml[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float mv = SANA ? ((16 * kk + 8 * half + u == n ? 1.0f : 0.0f) -
-                                 cs * mraw[kk][u])
-                              : mraw[kk][u];
-        __bf16 h, l;
-        split_bf16(mv, h, l);
-        mh[kk][u] = h;
-        ml[kk][u] = l;
-      }
+    // ---- this frame's M operand -> LDS (the previous frame's readers are
+    // done: barrier at the end of the last step); then fetch the next frame
+    put_m();
     if (i + 1 < F) fetch(dir == 0 ? f + 1 : f - 1);
     __syncthreads();
-    // ---- S = X M (+ c2 2^-e B)
-    f32x16_t acc;
+    // ---- S = X M (+ c2 2^-e B), the three split products on their own
+    // accumulators
+    f32x16_t acc, acc1, acc2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = c2 * bcur[r];
+    for (int r = 0; r < 16; ++r) {
+      acc[r] = c2 * bcur[r];
+      acc1[r] = 0.0f;
+      acc2[r] = 0.0f;
+    }
     const bf16_t* xh = &x_hi[buf][col * XP + half * 8];
     const bf16_t* xl = &x_lo[buf][col * XP + half * 8];
+    const bf16_t* mh = &m_hi[n * XP + half * 8];
+    const bf16_t* ml = &m_lo[n * XP + half * 8];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const bf16x8_t ah = *(const bf16x8_t*)(xh + kk * 16);
       const bf16x8_t al = *(const bf16x8_t*)(xl + kk * 16);
-      acc = mfma32x3(ah, al, mh[kk], ml[kk], acc);
+      const bf16x8_t bh = *(const bf16x8_t*)(mh + kk * 16);
+      const bf16x8_t bl = *(const bf16x8_t*)(ml + kk * 16);
+      acc = mfma32(ah, bh, acc);
+      acc1 = mfma32(ah, bl, acc1);
+      acc2 = mfma32(al, bh, acc2);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = acc[r];
+    for (int r = 0; r < 16; ++r) sv[r] = acc[r] + (acc1[r] + acc2[r]);
+    __syncthreads();  // M and this X buffer are read: free for the next frame
     if (SANA) {
       // row max |S| over all columns: 32 lanes of a half, then the waves
 #pragma unroll
