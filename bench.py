@@ -29,7 +29,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector, packed) / fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_traffic.json")
-SOFTMAX_SRC = os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", "softmax.hip")
+# the softmax kernel's sources (the kernel and the readout epilogue it includes)
+SOFTMAX_SRCS = [os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", n)
+                for n in ("softmax.hip", "readout_core.h", "hwa_internal.h")]
 
 
 def log(*a):
@@ -73,14 +75,22 @@ def algorithmic_work(cfg):
     }
 
 
+def softmax_sources_sha256():
+    """sha256 over the softmax kernel's source files, in order."""
+    h = hashlib.sha256()
+    for path in SOFTMAX_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def softmax_traffic():
     """HBM bytes per softmax launch from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was taken."""
+    summary, or None when the kernel's sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        with open(SOFTMAX_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = softmax_sources_sha256()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != sha:
