@@ -55,7 +55,9 @@ bool make_geom(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
   return true;
 }
 
-hwa_workspace_layout compute_layout(const Geom& g, int dtype) {
+// The layout of the documented intermediates; the softmax kernel's
+// work-queue counters follow them (*sched, if given), inside L.total.
+hwa_workspace_layout compute_layout(const Geom& g, int dtype, size_t* sched = nullptr) {
   hwa_workspace_layout L;
   const size_t bh = (size_t)g.B * g.H;
   const size_t dd = (size_t)g.d * g.d;
@@ -75,6 +77,8 @@ hwa_workspace_layout compute_layout(const Geom& g, int dtype) {
   L.bank_e = take(2 * bh * (g.nch + 1) * g.d * sizeof(int32_t));
   const size_t Np = (size_t)((g.N + 63) / 64 * 64);
   L.v_t = take(dtype == HWA_BF16 ? bh * g.d * Np * sizeof(bf16_t) : 0);
+  const size_t s = take(hwa::HWA_SCHED_WORDS * sizeof(unsigned));
+  if (sched) *sched = s;
   L.total = off;
   return L;
 }
@@ -175,7 +179,8 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
       (alpha && !aligned(alpha, 4)) || (text_state && !aligned(text_state, 4)))
     return HWA_ERR_INVALID_ARG;
 
-  const hwa_workspace_layout L = compute_layout(g, p->dtype);
+  size_t sched_off = 0;
+  const hwa_workspace_layout L = compute_layout(g, p->dtype, &sched_off);
   if (!p->workspace || p->workspace_bytes < L.total ||
       !aligned(p->workspace, kAlign))
     return HWA_ERR_WORKSPACE;
@@ -207,6 +212,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   int32_t* bank_e = (int32_t*)(ws + L.bank_e);
   float* decay = (float*)(ws + L.decay);
   bf16_t* v_t = (bf16_t*)(ws + L.v_t);
+  unsigned* sched = (unsigned*)(ws + sched_off);
 
   void* const* ev = p->stage_events;
   auto mark = [&](int i) {
@@ -216,7 +222,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   // readout in the epilogue (raw q only: no RoPE'd q on that path)
   const bool fuse = do_sm && do_lin && p->dtype == HWA_BF16 && qs == q;
   if (mark(0) != hipSuccess) return HWA_ERR_HIP;
-  if (hwa::launch_window_table(g, lohi, st) != hipSuccess) return HWA_ERR_HIP;
+  if (hwa::launch_window_table(g, lohi, st, sched) != hipSuccess) return HWA_ERR_HIP;
   if (mark(1) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && hwa::launch_stats(g, p->dtype, k, v, beta, p->conv_k,
                                   p->conv_v, true, A, Bm, st) != hipSuccess)
@@ -244,7 +250,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                             p->rms_weight, p->rms_eps, g.F, g.chunk, g.radius,
                             g.nch, g.B * g.H};
   if (do_sm && hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out, st,
-                                   fuse ? &ra : nullptr) != hipSuccess)
+                                   fuse ? &ra : nullptr, sched) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(7) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && !fuse &&

@@ -78,9 +78,15 @@ __device__ __forceinline__ void window_of(int t, int F, int chunk, int radius,
   hi = h > F - 1 ? F - 1 : h;
 }
 
+// Work-queue counters of the bf16 softmax kernel (one per XCD), kept in the
+// workspace and zeroed by the window-table kernel, which runs first.
+constexpr int HWA_SCHED_WORDS = 8;
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipGetLastError() after its launch(es).
-hipError_t launch_window_table(const Geom& g, int32_t* lohi, hipStream_t st);
+// The window table; also zeroes sched[0 .. HWA_SCHED_WORDS) when sched is not null.
+hipError_t launch_window_table(const Geom& g, int32_t* lohi, hipStream_t st,
+                               unsigned* sched = nullptr);
 
 // Per-call inputs of the linear-branch readout (device pointers; bank_e holds
 // the power-of-two exponents of the prefix bank rows, then the suffix's)
@@ -97,11 +103,12 @@ struct ReadoutArgs {
 
 // fuse != null (bf16 only): the softmax kernel also adds the linear-branch
 // readout y = RMSNorm(S_t q^) * sigmoid(gate) of its queries (q must then be
-// the raw q) before it writes out.
+// the raw q) before it writes out. sched (bf16 only): HWA_SCHED_WORDS
+// counters, zero at launch (the kernel leaves them non-zero).
 hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
                           const int32_t* lohi, void* out, hipStream_t st,
-                          const ReadoutArgs* fuse = nullptr);
+                          const ReadoutArgs* fuse, unsigned* sched);
 
 hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
                              hipStream_t st);

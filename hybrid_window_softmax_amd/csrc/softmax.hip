@@ -49,6 +49,8 @@ constexpr int SM_NW = 8;                // waves per workgroup
 constexpr int SM_QT = 32 * SM_NW;       // queries per workgroup
 constexpr int SM_KT = 64;   // keys per LDS tile
 constexpr int SM_THREADS = 64 * SM_NW;
+// workgroups per XCD beyond its share of the tiles (two rounds of its 32 CUs)
+constexpr int SM_SPARE = 64;
 #ifndef SM_PREFETCH
 #define SM_PREFETCH 2
 #endif
@@ -59,8 +61,9 @@ __host__ __device__ inline long long round_up64(long long n) {
 
 // ---------------------------------------------------------------- window table
 __global__ void window_table_kernel(int F, int chunk, int radius,
-                                    int32_t* lohi) {
+                                    int32_t* lohi, unsigned* zero, int nzero) {
   int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (zero && t < nzero) zero[t] = 0u;  // work-queue counters of the softmax kernel
   if (t >= F) return;
   int lo, hi;
   window_of(t, F, chunk, radius, lo, hi);
@@ -68,11 +71,12 @@ __global__ void window_table_kernel(int F, int chunk, int radius,
   lohi[F + t] = hi;
 }
 
-hipError_t launch_window_table(const Geom& g, int32_t* lohi, hipStream_t st) {
+hipError_t launch_window_table(const Geom& g, int32_t* lohi, hipStream_t st,
+                               unsigned* sched) {
   int threads = 256;
   int blocks = (g.F + threads - 1) / threads;
   hipLaunchKernelGGL(window_table_kernel, dim3(blocks), dim3(threads), 0, st,
-                     g.F, g.chunk, g.radius, lohi);
+                     g.F, g.chunk, g.radius, lohi, sched, HWA_SCHED_WORDS);
   return hipGetLastError();
 }
 
@@ -160,7 +164,8 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ vt, const int32_t* __restrict__ lohi,
     bf16_t* __restrict__ out, int F, int S, int chunk, int nch, long long N,
-    long long Np, int tiles_per_chunk, float scale_log2, ReadoutArgs ra, int fuse) {
+    long long Np, int tiles_per_chunk, float scale_log2, ReadoutArgs ra, int fuse,
+    unsigned* __restrict__ sched, int ntiles_total) {
   // the body uses device-only lambdas; the host pass needs only the stub
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KC = D / 8;          // 16-byte chunks per key
@@ -179,13 +184,33 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5;
   const int col = lane & 31;
-  // XCD-aware order: workgroup p is dispatched to XCD p % 8; give each XCD a
-  // contiguous run of logical tiles so that the query tiles of one (head,
-  // chunk), which all stream the same key range, share that XCD's L2
-  const int G = gridDim.x;
-  const int p = blockIdx.x;
-  const int xq = G / 8, xr = G % 8, xcd = p % 8;
-  const int L = xcd * xq + min(xcd, xr) + p / 8;
+  // Work queues. The logical tiles (head-major, then chunk, then query tile)
+  // form 8 contiguous ranges, one per XCD (workgroup p runs on XCD p % 8), so
+  // that the query tiles of one (head, chunk), which all stream the same key
+  // range, share that XCD's L2. A workgroup takes the next tile of its XCD's
+  // range from an atomic counter (sched[x], zero at launch) and, once that
+  // range is empty, of the other ranges. The grid holds a few more workgroups
+  // per XCD than its range has tiles: an XCD that runs faster than the others
+  // then takes over their last tiles instead of idling at the end, and the
+  // workgroups that find every range empty exit at once.
+  __shared__ int next_tile;
+  if (tid == 0) {
+    const int xq = ntiles_total / 8, xr = ntiles_total % 8;
+    const int home = blockIdx.x % 8;
+    int lt = -1;
+    for (int pr = 0; pr < 8; ++pr) {
+      const int x = (home + pr) % 8;
+      const unsigned i = atomicAdd(&sched[x], 1u);
+      if (i < (unsigned)(xq + (x < xr ? 1 : 0))) {
+        lt = x * xq + min(x, xr) + (int)i;
+        break;
+      }
+    }
+    next_tile = lt;
+  }
+  __syncthreads();
+  const int L = __builtin_amdgcn_readfirstlane(next_tile);
+  if (L < 0) return;
   const int per_bh = tiles_per_chunk * nch;
   const int bh = L / per_bh;
   const int c = (L % per_bh) / tiles_per_chunk;
@@ -657,19 +682,21 @@ __global__ __launch_bounds__(128) void softmax_f32_kernel(
 hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
                           const int32_t* lohi, void* out, hipStream_t st,
-                          const ReadoutArgs* fuse) {
+                          const ReadoutArgs* fuse, unsigned* sched) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)g.d);
   const int qpc = g.chunk * g.S;  // queries of a full chunk
   if (dtype == HWA_BF16) {
     const int tpc = (qpc + SM_QT - 1) / SM_QT;
-    dim3 grid(tpc * g.nch * g.B * g.H);
+    const int ntiles = tpc * g.nch * g.B * g.H;
+    // SM_SPARE extra workgroups per XCD take over tiles from slower XCDs
+    dim3 grid(ntiles + 8 * SM_SPARE);
     const long long Np = round_up64(g.N);
     const ReadoutArgs ra = fuse ? *fuse : ReadoutArgs{};
 #define SM_LAUNCH(DD)                                                        \
   hipLaunchKernelGGL(softmax_bf16_kernel<DD>, grid, dim3(SM_THREADS), 0, st, \
                      (const bf16_t*)q, (const bf16_t*)k, v_t, lohi,          \
                      (bf16_t*)out, g.F, g.S, g.chunk, g.nch, g.N, Np, tpc,   \
-                     scale_log2, ra, fuse ? 1 : 0)
+                     scale_log2, ra, fuse ? 1 : 0, sched, ntiles)
     if (g.d == 128) SM_LAUNCH(128);
     else SM_LAUNCH(64);
 #undef SM_LAUNCH

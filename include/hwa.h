@@ -123,7 +123,8 @@ typedef struct {
  *                                 unless a row exceeds 2^64, i.e. a diverging
  *                                 sana_scaled scan)
  *   v_t      bf16 [B, H, d, N]    v transposed (bf16 only, else unused)
- * n_ch = ceil(F / chunk).
+ * n_ch = ceil(F / chunk). The last 256 bytes before `total` are the work-queue
+ * counters of the softmax kernel (internal; each call zeroes them itself).
  */
 typedef struct {
   size_t lohi, stat_a, stat_b, map_m, bank_p, bank_q, decay, bank_e, v_t;
