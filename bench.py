@@ -9,7 +9,7 @@ records at its kernel boundaries on the call's stream, the roofline of the
 dominant kernel (the windowed softmax, bf16 MFMA) and the fp64 CPU oracle
 timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--rule vdn_solve]
+    python bench.py [--steps K] [--warmup W] [--workload long-clip-832x480-85f] [--rule vdn_solve]
 """
 
 from __future__ import annotations
@@ -135,7 +135,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", default="long-clip-832x480-85f",
+                    help="a name in hybrid_window_softmax_amd.inputs.WORKLOADS")
     ap.add_argument("--rule", default="vdn_solve")
     ap.add_argument("--cpu-heads", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -186,8 +187,8 @@ def main():
             del a, b, c
         return
 
-    cfg = inputs.CONFIGS[args.config]
-    log(f"bench: generating config {args.config} ({cfg['name']})")
+    cfg = inputs.WORKLOADS[args.workload]
+    log(f"bench: generating workload {args.workload}")
     inp = inputs.make(cfg)
     dev = torch.device("cuda:0")
     bf = cfg["dtype"] == "bf16"

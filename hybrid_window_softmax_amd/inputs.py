@@ -27,26 +27,26 @@ import numpy as np
 TID = dict(q=0, k=1, v=2, gate=3, beta=4, alpha=5, k_txt=6, v_txt=7,
            beta_txt=8, conv_k=9, conv_v=10, rms_weight=11)
 
-# The five workload shapes. Token counts per frame follow 832x480 (52x30
+# The five workloads, by name. Token counts per frame follow 832x480 (52x30
 # latent grid) and 1024x1024 (64x64) canvases at 16x spatial compression.
-CONFIGS = {
-    0: dict(name="tiny-f32", batch=1, heads=1, head_dim=16, frames=10,
+WORKLOADS = {
+    "tiny-f32": dict(name="tiny-f32", batch=1, heads=1, head_dim=16, frames=10,
             tokens_per_frame=16, dtype="f32", chunk=5, radius=1,
             rules=("vdn_solve",), c=0.5, text_tokens=0, alpha=(0.8, 1.0),
             seed=0),
-    1: dict(name="small-bf16-text", batch=1, heads=8, head_dim=64, frames=20,
+    "small-bf16-text": dict(name="small-bf16-text", batch=1, heads=8, head_dim=64, frames=20,
             tokens_per_frame=256, dtype="bf16", chunk=5, radius=1,
             rules=("vdn_solve",), c=0.5, text_tokens=64, alpha=(0.8, 1.0),
             seed=1),
-    2: dict(name="clip-832x480-31f", batch=1, heads=24, head_dim=128,
+    "clip-832x480-31f": dict(name="clip-832x480-31f", batch=1, heads=24, head_dim=128,
             frames=31, tokens_per_frame=1560, dtype="bf16", chunk=5,
             radius=1, rules=("vdn_solve",), c=0.5, text_tokens=256,
             alpha=(0.9, 1.0), seed=2),
-    3: dict(name="long-clip-832x480-85f", batch=1, heads=24, head_dim=128,
+    "long-clip-832x480-85f": dict(name="long-clip-832x480-85f", batch=1, heads=24, head_dim=128,
             frames=85, tokens_per_frame=1560, dtype="bf16", chunk=5,
             radius=1, rules=("vdn_solve", "sana_scaled", "vdn_scaled"),
             c=0.5, text_tokens=256, alpha=(0.9, 1.0), seed=3),
-    4: dict(name="canvas-1024x1024-64f", batch=1, heads=24, head_dim=128,
+    "canvas-1024x1024-64f": dict(name="canvas-1024x1024-64f", batch=1, heads=24, head_dim=128,
             frames=64, tokens_per_frame=4096, dtype="bf16", chunk=5,
             radius=1, rules=("vdn_solve",), c=0.5, text_tokens=256,
             alpha=(0.95, 1.0), seed=4),
@@ -127,13 +127,13 @@ def make(cfg, *, beta_zero=False, alpha_one=False, identity_conv=False,
          random_rms_weight=False, workers=None) -> Inputs:
     """Generate the inputs of a workload.
 
-    ``cfg`` is a key of :data:`CONFIGS` or a config dict. The switches replace
+    ``cfg`` is a key of :data:`WORKLOADS` or a workload dict. The switches replace
     a tensor by a constant for the special cases the tests use: beta = 0,
     alpha = 1, identity conv taps (1, 0, 0, 0); ``random_rms_weight`` draws
     the RMSNorm weight from U(0.5, 1.5) instead of ones.
     """
     if not isinstance(cfg, dict):
-        cfg = CONFIGS[int(cfg)]
+        cfg = WORKLOADS[cfg]
     cfg = dict(cfg)
     B, H, d = cfg["batch"], cfg["heads"], cfg["head_dim"]
     F, S = cfg["frames"], cfg["tokens_per_frame"]

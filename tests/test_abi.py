@@ -44,8 +44,8 @@ def test_window_bounds_bit_exact(F):
             assert lo == olo.tolist() and hi == ohi.tolist()
 
 
-def test_window_bounds_configs():
-    for cfg in inputs.CONFIGS.values():
+def test_window_bounds_workloads():
+    for cfg in inputs.WORKLOADS.values():
         lo, hi = hwa.window_bounds(cfg["frames"], cfg["chunk"], cfg["radius"])
         olo, ohi = oracle.window_bounds(cfg["frames"], cfg["chunk"], cfg["radius"])
         assert lo == olo.tolist() and hi == ohi.tolist()
@@ -148,7 +148,7 @@ def test_unsupported_and_workspace_codes():
 
 
 def test_workspace_layout_is_consistent():
-    for cfg in inputs.CONFIGS.values():
+    for cfg in inputs.WORKLOADS.values():
         p = hwa.make_params(cfg["batch"], cfg["heads"], cfg["head_dim"],
                             1 if cfg["dtype"] == "bf16" else 0)
         L = hwa.workspace_layout(cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"], p)

@@ -89,8 +89,8 @@ def _check_intermediates(case, ws, inter, cfg, tol):
             assert ep <= max(tol, 1e-5) and eq <= max(tol, 1e-5), (m, ep, eq)
 
 
-def test_config0_tiny_fp32():
-    got, ref = _full_check(inputs.CONFIGS[0], "vdn_solve", check_intermediates=True)
+def test_tiny_fp32_160tok():
+    got, ref = _full_check(inputs.WORKLOADS["tiny-f32"], "vdn_solve", check_intermediates=True)
     # no far field and no text state: the linear branch is exactly zero
     assert not np.any(got["y"])
 
@@ -132,8 +132,8 @@ def test_beta_zero_no_text_is_softmax():
     assert torch.equal(out, sm)
 
 
-def test_config1_small_bf16_text():
-    _full_check(inputs.CONFIGS[1], "vdn_solve", check_intermediates=True)
+def test_small_bf16_text_5120tok():
+    _full_check(inputs.WORKLOADS["small-bf16-text"], "vdn_solve", check_intermediates=True)
 
 
 @pytest.mark.parametrize("rule", oracle.RULES)
@@ -222,7 +222,7 @@ def test_batch2_rms_weight(dtype, d):
 
 
 def test_text_state_entry_point():
-    for cfg in (inputs.CONFIGS[1], inputs.tiny_config(text_tokens=16)):
+    for cfg in (inputs.WORKLOADS["small-bf16-text"], inputs.tiny_config(text_tokens=16)):
         inp = inputs.make(cfg)
         case = GpuCase(inp)
         got = case.text_state.cpu().numpy()
@@ -233,12 +233,12 @@ def test_text_state_entry_point():
 
 
 # ---------------------------------------------------------------- full sizes
-def _sampled_check(cfg_id, rules):
+def _sampled_check(name, rules):
     """Full-size workload in the launch configuration the benchmark times:
     the softmax branch and the sum on sampled query rows of every head, the
     linear branch on two whole heads."""
-    cfg = inputs.CONFIGS[cfg_id]
-    _say(f"case config{cfg_id} {cfg['name']}: generating inputs")
+    cfg = inputs.WORKLOADS[name]
+    _say(f"case {name}: generating inputs")
     inp = inputs.make(cfg)
     case = GpuCase(inp)
     rows = sample_rows(cfg)
@@ -246,7 +246,7 @@ def _sampled_check(cfg_id, rules):
     tol = TOL[cfg["dtype"]]
     heads_full = [0, H - 1]
     for rule in rules:
-        _say(f"case config{cfg_id} rule={rule}")
+        _say(f"case {name} rule={rule}")
         out, ws = case.run(rule, 0)
         sm, _ = case.run(rule, hwa.FLAG_SOFTMAX_ONLY, workspace=ws)
         lin, _ = case.run(rule, hwa.FLAG_LINEAR_ONLY, workspace=ws)
@@ -266,18 +266,18 @@ def _sampled_check(cfg_id, rules):
                                    oracle.rel_frobenius(o_rows[h], ref_sm + y_ref[rows]))
         _say(f"  {rule}: " + ", ".join(f"{k} {v:.3e}" for k, v in worst.items()))
         for k, v in worst.items():
-            assert v <= tol, f"config{cfg_id} {rule} {k}: {v:.3e} > {tol:g}"
+            assert v <= tol, f"{name} {rule} {k}: {v:.3e} > {tol:g}"
         del out, sm, lin, ws
         torch.cuda.empty_cache()
 
 
-def test_config2_full_size_sampled():
-    _sampled_check(2, ("vdn_solve",))
+def test_clip_48360tok_sampled():
+    _sampled_check("clip-832x480-31f", ("vdn_solve",))
 
 
-def test_config3_full_size_sampled_all_rules():
-    _sampled_check(3, oracle.RULES)
+def test_long_clip_132600tok_sampled_all_rules():
+    _sampled_check("long-clip-832x480-85f", oracle.RULES)
 
 
-def test_config4_full_size_sampled():
-    _sampled_check(4, ("vdn_solve",))
+def test_canvas_262144tok_sampled():
+    _sampled_check("canvas-1024x1024-64f", ("vdn_solve",))

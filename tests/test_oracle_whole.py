@@ -38,8 +38,8 @@ def _run(inp, rule="vdn_solve", text=True, flip=False):
     return outs
 
 
-def test_config0_has_no_far_field():
-    inp = inputs.make(0)
+def test_tiny_workload_has_no_far_field():
+    inp = inputs.make("tiny-f32")
     (out, o_sm, y, _), = _run(inp)
     # F = 10 frames with chunk 5, radius 1: every window is [0, 9] and there is
     # no text state, so the linear branch reads a zero state: y == 0 exactly
