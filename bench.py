@@ -66,11 +66,14 @@ def algorithmic_work(cfg):
         "inverse": dict(bytes=2 * mat, flops=2 * d * d * d * B * H * F),
         "scan": dict(bytes=4 * mat + 2 * B * H * F * d * 4 + 2 * bank,
                      flops=2 * 2 * d * d * d * B * H * F),
-        "decay": dict(bytes=B * H * F * d * 4 * 3, flops=0),
-        "readout": dict(bytes=4 * tok * d * io + 2 * bank, flops=2 * d * d * tok),
+        # decay products, then S_t of every frame (reads both gathered bank
+        # states and the decays, writes fp16 S_t)
+        "decay+state": dict(bytes=B * H * F * (3 * d * 4 + 2 * d * d * 4 + 2 * d * 4 + d * d * 2),
+                            flops=3 * d * d * B * H * F),
+        "readout": dict(bytes=4 * tok * d * io + B * H * F * d * d * 2, flops=2 * d * d * tok),
         # bf16 calls fuse the readout into the softmax kernel's epilogue: q and
-        # out are not re-read, the gate and the banks are
-        "softmax+readout": dict(bytes=4 * tok * d * io + tok * d * io + 2 * bank,
+        # out are not re-read, the gate and S_t are
+        "softmax+readout": dict(bytes=4 * tok * d * io + tok * d * io + B * H * F * d * d * 2,
                                 flops=4 * d * window_pairs(cfg) * B * H + 2 * d * d * tok),
     }
 

@@ -55,9 +55,14 @@ bool make_geom(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
   return true;
 }
 
-// The layout of the documented intermediates; the softmax kernel's
-// work-queue counters follow them (*sched, if given), inside L.total.
-hwa_workspace_layout compute_layout(const Geom& g, int dtype, size_t* sched = nullptr) {
+// Internal workspace regions that follow the documented intermediates
+// (inside L.total): the bf16 readouts' S_t of every frame (fp16) and its
+// scaled eps, then the softmax kernel's work-queue counters.
+struct Internal {
+  size_t st16 = 0, st_eps = 0, sched = 0;
+};
+
+hwa_workspace_layout compute_layout(const Geom& g, int dtype, Internal* in = nullptr) {
   hwa_workspace_layout L;
   const size_t bh = (size_t)g.B * g.H;
   const size_t dd = (size_t)g.d * g.d;
@@ -77,8 +82,11 @@ hwa_workspace_layout compute_layout(const Geom& g, int dtype, size_t* sched = nu
   L.bank_e = take(2 * bh * (g.nch + 1) * g.d * sizeof(int32_t));
   const size_t Np = (size_t)((g.N + 63) / 64 * 64);
   L.v_t = take(dtype == HWA_BF16 ? bh * g.d * Np * sizeof(bf16_t) : 0);
-  const size_t s = take(hwa::HWA_SCHED_WORDS * sizeof(unsigned));
-  if (sched) *sched = s;
+  Internal x;
+  x.st16 = take(dtype == HWA_BF16 ? bh * g.F * dd * sizeof(_Float16) : 0);
+  x.st_eps = take(dtype == HWA_BF16 ? bh * g.F * sizeof(float) : 0);
+  x.sched = take(hwa::HWA_SCHED_WORDS * sizeof(unsigned));
+  if (in) *in = x;
   L.total = off;
   return L;
 }
@@ -179,8 +187,8 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
       (alpha && !aligned(alpha, 4)) || (text_state && !aligned(text_state, 4)))
     return HWA_ERR_INVALID_ARG;
 
-  size_t sched_off = 0;
-  const hwa_workspace_layout L = compute_layout(g, p->dtype, &sched_off);
+  Internal X;
+  const hwa_workspace_layout L = compute_layout(g, p->dtype, &X);
   if (!p->workspace || p->workspace_bytes < L.total ||
       !aligned(p->workspace, kAlign))
     return HWA_ERR_WORKSPACE;
@@ -212,7 +220,9 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   int32_t* bank_e = (int32_t*)(ws + L.bank_e);
   float* decay = (float*)(ws + L.decay);
   bf16_t* v_t = (bf16_t*)(ws + L.v_t);
-  unsigned* sched = (unsigned*)(ws + sched_off);
+  _Float16* st16 = (_Float16*)(ws + X.st16);
+  float* st_eps = (float*)(ws + X.st_eps);
+  unsigned* sched = (unsigned*)(ws + X.sched);
 
   void* const* ev = p->stage_events;
   auto mark = [&](int i) {
@@ -241,21 +251,23 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   if (mark(4) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && hwa::launch_decay(g, alpha, lohi, decay, st) != hipSuccess)
     return HWA_ERR_HIP;
+  if (do_lin && p->dtype == HWA_BF16 &&
+      hwa::launch_state(g, decay, bank_p, bank_q, bank_e, p->rms_eps, st16, st_eps,
+                        st) != hipSuccess)
+    return HWA_ERR_HIP;
   if (mark(5) != hipSuccess) return HWA_ERR_HIP;
   if (do_sm && p->dtype == HWA_BF16 &&
       hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(6) != hipSuccess) return HWA_ERR_HIP;
-  const hwa::ReadoutArgs ra{(const bf16_t*)gate, decay, bank_p, bank_q, bank_e,
-                            p->rms_weight, p->rms_eps, g.F, g.chunk, g.radius,
-                            g.nch, g.B * g.H};
+  const hwa::ReadoutArgs ra{(const bf16_t*)gate, st16, st_eps, p->rms_weight, g.F};
   if (do_sm && hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out, st,
                                    fuse ? &ra : nullptr, sched) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(7) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && !fuse &&
       hwa::launch_readout(g, p->dtype, q, gate, decay, lohi, bank_p, bank_q,
-                          bank_e, p->rms_weight, p->rms_eps, do_sm, out,
+                          bank_e, st16, st_eps, p->rms_weight, p->rms_eps, do_sm, out,
                           st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(8) != hipSuccess) return HWA_ERR_HIP;

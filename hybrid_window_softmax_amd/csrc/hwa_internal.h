@@ -88,18 +88,22 @@ constexpr int HWA_SCHED_WORDS = 8;
 hipError_t launch_window_table(const Geom& g, int32_t* lohi, hipStream_t st,
                                unsigned* sched = nullptr);
 
-// Per-call inputs of the linear-branch readout (device pointers; bank_e holds
-// the power-of-two exponents of the prefix bank rows, then the suffix's)
+// Per-call inputs of the bf16 linear-branch readout (device pointers)
 struct ReadoutArgs {
   const bf16_t* gate;
-  const float* decay;  // [B*H, F, 2, d]: a_t then b_t
-  const float* bank_p;
-  const float* bank_q;
-  const int32_t* bank_e;
-  const float* rms_w;  // [d] or null (ones)
-  float eps;
-  int F, chunk, radius, nch, BH;
+  const _Float16* st;    // [B*H, F, d, d] S_t of every frame, scaled (launch_state)
+  const float* st_eps;   // [B*H, F] RMSNorm eps at that scale
+  const float* rms_w;    // [d] or null (ones)
+  int F;
 };
+
+// S_t = P_{lo-1} diag(a_t) + Q_{hi+1} diag(b_t) of every (b, h, t) for the
+// bf16 readouts: fp16, scaled by the power of two that puts its largest entry
+// in [2^14, 2^15), and st_eps = eps at the same scale (bank_e holds the
+// power-of-two exponents of the prefix bank rows, then the suffix's).
+hipError_t launch_state(const Geom& g, const float* decay, const float* bank_p,
+                        const float* bank_q, const int32_t* bank_e, float eps,
+                        _Float16* st, float* st_eps, hipStream_t st_stream);
 
 // fuse != null (bf16 only): the softmax kernel also adds the linear-branch
 // readout y = RMSNorm(S_t q^) * sigmoid(gate) of its queries (q must then be
@@ -138,10 +142,13 @@ hipError_t launch_scan(const Geom& g, int dtype, int rule, float c,
 hipError_t launch_decay(const Geom& g, const float* alpha, const int32_t* lohi,
                         float* decay, hipStream_t st);
 
+// fp32: forms S_t itself from the banks; bf16: reads it from st / st_eps
+// (launch_state) and ignores decay, banks and rms_eps.
 hipError_t launch_readout(const Geom& g, int dtype, const void* q,
                           const void* gate, const float* decay,
                           const int32_t* lohi, const float* bank_p,
                           const float* bank_q, const int32_t* bank_e,
+                          const _Float16* st16, const float* st_eps,
                           const float* rms_weight, float rms_eps,
                           bool accumulate, void* out, hipStream_t st);
 

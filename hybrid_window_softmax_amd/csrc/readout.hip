@@ -123,8 +123,107 @@ __global__ __launch_bounds__(256) void readout_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bf16 S_t
+// One workgroup per (b, h, t): the two gathered states' rows are brought to
+// one power-of-two scale 2^E (the bank rows carry exponents), the bridge
+// decays applied, then the whole matrix is scaled by 2^-k so that its largest
+// entry lies in [2^14, 2^15): fp16 then keeps every entry down to 2^-28 of
+// the largest with 11 significant bits, and the RMSNorm is unchanged when
+// eps is scaled by 2^-2(E+k) as well (the scale-up is capped at 2^40 so that
+// the scaled eps stays finite; an all-zero S_t keeps k = 0).
+template <int D>
+__global__ __launch_bounds__(256) void state_kernel(
+    const float* __restrict__ decay, const float* __restrict__ bank_p,
+    const float* __restrict__ bank_q, const int32_t* __restrict__ bank_e, float eps,
+    _Float16* __restrict__ st, float* __restrict__ st_eps, int F, int chunk, int radius,
+    int nch, int BH) {
+  constexpr int NT = 256;
+  constexpr int NX = D * D / (NT * 8);  // groups of eight columns per thread
+  static_assert(D * D % (NT * 8) == 0, "whole groups");
+  __shared__ float dec[2][D];
+  __shared__ int rowexp[2][D];
+  __shared__ int emax;
+  __shared__ unsigned vmax;  // bits of the largest |entry| (a non-negative float)
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x, bh = blockIdx.y;
+  const int c = t / chunk;
+  const int slot_p = max(0, c - radius);
+  const int slot_q = min(nch, c + radius + 1);
+  const float* dct = decay + ((long long)bh * F + t) * 2 * D;
+  const int32_t* ep = bank_e + ((long long)bh * (nch + 1) + slot_p) * D;
+  const int32_t* eq = bank_e + (long long)BH * (nch + 1) * D +
+                      ((long long)bh * (nch + 1) + slot_q) * D;
+  for (int j = tid; j < D; j += NT) {
+    dec[0][j] = dct[j];
+    dec[1][j] = dct[D + j];
+    rowexp[0][j] = ep[j];
+    rowexp[1][j] = eq[j];
+  }
+  if (tid == 0) {
+    emax = INT32_MIN;
+    vmax = 0u;
+  }
+  __syncthreads();
+  if (tid < D) atomicMax(&emax, max(rowexp[0][tid], rowexp[1][tid]));
+  __syncthreads();
+  const int E = emax;
+  const float* Pm = bank_p + ((long long)bh * (nch + 1) + slot_p) * D * D;
+  const float* Qm = bank_q + ((long long)bh * (nch + 1) + slot_q) * D * D;
+  float v[NX][8];
+  float vm = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NX; ++s) {
+    const int x = (tid + s * NT) * 8;
+    const int i = x / D, j = x % D;
+    const float4 p0 = *(const float4*)&Pm[x], p1 = *(const float4*)&Pm[x + 4];
+    const float4 q0 = *(const float4*)&Qm[x], q1 = *(const float4*)&Qm[x + 4];
+    const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const int sp = rowexp[0][i] - E, sq = rowexp[1][i] - E;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[s][u] = ldexpf(pv[u], sp) * dec[0][j + u] + ldexpf(qv[u], sq) * dec[1][j + u];
+      vm = fmaxf(vm, fabsf(v[s][u]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) vm = fmaxf(vm, __shfl_xor(vm, off));
+  if ((tid & 63) == 0) atomicMax(&vmax, __float_as_uint(vm));
+  __syncthreads();
+  const float m = __uint_as_float(vmax);
+  int k = 0;
+  if (m > 0.0f) {
+    int ex;
+    frexpf(m, &ex);
+    k = max(ex - 15, -40);
+  }
+  _Float16* dst = st + ((long long)bh * F + t) * D * D;
+#pragma unroll
+  for (int s = 0; s < NX; ++s) {
+    const int x = (tid + s * NT) * 8;
+    f16x8_t h8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) h8[u] = (_Float16)ldexpf(v[s][u], -k);
+    *(f16x8_t*)&dst[x] = h8;
+  }
+  if (tid == 0) st_eps[(long long)bh * F + t] = ldexpf(eps, -2 * (E + k));
+}
+
+hipError_t launch_state(const Geom& g, const float* decay, const float* bank_p,
+                        const float* bank_q, const int32_t* bank_e, float eps,
+                        _Float16* st, float* st_eps, hipStream_t s) {
+  dim3 grid(g.F, g.B * g.H);
+#define ST_LAUNCH(DD)                                                             \
+  hipLaunchKernelGGL(state_kernel<DD>, grid, dim3(256), 0, s, decay, bank_p, bank_q, \
+                     bank_e, eps, st, st_eps, g.F, g.chunk, g.radius, g.nch, g.B * g.H)
+  if (g.d == 128) ST_LAUNCH(128);
+  else ST_LAUNCH(64);
+#undef ST_LAUNCH
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- bf16 MFMA
-// A workgroup takes up to 1024 tokens of one frame: it forms S_t once in LDS,
+// A workgroup takes up to 1024 tokens of one frame: it brings S_t into LDS,
 // then each wave streams 32 tokens at a time, q of its next tokens loaded
 // while the current ones go through the MFMAs (readout_core.h).
 template <int D>
@@ -136,7 +235,14 @@ __global__ __launch_bounds__(256, 2) void readout_mfma_kernel(
   const int t = blockIdx.y;
   const int bh = blockIdx.z;
   const int tok0 = blockIdx.x * tok_per_wg;
-  const float eps_s = build_st<D, 256>(L, a, bh, t, tid);
+  {
+    StateChunks<D, 256> stc;
+    stc.load(a.st + ((long long)bh * a.F + t) * D * D, tid);
+    load_weight<D, 256>(L, a.rms_w, tid);
+    stc.store(L, tid);
+  }
+  const float eps_s = a.st_eps[(long long)bh * a.F + t];
+  __syncthreads();
 
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -208,6 +314,7 @@ hipError_t launch_readout(const Geom& g, int dtype, const void* q,
                           const void* gate, const float* decay,
                           const int32_t* lohi, const float* bank_p,
                           const float* bank_q, const int32_t* bank_e,
+                          const _Float16* st16, const float* st_eps,
                           const float* rms_weight, float rms_eps,
                           bool accumulate, void* out, hipStream_t st) {
   if (dtype == HWA_BF16) {
@@ -215,8 +322,7 @@ hipError_t launch_readout(const Geom& g, int dtype, const void* q,
     const int pieces = (g.S + 1023) / 1024;
     const int per = ((g.S + pieces - 1) / pieces + 127) / 128 * 128;
     dim3 grid((g.S + per - 1) / per, g.F, g.B * g.H);
-    const ReadoutArgs ra{(const bf16_t*)gate, decay, bank_p, bank_q, bank_e, rms_weight,
-                         rms_eps, g.F, g.chunk, g.radius, g.nch, g.B * g.H};
+    const ReadoutArgs ra{(const bf16_t*)gate, st16, st_eps, rms_weight, g.F};
 #define RM_LAUNCH(DD)                                                        \
   hipLaunchKernelGGL(readout_mfma_kernel<DD>, grid, dim3(256), 0, st,        \
                      (const bf16_t*)q, ra, (int)accumulate, (bf16_t*)out, g.S, \

@@ -1,17 +1,15 @@
 // Device code shared by the bf16 readouts of the linear branch: the
 // standalone readout kernel and the epilogue of the softmax kernel (VDN-H3
-// article, "Step 4" bridge mechanism and "Step 5: readout and gating"):
-//   S_t = P_{lo-1} diag(a_t) + Q_{hi+1} diag(b_t)
+// article, "Step 5: readout and gating"):
 //   o_n = S_t q^_n,  q^_n = L2(SiLU(q_n))
 //   y_n = o_n / sqrt(mean(o_n^2) + eps) * w * sigmoid(g_n),  out_n = addend_n + y_n
-// o = S_t q^ runs as one fp16 MFMA product per step (v_mfma_f32_32x32x16_f16,
-// fp32 accumulation). S_t sits in LDS as the A operand (rows = output
-// channels), scaled by an exact power of two 2^-k that puts its largest entry
-// in [2^14, 2^15): fp16 then holds every entry down to 2^-28 of the largest
-// with 11 significant bits, and the RMSNorm is unchanged when eps is scaled
-// by 2^-2k as well. Each lane forms q^ of one token in registers as the B
-// operand (|q^| <= 1, so fp16 needs no scaling). The output block holds one
-// token per lane, so the RMSNorm needs one exchange between the lane halves.
+// S_t comes ready from state_kernel (fp16, scaled by a power of two, with eps
+// scaled to match). o = S_t q^ runs as one fp16 MFMA product per step
+// (v_mfma_f32_32x32x16_f16, fp32 accumulation): S_t sits in LDS as the A
+// operand (rows = output channels); each lane forms q^ of one token in
+// registers as the B operand (|q^| <= 1, so fp16 needs no scaling). The
+// output block holds one token per lane, so the RMSNorm needs one exchange
+// between the lane halves.
 
 #pragma once
 
@@ -26,88 +24,34 @@ template <int D>
 struct ReadoutLds {
   static constexpr int SP = D + 8;  // padded row (fp16): 16-byte aligned rows
   _Float16 st[D * SP];
-  float dec[2][D];
-  int rowexp[2][D];
   float w[D];
-  int emax;
-  unsigned vmax;  // bits of the largest |entry| (a non-negative float)
 };
 
-// Forms S_t of frame t of head bh in L (every thread of the NT-thread
-// workgroup calls it; it synchronises the workgroup). The two gathered
-// states' rows are brought to one power-of-two scale 2^E, then the whole
-// matrix to 2^-k; returns eps scaled by 2^-2(E+k) to match.
+// S_t of one frame (fp16, row-major d x d as state_kernel writes it) on its
+// way from global memory to LDS: each of the NT threads of the workgroup
+// holds NCH 16-byte chunks, loaded with one 1 KB run per wave instruction.
 template <int D, int NT>
-__device__ __forceinline__ float build_st(ReadoutLds<D>& L, const ReadoutArgs& a, int bh,
-                                          int t, int tid) {
-  constexpr int SP = ReadoutLds<D>::SP;
-  constexpr int NX = D * D / (NT * 8);  // groups of eight columns per thread
-  static_assert(D * D % (NT * 8) == 0, "whole groups");
-  const int c = t / a.chunk;
-  const int slot_p = max(0, c - a.radius);
-  const int slot_q = min(a.nch, c + a.radius + 1);
-  const float* dct = a.decay + ((long long)bh * a.F + t) * 2 * D;
-  const int32_t* ep = a.bank_e + ((long long)bh * (a.nch + 1) + slot_p) * D;
-  const int32_t* eq = a.bank_e + (long long)a.BH * (a.nch + 1) * D +
-                      ((long long)bh * (a.nch + 1) + slot_q) * D;
-  for (int j = tid; j < D; j += NT) {
-    L.dec[0][j] = dct[j];
-    L.dec[1][j] = dct[D + j];
-    L.rowexp[0][j] = ep[j];
-    L.rowexp[1][j] = eq[j];
-    L.w[j] = a.rms_w ? a.rms_w[j] : 1.0f;
-  }
-  if (tid == 0) {
-    L.emax = INT32_MIN;
-    L.vmax = 0u;
-  }
-  __syncthreads();
-  if (tid < D) atomicMax(&L.emax, max(L.rowexp[0][tid], L.rowexp[1][tid]));
-  __syncthreads();
-  const int E = L.emax;
-  const float* Pm = a.bank_p + ((long long)bh * (a.nch + 1) + slot_p) * D * D;
-  const float* Qm = a.bank_q + ((long long)bh * (a.nch + 1) + slot_q) * D * D;
-  // entries in registers (eight consecutive columns per group) and their max
-  float v[NX][8];
-  float vm = 0.0f;
+struct StateChunks {
+  static constexpr int NCH = D * D / 8 / NT;
+  static_assert(D * D / 8 % NT == 0, "whole chunks per thread");
+  u32x4_t c[NCH];
+  __device__ __forceinline__ void load(const _Float16* src, int tid) {
 #pragma unroll
-  for (int s = 0; s < NX; ++s) {
-    const int x = (tid + s * NT) * 8;
-    const int i = x / D, j = x % D;
-    const float4 p0 = *(const float4*)&Pm[x], p1 = *(const float4*)&Pm[x + 4];
-    const float4 q0 = *(const float4*)&Qm[x], q1 = *(const float4*)&Qm[x + 4];
-    const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    const int sp = L.rowexp[0][i] - E, sq = L.rowexp[1][i] - E;
+    for (int i = 0; i < NCH; ++i) c[i] = *(const u32x4_t*)(src + (i * NT + tid) * 8);
+  }
+  __device__ __forceinline__ void store(ReadoutLds<D>& L, int tid) const {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v[s][u] = ldexpf(pv[u], sp) * L.dec[0][j + u] + ldexpf(qv[u], sq) * L.dec[1][j + u];
-      vm = fmaxf(vm, fabsf(v[s][u]));
+    for (int i = 0; i < NCH; ++i) {
+      const int x = (i * NT + tid) * 8;
+      *(u32x4_t*)&L.st[(x / D) * ReadoutLds<D>::SP + x % D] = c[i];
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) vm = fmaxf(vm, __shfl_xor(vm, off));
-  if ((tid & 63) == 0) atomicMax(&L.vmax, __float_as_uint(vm));
-  __syncthreads();
-  // largest entry -> [2^14, 2^15); the scale-up is capped at 2^40 so that the
-  // scaled eps stays finite (an all-zero S_t keeps k = 0)
-  const float m = __uint_as_float(L.vmax);
-  int k = 0;
-  if (m > 0.0f) {
-    int ex;
-    frexpf(m, &ex);
-    k = max(ex - 15, -40);
-  }
-#pragma unroll
-  for (int s = 0; s < NX; ++s) {
-    const int x = (tid + s * NT) * 8;
-    f16x8_t h8;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) h8[u] = (_Float16)ldexpf(v[s][u], -k);
-    *(f16x8_t*)&L.st[(x / D) * SP + x % D] = h8;
-  }
-  __syncthreads();
-  return ldexpf(a.eps, -2 * (E + k));
+};
+
+// RMSNorm weight into L (every thread of the NT-thread workgroup calls it)
+template <int D, int NT>
+__device__ __forceinline__ void load_weight(ReadoutLds<D>& L, const float* rms_w, int tid) {
+  for (int j = tid; j < D; j += NT) L.w[j] = rms_w ? rms_w[j] : 1.0f;
 }
 
 // y of this lane's token (lane % 32 of the calling wave; the wave must be

@@ -560,7 +560,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   const int t_first = (int)(q_tile0 / S), t_last = (int)(q_last / S);
   const int my_t = my_q < q_end ? (int)(my_q / S) : -1;
   // the gate rows of the tile's queries go to the K/V stage LDS (free after
-  // the drain) by direct loads, so their latency hides behind the S_t build:
+  // the drain) by direct loads, alongside S_t of the first frame:
   // 16-byte chunk c of row r sits at slot r*CH + (c ^ (r % CH)); rows past
   // the head's end read zeros (never used)
   constexpr int CH = D / 8;                     // 16-byte chunks per row
@@ -586,14 +586,16 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     const bf16_t* src = slot < KSLOTS ? &k_lds[0][0] + slot * 8 : &v_lds[0][0] + (slot - KSLOTS) * 8;
     return *(const uint2*)(src + half * 4);
   };
-  bool gate_ready = false;
+  StateChunks<D, SM_THREADS> stc;  // S_t of frame t, global -> registers -> LDS
+  stc.load(ra.st + ((long long)bh * ra.F + t_first) * D * D, tid);
+  load_weight<D, SM_THREADS>(rl, ra.rms_w, tid);
   for (int t = t_first; t <= t_last; ++t) {
-    const float eps_s = build_st<D, SM_THREADS>(rl, ra, bh, t, tid);
-    if (!gate_ready) {  // every wave's gate loads have landed
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      gate_ready = true;
-    }
+    if (t > t_first) stc.load(ra.st + ((long long)bh * ra.F + t) * D * D, tid);
+    const float eps_s = ra.st_eps[(long long)bh * ra.F + t];
+    stc.store(rl, tid);
+    // S_t and, the first time, every wave's gate rows have landed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     const bool mine = my_t == t;
     if (__builtin_amdgcn_ballot_w64(mine) != 0)
       readout_token<D, KOff>(rl, eps_s, qraw, qlane, mine, orow, [&]() {}, gate_at,

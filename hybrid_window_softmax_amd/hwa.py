@@ -22,7 +22,8 @@ FLAG_SOFTMAX_ONLY = 1
 FLAG_LINEAR_ONLY = 2
 FLAG_KEEP_INTERMEDIATES = 4
 NUM_STAGE_EVENTS = 9
-STAGES = ("window", "stats", "inverse", "scan", "decay", "vtranspose", "softmax", "readout")
+STAGES = ("window", "stats", "inverse", "scan", "decay+state", "vtranspose", "softmax",
+          "readout")
 
 HWA_OK = 0
 HWA_ERR_INVALID_ARG = 1

@@ -96,7 +96,8 @@ typedef struct {
                          /* boundaries of hybrid_attn_fwd, for per-kernel     */
                          /* timing: [0] start, then after [1] window table,   */
                          /* [2] statistics, [3] inverses, [4] scan, [5] decay */
-                         /* products, [6] V transpose, [7] softmax (with the  */
+                         /* products and (bf16) S_t of every frame, [6] V    */
+                         /* transpose, [7] softmax (with the                  */
                          /* linear-branch readout fused in, on bf16 calls     */
                          /* without q_rope that run both branches), [8]       */
                          /* separate readout (a skipped stage records its     */
@@ -123,8 +124,10 @@ typedef struct {
  *                                 unless a row exceeds 2^64, i.e. a diverging
  *                                 sana_scaled scan)
  *   v_t      bf16 [B, H, d, N]    v transposed (bf16 only, else unused)
- * n_ch = ceil(F / chunk). The last 256 bytes before `total` are the work-queue
- * counters of the softmax kernel (internal; each call zeroes them itself).
+ * n_ch = ceil(F / chunk). Internal scratch follows v_t, inside `total`: on
+ * bf16 calls S_t of every frame (fp16, scaled by a power of two) and its
+ * scaled RMSNorm eps, then the softmax kernel's work-queue counters (each call
+ * zeroes them itself).
  */
 typedef struct {
   size_t lohi, stat_a, stat_b, map_m, bank_p, bank_q, decay, bank_e, v_t;
