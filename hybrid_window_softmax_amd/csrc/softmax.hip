@@ -483,8 +483,18 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   // V stage 1 is read (times P = 0) by step 0's PV: make it finite
   for (int x = tid; x < D * SM_KT / 8; x += SM_THREADS)
     *(u32x4*)&v_lds[1][x * 8] = u32x4{0u, 0u, 0u, 0u};
+  // fused readout: S_t of the tile's first frame goes into LDS now, while the
+  // first key tiles load (the main loop leaves that LDS alone)
+  __shared__ ReadoutLds<D> rl;
+  const int t_first = (int)(q_tile0 / S);
+  StateChunks<D, SM_THREADS> stc;  // S_t of a frame, global -> registers -> LDS
+  if (fuse) stc.load(ra.st + ((long long)bh * ra.F + t_first) * D * D, tid);
   dma_k(kt_first, 0);
   if (ntiles > 1) dma_k(kt_first + SM_KT, 1);
+  if (fuse) {
+    load_weight<D, SM_THREADS>(rl, ra.rms_w, tid);
+    stc.store(rl, tid);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   qk_full(&k_lds[0][0], sa);
@@ -546,7 +556,6 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   // every frame from the first query's to the last's). qreg holds raw q
   // (no RoPE on this path) in the chunk order of the QK operand; S_t's
   // columns are read in the same order.
-  __shared__ ReadoutLds<D> rl;
   // chunk kk of the lane half: channels 8 * (8 * (kk / 4) + op_chunk(kk % 4, half)),
   // a lane part 16 * half plus a compile-time part
   struct KOff {
@@ -557,7 +566,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) qraw[kk] = __builtin_bit_cast(u32x4, qreg[kk]);
   const long long q_last = min(q_tile0 + SM_QT, q_end) - 1;
-  const int t_first = (int)(q_tile0 / S), t_last = (int)(q_last / S);
+  const int t_last = (int)(q_last / S);
   const int my_t = my_q < q_end ? (int)(my_q / S) : -1;
   // the gate rows of the tile's queries go to the K/V stage LDS (free after
   // the drain) by direct loads, alongside S_t of the first frame:
@@ -586,13 +595,13 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     const bf16_t* src = slot < KSLOTS ? &k_lds[0][0] + slot * 8 : &v_lds[0][0] + (slot - KSLOTS) * 8;
     return *(const uint2*)(src + half * 4);
   };
-  StateChunks<D, SM_THREADS> stc;  // S_t of frame t, global -> registers -> LDS
-  stc.load(ra.st + ((long long)bh * ra.F + t_first) * D * D, tid);
-  load_weight<D, SM_THREADS>(rl, ra.rms_w, tid);
   for (int t = t_first; t <= t_last; ++t) {
-    if (t > t_first) stc.load(ra.st + ((long long)bh * ra.F + t) * D * D, tid);
+    // S_t of the first frame is in LDS since the prologue
+    if (t > t_first) {
+      stc.load(ra.st + ((long long)bh * ra.F + t) * D * D, tid);
+      stc.store(rl, tid);
+    }
     const float eps_s = ra.st_eps[(long long)bh * ra.F + t];
-    stc.store(rl, tid);
     // S_t and, the first time, every wave's gate rows have landed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
