@@ -497,6 +497,11 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // A wave whose 32 queries all lie past the chunk's end (the last, partial
+  // tile of a chunk) only loads its share of every tile and keeps the
+  // barriers: the other wave on its SIMD then has the matrix core alone.
+  const bool wave_active = q_tile0 + wave * 32 < q_end;  // wave-uniform
+  if (wave_active) {
   qk_full(&k_lds[0][0], sa);
   __syncthreads();  // K stage 0 is refilled in step 0
   mask(0, sa);
@@ -523,6 +528,17 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     };
     if (last % 2 == 0) drain(pa);
     else drain(pb);
+  }
+  } else {
+    // the same loads and barriers as a step of the active waves
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const long long kt0 = kt_first + (long long)it * SM_KT;
+      dma_k(kt0 + 2 * SM_KT, it & 1);
+      dma_v(kt0, it & 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
