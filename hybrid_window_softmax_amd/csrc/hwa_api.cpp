@@ -55,9 +55,9 @@ bool make_geom(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
   return true;
 }
 
-// Internal workspace regions that follow the documented intermediates
-// (inside L.total): the bf16 readouts' S_t of every frame (fp16) and its
-// scaled eps, then the softmax kernel's work-queue counters.
+// Workspace regions the launch sequence needs besides the layout's fields:
+// S_t and its eps (also in the layout) and the softmax kernel's work-queue
+// counters (internal, the last region inside L.total).
 struct Internal {
   size_t st16 = 0, st_eps = 0, sched = 0;
 };
@@ -83,8 +83,8 @@ hwa_workspace_layout compute_layout(const Geom& g, int dtype, Internal* in = nul
   const size_t Np = (size_t)((g.N + 63) / 64 * 64);
   L.v_t = take(dtype == HWA_BF16 ? bh * g.d * Np * sizeof(bf16_t) : 0);
   Internal x;
-  x.st16 = take(dtype == HWA_BF16 ? bh * g.F * dd * sizeof(_Float16) : 0);
-  x.st_eps = take(dtype == HWA_BF16 ? bh * g.F * sizeof(float) : 0);
+  x.st16 = L.st16 = take(dtype == HWA_BF16 ? bh * g.F * dd * sizeof(_Float16) : 0);
+  x.st_eps = L.st_eps = take(dtype == HWA_BF16 ? bh * g.F * sizeof(float) : 0);
   x.sched = take(hwa::HWA_SCHED_WORDS * sizeof(unsigned));
   if (in) *in = x;
   L.total = off;

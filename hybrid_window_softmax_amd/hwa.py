@@ -63,7 +63,7 @@ class Params(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("lohi", "stat_a", "stat_b", "map_m", "bank_p", "bank_q", "decay",
-                 "bank_e", "v_t", "total")]
+                 "bank_e", "v_t", "st16", "st_eps", "total")]
 
 
 class HwaError(RuntimeError):

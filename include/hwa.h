@@ -124,13 +124,15 @@ typedef struct {
  *                                 unless a row exceeds 2^64, i.e. a diverging
  *                                 sana_scaled scan)
  *   v_t      bf16 [B, H, d, N]    v transposed (bf16 only, else unused)
- * n_ch = ceil(F / chunk). Internal scratch follows v_t, inside `total`: on
- * bf16 calls S_t of every frame (fp16, scaled by a power of two) and its
- * scaled RMSNorm eps, then the softmax kernel's work-queue counters (each call
- * zeroes them itself).
+ *   st16     fp16 [B, H, F, d, d] (bf16 only) S_t = P_{lo-1} diag(a_t) +
+ *                                 Q_{hi+1} diag(b_t) of every frame, times 2^-m
+ *   st_eps   [B, H, F]            (bf16 only) rms_eps * 2^-2m, the same m
+ * n_ch = ceil(F / chunk). The last 256 bytes before `total` hold the softmax
+ * kernel's work-queue counters (internal; each call zeroes them itself).
  */
 typedef struct {
   size_t lohi, stat_a, stat_b, map_m, bank_p, bank_q, decay, bank_e, v_t;
+  size_t st16, st_eps;
   size_t total;
 } hwa_workspace_layout;
 

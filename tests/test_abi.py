@@ -153,7 +153,7 @@ def test_workspace_layout_is_consistent():
                             1 if cfg["dtype"] == "bf16" else 0)
         L = hwa.workspace_layout(cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"], p)
         offs = [L[k] for k in ("lohi", "stat_a", "stat_b", "map_m", "bank_p", "bank_q",
-                               "decay", "bank_e", "v_t")]
+                               "decay", "bank_e", "v_t", "st16", "st_eps")]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         assert L["total"] == hwa.workspace_bytes(cfg["frames"], cfg["tokens_per_frame"],
                                                  cfg["chunk"], p)

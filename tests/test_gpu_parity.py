@@ -87,6 +87,17 @@ def _check_intermediates(case, ws, inter, cfg, tol):
             ep = oracle.rel_frobenius(P, it["prefix"][idx])
             eq = oracle.rel_frobenius(Q, it["suffix"][idx])
             assert ep <= max(tol, 1e-5) and eq <= max(tol, 1e-5), (m, ep, eq)
+    if cfg["dtype"] == "bf16":
+        # S_t of every frame (fp16 times 2^-m, with eps times 2^-2m): the
+        # gathered, bridged state of "Step 4" within fp16 rounding (2^-11)
+        st = ws_view(ws, L["st16"], (B, H, F, d, d), torch.float16).cpu().numpy().astype(np.float64)
+        se = ws_view(ws, L["st_eps"], (B, H, F)).cpu().numpy().astype(np.float64)
+        for (b, h), it in inter.items():
+            scale = np.sqrt(np.float64(np.float32(1e-6)) / se[b, h])  # 2^m exactly
+            assert np.allclose(np.log2(scale), np.round(np.log2(scale)))
+            for t in range(F):
+                e_st = oracle.rel_frobenius(st[b, h, t] * scale[t], it["states"][t])
+                assert e_st <= 2e-3, (b, h, t, e_st)
 
 
 def test_tiny_fp32_160tok():
