@@ -232,6 +232,33 @@ def test_batch2_rms_weight(dtype, d):
     _full_check(cfg, "vdn_solve", check_intermediates=True, random_rms_weight=True)
 
 
+def _sweep_case(i):
+    """Shape i of a seeded sweep over head dim, frames, tokens per frame (1 to
+    300: partial query and key tiles, tiles spanning frames), chunk, radius,
+    heads, batch, rule and text tokens; bf16 throughout."""
+    rng = np.random.default_rng(2024)
+    for _ in range(i + 1):
+        d = int(rng.choice([64, 128]))
+        F = int(rng.integers(1, 24))
+        S = int(rng.choice([1, 3, 17, 33, 64, 65, 100, 127, 200, 256, 300]))
+        chunk = int(rng.integers(1, 8))
+        radius = int(rng.integers(0, 4))
+        heads = int(rng.integers(1, 4))
+        batch = int(rng.integers(1, 3))
+        rule = str(rng.choice(["vdn_solve", "sana_scaled", "vdn_scaled"]))
+        text = int(rng.choice([0, 8, 32]))
+    cfg = inputs.tiny_config(frames=F, text_tokens=text, head_dim=d, tokens_per_frame=S,
+                             dtype="bf16", heads=heads, batch=batch, rule=rule, chunk=chunk,
+                             radius=radius, seed=200 + i)
+    return cfg, rule, text > 0
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_shape_sweep_bf16(i):
+    cfg, rule, text = _sweep_case(i)
+    _full_check(cfg, rule, text=text, check_intermediates=True)
+
+
 def test_text_state_entry_point():
     for cfg in (inputs.WORKLOADS["small-bf16-text"], inputs.tiny_config(text_tokens=16)):
         inp = inputs.make(cfg)
