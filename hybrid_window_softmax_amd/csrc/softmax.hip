@@ -438,10 +438,10 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
         // the empty volatile asm statements pin this pair between the MFMAs of
         // its group: instruction selection may otherwise move pure arithmetic
         // across the (memory-ordered) scheduling barriers
-        float s0 = sc[blk][r], s1 = sc[blk][r + 1];
-        asm volatile("" : "+v"(s0), "+v"(s1));
-        const f32x2 e2 = {__builtin_amdgcn_exp2f(fmaf(s0, scale_log2, -mb)),
-                          __builtin_amdgcn_exp2f(fmaf(s1, scale_log2, -mb))};
+        f32x2 s01 = {sc[blk][r], sc[blk][r + 1]};
+        asm volatile("" : "+v"(s01));
+        const f32x2 e2 = {__builtin_amdgcn_exp2f(fmaf(s01[0], scale_log2, -mb)),
+                          __builtin_amdgcn_exp2f(fmaf(s01[1], scale_log2, -mb))};
         bf16x2_t p2 = __builtin_convertvector(e2, bf16x2_t);
         asm volatile("" : "+v"(p2));
         pc[blk * 2 + r / 8][r % 8] = p2[0];
