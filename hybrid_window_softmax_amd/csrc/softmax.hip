@@ -268,15 +268,16 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   // buffer descriptor of a tile: base at the tile's first byte, num_records =
   // bytes left in this head (clamped to 32 bits), so K rows past N read zeros
   // (they are masked or never read); all fields wave-uniform
+  // (a head holds fewer than 2^31 bytes on this path, which the ABI enforces,
+  // so byte offsets fit in 32 unsigned bits even a few tiles past its end)
   auto tile_rsrc = [&] __device__(const bf16_t* head, long long head_elems, long long first)
                        __attribute__((always_inline)) {
     const unsigned long long base = (unsigned long long)(head + first);
-    const long long left = (head_elems - first) * 2;
+    const unsigned hb = (unsigned)(head_elems * 2), fb = (unsigned)(first * 2);
     hwa_i32x4 r;
     r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)(base & 0xffffffffu));
     r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(base >> 32));  // stride 0
-    r[2] = __builtin_amdgcn_readfirstlane(
-        (int)(unsigned)(left <= 0 ? 0 : (left > 0xfffffff0LL ? 0xfffffff0LL : left)));
+    r[2] = __builtin_amdgcn_readfirstlane((int)(fb < hb ? hb - fb : 0u));
     r[3] = 0x00020000;  // raw buffer, 32-bit data format
     return r;
   };
