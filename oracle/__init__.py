@@ -8,7 +8,9 @@ method's definition so that the two can be compared.
 
 Source of the definition: the VDN-H3 article ("VDN-Minimax-H3", icman.com.cn
 news 81972), its sections on the far field, the five steps of the
-bidirectional linear branch, the update-rule table and the text state.
+bidirectional linear branch, the update-rule table and the text state; and,
+for the backward pass of the windowed softmax branch, the chain rule through
+that softmax (``softmax_grad``).
 
 Every public function says which passage it follows and how it is pinned
 (see ``tests/test_oracle_*.py``). No function here is "parity unpinned".
@@ -33,4 +35,9 @@ from .hybrid_attn import (  # noqa: F401
     hybrid_attn,
     text_state,
     rel_frobenius,
+)
+from .softmax_grad import (  # noqa: F401
+    softmax_lse,
+    softmax_branch_grad,
+    softmax_grad_rows,
 )
