@@ -10,6 +10,11 @@ dominant kernel (the windowed softmax, bf16 MFMA) and the fp64 CPU oracle
 timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload long-clip-832x480-85f] [--rule vdn_solve]
+
+With --softmax-bwd it instead times the backward of the windowed softmax
+branch (hwa_softmax_bwd: dq, dk, dv from q, k, v, the branch output, its
+log-sum-exp and the upstream gradient) on the same workload and prints that
+line.
 """
 
 from __future__ import annotations
@@ -133,6 +138,131 @@ def cpu_baseline(inp, rule, heads_run=1):
                       f"{dt:.1f} s wall, scaled by heads"}
 
 
+def softmax_bwd_cpu_baseline(inp, g_host, heads_run=1):
+    """The oracle's windowed-softmax gradient on `heads_run` whole heads,
+    scaled to the whole job's tokens/s."""
+    import numpy as np
+    import oracle
+    from hybrid_window_softmax_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    cfg = inp.cfg
+    S = cfg["tokens_per_frame"]
+    lo, hi = oracle.window_bounds(cfg["frames"], cfg["chunk"], cfg["radius"])
+    t0 = time.perf_counter()
+    for h in range(heads_run):
+        g = inputs.bf16_bits_to_f32(g_host[0, h]) if g_host.dtype == np.uint16 else g_host[0, h]
+        oracle.softmax_branch_grad(inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h),
+                                   g.astype(np.float64), S, lo, hi)
+    dt = time.perf_counter() - t0
+    N = cfg["frames"] * S
+    total_s = dt * cfg["heads"] * cfg["batch"] / heads_run
+    return {"value": N * cfg["batch"] / total_s, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads_run} of {cfg['heads']} heads (all {N} tokens of each), "
+                      f"{dt:.1f} s wall, scaled by heads"}
+
+
+def bench_softmax_bwd(args, cfg, inp, up):
+    """One step = one hwa_softmax_bwd over the whole workload (inputs, the
+    branch output and its log-sum-exp resident in HBM)."""
+    import torch
+    from hybrid_window_softmax_amd import hwa, inputs
+    g_host = inputs.grad_output(cfg)
+    q, k, v, g = up(inp.q), up(inp.k), up(inp.v), up(g_host)
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+    B, H, N, d = q.shape
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o, ws_f = hwa.hybrid_attn_fwd(q, k, v, None, None, None, None, None, None, F, S,
+                                  cfg["chunk"], cfg["radius"], flags=hwa.FLAG_SOFTMAX_ONLY,
+                                  softmax_lse=lse)
+    del ws_f
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def call(events=None, ws=None):
+        return hwa.softmax_bwd(q, k, v, o, lse, g, F, S, cfg["chunk"], cfg["radius"], dq=dq,
+                               dk=dk, dv=dv, workspace=ws, stage_events=events)[3]
+
+    log("bench: softmax backward warmup")
+    ws = call()
+    for _ in range(max(0, args.warmup - 1)):
+        call(ws=ws)
+    torch.cuda.synchronize()
+    timer = hwa.StageTimer(args.steps, hwa.NUM_BWD_STAGE_EVENTS, hwa.BWD_STAGES)
+    log(f"bench: timing {args.steps} backward steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(events=timer.sets[i], ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage = timer.stage_ms()
+    timer.close()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    log("bench: stage ms " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()))
+    pairs = window_pairs(cfg) * B * H
+    io = 2 if cfg["dtype"] == "bf16" else 4
+    tok = B * H * N
+    # executed products per query-key pair: dq recomputes S and dP and forms
+    # dQ (3 x 2d flop); dk/dv recomputes S and dP and forms dV and dK (4 x 2d)
+    work = {
+        # read o and g, write delta and lse2; bf16 also reads q, k, g and
+        # writes their transposes
+        "prep": dict(bytes=tok * (2 * d * io + 4 + 8) + (6 * tok * d * io if io == 2 else 0),
+                     flops=0),
+        "dq": dict(bytes=0, flops=6 * d * pairs),
+        "dkdv": dict(bytes=0, flops=8 * d * pairs),
+    }
+    kernels = {}
+    for name, w in work.items():
+        sec = stage[name] / 1000.0
+        rec = {"ms": round(stage[name], 4)}
+        if w["bytes"]:
+            rec["hbm_GBs"] = round(w["bytes"] / sec / 1e9, 1)
+            rec["hbm_frac"] = round(w["bytes"] / sec / 1e9 / PEAK_HBM_GBS, 4)
+        if w["flops"]:
+            rec["TFLOPs"] = round(w["flops"] / sec / 1e12, 2)
+            rec["frac"] = round(w["flops"] / sec / 1e12 / PEAK_BF16_TFLOPS, 4)
+        kernels[name] = rec
+    dom = "dkdv"
+    achieved = work[dom]["flops"] / (stage[dom] / 1000.0) / 1e12
+    roofline = {"kernel": "softmax_bwd_dkdv_kernel", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": work[dom]["flops"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle's gradient on a sample")
+        del q, k, v, g, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        cpu = softmax_bwd_cpu_baseline(inp, g_host, args.cpu_heads)
+    return {
+        "metric": "windowed-softmax backward (dq, dk, dv) tokens/s",
+        "value": round(B * N / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: B{B} H{H} d{d} F{F} x S{S} = {N} tokens, "
+                               f"chunk {cfg['chunk']} radius {cfg['radius']}, softmax branch "
+                               f"backward",
+                   "tokens": N, "heads": H, "head_dim": d},
+        # the method's five products per pair (S, dP, dV, dK, dQ), over the step
+        "algorithmic_TFLOPs": round(10 * d * pairs / (ms / 1000.0) / 1e12, 2),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +276,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (three times), the "
                          "reference kernel for scaling HBM byte counters")
+    ap.add_argument("--softmax-bwd", action="store_true",
+                    help="time the windowed-softmax backward (hwa_softmax_bwd) instead")
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time the vendor library's square bf16 GEMMs (torch.matmul on "
                          "hipBLASLt), the practical MFMA rate this GPU sustains, for context")
@@ -202,6 +334,10 @@ def main():
         if bf and a.dtype.name == "uint16":
             return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
+
+    if args.softmax_bwd:
+        print(json.dumps(bench_softmax_bwd(args, cfg, inp, up)), flush=True)
+        return
 
     t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
                                           "conv_v", "rms_weight", "k_txt", "v_txt",

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhwa.so")
 
-SOURCES = ["hwa_api.cpp", "softmax.hip", "stats.hip", "factor.hip",
+SOURCES = ["hwa_api.cpp", "softmax.hip", "softmax_bwd.hip", "stats.hip", "factor.hip",
            "scan.hip", "readout.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,8 +1,10 @@
-// C ABI of libhwa: argument validation, workspace layout and the launch
-// sequence of the hybrid attention forward. Declarations and semantics are
+// C ABI of libhwa: argument validation, workspace layouts and the launch
+// sequences of the hybrid attention forward and of the softmax branch's
+// backward. Declarations and semantics are
 // in include/hwa.h.
 
 #include <math.h>
+#include <stddef.h>
 #include <string.h>
 
 #include "hwa_internal.h"
@@ -21,9 +23,24 @@ bool head_dim_ok(int d, int dtype) {
   return d == 16 || d == 32 || d == 64 || d == 128;
 }
 
+// The struct as first published ended at stage_events; fields after it are
+// read only when the caller's struct_size covers them.
+constexpr size_t kParamsV1 = offsetof(hwa_params, softmax_lse);
+
+template <typename T>
+T field_or_null(const hwa_params* p, T hwa_params::*f, size_t off) {
+  return p->struct_size >= off + sizeof(T) ? p->*f : nullptr;
+}
+float* lse_out_of(const hwa_params* p) {
+  return field_or_null(p, &hwa_params::softmax_lse, offsetof(hwa_params, softmax_lse));
+}
+void* sm_out_of(const hwa_params* p) {
+  return field_or_null(p, &hwa_params::softmax_out, offsetof(hwa_params, softmax_out));
+}
+
 // Basic checks on the params struct shared by every entry point.
 hwa_status check_params(const hwa_params* p) {
-  if (!p || p->struct_size < sizeof(hwa_params)) return HWA_ERR_INVALID_ARG;
+  if (!p || p->struct_size < kParamsV1) return HWA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->heads < 1) return HWA_ERR_INVALID_ARG;
   if (p->dtype != HWA_F32 && p->dtype != HWA_BF16) return HWA_ERR_INVALID_ARG;
   if (p->head_dim < 1) return HWA_ERR_INVALID_ARG;
@@ -171,6 +188,9 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   if (!q || !k || !v || !out) return HWA_ERR_INVALID_ARG;
   if (do_lin && (!beta || !alpha || !gate || !p->conv_k || !p->conv_v))
     return HWA_ERR_INVALID_ARG;
+  float* lse_out = lse_out_of(p);
+  void* sm_out = sm_out_of(p);
+  if (!do_sm && (lse_out || sm_out)) return HWA_ERR_INVALID_ARG;
   if (!isfinite(p->c) || !isfinite(p->text_scale) || !(p->rms_eps > 0.0f) ||
       !isfinite(p->rms_eps))
     return HWA_ERR_INVALID_ARG;
@@ -184,7 +204,8 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   if (!aligned(q, va) || !aligned(k, va) || !aligned(v, va) ||
       !aligned(out, va) || !aligned(qs, va) || !aligned(ks, va) ||
       (gate && !aligned(gate, va)) || (beta && !aligned(beta, 4)) ||
-      (alpha && !aligned(alpha, 4)) || (text_state && !aligned(text_state, 4)))
+      (alpha && !aligned(alpha, 4)) || (text_state && !aligned(text_state, 4)) ||
+      (lse_out && !aligned(lse_out, 4)) || (sm_out && !aligned(sm_out, va)))
     return HWA_ERR_INVALID_ARG;
 
   Internal X;
@@ -206,8 +227,14 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
       {text_state, bh * (size_t)g.d * g.d * sizeof(float)},
       {p->workspace, p->workspace_bytes},
   };
+  const size_t lse_bytes = bh * (size_t)g.N * sizeof(float);
   for (const auto& in : ins)
-    if (overlaps(out, io_bytes, in.ptr, in.n)) return HWA_ERR_INVALID_ARG;
+    if (overlaps(out, io_bytes, in.ptr, in.n) || overlaps(sm_out, io_bytes, in.ptr, in.n) ||
+        overlaps(lse_out, lse_bytes, in.ptr, in.n))
+      return HWA_ERR_INVALID_ARG;
+  if (overlaps(sm_out, io_bytes, out, io_bytes) || overlaps(lse_out, lse_bytes, out, io_bytes) ||
+      overlaps(lse_out, lse_bytes, sm_out, io_bytes))
+    return HWA_ERR_INVALID_ARG;
 
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)p->workspace;
@@ -262,7 +289,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   if (mark(6) != hipSuccess) return HWA_ERR_HIP;
   const hwa::ReadoutArgs ra{(const bf16_t*)gate, st16, st_eps, p->rms_weight, g.F};
   if (do_sm && hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out, st,
-                                   fuse ? &ra : nullptr, sched) != hipSuccess)
+                                   fuse ? &ra : nullptr, sched, lse_out, sm_out) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(7) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && !fuse &&
@@ -271,6 +298,116 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                           st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(8) != hipSuccess) return HWA_ERR_HIP;
+  return HWA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of hwa_softmax_bwd: window table, delta and lse2 [B*H, Np] fp32,
+// and on bf16 the transposed copies q_t, k_t, g_t [B*H, d, Np] bf16.
+struct BwdLayout {
+  size_t lohi, delta, lse2, q_t, k_t, g_t, total;
+};
+
+BwdLayout bwd_layout(const Geom& g, int dtype) {
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t Np = (size_t)((g.N + 63) / 64 * 64);
+  const size_t tr = dtype == HWA_BF16 ? bh * g.d * Np * sizeof(bf16_t) : 0;
+  L.lohi = take(2 * (size_t)g.F * sizeof(int32_t));
+  L.delta = take(bh * Np * sizeof(float));
+  L.lse2 = take(bh * Np * sizeof(float));
+  L.q_t = take(tr);
+  L.k_t = take(tr);
+  L.g_t = take(tr);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
+                                       int32_t chunk, const hwa_params* p) {
+  if (check_params(p) != HWA_OK) return 0;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, chunk, 0, p, g)) return 0;
+  return bwd_layout(g, p->dtype).total;
+}
+
+hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
+                           const void* o_sm, const float* lse, const void* d_o,
+                           int32_t frames, int32_t tokens_per_frame,
+                           int32_t chunk, int32_t radius, void* dq, void* dk,
+                           void* dv, void* stream, const hwa_params* p) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, chunk, radius, p, g))
+    return HWA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o_sm || !lse || !d_o || !dq || !dk || !dv)
+    return HWA_ERR_INVALID_ARG;
+  const size_t va = 16;  // 16-byte row loads on both dtypes
+  if (!aligned(q, va) || !aligned(k, va) || !aligned(v, va) || !aligned(o_sm, va) ||
+      !aligned(d_o, va) || !aligned(dq, va) || !aligned(dk, va) || !aligned(dv, va) ||
+      !aligned(lse, 4))
+    return HWA_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(g, p->dtype);
+  if (!p->workspace || p->workspace_bytes < L.total || !aligned(p->workspace, kAlign))
+    return HWA_ERR_WORKSPACE;
+  const size_t es = p->dtype == HWA_BF16 ? 2 : 4;
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t io_bytes = bh * (size_t)g.N * g.d * es;
+  const struct { const void* ptr; size_t n; } ins[] = {
+      {q, io_bytes}, {k, io_bytes}, {v, io_bytes}, {o_sm, io_bytes}, {d_o, io_bytes},
+      {lse, bh * (size_t)g.N * sizeof(float)}, {p->workspace, p->workspace_bytes},
+  };
+  void* outs[] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (const auto& in : ins)
+      if (overlaps(outs[i], io_bytes, in.ptr, in.n)) return HWA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], io_bytes, outs[j], io_bytes)) return HWA_ERR_INVALID_ARG;
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)p->workspace;
+  int32_t* lohi = (int32_t*)(ws + L.lohi);
+  float* delta = (float*)(ws + L.delta);
+  float* lse2 = (float*)(ws + L.lse2);
+  bf16_t* q_t = (bf16_t*)(ws + L.q_t);
+  bf16_t* k_t = (bf16_t*)(ws + L.k_t);
+  bf16_t* g_t = (bf16_t*)(ws + L.g_t);
+  void* const* ev = p->stage_events;
+  auto mark = [&](int i) {
+    return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+  };
+  if (mark(0) != hipSuccess) return HWA_ERR_HIP;
+  if (hwa::launch_window_table(g, lohi, st) != hipSuccess) return HWA_ERR_HIP;
+  if (hwa::launch_bwd_prep(g, p->dtype, o_sm, d_o, lse, delta, lse2, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (p->dtype == HWA_BF16) {
+    if (hwa::launch_vtranspose(g, (const bf16_t*)q, q_t, st) != hipSuccess ||
+        hwa::launch_vtranspose(g, (const bf16_t*)k, k_t, st) != hipSuccess ||
+        hwa::launch_vtranspose(g, (const bf16_t*)d_o, g_t, st) != hipSuccess)
+      return HWA_ERR_HIP;
+  }
+  if (mark(1) != hipSuccess) return HWA_ERR_HIP;
+  for (int part = 0; part < 2; ++part) {
+    if (hwa::launch_softmax_bwd(g, p->dtype, part, q, k, v, d_o, q_t, k_t, g_t, lse2, delta,
+                                lohi, dq, dk, dv, st) != hipSuccess)
+      return HWA_ERR_HIP;
+    if (mark(2 + part) != hipSuccess) return HWA_ERR_HIP;
+  }
   return HWA_OK;
 }
 

@@ -108,11 +108,14 @@ hipError_t launch_state(const Geom& g, const float* decay, const float* bank_p,
 // fuse != null (bf16 only): the softmax kernel also adds the linear-branch
 // readout y = RMSNorm(S_t q^) * sigmoid(gate) of its queries (q must then be
 // the raw q) before it writes out. sched (bf16 only): HWA_SCHED_WORDS
-// counters, zero at launch (the kernel leaves them non-zero).
+// counters, zero at launch (the kernel leaves them non-zero). lse (or null):
+// [B*H, N] fp32 log-sum-exp of each query's scaled scores; sm_out (or null):
+// o_sm alone, in the I/O dtype.
 hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
                           const int32_t* lohi, void* out, hipStream_t st,
-                          const ReadoutArgs* fuse, unsigned* sched);
+                          const ReadoutArgs* fuse, unsigned* sched, float* lse,
+                          void* sm_out);
 
 hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
                              hipStream_t st);
@@ -151,6 +154,20 @@ hipError_t launch_readout(const Geom& g, int dtype, const void* q,
                           const _Float16* st16, const float* st_eps,
                           const float* rms_weight, float rms_eps,
                           bool accumulate, void* out, hipStream_t st);
+
+// Backward of the softmax branch. delta = g . o_sm and lse2 = lse * log2(e)
+// per query, [B*H, Np] (Np = N rounded up to 64, zeros past N).
+hipError_t launch_bwd_prep(const Geom& g, int dtype, const void* o, const void* go,
+                           const float* lse, float* delta, float* lse2, hipStream_t st);
+
+// part 0: dq; part 1: dk and dv; from q, k, v, the upstream gradient go and
+// the prep arrays; bf16 also reads the transposed copies q_t, k_t, g_t
+// [B*H, d, Np] (launch_vtranspose).
+hipError_t launch_softmax_bwd(const Geom& g, int dtype, int part, const void* q, const void* k,
+                              const void* v, const void* go, const bf16_t* q_t,
+                              const bf16_t* k_t, const bf16_t* g_t, const float* lse2,
+                              const float* delta, const int32_t* lohi, void* dq, void* dk,
+                              void* dv, hipStream_t st);
 
 }  // namespace hwa
 

@@ -27,17 +27,7 @@
 
 #include "hwa_internal.h"
 #include "readout_core.h"
-
-// MUBUF direct load global -> LDS (buffer_load_dword* ... lds): lane l of a
-// wave writes its bytes at the LDS address in M0 + 16 * l (dwordx4); lanes
-// whose offset lies past the descriptor's num_records read zeros. Unlike the
-// FLAT-encoded global_load_lds, it is not counted as an LDS access by the
-// compiler's wait-count tracking, so waits for ds_read results stay counted.
-typedef int hwa_i32x4 __attribute__((ext_vector_type(4)));
-extern "C" __device__ void hwa_raw_buffer_load_lds(hwa_i32x4 rsrc,
-                                                   __attribute__((address_space(3))) void* lds,
-                                                   int size, int voffset, int soffset, int offset,
-                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+#include "attn_tile.h"
 
 namespace hwa {
 
@@ -56,10 +46,6 @@ constexpr int SM_SPARE = 128;
 #ifndef SM_PREFETCH
 #define SM_PREFETCH 2
 #endif
-
-__host__ __device__ inline long long round_up64(long long n) {
-  return (n + 63) / 64 * 64;
-}
 
 // ---------------------------------------------------------------- window table
 __global__ void window_table_kernel(int F, int chunk, int radius,
@@ -129,14 +115,6 @@ hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
-// Row of the 32-row MFMA block that lands on "16 consecutive keys per lane
-// half": MFMA output row m is held by lane half (m / 4) % 2 in register
-// 4 * (m / 8) + m % 4; loading tile key perm32(m) into row m makes register r
-// of half h hold key 16 * h + r.
-__device__ __forceinline__ int perm32(int m) {
-  return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-}
-
 // LDS tiles are unpadded rows of 128 bytes (8 chunks of 16 bytes): V^T as
 // [d][64 keys], K as [d / 64][64 rows][64 d] where LDS row m of the key tile
 // holds key 32 * (m / 32) + perm32(m % 32). Row m keeps logical chunk c at
@@ -156,10 +134,6 @@ __device__ __forceinline__ int perm32(int m) {
 // Two K and two V stages (64 KB at d = 128); the loop is unrolled by two so
 // that stage indices are compile-time. Eight waves (256 queries) share every
 // tile; one workgroup per CU (two waves per SIMD).
-__device__ __forceinline__ int swz(int m) { return (m >> 1) & 7; }
-__device__ __forceinline__ int op_chunk(int j, int half) {
-  return 2 * half + 4 * (j / 2) + (j % 2);
-}
 
 template <int D>
 __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
@@ -167,7 +141,8 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     const bf16_t* __restrict__ vt, const int32_t* __restrict__ lohi,
     bf16_t* __restrict__ out, int F, int S, int chunk, int nch, long long N,
     long long Np, int tiles_per_chunk, float scale_log2, ReadoutArgs ra, int fuse,
-    unsigned* __restrict__ sched, int ntiles_total) {
+    unsigned* __restrict__ sched, int ntiles_total, float* __restrict__ lse_out,
+    bf16_t* __restrict__ sm_out) {
   // the body uses device-only lambdas; the host pass needs only the stub
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KC = D / 8;          // 16-byte chunks per key
@@ -546,6 +521,10 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   // ---- normalise: lane holds d = 32*dblk + 8*(r/4) + 4*half + r%4, as bf16
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
+  // log sum_m exp(s_m / sqrt(d)) = (m_run * scale_log2 + log2(l_tot)) * ln 2
+  if (lse_out && half == 0 && my_q < q_end)
+    lse_out[(long long)bh * N + my_q] =
+        (m_run * scale_log2 + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
   uint2 osm[D / 32][4];
 #pragma unroll
   for (int dblk = 0; dblk < D / 32; ++dblk)
@@ -557,6 +536,14 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
                                  __builtin_bit_cast(uint32_t, __builtin_convertvector(b2, bf16x2)));
     }
   bf16_t* orow = out + (long long)bh * N * D + my_q * D;
+  if (sm_out && my_q < q_end) {
+    bf16_t* srow = sm_out + (long long)bh * N * D + my_q * D;
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(uint2*)(srow + dblk * 32 + g4 * 8 + half * 4) = osm[dblk][g4];
+  }
   if (!fuse) {
     if (my_q < q_end) {
 #pragma unroll
@@ -639,7 +626,8 @@ __global__ __launch_bounds__(128) void softmax_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const int32_t* __restrict__ lohi,
     float* __restrict__ out, int F, int S, int chunk, long long N,
-    int tiles_per_chunk, float scale_log2) {
+    int tiles_per_chunk, float scale_log2, float* __restrict__ lse_out,
+    float* __restrict__ sm_out) {
   constexpr int QT = 128, KT = 32;
   __shared__ float k_lds[KT][D];
   __shared__ float v_lds[KT][D];
@@ -706,13 +694,22 @@ __global__ __launch_bounds__(128) void softmax_f32_kernel(
     float* orow = out + (long long)bh * N * D + my_q * D;
 #pragma unroll
     for (int i = 0; i < D; ++i) orow[i] = o[i] * inv;
+    if (sm_out) {
+      float* srow = sm_out + (long long)bh * N * D + my_q * D;
+#pragma unroll
+      for (int i = 0; i < D; ++i) srow[i] = o[i] * inv;
+    }
+    // log sum_m exp(s_m / sqrt(d)); m_run is a raw score q.k
+    if (lse_out)
+      lse_out[(long long)bh * N + my_q] = m_run * (scale_log2 * 0.6931471805599453f) + logf(l_run);
   }
 }
 
 hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
                           const int32_t* lohi, void* out, hipStream_t st,
-                          const ReadoutArgs* fuse, unsigned* sched) {
+                          const ReadoutArgs* fuse, unsigned* sched, float* lse,
+                          void* sm_out) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)g.d);
   const int qpc = g.chunk * g.S;  // queries of a full chunk
   if (dtype == HWA_BF16) {
@@ -726,7 +723,8 @@ hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
   hipLaunchKernelGGL(softmax_bf16_kernel<DD>, grid, dim3(SM_THREADS), 0, st, \
                      (const bf16_t*)q, (const bf16_t*)k, v_t, lohi,          \
                      (bf16_t*)out, g.F, g.S, g.chunk, g.nch, g.N, Np, tpc,   \
-                     scale_log2, ra, fuse ? 1 : 0, sched, ntiles)
+                     scale_log2, ra, fuse ? 1 : 0, sched, ntiles, lse,       \
+                     (bf16_t*)sm_out)
     if (g.d == 128) SM_LAUNCH(128);
     else SM_LAUNCH(64);
 #undef SM_LAUNCH
@@ -736,7 +734,8 @@ hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
 #define SF_LAUNCH(DD)                                                          \
   hipLaunchKernelGGL(softmax_f32_kernel<DD>, grid, dim3(128), 0, st,           \
                      (const float*)q, (const float*)k, (const float*)v, lohi,  \
-                     (float*)out, g.F, g.S, g.chunk, g.N, tpc, scale_log2)
+                     (float*)out, g.F, g.S, g.chunk, g.N, tpc, scale_log2,     \
+                     lse, (float*)sm_out)
     switch (g.d) {
       case 16: SF_LAUNCH(16); break;
       case 32: SF_LAUNCH(32); break;

@@ -24,6 +24,8 @@ FLAG_KEEP_INTERMEDIATES = 4
 NUM_STAGE_EVENTS = 9
 STAGES = ("window", "stats", "inverse", "scan", "decay+state", "vtranspose", "softmax",
           "readout")
+NUM_BWD_STAGE_EVENTS = 4
+BWD_STAGES = ("prep", "dq", "dkdv")
 
 HWA_OK = 0
 HWA_ERR_INVALID_ARG = 1
@@ -35,7 +37,7 @@ HWA_BF16 = 1
 
 EXPORTS = ("hybrid_attn_fwd", "hwa_workspace_bytes", "hwa_get_workspace_layout",
            "hwa_window_bounds", "hwa_text_state", "hwa_text_state_workspace_bytes",
-           "hwa_status_string")
+           "hwa_softmax_bwd", "hwa_softmax_bwd_workspace_bytes", "hwa_status_string")
 
 
 class Params(ctypes.Structure):
@@ -57,6 +59,8 @@ class Params(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("flags", ctypes.c_uint32),
         ("stage_events", ctypes.c_void_p),
+        ("softmax_lse", ctypes.c_void_p),
+        ("softmax_out", ctypes.c_void_p),
     ]
 
 
@@ -96,6 +100,11 @@ def lib():
         L.hwa_text_state.restype = ctypes.c_int
         L.hwa_text_state_workspace_bytes.argtypes = [i32, PP]
         L.hwa_text_state_workspace_bytes.restype = sz
+        L.hwa_softmax_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp,
+                                      vp, vp, PP]
+        L.hwa_softmax_bwd.restype = ctypes.c_int
+        L.hwa_softmax_bwd_workspace_bytes.argtypes = [i32, i32, i32, PP]
+        L.hwa_softmax_bwd_workspace_bytes.restype = sz
         L.hwa_status_string.argtypes = [ctypes.c_int]
         L.hwa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -170,13 +179,16 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
                     radius: int = 1, rule: str = "vdn_solve", c: float = 0.5,
                     text_scale: float = 0.5, rms_eps: float = 1e-6,
                     rms_weight=None, q_rope=None, k_rope=None, flags: int = 0,
-                    out=None, workspace=None, stream=None, stage_events=None):
+                    out=None, workspace=None, stream=None, stage_events=None,
+                    softmax_lse=None, softmax_out=None):
     """out = windowed softmax + delta-rule linear branch (see include/hwa.h).
 
     q, k, v, gate: [B, H, N, d] bf16 or fp32 CUDA tensors; beta [B, H, N],
     alpha [B, H, F, d], text_state [B, H, d, d] (or None), conv_k/conv_v
     [H, d, 4], rms_weight [d] (or None): fp32. ``stage_events``: optional
     ctypes array of NUM_STAGE_EVENTS hipEvent_t (see :class:`StageTimer`).
+    ``softmax_lse`` ([B, H, N] fp32) and ``softmax_out`` (like q), when
+    given, receive the softmax branch's log-sum-exp and output.
     Returns (out, workspace).
     """
     B, H, N, d = q.shape
@@ -191,8 +203,12 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
     _check(conv_k, "conv_k", torch.float32, (H, d, 4), dev)
     _check(conv_v, "conv_v", torch.float32, (H, d, 4), dev)
     _check(rms_weight, "rms_weight", torch.float32, (d,), dev)
+    _check(softmax_lse, "softmax_lse", torch.float32, (B, H, N), dev)
+    _check(softmax_out, "softmax_out", q.dtype, (B, H, N, d), dev)
     p = make_params(B, H, d, q.dtype, c, text_scale, rms_eps, conv_k, conv_v, rms_weight,
                     q_rope, k_rope, None, flags)
+    p.softmax_lse = None if softmax_lse is None else softmax_lse.data_ptr()
+    p.softmax_out = None if softmax_out is None else softmax_out.data_ptr()
     need = workspace_bytes(frames, tokens_per_frame, chunk, p)
     if workspace is None:
         workspace = alloc_workspace(need, dev)
@@ -210,6 +226,43 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
     if code != HWA_OK:
         raise HwaError(code)
     return out, workspace
+
+
+def softmax_bwd(q, k, v, o_sm, lse, d_o, frames: int, tokens_per_frame: int,
+                chunk: int = 5, radius: int = 1, dq=None, dk=None, dv=None,
+                workspace=None, stream=None, stage_events=None):
+    """(dq, dk, dv) of the windowed softmax branch (hwa_softmax_bwd).
+
+    q, k, v, o_sm, d_o: [B, H, N, d] bf16 or fp32 CUDA tensors (o_sm and lse
+    from a forward call with ``softmax_out`` / ``softmax_lse``, or with
+    FLAG_SOFTMAX_ONLY); lse [B, H, N] fp32. ``stage_events``: optional ctypes
+    array of NUM_BWD_STAGE_EVENTS hipEvent_t. Returns (dq, dk, dv, workspace).
+    """
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o_sm", o_sm), ("d_o", d_o),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, q.dtype, (B, H, N, d), dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    p = make_params(B, H, d, q.dtype)
+    need = int(lib().hwa_softmax_bwd_workspace_bytes(frames, tokens_per_frame, chunk,
+                                                     ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if stage_events is not None:
+        p.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    st = _stream(dev) if stream is None else ctypes.c_void_p(stream)
+    code = lib().hwa_softmax_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o_sm), _ptr(lse), _ptr(d_o),
+                                 frames, tokens_per_frame, chunk, radius, _ptr(dq), _ptr(dk),
+                                 _ptr(dv), st, ctypes.byref(p))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return dq, dk, dv, workspace
 
 
 def text_state(k_txt, v_txt, beta_txt, workspace=None, out=None):
@@ -237,7 +290,8 @@ class StageTimer:
     """hipEvents recorded by the library at its kernel boundaries on the
     call's stream (hwa_params.stage_events); yields per-kernel durations."""
 
-    def __init__(self, steps: int):
+    def __init__(self, steps: int, n_events: int = NUM_STAGE_EVENTS, names=STAGES):
+        self.n_events, self.names = n_events, names
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
@@ -245,8 +299,8 @@ class StageTimer:
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.sets = []
         for _ in range(steps):
-            arr = (ctypes.c_void_p * NUM_STAGE_EVENTS)()
-            for i in range(NUM_STAGE_EVENTS):
+            arr = (ctypes.c_void_p * self.n_events)()
+            for i in range(self.n_events):
                 ev = ctypes.c_void_p()
                 if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
                     raise RuntimeError("hipEventCreate failed")
@@ -256,17 +310,17 @@ class StageTimer:
     def stage_ms(self) -> dict:
         """Mean duration (ms) of every stage over the recorded steps; call
         after the stream has been synchronised."""
-        tot = [0.0] * (NUM_STAGE_EVENTS - 1)
+        tot = [0.0] * (self.n_events - 1)
         ms = ctypes.c_float()
         for arr in self.sets:
-            for i in range(NUM_STAGE_EVENTS - 1):
+            for i in range(self.n_events - 1):
                 if self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[i], arr[i + 1]) != 0:
                     raise RuntimeError("hipEventElapsedTime failed")
                 tot[i] += ms.value
-        return {s: t / len(self.sets) for s, t in zip(STAGES, tot)}
+        return {s: t / len(self.sets) for s, t in zip(self.names, tot)}
 
     def close(self):
         for arr in self.sets:
-            for i in range(NUM_STAGE_EVENTS):
+            for i in range(self.n_events):
                 self.hip.hipEventDestroy(arr[i])
         self.sets = []

@@ -7,7 +7,8 @@ oracle (tests only) take their inputs from here.
 Each tensor slice is drawn from ``numpy.random.default_rng([seed, tensor_id,
 b, h])`` so that a slice can be regenerated on its own. Tensor ids: q 0, k 1,
 v 2, gate 3, beta 4, alpha 5, text-k 6, text-v 7, text-beta 8, conv_k 9,
-conv_v 10, RMSNorm weight 11 (drawn only when asked for).
+conv_v 10, RMSNorm weight 11 (drawn only when asked for), upstream gradient of
+the softmax branch 12 (:func:`grad_output`, for the backward pass).
 
 Distributions (the workloads of the hybrid attention on video-DiT latents):
 q, k, v, gate ~ N(0, 1); beta ~ U(0, 1) per (head, token); alpha ~ U(lo, hi)
@@ -25,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TID = dict(q=0, k=1, v=2, gate=3, beta=4, alpha=5, k_txt=6, v_txt=7,
-           beta_txt=8, conv_k=9, conv_v=10, rms_weight=11)
+           beta_txt=8, conv_k=9, conv_v=10, rms_weight=11, d_out=12)
 
 # The five workloads, by name. Token counts per frame follow 832x480 (52x30
 # latent grid) and 1024x1024 (64x64) canvases at 16x spatial compression.
@@ -197,3 +198,19 @@ def make(cfg, *, beta_zero=False, alpha_one=False, identity_conv=False,
     return Inputs(cfg=cfg, q=q, k=k, v=v, gate=gate, beta=beta, alpha=alpha,
                   conv_k=conv_k, conv_v=conv_v, rms_weight=rms_weight,
                   k_txt=k_txt, v_txt=v_txt, beta_txt=beta_txt)
+
+
+def grad_output(cfg) -> np.ndarray:
+    """Upstream gradient dL/do ~ N(0, 1) of a workload, [B, H, N, d] in its
+    I/O dtype (uint16 bf16 bits or float32), drawn like q."""
+    if not isinstance(cfg, dict):
+        cfg = WORKLOADS[cfg]
+    B, H, d = cfg["batch"], cfg["heads"], cfg["head_dim"]
+    N = cfg["frames"] * cfg["tokens_per_frame"]
+    bf16 = cfg["dtype"] == "bf16"
+    out = np.empty((B, H, N, d), dtype=np.uint16 if bf16 else np.float32)
+    for b in range(B):
+        for h in range(H):
+            x = _draw(cfg["seed"], "d_out", b, h, (N, d), "normal")
+            out[b, h] = f32_to_bf16_bits(x) if bf16 else x
+    return out

@@ -102,6 +102,14 @@ typedef struct {
                          /* without q_rope that run both branches), [8]       */
                          /* separate readout (a skipped stage records its     */
                          /* event with the previous one)                      */
+  /* Fields below were added later; a caller whose struct_size ends before   */
+  /* them gets NULL for each.                                                 */
+  float* softmax_lse;    /* NULL, or [B,H,N] fp32: hybrid_attn_fwd writes      */
+                         /* lse_n = log sum_m exp(q_n . k_m / sqrt(d)) over    */
+                         /* query n's window (the softmax branch's normaliser, */
+                         /* for hwa_softmax_bwd)                               */
+  void* softmax_out;     /* NULL, or [B,H,N,d] dtype: hybrid_attn_fwd also     */
+                         /* writes o_sm alone there (for hwa_softmax_bwd)      */
 } hwa_params;
 
 #define HWA_NUM_STAGE_EVENTS 9
@@ -162,6 +170,12 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                            int32_t chunk, int32_t radius, int32_t rule,
                            void* out, void* stream, const hwa_params* p);
 
+/*
+ * softmax_lse and softmax_out (when not NULL) are written by calls that run
+ * the softmax branch; they must not overlap each other, out, an input or the
+ * workspace. With HWA_FLAG_LINEAR_ONLY they must be NULL.
+ */
+
 /* Workspace bytes hybrid_attn_fwd needs for these sizes (0 on bad args). */
 size_t hwa_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
                            int32_t chunk, const hwa_params* p);
@@ -202,6 +216,50 @@ hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
 
 size_t hwa_text_state_workspace_bytes(int32_t text_tokens,
                                       const hwa_params* p);
+
+/*
+ * hwa_softmax_bwd -- gradient of the windowed softmax branch o_sm (article,
+ * "What the far field outside the window is"; needed to train the hybrid
+ * attention as its "Training" section does). For a loss L with upstream
+ * gradient g = dL/do_sm, s_nm = q_n . k_m / sqrt(d), p_nm = exp(s_nm - lse_n)
+ * over query n's window and delta_n = g_n . o_n:
+ *   dv_m = sum_n p_nm g_n
+ *   ds_nm = p_nm (g_n . v_m - delta_n)
+ *   dq_n = sum_m ds_nm k_m / sqrt(d),   dk_m = sum_n ds_nm q_n / sqrt(d)
+ * (sums over the query-key pairs of the window: query frame t, key frames
+ * lo_t .. hi_t). For out = o_sm + y, g is dL/dout itself.
+ *
+ *   q, k, v    [B, H, N, d] dtype  the softmax branch's inputs (q_rope/k_rope
+ *                                  if the forward used them)
+ *   o_sm       [B, H, N, d] dtype  its output: softmax_out of the forward, or
+ *                                  out of a HWA_FLAG_SOFTMAX_ONLY call
+ *   lse        [B, H, N]    fp32   softmax_lse of the same forward call
+ *   d_o        [B, H, N, d] dtype  g
+ *   frames .. radius               as for hybrid_attn_fwd
+ *   dq, dk, dv [B, H, N, d] dtype  written (bf16: rounded from fp32
+ *                                  accumulation); must not overlap each other,
+ *                                  an input or the workspace
+ *   p          batch, heads, head_dim, dtype, workspace (>= hwa_softmax_bwd_
+ *              workspace_bytes), stage_events (NULL, or
+ *              HWA_NUM_BWD_STAGE_EVENTS events recorded at [0] start, [1]
+ *              after the window table, delta, lse scaling and transposes,
+ *              [2] after the dq kernel, [3] after the dk/dv kernel); the
+ *              other fields are ignored
+ * Returns HWA_OK, or an error status before anything is enqueued.
+ */
+#define HWA_NUM_BWD_STAGE_EVENTS 4
+
+hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
+                           const void* o_sm, const float* lse, const void* d_o,
+                           int32_t frames, int32_t tokens_per_frame,
+                           int32_t chunk, int32_t radius, void* dq, void* dk,
+                           void* dv, void* stream, const hwa_params* p);
+
+/* Workspace bytes hwa_softmax_bwd needs (0 on bad args): the window table,
+ * delta and lse * log2(e) per query, and on bf16 transposed copies of q, k
+ * and d_o (3 * B * H * d * roundup(N, 64) * 2 bytes). */
+size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
+                                       int32_t chunk, const hwa_params* p);
 
 /* Static English text of a status. */
 const char* hwa_status_string(hwa_status s);

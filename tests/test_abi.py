@@ -172,3 +172,80 @@ def test_text_state_validation():
     assert L.hwa_text_state(vp(BASE), vp(BASE + (1 << 36)), vp(BASE + (2 << 36)), 16,
                             vp(BASE + (3 << 36)), None, ctypes.byref(p)) == E.HWA_ERR_WORKSPACE
     assert L.hwa_text_state_workspace_bytes(16, ctypes.byref(p)) > 0
+
+
+@no_gpu
+def test_softmax_outputs_validation_and_struct_evolution():
+    E = hwa
+    # a caller built against the first struct (ending at stage_events) is
+    # accepted and its missing fields read as NULL
+    p = _params()
+    p.struct_size = hwa.Params.softmax_lse.offset
+    p.softmax_lse = BASE + (11 << 36)  # beyond the caller's struct: ignored
+    assert _call(p) == E.HWA_ERR_WORKSPACE
+    p.struct_size = hwa.Params.softmax_lse.offset - 1
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+    # outputs of the softmax branch must not overlap out, an input, each other
+    p = _with_ws(_params())
+    p.softmax_lse = BASE + (9 << 36)                    # = out
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+    p.softmax_lse = BASE + (3 << 36)                    # = q
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+    p.softmax_lse = BASE + (11 << 36)
+    p.softmax_out = BASE + (11 << 36)                   # = softmax_lse
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+    p.softmax_out = BASE + (12 << 36) + 2               # misaligned
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+    # no softmax branch, nothing to write there
+    p = _with_ws(_params(flags=hwa.FLAG_LINEAR_ONLY))
+    p.softmax_lse = BASE + (11 << 36)
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+
+
+def _bwd_call(p, F=10, S=16, chunk=5, radius=1, **ptrs):
+    d = dict(q=BASE + (3 << 36), k=BASE + (4 << 36), v=BASE + (5 << 36), o=BASE + (6 << 36),
+             lse=BASE + (7 << 36), g=BASE + (8 << 36), dq=BASE + (9 << 36),
+             dk=BASE + (11 << 36), dv=BASE + (12 << 36))
+    d.update(ptrs)
+    vp = ctypes.c_void_p
+    return hwa.lib().hwa_softmax_bwd(vp(d["q"]), vp(d["k"]), vp(d["v"]), vp(d["o"]),
+                                     vp(d["lse"]), vp(d["g"]), F, S, chunk, radius,
+                                     vp(d["dq"]), vp(d["dk"]), vp(d["dv"]), None,
+                                     ctypes.byref(p))
+
+
+def _bwd_ws(p, F=10, S=16, chunk=5, extra=0):
+    n = hwa.lib().hwa_softmax_bwd_workspace_bytes(F, S, chunk, ctypes.byref(p))
+    assert n > 0
+    p.workspace = BASE + (10 << 36)
+    p.workspace_bytes = n + extra
+    return p
+
+
+@no_gpu
+def test_softmax_bwd_validation():
+    E = hwa
+    p = _bwd_ws(_params())
+    for name in ("q", "k", "v", "o", "lse", "g", "dq", "dk", "dv"):
+        assert _bwd_call(p, **{name: None}) == E.HWA_ERR_INVALID_ARG, name
+    assert _bwd_call(p, F=0) == E.HWA_ERR_INVALID_ARG
+    assert _bwd_call(p, radius=-1) == E.HWA_ERR_INVALID_ARG
+    assert _bwd_call(p, q=BASE + 8) == E.HWA_ERR_INVALID_ARG            # misaligned
+    assert _bwd_call(p, dk=BASE + (9 << 36)) == E.HWA_ERR_INVALID_ARG   # dk aliases dq
+    assert _bwd_call(p, dv=BASE + (5 << 36)) == E.HWA_ERR_INVALID_ARG   # dv aliases v
+    assert _bwd_call(p, dq=p.workspace) == E.HWA_ERR_INVALID_ARG        # dq in the workspace
+    assert _bwd_call(_bwd_ws(_params(), extra=-256)) == E.HWA_ERR_WORKSPACE
+    assert _bwd_call(_params()) == E.HWA_ERR_WORKSPACE
+    assert _bwd_call(_params(head_dim=16, dtype=1)) == E.HWA_ERR_UNSUPPORTED
+
+
+def test_softmax_bwd_workspace_bytes():
+    L = hwa.lib()
+    for dt in (0, 1):
+        p = hwa.make_params(2, 3, 64, dt)
+        n = L.hwa_softmax_bwd_workspace_bytes(10, 100, 5, ctypes.byref(p))
+        Np = (10 * 100 + 63) // 64 * 64
+        # delta and lse2 per query, plus (bf16) three transposed bf16 copies
+        need = 2 * 6 * Np * 4 + (3 * 6 * 64 * Np * 2 if dt == 1 else 0)
+        assert need <= n <= need + 8 * 256
+    assert L.hwa_softmax_bwd_workspace_bytes(0, 100, 5, ctypes.byref(p)) == 0
