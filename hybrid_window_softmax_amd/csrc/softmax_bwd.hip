@@ -23,6 +23,8 @@
 // The contractions over queries (keys) read their other operand from a
 // transposed copy [B, H, d, Np] of q and g (k), made by the V-transpose kernel.
 
+#include <type_traits>
+
 #include "attn_tile.h"
 
 namespace hwa {
@@ -291,6 +293,21 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- bf16 dk, dv
+// Per wave: 32 keys (K and V rows as B operands in registers; dK^T and dV^T,
+// d x 32, accumulate in registers). The queries of the window stream through
+// LDS in tiles of 64 = two blocks of 32. Per block b: A(b) = the products
+// S(b) = Q_b K^T and dP(b) = G_b V^T; VALU(b) = p and ds of its 16 x 32
+// entries per lane (bf16 B operands); B(b) = dV^T += G_b^T P(b) and
+// dK^T += Q_b^T dS(b). One stream of MFMAs per step (one block): B(b - 1)
+// then A(b + 1), with VALU(b) spread over it, so that the exp work of one
+// block runs under the products of its neighbours (one wave per SIMD).
+// Row tiles (Q, G: read by A) and column tiles (Q^T, G^T, with lse2 and
+// delta: read by B and VALU) have their own two stages; per tile `it`:
+//   step X: B(it-1, 1) | A(it, 1) | VALU(it, 0); barrier
+//   step Y: loads row(it+2), col(it+1); B(it, 0) | A(it+1, 0) | VALU(it, 1);
+//           wait for the loads; barrier
+// so every stage is refilled only after the barrier that follows its last
+// reader, and lands before the barrier that precedes its first reader.
 constexpr int DK_NW = 4;
 constexpr int DK_KT = 32 * DK_NW;
 
@@ -302,14 +319,14 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
     const int32_t* __restrict__ lohi, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int F,
     int S, int chunk, int nch, long long N, long long Np, int tiles_per_chunk, int ntiles,
     float scale_log2, float scale) {
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int RPW = BT * D / 8 / 64 / DK_NW;
   static_assert(BT * D / 8 % (64 * DK_NW) == 0, "uniform loads per wave");
-  __shared__ __attribute__((aligned(16))) bf16_t q_lds[2][BT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t g_lds[2][BT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t qt_lds[2][D * BT];
-  __shared__ __attribute__((aligned(16))) bf16_t gt_lds[2][D * BT];
-  __shared__ __attribute__((aligned(16))) float l2_lds[2][BT];
-  __shared__ __attribute__((aligned(16))) float dl_lds[2][BT];
+  constexpr int NA = D / 8, NB = D / 8, NG = NA + NB;  // MFMAs of A(b), B(b), a step
+  constexpr int PF = 2;                                // operand reads ahead of their MFMA
+  __shared__ __attribute__((aligned(16))) bf16_t row_lds[2][2][BT * D];  // [stage][Q, G]
+  __shared__ __attribute__((aligned(16))) bf16_t col_lds[2][2][D * BT];  // [stage][Q^T, G^T]
+  __shared__ __attribute__((aligned(16))) float ls_lds[2][2][BT];        // [stage][lse2, delta]
 
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   if (L >= ntiles) return;
@@ -342,25 +359,33 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
     r_off[j] = rowtile_off<D>(slot);
     c_off[j] = coltile_off(slot, Np);
   }
-  auto load_tile = [&](long long qt0, int st) __attribute__((always_inline)) {
+  const long long toff = (long long)bh * D * Np;
+  auto load_rows = [&](int it, int st) __attribute__((always_inline)) {
+    const long long qt0 = qt_first + (long long)it * BT;
     const hwa_i32x4 rq = tile_desc(q + hoff, N * D, qt0 * D, 2);
     const hwa_i32x4 rg = tile_desc(g + hoff, N * D, qt0 * D, 2);
-    const hwa_i32x4 rqt = tile_desc(q_t + (long long)bh * D * Np, (long long)D * Np, qt0, 2);
-    const hwa_i32x4 rgt = tile_desc(g_t + (long long)bh * D * Np, (long long)D * Np, qt0, 2);
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const int s0 = (wave + DK_NW * j) * 512;
-      hwa_raw_buffer_load_lds(rq, (lds_void*)&q_lds[st][s0], 16, r_off[j], 0, 0, 0);
-      hwa_raw_buffer_load_lds(rg, (lds_void*)&g_lds[st][s0], 16, r_off[j], 0, 0, 0);
-      hwa_raw_buffer_load_lds(rqt, (lds_void*)&qt_lds[st][s0], 16, c_off[j], 0, 0, 0);
-      hwa_raw_buffer_load_lds(rgt, (lds_void*)&gt_lds[st][s0], 16, c_off[j], 0, 0, 0);
+      hwa_raw_buffer_load_lds(rq, (lds_void*)&row_lds[st][0][s0], 16, r_off[j], 0, 0, 0);
+      hwa_raw_buffer_load_lds(rg, (lds_void*)&row_lds[st][1][s0], 16, r_off[j], 0, 0, 0);
+    }
+  };
+  auto load_cols = [&](int it, int st) __attribute__((always_inline)) {
+    const long long qt0 = qt_first + (long long)it * BT;
+    const hwa_i32x4 rqt = tile_desc(q_t + toff, (long long)D * Np, qt0, 2);
+    const hwa_i32x4 rgt = tile_desc(g_t + toff, (long long)D * Np, qt0, 2);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int s0 = (wave + DK_NW * j) * 512;
+      hwa_raw_buffer_load_lds(rqt, (lds_void*)&col_lds[st][0][s0], 16, c_off[j], 0, 0, 0);
+      hwa_raw_buffer_load_lds(rgt, (lds_void*)&col_lds[st][1][s0], 16, c_off[j], 0, 0, 0);
     }
     // lse2 and delta of the tile's 64 queries: one dword per lane
     if (wave < 2) {
       const float* src = (wave == 0 ? lse2 : delta) + (long long)bh * Np;
-      const hwa_i32x4 rs = tile_desc(src, Np, qt0, 4);
-      float* dst = wave == 0 ? &l2_lds[st][0] : &dl_lds[st][0];
-      hwa_raw_buffer_load_lds(rs, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
+      hwa_raw_buffer_load_lds(tile_desc(src, Np, qt0, 4), (lds_void*)&ls_lds[st][wave][0], 4,
+                              lane * 4, 0, 0, 0);
     }
   };
   int off[4];
@@ -375,68 +400,135 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
       acc_k[j][r] = 0.0f;
       acc_v[j][r] = 0.0f;
     }
+  // S and dP of the two blocks of a tile; bf16 P and dS of the two blocks
+  // (zero until first written: the prologue's VALU runs on block 1)
+  f32x16 s_b[2], p_b[2];
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s_b[b2][r] = 0.0f;
+      p_b[b2][r] = 0.0f;
+    }
+  bf16x8 pb[2][2], dsb[2][2];
 
-  load_tile(qt_first, 0);
+  // A operand of MFMA a of A(blk): S = Q K^T and dP = G V^T alternate
+  auto a_op = [&](int st, int blk, int a) __attribute__((always_inline)) {
+    return row_op<D>(&row_lds[st][a % 2][0], blk, a / 2, off);
+  };
+  // MFMA a of A(blk) into s_b / p_b [blk]
+  // B operand order, MFMA j of B(blk): G^T (dV) and Q^T (dK) alternate over
+  // the channel blocks, then the two 16-query steps
+  auto b_op = [&](int st, int blk, int j) __attribute__((always_inline)) {
+    const int which = j % 2, dblk = (j / 2) % (D / 32), s2 = j / (D / 16);
+    return col_op(&col_lds[st][which ^ 1][0], dblk, 2 * blk + s2, off);
+  };
+  // one probability / ds register r of block blk (query row 32 blk + 16 half + r
+  // of the tile; l2v, dlv: lse2 and delta of the lane's 16 rows)
+  auto valu_reg = [&](int blk, int r, int lo_rel, int hi_rel, const f32x4 (&l2v)[4],
+                      const f32x4 (&dlv)[4]) __attribute__((always_inline)) {
+    const int qr = blk * 32 + half * 16 + r;
+    const float l2 = l2v[r / 4][r % 4];
+    const float dl = dlv[r / 4][r % 4];
+    float sv = s_b[blk][r];
+    asm volatile("" : "+v"(sv));
+    float p = __builtin_amdgcn_exp2f(fmaf(sv, scale_log2, -l2));
+    p = (qr >= lo_rel && qr < hi_rel) ? p : 0.0f;
+    pb[blk][r / 8][r % 8] = (__bf16)p;
+    dsb[blk][r / 8][r % 8] = (__bf16)(p * (p_b[blk][r] - dl));
+  };
+
+  // One step: B(b_blk) from column stage b_st (if do_b), then A(a_blk) from
+  // row stage a_st (if do_a), with VALU(v_blk) of column stage v_st spread
+  // over the MFMAs. All block indices are compile-time; stages and flags are
+  // wave-uniform.
+  auto step = [&](auto b_tag, auto a_tag, auto v_tag, int b_st, int a_st, int v_st, bool do_b,
+                  bool do_a, long long v_qt0) __attribute__((always_inline)) {
+    constexpr int BB = decltype(b_tag)::value, AB = decltype(a_tag)::value,
+                  VB = decltype(v_tag)::value;
+    const int lo_rel = (int)(qw_begin - v_qt0), hi_rel = (int)(qw_end - v_qt0);
+    f32x4 l2v[4], dlv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l2v[i] = *(const f32x4*)&ls_lds[v_st][0][32 * VB + 16 * half + 4 * i];
+      dlv[i] = *(const f32x4*)&ls_lds[v_st][1][32 * VB + 16 * half + 4 * i];
+    }
+    if (do_a) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s_b[AB][r] = 0.0f;
+        p_b[AB][r] = 0.0f;
+      }
+    }
+    bf16x8 opa[PF + 1];
+    auto op_read = [&](int gi) __attribute__((always_inline)) {
+      if (gi < NB) return b_op(b_st, BB, gi);
+      return a_op(a_st, AB, gi - NB);
+    };
+    const int g_first = do_b ? 0 : NB, g_last = do_a ? NG : NB;  // uniform
+#pragma unroll
+    for (int gi = 0; gi < PF; ++gi)
+      if (gi >= g_first && gi < g_last) opa[gi] = op_read(gi);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      if (gi + PF < NG && gi + PF >= g_first && gi + PF < g_last)
+        opa[(gi + PF) % (PF + 1)] = op_read(gi + PF);
+      if (gi >= g_first && gi < g_last) {
+        if (gi < NB) {
+          const int which = gi % 2, dblk = (gi / 2) % (D / 32), s2 = gi / (D / 16);
+          if (which == 0)
+            acc_v[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[gi % (PF + 1)],
+                                                                  pb[BB][s2], acc_v[dblk], 0, 0, 0);
+          else
+            acc_k[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[gi % (PF + 1)],
+                                                                  dsb[BB][s2], acc_k[dblk], 0, 0, 0);
+        } else {
+          const int a = gi - NB;
+          if (a % 2 == 0)
+            s_b[AB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[gi % (PF + 1)], kreg[a / 2],
+                                                              s_b[AB], 0, 0, 0);
+          else
+            p_b[AB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[gi % (PF + 1)], vreg[a / 2],
+                                                              p_b[AB], 0, 0, 0);
+        }
+      }
+      // VALU(v_blk): 16 registers spread over the NG MFMA slots
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((r * NG) / 16 == gi) valu_reg(VB, r, lo_rel, hi_rel, l2v, dlv);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+
+  // prologue: row tiles 0 and 1, column tile 0; A(0, 0)
+  load_rows(0, 0);
+  if (ntl > 1) load_rows(1, 1);
+  load_cols(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  step(B1{}, B0{}, B1{}, 0, 0, 0, false, true, qt_first);  // A(0,0) only (VALU result unused)
   for (int it = 0; it < ntl; ++it) {
     const int st = it & 1;
     const long long qt0 = qt_first + (long long)it * BT;
-    if (it + 1 < ntl) load_tile(qt0 + BT, st ^ 1);
-    const bf16_t* qs = &q_lds[st][0];
-    const bf16_t* gs = &g_lds[st][0];
-    const bf16_t* qts = &qt_lds[st][0];
-    const bf16_t* gts = &gt_lds[st][0];
-    const int lo_rel = (int)(qw_begin - qt0), hi_rel = (int)(qw_end - qt0);
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.0f;
-        dp[r] = 0.0f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(qs, blk, kk, off), kreg[kk], s, 0,
-                                                    0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(gs, blk, kk, off), vreg[kk], dp,
-                                                     0, 0, 0);
-      }
-      // register r of half h holds query qt0 + 32 blk + 16 h + r
-      const f32x4* l2v = (const f32x4*)&l2_lds[st][32 * blk + 16 * half];
-      const f32x4* dlv = (const f32x4*)&dl_lds[st][32 * blk + 16 * half];
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 l2 = l2v[i], dl = dlv[i];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * i + u;
-          const int qr = blk * 32 + half * 16 + r;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -l2[u]));
-          p = (qr >= lo_rel && qr < hi_rel) ? p : 0.0f;
-          pb[r / 8][r % 8] = (__bf16)p;
-          dsb[r / 8][r % 8] = (__bf16)(p * (dp[r] - dl[u]));
-        }
-      }
-#pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          acc_v[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              col_op(gts, dblk, 2 * blk + s2, off), pb[s2], acc_v[dblk], 0, 0, 0);
-          acc_k[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              col_op(qts, dblk, 2 * blk + s2, off), dsb[s2], acc_k[dblk], 0, 0, 0);
-        }
-    }
+    // X: B(it-1, 1) | A(it, 1) | VALU(it, 0)
+    step(B1{}, B1{}, B0{}, st ^ 1, st, st, it > 0, true, qt0);
+    __syncthreads();
+    // Y: B(it, 0) | A(it+1, 0) | VALU(it, 1)
+    if (it + 2 < ntl) load_rows(it + 2, st);
+    if (it + 1 < ntl) load_cols(it + 1, st ^ 1);
+    step(B0{}, B0{}, B1{}, st, st ^ 1, st, true, it + 1 < ntl, qt0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  // drain: B(ntl-1, 1)
+  step(B1{}, B0{}, B0{}, (ntl - 1) & 1, 0, (ntl - 1) & 1, true, false, qt_first);
   if (k_ok) {
     store_rows<D>(dk + hoff + my_k * D, acc_k, scale, half);
     store_rows<D>(dv + hoff + my_k * D, acc_v, 1.0f, half);
   }
+#endif
 }
 
 // ---------------------------------------------------------------- fp32 VALU
