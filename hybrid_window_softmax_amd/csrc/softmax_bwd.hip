@@ -268,18 +268,28 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
                                                           pT[blk], 0, 0, 0);
       }
     }
-    // register r of half h in block blk holds key kt0 + 32 blk + 16 h + r
+    // register r of half h in block blk holds key kt0 + 32 blk + 16 h + r;
+    // keys outside the window occur in the first and last tiles only
     const int lo_rel = (int)(k_begin - kt0), hi_rel = (int)(k_end - kt0);
+    float pr[2][16];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[blk][r] = __builtin_amdgcn_exp2f(fmaf(sT[blk][r], scale_log2, -l2q));
+    if (lo_rel > 0 || hi_rel < BT) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = blk * 32 + half * 16 + r;
+          if (key < lo_rel || key >= hi_rel) pr[blk][r] = 0.0f;
+        }
+    }
     bf16x8 dsb[4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = blk * 32 + half * 16 + r;
-        float p = __builtin_amdgcn_exp2f(fmaf(sT[blk][r], scale_log2, -l2q));
-        p = (key >= lo_rel && key < hi_rel) ? p : 0.0f;
-        dsb[blk * 2 + r / 8][r % 8] = (__bf16)(p * (pT[blk][r] - dlq));
-      }
+      for (int r = 0; r < 16; ++r) dsb[blk * 2 + r / 8][r % 8] = (__bf16)(pr[blk][r] * (pT[blk][r] - dlq));
 #pragma unroll
     for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
@@ -323,7 +333,10 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
   constexpr int RPW = BT * D / 8 / 64 / DK_NW;
   static_assert(BT * D / 8 % (64 * DK_NW) == 0, "uniform loads per wave");
   constexpr int NA = D / 8, NB = D / 8, NG = NA + NB;  // MFMAs of A(b), B(b), a step
-  constexpr int PF = 2;                                // operand reads ahead of their MFMA
+#ifndef DK_PF
+#define DK_PF 3
+#endif
+  constexpr int PF = DK_PF;                            // operand reads ahead of their MFMA
   __shared__ __attribute__((aligned(16))) bf16_t row_lds[2][2][BT * D];  // [stage][Q, G]
   __shared__ __attribute__((aligned(16))) bf16_t col_lds[2][2][D * BT];  // [stage][Q^T, G^T]
   __shared__ __attribute__((aligned(16))) float ls_lds[2][2][BT];        // [stage][lse2, delta]
@@ -388,6 +401,15 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
                               lane * 4, 0, 0, 0);
     }
   };
+  // Rows of column tile `it` outside the window [qw_begin, qw_end) get
+  // lse2 = +inf, so that p = exp2(s * scale_log2 - lse2) = 0 and ds = 0 there.
+  // Called by wave 0, which loaded lse2, after its loads landed and before the
+  // barrier that publishes the tile.
+  auto mask_cols = [&](int it, int st) __attribute__((always_inline)) {
+    const long long qt0 = qt_first + (long long)it * BT;
+    const long long qn = qt0 + lane;
+    if (qn < qw_begin || qn >= qw_end) ls_lds[st][0][lane] = __builtin_inff();
+  };
   int off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) off[j] = col * 64 + ((op_chunk(j, half) ^ swz(col)) * 8);
@@ -424,29 +446,29 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
     return col_op(&col_lds[st][which ^ 1][0], dblk, 2 * blk + s2, off);
   };
   // one probability / ds register r of block blk (query row 32 blk + 16 half + r
-  // of the tile; l2v, dlv: lse2 and delta of the lane's 16 rows)
-  auto valu_reg = [&](int blk, int r, int lo_rel, int hi_rel, const f32x4 (&l2v)[4],
-                      const f32x4 (&dlv)[4]) __attribute__((always_inline)) {
-    const int qr = blk * 32 + half * 16 + r;
+  // of the tile; l2v, dlv: lse2 and delta of the lane's 16 rows; lse2 = +inf
+  // outside the window)
+  auto valu_reg = [&](int blk, int r, const f32x4 (&l2v)[4], const f32x4 (&dlv)[4])
+                      __attribute__((always_inline)) {
     const float l2 = l2v[r / 4][r % 4];
     const float dl = dlv[r / 4][r % 4];
     float sv = s_b[blk][r];
     asm volatile("" : "+v"(sv));
-    float p = __builtin_amdgcn_exp2f(fmaf(sv, scale_log2, -l2));
-    p = (qr >= lo_rel && qr < hi_rel) ? p : 0.0f;
+    const float p = __builtin_amdgcn_exp2f(fmaf(sv, scale_log2, -l2));
     pb[blk][r / 8][r % 8] = (__bf16)p;
     dsb[blk][r / 8][r % 8] = (__bf16)(p * (p_b[blk][r] - dl));
   };
 
-  // One step: B(b_blk) from column stage b_st (if do_b), then A(a_blk) from
-  // row stage a_st (if do_a), with VALU(v_blk) of column stage v_st spread
-  // over the MFMAs. All block indices are compile-time; stages and flags are
-  // wave-uniform.
-  auto step = [&](auto b_tag, auto a_tag, auto v_tag, int b_st, int a_st, int v_st, bool do_b,
-                  bool do_a, long long v_qt0) __attribute__((always_inline)) {
+  // One step: B(b_blk) from column stage b_st (if DO_B), then A(a_blk) from
+  // row stage a_st (if DO_A), with VALU(v_blk) of column stage v_st spread
+  // over the MFMAs (if DO_V). Block indices and flags are compile-time (the
+  // first and last tiles are peeled), stages wave-uniform.
+  auto step = [&](auto b_tag, auto a_tag, auto v_tag, auto flags, int b_st, int a_st, int v_st)
+                  __attribute__((always_inline)) {
     constexpr int BB = decltype(b_tag)::value, AB = decltype(a_tag)::value,
                   VB = decltype(v_tag)::value;
-    const int lo_rel = (int)(qw_begin - v_qt0), hi_rel = (int)(qw_end - v_qt0);
+    constexpr int FL = decltype(flags)::value;
+    constexpr bool do_b = FL & 1, do_a = FL & 2, do_v = FL & 4;
     f32x4 l2v[4], dlv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -465,7 +487,7 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
       if (gi < NB) return b_op(b_st, BB, gi);
       return a_op(a_st, AB, gi - NB);
     };
-    const int g_first = do_b ? 0 : NB, g_last = do_a ? NG : NB;  // uniform
+    constexpr int g_first = do_b ? 0 : NB, g_last = do_a ? NG : NB;
 #pragma unroll
     for (int gi = 0; gi < PF; ++gi)
       if (gi >= g_first && gi < g_last) opa[gi] = op_read(gi);
@@ -493,37 +515,61 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
         }
       }
       // VALU(v_blk): 16 registers spread over the NG MFMA slots
+      if (do_v) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if ((r * NG) / 16 == gi) valu_reg(VB, r, lo_rel, hi_rel, l2v, dlv);
+        for (int r = 0; r < 16; ++r)
+          if ((r * NG) / 16 == gi) valu_reg(VB, r, l2v, dlv);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   typedef std::integral_constant<int, 0> B0;
   typedef std::integral_constant<int, 1> B1;
+  // step flags: 1 = B, 2 = A, 4 = VALU
+  typedef std::integral_constant<int, 2> F_A;
+  typedef std::integral_constant<int, 6> F_AV;
+  typedef std::integral_constant<int, 7> F_BAV;
+  typedef std::integral_constant<int, 5> F_BV;
+  typedef std::integral_constant<int, 1> F_B;
 
   // prologue: row tiles 0 and 1, column tile 0; A(0, 0)
   load_rows(0, 0);
   if (ntl > 1) load_rows(1, 1);
   load_cols(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (wave == 0) mask_cols(0, 0);
   __syncthreads();
-  step(B1{}, B0{}, B1{}, 0, 0, 0, false, true, qt_first);  // A(0,0) only (VALU result unused)
-  for (int it = 0; it < ntl; ++it) {
+  step(B1{}, B0{}, B1{}, F_A{}, 0, 0, 0);
+  // X: B(it-1, 1) | A(it, 1) | VALU(it, 0); then Y: loads row(it+2) and
+  // col(it+1), B(it, 0) | A(it+1, 0) | VALU(it, 1)
+  auto tile_x = [&](auto fl, int it) __attribute__((always_inline)) {
     const int st = it & 1;
-    const long long qt0 = qt_first + (long long)it * BT;
-    // X: B(it-1, 1) | A(it, 1) | VALU(it, 0)
-    step(B1{}, B1{}, B0{}, st ^ 1, st, st, it > 0, true, qt0);
-    __syncthreads();
-    // Y: B(it, 0) | A(it+1, 0) | VALU(it, 1)
-    if (it + 2 < ntl) load_rows(it + 2, st);
-    if (it + 1 < ntl) load_cols(it + 1, st ^ 1);
-    step(B0{}, B0{}, B1{}, st, st ^ 1, st, true, it + 1 < ntl, qt0);
+    step(B1{}, B1{}, B0{}, fl, st ^ 1, st, st);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  auto tile_y = [&](auto fl, int it) __attribute__((always_inline)) {
+    const int st = it & 1;
+    if (it + 2 < ntl) load_rows(it + 2, st);
+    if (it + 1 < ntl) load_cols(it + 1, st ^ 1);
+    step(B0{}, B0{}, B1{}, fl, st, st ^ 1, st);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (wave == 0 && it + 1 < ntl) mask_cols(it + 1, st ^ 1);
+    __syncthreads();
+  };
+  // first tile: nothing pending for B in X
+  tile_x(F_AV{}, 0);
+  if (ntl > 1) {
+    tile_y(F_BAV{}, 0);
+    for (int it = 1; it + 1 < ntl; ++it) {
+      tile_x(F_BAV{}, it);
+      tile_y(F_BAV{}, it);
+    }
+    tile_x(F_BAV{}, ntl - 1);
   }
+  tile_y(F_BV{}, ntl - 1);  // last tile: no A(ntl, 0)
   // drain: B(ntl-1, 1)
-  step(B1{}, B0{}, B0{}, (ntl - 1) & 1, 0, (ntl - 1) & 1, true, false, qt_first);
+  step(B1{}, B0{}, B0{}, F_B{}, (ntl - 1) & 1, 0, 0);
   if (k_ok) {
     store_rows<D>(dk + hoff + my_k * D, acc_k, scale, half);
     store_rows<D>(dv + hoff + my_k * D, acc_v, 1.0f, half);
