@@ -128,6 +128,23 @@ __device__ __forceinline__ void store_rows(bf16_t* dst_row, const f32x16 (&acc)[
 
 }  // namespace
 
+// Direct load of 16 bytes per lane into LDS (lane l writes lds + 16 l; lanes
+// whose offset lies past the descriptor's num_records write zeros), written
+// out so that the compiler's wait-count tracking does not treat it as an LDS
+// write that every later LDS read must wait for (with the intrinsic, the dk/dv
+// kernel's operand reads each waited for all loads in flight). The kernel
+// orders it itself: s_waitcnt vmcnt(0) before the barrier that publishes a
+// stage. It has no register result, and the compiler's own vmcnt waits stay
+// sufficient (loads complete in issue order, so extra loads issued after a
+// tracked one only make its wait stricter). The nop is the wait state between
+// the M0 write and its use.
+__device__ __forceinline__ void dma16(hwa_i32x4 rsrc, __attribute__((address_space(3))) void* lds,
+                                      int voffset) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(rsrc), "{m0}"(base) : "memory");
+}
+
 // ---------------------------------------------------------------- prep
 // delta_n = g_n . o_n (fp32 from the I/O dtype) and lse2_n = lse_n * log2(e)
 // for every query, [B*H, Np] with zeros past N. LPQ lanes share a query, each
@@ -314,8 +331,8 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
 // Row tiles (Q, G: read by A) and column tiles (Q^T, G^T, with lse2 and
 // delta: read by B and VALU) have their own two stages; per tile `it`:
 //   step X: B(it-1, 1) | A(it, 1) | VALU(it, 0); barrier
-//   step Y: loads row(it+2), col(it+1); B(it, 0) | A(it+1, 0) | VALU(it, 1);
-//           wait for the loads; barrier
+//   step Y: loads of col(it+1) and row(it+2) with the first MFMA;
+//           B(it, 0) | A(it+1, 0) | VALU(it, 1); wait for the loads; barrier
 // so every stage is refilled only after the barrier that follows its last
 // reader, and lands before the barrier that precedes its first reader.
 constexpr int DK_NW = 4;
@@ -339,7 +356,9 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
   constexpr int PF = DK_PF;                            // operand reads ahead of their MFMA
   __shared__ __attribute__((aligned(16))) bf16_t row_lds[2][2][BT * D];  // [stage][Q, G]
   __shared__ __attribute__((aligned(16))) bf16_t col_lds[2][2][D * BT];  // [stage][Q^T, G^T]
-  __shared__ __attribute__((aligned(16))) float ls_lds[2][2][BT];        // [stage][lse2, delta]
+  // [stage][lse2, delta]: 64 values, then the padding that the rest of the
+  // wave's 16-byte direct load writes
+  __shared__ __attribute__((aligned(16))) float ls_lds[2][2][4 * 64];
 
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   if (L >= ntiles) return;
@@ -373,42 +392,62 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
     c_off[j] = coltile_off(slot, Np);
   }
   const long long toff = (long long)bh * D * Np;
-  auto load_rows = [&](int it, int st) __attribute__((always_inline)) {
-    const long long qt0 = qt_first + (long long)it * BT;
-    const hwa_i32x4 rq = tile_desc(q + hoff, N * D, qt0 * D, 2);
-    const hwa_i32x4 rg = tile_desc(g + hoff, N * D, qt0 * D, 2);
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int s0 = (wave + DK_NW * j) * 512;
-      hwa_raw_buffer_load_lds(rq, (lds_void*)&row_lds[st][0][s0], 16, r_off[j], 0, 0, 0);
-      hwa_raw_buffer_load_lds(rg, (lds_void*)&row_lds[st][1][s0], 16, r_off[j], 0, 0, 0);
+  // Direct loads of a step, one instruction per call: column tile `ic` into
+  // column stage SC (Q^T then G^T, then lse2 / delta on waves 0 and 1), then
+  // row tile `ir` into row stage SR (Q then G); a tile index < 0 skips it.
+  // Stage indices are compile-time (the tile loop runs over pairs of tiles).
+  constexpr int NLD = 4 * RPW + 1;  // instructions per step (at most)
+  struct Loads {
+    hwa_i32x4 rq, rg, rqt, rgt, rls;
+    int ic, ir;
+  };
+  auto make_loads = [&](int ic, int ir) __attribute__((always_inline)) {
+    Loads l;
+    l.ic = ic;
+    l.ir = ir;
+    const long long qc = qt_first + (long long)(ic < 0 ? 0 : ic) * BT;
+    const long long qr = qt_first + (long long)(ir < 0 ? 0 : ir) * BT;
+    l.rqt = tile_desc(q_t + toff, (long long)D * Np, qc, 2);
+    l.rgt = tile_desc(g_t + toff, (long long)D * Np, qc, 2);
+    l.rls = tile_desc((wave == 0 ? lse2 : delta) + (long long)bh * Np, Np, qc, 4);
+    l.rq = tile_desc(q + hoff, N * D, qr * D, 2);
+    l.rg = tile_desc(g + hoff, N * D, qr * D, 2);
+    return l;
+  };
+  auto issue = [&](auto sc_tag, auto sr_tag, const Loads& l, int j)
+                   __attribute__((always_inline)) {
+    constexpr int SC = decltype(sc_tag)::value, SR = decltype(sr_tag)::value;
+    if (j < 2 * RPW) {
+      if (l.ic >= 0) {
+        const int jj = j % RPW, s0 = (wave + DK_NW * jj) * 512;
+        dma16(j < RPW ? l.rqt : l.rgt, (lds_void*)&col_lds[SC][j < RPW ? 0 : 1][s0], c_off[jj]);
+      }
+    } else if (j == 2 * RPW) {
+      // lse2 and delta of the tile's 64 queries: lanes 0..15, 16 bytes each
+      // (the 16-byte form, like every other load here: the compiler does not
+      // make LDS reads wait for it); the other lanes fill the padding
+      if (l.ic >= 0 && wave < 2)
+        dma16(l.rls, (lds_void*)&ls_lds[SC][wave][0], lane * 16);
+    } else if (j < NLD) {
+      if (l.ir >= 0) {
+        const int jr = j - 2 * RPW - 1, jj = jr % RPW, s0 = (wave + DK_NW * jj) * 512;
+        dma16(jr < RPW ? l.rq : l.rg, (lds_void*)&row_lds[SR][jr < RPW ? 0 : 1][s0], r_off[jj]);
+      }
     }
   };
-  auto load_cols = [&](int it, int st) __attribute__((always_inline)) {
-    const long long qt0 = qt_first + (long long)it * BT;
-    const hwa_i32x4 rqt = tile_desc(q_t + toff, (long long)D * Np, qt0, 2);
-    const hwa_i32x4 rgt = tile_desc(g_t + toff, (long long)D * Np, qt0, 2);
+  auto load_all = [&](auto sc_tag, auto sr_tag, const Loads& l) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int s0 = (wave + DK_NW * j) * 512;
-      hwa_raw_buffer_load_lds(rqt, (lds_void*)&col_lds[st][0][s0], 16, c_off[j], 0, 0, 0);
-      hwa_raw_buffer_load_lds(rgt, (lds_void*)&col_lds[st][1][s0], 16, c_off[j], 0, 0, 0);
-    }
-    // lse2 and delta of the tile's 64 queries: one dword per lane
-    if (wave < 2) {
-      const float* src = (wave == 0 ? lse2 : delta) + (long long)bh * Np;
-      hwa_raw_buffer_load_lds(tile_desc(src, Np, qt0, 4), (lds_void*)&ls_lds[st][wave][0], 4,
-                              lane * 4, 0, 0, 0);
-    }
+    for (int j = 0; j < NLD; ++j) issue(sc_tag, sr_tag, l, j);
   };
   // Rows of column tile `it` outside the window [qw_begin, qw_end) get
   // lse2 = +inf, so that p = exp2(s * scale_log2 - lse2) = 0 and ds = 0 there.
   // Called by wave 0, which loaded lse2, after its loads landed and before the
   // barrier that publishes the tile.
-  auto mask_cols = [&](int it, int st) __attribute__((always_inline)) {
+  auto mask_cols = [&](auto st_tag, int it) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_tag)::value;
     const long long qt0 = qt_first + (long long)it * BT;
     const long long qn = qt0 + lane;
-    if (qn < qw_begin || qn >= qw_end) ls_lds[st][0][lane] = __builtin_inff();
+    if (qn < qw_begin || qn >= qw_end) ls_lds[ST][0][lane] = __builtin_inff();
   };
   int off[4];
 #pragma unroll
@@ -463,10 +502,12 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
   // row stage a_st (if DO_A), with VALU(v_blk) of column stage v_st spread
   // over the MFMAs (if DO_V). Block indices and flags are compile-time (the
   // first and last tiles are peeled), stages wave-uniform.
-  auto step = [&](auto b_tag, auto a_tag, auto v_tag, auto flags, int b_st, int a_st, int v_st)
-                  __attribute__((always_inline)) {
+  auto step = [&](auto b_tag, auto a_tag, auto v_tag, auto flags, auto bst_tag, auto ast_tag,
+                  auto vst_tag, auto&& loader) __attribute__((always_inline)) {
     constexpr int BB = decltype(b_tag)::value, AB = decltype(a_tag)::value,
                   VB = decltype(v_tag)::value;
+    constexpr int b_st = decltype(bst_tag)::value, a_st = decltype(ast_tag)::value,
+                  v_st = decltype(vst_tag)::value;
     constexpr int FL = decltype(flags)::value;
     constexpr bool do_b = FL & 1, do_a = FL & 2, do_v = FL & 4;
     f32x4 l2v[4], dlv[4];
@@ -520,6 +561,13 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
         for (int r = 0; r < 16; ++r)
           if ((r * NG) / 16 == gi) valu_reg(VB, r, l2v, dlv);
       }
+      // this step's direct loads, all with the first MFMA (measured at
+      // 132,600 tokens: 1.5 % faster than half with the first and half at
+      // mid-step; one after every other MFMA was 15 times slower)
+      if (gi == 0) {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) loader(j);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -532,44 +580,63 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
   typedef std::integral_constant<int, 5> F_BV;
   typedef std::integral_constant<int, 1> F_B;
 
+  auto no_loads = [](int) {};
   // prologue: row tiles 0 and 1, column tile 0; A(0, 0)
-  load_rows(0, 0);
-  if (ntl > 1) load_rows(1, 1);
-  load_cols(0, 0);
+  load_all(B0{}, B0{}, make_loads(0, 0));
+  if (ntl > 1) load_all(B0{}, B1{}, make_loads(-1, 1));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (wave == 0) mask_cols(0, 0);
+  if (wave == 0) mask_cols(B0{}, 0);
   __syncthreads();
-  step(B1{}, B0{}, B1{}, F_A{}, 0, 0, 0);
-  // X: B(it-1, 1) | A(it, 1) | VALU(it, 0); then Y: loads row(it+2) and
-  // col(it+1), B(it, 0) | A(it+1, 0) | VALU(it, 1)
-  auto tile_x = [&](auto fl, int it) __attribute__((always_inline)) {
-    const int st = it & 1;
-    step(B1{}, B1{}, B0{}, fl, st ^ 1, st, st);
+  step(B1{}, B0{}, B1{}, F_A{}, B0{}, B0{}, B0{}, no_loads);
+  // tile `it` in stage ST = it % 2 (compile-time: the loop runs over pairs
+  // of tiles). X: B(it-1, 1) | A(it, 1) | VALU(it, 0); then Y: B(it, 0) |
+  // A(it+1, 0) | VALU(it, 1) with the loads of col(it+1) and row(it+2)
+  auto tile_x = [&](auto fl, auto st_tag, int it) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_tag)::value;
+    typedef std::integral_constant<int, ST ^ 1> SO;
+    step(B1{}, B1{}, B0{}, fl, SO{}, st_tag, st_tag, no_loads);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  auto tile_y = [&](auto fl, int it) __attribute__((always_inline)) {
-    const int st = it & 1;
-    if (it + 2 < ntl) load_rows(it + 2, st);
-    if (it + 1 < ntl) load_cols(it + 1, st ^ 1);
-    step(B0{}, B0{}, B1{}, fl, st, st ^ 1, st);
+  auto tile_y = [&](auto fl, auto st_tag, int it) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_tag)::value;
+    typedef std::integral_constant<int, ST ^ 1> SO;
+    const Loads l = make_loads(it + 1 < ntl ? it + 1 : -1, it + 2 < ntl ? it + 2 : -1);
+    step(B0{}, B0{}, B1{}, fl, st_tag, SO{}, st_tag, [&](int j) { issue(SO{}, st_tag, l, j); });
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (wave == 0 && it + 1 < ntl) mask_cols(it + 1, st ^ 1);
+    if (wave == 0 && it + 1 < ntl) mask_cols(SO{}, it + 1);
     __syncthreads();
   };
-  // first tile: nothing pending for B in X
-  tile_x(F_AV{}, 0);
-  if (ntl > 1) {
-    tile_y(F_BAV{}, 0);
-    for (int it = 1; it + 1 < ntl; ++it) {
-      tile_x(F_BAV{}, it);
-      tile_y(F_BAV{}, it);
+  // drain: B(last, 1) from the last tile's column stage
+  auto drain = [&](auto st_tag) __attribute__((always_inline)) {
+    step(B1{}, B0{}, B0{}, F_B{}, st_tag, B0{}, B0{}, no_loads);
+  };
+  // first tile: nothing pending for B in X; last tile: no A(ntl, 0) in Y
+  tile_x(F_AV{}, B0{}, 0);
+  if (ntl == 1) {
+    tile_y(F_BV{}, B0{}, 0);
+    drain(B0{});
+  } else {
+    tile_y(F_BAV{}, B0{}, 0);
+    int it = 1;
+    for (; it + 2 < ntl; it += 2) {
+      tile_x(F_BAV{}, B1{}, it);
+      tile_y(F_BAV{}, B1{}, it);
+      tile_x(F_BAV{}, B0{}, it + 1);
+      tile_y(F_BAV{}, B0{}, it + 1);
     }
-    tile_x(F_BAV{}, ntl - 1);
+    if (it + 1 < ntl) {  // tiles it (odd) and the last, it + 1
+      tile_x(F_BAV{}, B1{}, it);
+      tile_y(F_BAV{}, B1{}, it);
+      tile_x(F_BAV{}, B0{}, it + 1);
+      tile_y(F_BV{}, B0{}, it + 1);
+      drain(B0{});
+    } else {  // the last tile, it (odd)
+      tile_x(F_BAV{}, B1{}, it);
+      tile_y(F_BV{}, B1{}, it);
+      drain(B1{});
+    }
   }
-  tile_y(F_BV{}, ntl - 1);  // last tile: no A(ntl, 0)
-  // drain: B(ntl-1, 1)
-  step(B1{}, B0{}, B0{}, F_B{}, (ntl - 1) & 1, 0, 0);
   if (k_ok) {
     store_rows<D>(dk + hoff + my_k * D, acc_k, scale, half);
     store_rows<D>(dv + hoff + my_k * D, acc_v, 1.0f, half);
