@@ -34,9 +34,14 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector, packed) / fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_traffic.json")
-# the softmax kernel's sources (the kernel and the readout epilogue it includes)
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_bwd_traffic.json")
+# the softmax kernel's sources (the kernel, the readout epilogue and the tile
+# helpers it includes)
 SOFTMAX_SRCS = [os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", n)
-                for n in ("softmax.hip", "readout_core.h", "hwa_internal.h")]
+                for n in ("softmax.hip", "readout_core.h", "attn_tile.h", "hwa_internal.h")]
+# the backward kernels' sources
+SOFTMAX_BWD_SRCS = [os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", n)
+                    for n in ("softmax_bwd.hip", "attn_tile.h", "hwa_internal.h")]
 
 
 def log(*a):
@@ -83,27 +88,36 @@ def algorithmic_work(cfg):
     }
 
 
-def softmax_sources_sha256():
-    """sha256 over the softmax kernel's source files, in order."""
+def sources_sha256(paths=None):
+    """sha256 over a kernel's source files, in order (default: the forward
+    softmax kernel's)."""
     h = hashlib.sha256()
-    for path in SOFTMAX_SRCS:
+    for path in paths or SOFTMAX_SRCS:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def softmax_traffic():
-    """HBM bytes per softmax launch from the committed rocprofv3 counter
+def softmax_sources_sha256():
+    return sources_sha256(SOFTMAX_SRCS)
+
+
+def recorded_traffic(path=TRAFFIC_FILE, srcs=None):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
     summary, or None when the kernel's sources changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
-        sha = softmax_sources_sha256()
+        sha = sources_sha256(srcs or SOFTMAX_SRCS)
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != sha:
         return None
     return rec.get("bytes_per_launch")
+
+
+def softmax_traffic():
+    return recorded_traffic(TRAFFIC_FILE, SOFTMAX_SRCS)
 
 
 def cpu_baseline(inp, rule, heads_run=1):
@@ -230,7 +244,8 @@ def bench_softmax_bwd(args, cfg, inp, up):
     achieved = work[dom]["flops"] / (stage[dom] / 1000.0) / 1e12
     roofline = {"kernel": "softmax_bwd_dkdv_kernel", "bound": "mfma",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(BWD_TRAFFIC_FILE, SOFTMAX_BWD_SRCS),
                 "algorithmic_flops_per_launch": work[dom]["flops"]}
     cpu = None
     if not args.no_cpu_baseline:
