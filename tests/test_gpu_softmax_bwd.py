@@ -126,7 +126,7 @@ def _key_rows(cfg, chunks, seed):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def _check_sampled(name, heads):
+def _check_sampled(name, heads, chunks=3):
     inp = inputs.make(name)
     c = inp.cfg
     print(f"case {name}: sampled rows of heads {heads} + sums over every head", flush=True)
@@ -147,7 +147,7 @@ def _check_sampled(name, heads):
             assert np.linalg.norm(dvs - gs) <= 1e-2 * np.linalg.norm(gs), (b, h)
             assert np.linalg.norm(dkh.sum(axis=0)) <= 1e-2 * np.linalg.norm(dkh), (b, h)
     qrows = sample_rows(c, n_random=32, seed=5)
-    krows = _key_rows(c, sorted({0, nch // 2, nch - 1}), seed=6)
+    krows = _key_rows(c, sorted({0, nch // 2, nch - 1})[:chunks], seed=6)
     for (b, h) in heads:
         q, k, v = (inp.f64(n, b, h) for n in ("q", "k", "v"))
         g = _g64(inp, g_host, b, h)
@@ -166,6 +166,10 @@ def test_clip_48360tok_sampled():
 
 def test_long_clip_132600tok_sampled():
     _check_sampled("long-clip-832x480-85f", [(0, 5)])
+
+
+def test_canvas_262144tok_sampled():
+    _check_sampled("canvas-1024x1024-64f", [(0, 17)], chunks=2)
 
 
 @pytest.mark.parametrize("name", ["tiny-f32", "small-bf16-text"])

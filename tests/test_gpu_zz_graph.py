@@ -58,3 +58,52 @@ def test_repeat_and_graph_replay_bit_exact(name):
         _say(f"  replay {r}: {mism} elements differ from the eager call")
         assert mism == 0
     del graph
+
+
+@pytest.mark.parametrize("name", ["small-bf16-text", "tiny-f32"])
+def test_softmax_bwd_repeat_and_graph_replay_bit_exact(name):
+    # the backward enqueues only kernels too and has no atomics: each output
+    # element is one fixed sum, so repeats and replays agree bit for bit
+    from hybrid_window_softmax_amd import hwa
+    from harness import to_dev
+    cfg = inputs.WORKLOADS[name]
+    _say(f"case {name}: softmax backward, eager calls, then a graph replayed three times")
+    inp = inputs.make(cfg)
+    bf = cfg["dtype"] == "bf16"
+    q, k, v = (to_dev(getattr(inp, n), bf) for n in ("q", "k", "v"))
+    g = to_dev(inputs.grad_output(cfg), bf)
+    B, H, N, d = q.shape
+    F, S, ch, r = cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"], cfg["radius"]
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    o, _ = hwa.hybrid_attn_fwd(q, k, v, None, None, None, None, None, None, F, S, ch, r,
+                               flags=hwa.FLAG_SOFTMAX_ONLY, softmax_lse=lse)
+    ref = hwa.softmax_bwd(q, k, v, o, lse, g, F, S, ch, r)
+    ws = ref[3]
+    again = hwa.softmax_bwd(q, k, v, o, lse, g, F, S, ch, r, workspace=ws)
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+    for x, y in zip(ref[:3], again[:3]):
+        assert torch.equal(bits(x), bits(y))
+    outs = [torch.empty_like(q) for _ in range(3)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        hwa.softmax_bwd(q, k, v, o, lse, g, F, S, ch, r, *outs, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hwa.softmax_bwd(q, k, v, o, lse, g, F, S, ch, r, *outs, workspace=ws)
+    for rep in range(3):
+        for t in outs:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        mism = sum(int((bits(a) != bits(b)).sum()) for a, b in zip(outs, ref[:3]))
+        _say(f"  replay {rep}: {mism} elements differ from the eager call")
+        assert mism == 0
+    del graph
