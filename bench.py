@@ -222,10 +222,8 @@ def bench_softmax_bwd(args, cfg, inp, up):
     # executed products per query-key pair: dq recomputes S and dP and forms
     # dQ (3 x 2d flop); dk/dv recomputes S and dP and forms dV and dK (4 x 2d)
     work = {
-        # read o and g, write delta and lse2; bf16 also reads q, k, g and
-        # writes their transposes
-        "prep": dict(bytes=tok * (2 * d * io + 4 + 8) + (6 * tok * d * io if io == 2 else 0),
-                     flops=0),
+        # read o, g and lse, write delta and lse2
+        "prep": dict(bytes=tok * (2 * d * io + 4 + 8), flops=0),
         "dq": dict(bytes=0, flops=6 * d * pairs),
         "dkdv": dict(bytes=0, flops=8 * d * pairs),
     }

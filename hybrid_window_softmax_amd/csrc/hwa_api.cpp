@@ -305,10 +305,9 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
 
 namespace {
 
-// Workspace of hwa_softmax_bwd: window table, delta and lse2 [B*H, Np] fp32,
-// and on bf16 the transposed copies q_t, k_t, g_t [B*H, d, Np] bf16.
+// Workspace of hwa_softmax_bwd: window table, delta and lse2 [B*H, Np] fp32.
 struct BwdLayout {
-  size_t lohi, delta, lse2, q_t, k_t, g_t, total;
+  size_t lohi, delta, lse2, total;
 };
 
 BwdLayout bwd_layout(const Geom& g, int dtype) {
@@ -319,15 +318,12 @@ BwdLayout bwd_layout(const Geom& g, int dtype) {
     off = align_up(off + bytes);
     return o;
   };
+  (void)dtype;
   const size_t bh = (size_t)g.B * g.H;
   const size_t Np = (size_t)((g.N + 63) / 64 * 64);
-  const size_t tr = dtype == HWA_BF16 ? bh * g.d * Np * sizeof(bf16_t) : 0;
   L.lohi = take(2 * (size_t)g.F * sizeof(int32_t));
   L.delta = take(bh * Np * sizeof(float));
   L.lse2 = take(bh * Np * sizeof(float));
-  L.q_t = take(tr);
-  L.k_t = take(tr);
-  L.g_t = take(tr);
   L.total = off;
   return L;
 }
@@ -384,9 +380,6 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
   int32_t* lohi = (int32_t*)(ws + L.lohi);
   float* delta = (float*)(ws + L.delta);
   float* lse2 = (float*)(ws + L.lse2);
-  bf16_t* q_t = (bf16_t*)(ws + L.q_t);
-  bf16_t* k_t = (bf16_t*)(ws + L.k_t);
-  bf16_t* g_t = (bf16_t*)(ws + L.g_t);
   void* const* ev = p->stage_events;
   auto mark = [&](int i) {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
@@ -395,16 +388,10 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
   if (hwa::launch_window_table(g, lohi, st) != hipSuccess) return HWA_ERR_HIP;
   if (hwa::launch_bwd_prep(g, p->dtype, o_sm, d_o, lse, delta, lse2, st) != hipSuccess)
     return HWA_ERR_HIP;
-  if (p->dtype == HWA_BF16) {
-    if (hwa::launch_vtranspose(g, (const bf16_t*)q, q_t, st) != hipSuccess ||
-        hwa::launch_vtranspose(g, (const bf16_t*)k, k_t, st) != hipSuccess ||
-        hwa::launch_vtranspose(g, (const bf16_t*)d_o, g_t, st) != hipSuccess)
-      return HWA_ERR_HIP;
-  }
   if (mark(1) != hipSuccess) return HWA_ERR_HIP;
   for (int part = 0; part < 2; ++part) {
-    if (hwa::launch_softmax_bwd(g, p->dtype, part, q, k, v, d_o, q_t, k_t, g_t, lse2, delta,
-                                lohi, dq, dk, dv, st) != hipSuccess)
+    if (hwa::launch_softmax_bwd(g, p->dtype, part, q, k, v, d_o, lse2, delta, lohi, dq, dk,
+                                dv, st) != hipSuccess)
       return HWA_ERR_HIP;
     if (mark(2 + part) != hipSuccess) return HWA_ERR_HIP;
   }

@@ -161,11 +161,9 @@ hipError_t launch_bwd_prep(const Geom& g, int dtype, const void* o, const void* 
                            const float* lse, float* delta, float* lse2, hipStream_t st);
 
 // part 0: dq; part 1: dk and dv; from q, k, v, the upstream gradient go and
-// the prep arrays; bf16 also reads the transposed copies q_t, k_t, g_t
-// [B*H, d, Np] (launch_vtranspose).
+// the prep arrays.
 hipError_t launch_softmax_bwd(const Geom& g, int dtype, int part, const void* q, const void* k,
-                              const void* v, const void* go, const bf16_t* q_t,
-                              const bf16_t* k_t, const bf16_t* g_t, const float* lse2,
+                              const void* v, const void* go, const float* lse2,
                               const float* delta, const int32_t* lohi, void* dq, void* dk,
                               void* dv, hipStream_t st);
 

@@ -20,8 +20,8 @@
 //    streams the queries of the chunk's window in tiles of 64: S = Q K^T and
 //    dP = G V^T leave one key per lane (query rows permuted), and
 //    dV^T += G^T P, dK^T += Q^T dS take P and dS straight from registers.
-// The contractions over queries (keys) read their other operand from a
-// transposed copy [B, H, d, Np] of q and g (k), made by the V-transpose kernel.
+// The contractions over queries (keys) read their other operand from the
+// same row tiles with the gfx950 LDS transpose read (tr_op).
 
 #include <type_traits>
 
@@ -35,6 +35,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BT = 64;  // rows (keys or queries) per streamed LDS tile
@@ -89,6 +90,40 @@ __device__ __forceinline__ bf16x8 row_op(const bf16_t* t, int blk, int kk, const
 // From a [D][64] tile: rows 32 * dblk + col, step j of the 64 columns.
 __device__ __forceinline__ bf16x8 col_op(const bf16_t* t, int dblk, int j, const int (&off)[4]) {
   return *(const bf16x8*)(t + dblk * (32 * BT) + off[j]);
+}
+
+// A operand with the contraction over the rows of a row tile, read with the
+// gfx950 LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte chunks that lanes i / 4 + 4 e
+// (e = 0..3) address. So if lane j of a group addresses row r0 + j / 4,
+// channels c0 + 4 (j % 4) .. + 3, lane i receives channel c0 + i of rows
+// r0 .. r0 + 3. For step j of a 64-row contraction (as op_chunk orders it)
+// and channel block dblk, lane (col, half) gets channel 32 dblk + col of the
+// logical rows 32 (j / 2) + 16 half + 8 (j % 2) + 0..7, two reads of four:
+// the rows that register block j holds in a permuted S / P block. Logical
+// row q sits in LDS row 32 (q / 32) + perm32^-1(q % 32) of the tile.
+__device__ __forceinline__ int inv_perm32(int x) {
+  return 8 * ((x >> 2) & 3) + 4 * (x >> 4) + (x & 3);
+}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ bf16x8 tr_op(const bf16_t* t, int dblk, int j, int lane) {
+  const int grp = lane >> 4, i = lane & 15;
+  const int r0 = 32 * (j / 2) + 16 * (grp >> 1) + 8 * (j % 2) + (i >> 2);
+  const int ch = 32 * dblk + 16 * (grp & 1) + 4 * (i & 3);
+  i16x4 part[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = r0 + 4 * h;
+    const int m = 32 * (q >> 5) + inv_perm32(q & 31);
+    const int c = (ch & 63) >> 3;
+    const int off = (ch >> 6) * (BT * 64) + m * 64 + ((c ^ swz(m)) << 3) + (ch & 7);
+    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(t + off));
+  }
+  const i16x4 a = part[0], b = part[1];
+  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
 }
 
 // B operand of a row held in registers: row `row` of a row-major [*, D]
@@ -193,9 +228,8 @@ constexpr int DQ_QT = 32 * DQ_NW;
 template <int D>
 __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ g, const bf16_t* __restrict__ k_t,
-    const float* __restrict__ lse2, const float* __restrict__ delta,
-    const int32_t* __restrict__ lohi, bf16_t* __restrict__ dq, int F, int S, int chunk,
+    const bf16_t* __restrict__ g, const float* __restrict__ lse2,
+    const float* __restrict__ delta, const int32_t* __restrict__ lohi, bf16_t* __restrict__ dq, int F, int S, int chunk,
     int nch, long long N, long long Np, int tiles_per_chunk, int ntiles, float scale_log2,
     float scale) {
   constexpr int NT = 64 * DQ_NW;
@@ -203,7 +237,6 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
   static_assert(BT * D / 8 % (64 * DQ_NW) == 0, "uniform loads per wave");
   __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][BT * D];
   __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][BT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t kt_lds[2][D * BT];
 
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   if (L >= ntiles) return;
@@ -230,23 +263,17 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
   const float l2q = q_ok ? lse2[(long long)bh * Np + my_q] : 0.0f;
   const float dlq = q_ok ? delta[(long long)bh * Np + my_q] : 0.0f;
 
-  int r_off[RPW], c_off[RPW];
+  int r_off[RPW];
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int slot = (wave + DQ_NW * j) * 64 + lane;
-    r_off[j] = rowtile_off<D>(slot);
-    c_off[j] = coltile_off(slot, Np);
-  }
+  for (int j = 0; j < RPW; ++j) r_off[j] = rowtile_off<D>((wave + DQ_NW * j) * 64 + lane);
   auto load_tile = [&](long long kt0, int st) __attribute__((always_inline)) {
     const hwa_i32x4 rk = tile_desc(k + hoff, N * D, kt0 * D, 2);
     const hwa_i32x4 rv = tile_desc(v + hoff, N * D, kt0 * D, 2);
-    const hwa_i32x4 rt = tile_desc(k_t + (long long)bh * D * Np, (long long)D * Np, kt0, 2);
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const int s0 = (wave + DQ_NW * j) * 512;
       hwa_raw_buffer_load_lds(rk, (lds_void*)&k_lds[st][s0], 16, r_off[j], 0, 0, 0);
       hwa_raw_buffer_load_lds(rv, (lds_void*)&v_lds[st][s0], 16, r_off[j], 0, 0, 0);
-      hwa_raw_buffer_load_lds(rt, (lds_void*)&kt_lds[st][s0], 16, c_off[j], 0, 0, 0);
     }
   };
   int off[4];
@@ -268,7 +295,6 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
     if (it + 1 < ntl) load_tile(kt0 + BT, st ^ 1);
     const bf16_t* ks = &k_lds[st][0];
     const bf16_t* vs = &v_lds[st][0];
-    const bf16_t* kts = &kt_lds[st][0];
     f32x16 sT[2], pT[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -311,7 +337,7 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
     for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_op(kts, dblk, j, off), dsb[j],
+        acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(ks, dblk, j, lane), dsb[j],
                                                             acc[dblk], 0, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -328,11 +354,13 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void softmax_bwd_dq_kernel(
 // dK^T += Q_b^T dS(b). One stream of MFMAs per step (one block): B(b - 1)
 // then A(b + 1), with VALU(b) spread over it, so that the exp work of one
 // block runs under the products of its neighbours (one wave per SIMD).
-// Row tiles (Q, G: read by A) and column tiles (Q^T, G^T, with lse2 and
-// delta: read by B and VALU) have their own two stages; per tile `it`:
+// B reads its operands G^T and Q^T from the same row tiles as A, with the
+// LDS transpose read (tr_op). A tile serves A one block before B, so the
+// query tiles (Q, G, lse2, delta) rotate through three stages; per tile `it`:
 //   step X: B(it-1, 1) | A(it, 1) | VALU(it, 0); barrier
-//   step Y: loads of col(it+1) and row(it+2) with the first MFMA;
-//           B(it, 0) | A(it+1, 0) | VALU(it, 1); wait for the loads; barrier
+//   step Y: loads of tile it+2 (into the stage of tile it-1) with the first
+//           MFMA; B(it, 0) | A(it+1, 0) | VALU(it, 1); wait for the loads;
+//           barrier
 // so every stage is refilled only after the barrier that follows its last
 // reader, and lands before the barrier that precedes its first reader.
 constexpr int DK_NW = 4;
@@ -341,8 +369,7 @@ constexpr int DK_KT = 32 * DK_NW;
 template <int D>
 __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ g, const bf16_t* __restrict__ q_t, const bf16_t* __restrict__ g_t,
-    const float* __restrict__ lse2, const float* __restrict__ delta,
+    const bf16_t* __restrict__ g, const float* __restrict__ lse2, const float* __restrict__ delta,
     const int32_t* __restrict__ lohi, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int F,
     int S, int chunk, int nch, long long N, long long Np, int tiles_per_chunk, int ntiles,
     float scale_log2, float scale) {
@@ -354,11 +381,12 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
 #define DK_PF 3
 #endif
   constexpr int PF = DK_PF;                            // operand reads ahead of their MFMA
-  __shared__ __attribute__((aligned(16))) bf16_t row_lds[2][2][BT * D];  // [stage][Q, G]
-  __shared__ __attribute__((aligned(16))) bf16_t col_lds[2][2][D * BT];  // [stage][Q^T, G^T]
-  // [stage][lse2, delta]: 64 values, then the padding that the rest of the
-  // wave's 16-byte direct load writes
-  __shared__ __attribute__((aligned(16))) float ls_lds[2][2][4 * 64];
+  // three stages of a query tile: Q, G (row-major, permuted rows, swizzled)
+  // and [lse2, delta] (64 values, then the padding that the rest of the
+  // wave's 16-byte direct load writes)
+  __shared__ __attribute__((aligned(16))) bf16_t q_lds[3][BT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t g_lds[3][BT * D];
+  __shared__ __attribute__((aligned(16))) float ls_lds[3][2][4 * 64];
 
   const int L = xcd_tile(blockIdx.x, gridDim.x);
   if (L >= ntiles) return;
@@ -384,70 +412,51 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
   load_row_operand<D>(k + hoff, my_k, k_ok, half, kreg);
   load_row_operand<D>(v + hoff, my_k, k_ok, half, vreg);
 
-  int r_off[RPW], c_off[RPW];
+  int r_off[RPW];
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int slot = (wave + DK_NW * j) * 64 + lane;
-    r_off[j] = rowtile_off<D>(slot);
-    c_off[j] = coltile_off(slot, Np);
-  }
-  const long long toff = (long long)bh * D * Np;
-  // Direct loads of a step, one instruction per call: column tile `ic` into
-  // column stage SC (Q^T then G^T, then lse2 / delta on waves 0 and 1), then
-  // row tile `ir` into row stage SR (Q then G); a tile index < 0 skips it.
-  // Stage indices are compile-time (the tile loop runs over pairs of tiles).
-  constexpr int NLD = 4 * RPW + 1;  // instructions per step (at most)
+  for (int j = 0; j < RPW; ++j) r_off[j] = rowtile_off<D>((wave + DK_NW * j) * 64 + lane);
+  // Direct loads of query tile `u` (< 0: none) into stage SU (compile-time:
+  // the tile loop is unrolled over the three stages), one instruction per
+  // call: Q, then G, then lse2 / delta on waves 0 and 1.
+  constexpr int NLD = 2 * RPW + 1;  // instructions per step (at most)
   struct Loads {
-    hwa_i32x4 rq, rg, rqt, rgt, rls;
-    int ic, ir;
+    hwa_i32x4 rq, rg, rls;
+    int u;
   };
-  auto make_loads = [&](int ic, int ir) __attribute__((always_inline)) {
+  auto make_loads = [&](int u) __attribute__((always_inline)) {
     Loads l;
-    l.ic = ic;
-    l.ir = ir;
-    const long long qc = qt_first + (long long)(ic < 0 ? 0 : ic) * BT;
-    const long long qr = qt_first + (long long)(ir < 0 ? 0 : ir) * BT;
-    l.rqt = tile_desc(q_t + toff, (long long)D * Np, qc, 2);
-    l.rgt = tile_desc(g_t + toff, (long long)D * Np, qc, 2);
-    l.rls = tile_desc((wave == 0 ? lse2 : delta) + (long long)bh * Np, Np, qc, 4);
-    l.rq = tile_desc(q + hoff, N * D, qr * D, 2);
-    l.rg = tile_desc(g + hoff, N * D, qr * D, 2);
+    l.u = u;
+    const long long qt0 = qt_first + (long long)(u < 0 ? 0 : u) * BT;
+    l.rq = tile_desc(q + hoff, N * D, qt0 * D, 2);
+    l.rg = tile_desc(g + hoff, N * D, qt0 * D, 2);
+    l.rls = tile_desc((wave == 0 ? lse2 : delta) + (long long)bh * Np, Np, qt0, 4);
     return l;
   };
-  auto issue = [&](auto sc_tag, auto sr_tag, const Loads& l, int j)
-                   __attribute__((always_inline)) {
-    constexpr int SC = decltype(sc_tag)::value, SR = decltype(sr_tag)::value;
+  auto issue = [&](auto su_tag, const Loads& l, int j) __attribute__((always_inline)) {
+    constexpr int SU = decltype(su_tag)::value;
+    if (l.u < 0) return;
     if (j < 2 * RPW) {
-      if (l.ic >= 0) {
-        const int jj = j % RPW, s0 = (wave + DK_NW * jj) * 512;
-        dma16(j < RPW ? l.rqt : l.rgt, (lds_void*)&col_lds[SC][j < RPW ? 0 : 1][s0], c_off[jj]);
-      }
-    } else if (j == 2 * RPW) {
-      // lse2 and delta of the tile's 64 queries: lanes 0..15, 16 bytes each
-      // (the 16-byte form, like every other load here: the compiler does not
-      // make LDS reads wait for it); the other lanes fill the padding
-      if (l.ic >= 0 && wave < 2)
-        dma16(l.rls, (lds_void*)&ls_lds[SC][wave][0], lane * 16);
-    } else if (j < NLD) {
-      if (l.ir >= 0) {
-        const int jr = j - 2 * RPW - 1, jj = jr % RPW, s0 = (wave + DK_NW * jj) * 512;
-        dma16(jr < RPW ? l.rq : l.rg, (lds_void*)&row_lds[SR][jr < RPW ? 0 : 1][s0], r_off[jj]);
-      }
+      const int jj = j % RPW, s0 = (wave + DK_NW * jj) * 512;
+      dma16(j < RPW ? l.rq : l.rg, (lds_void*)(j < RPW ? &q_lds[SU][s0] : &g_lds[SU][s0]),
+            r_off[jj]);
+    } else if (j == 2 * RPW && wave < 2) {
+      // lse2 and delta of the tile's 64 queries: lanes 0..15, 16 bytes each;
+      // the other lanes fill the padding
+      dma16(l.rls, (lds_void*)&ls_lds[SU][wave][0], lane * 16);
     }
   };
-  auto load_all = [&](auto sc_tag, auto sr_tag, const Loads& l) __attribute__((always_inline)) {
+  auto load_all = [&](auto su_tag, const Loads& l) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) issue(sc_tag, sr_tag, l, j);
+    for (int j = 0; j < NLD; ++j) issue(su_tag, l, j);
   };
-  // Rows of column tile `it` outside the window [qw_begin, qw_end) get
-  // lse2 = +inf, so that p = exp2(s * scale_log2 - lse2) = 0 and ds = 0 there.
-  // Called by wave 0, which loaded lse2, after its loads landed and before the
-  // barrier that publishes the tile.
-  auto mask_cols = [&](auto st_tag, int it) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
-    const long long qt0 = qt_first + (long long)it * BT;
-    const long long qn = qt0 + lane;
-    if (qn < qw_begin || qn >= qw_end) ls_lds[ST][0][lane] = __builtin_inff();
+  // Rows of tile `u` outside the window [qw_begin, qw_end) get lse2 = +inf,
+  // so that p = exp2(s * scale_log2 - lse2) = 0 and ds = 0 there. Called by
+  // wave 0, which loaded lse2, after its loads landed and before the barrier
+  // that publishes the tile.
+  auto mask_rows = [&](auto su_tag, int u) __attribute__((always_inline)) {
+    constexpr int SU = decltype(su_tag)::value;
+    const long long qn = qt_first + (long long)u * BT + lane;
+    if (qn < qw_begin || qn >= qw_end) ls_lds[SU][0][lane] = __builtin_inff();
   };
   int off[4];
 #pragma unroll
@@ -475,14 +484,14 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
 
   // A operand of MFMA a of A(blk): S = Q K^T and dP = G V^T alternate
   auto a_op = [&](int st, int blk, int a) __attribute__((always_inline)) {
-    return row_op<D>(&row_lds[st][a % 2][0], blk, a / 2, off);
+    return row_op<D>(a % 2 ? &g_lds[st][0] : &q_lds[st][0], blk, a / 2, off);
   };
-  // MFMA a of A(blk) into s_b / p_b [blk]
   // B operand order, MFMA j of B(blk): G^T (dV) and Q^T (dK) alternate over
-  // the channel blocks, then the two 16-query steps
+  // the channel blocks, then the two 16-query steps; read transposed from the
+  // row tiles
   auto b_op = [&](int st, int blk, int j) __attribute__((always_inline)) {
     const int which = j % 2, dblk = (j / 2) % (D / 32), s2 = j / (D / 16);
-    return col_op(&col_lds[st][which ^ 1][0], dblk, 2 * blk + s2, off);
+    return tr_op<D>(which ? &q_lds[st][0] : &g_lds[st][0], dblk, 2 * blk + s2, lane);
   };
   // one probability / ds register r of block blk (query row 32 blk + 16 half + r
   // of the tile; l2v, dlv: lse2 and delta of the lane's 16 rows; lse2 = +inf
@@ -580,36 +589,52 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
   typedef std::integral_constant<int, 5> F_BV;
   typedef std::integral_constant<int, 1> F_B;
 
+  typedef std::integral_constant<int, 2> B2;
   auto no_loads = [](int) {};
-  // prologue: row tiles 0 and 1, column tile 0; A(0, 0)
-  load_all(B0{}, B0{}, make_loads(0, 0));
-  if (ntl > 1) load_all(B0{}, B1{}, make_loads(-1, 1));
+  // prologue: tiles 0 and 1 into stages 0 and 1; A(0, 0)
+  load_all(B0{}, make_loads(0));
+  load_all(B1{}, make_loads(ntl > 1 ? 1 : -1));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (wave == 0) mask_cols(B0{}, 0);
+  if (wave == 0) {
+    mask_rows(B0{}, 0);
+    if (ntl > 1) mask_rows(B1{}, 1);
+  }
   __syncthreads();
   step(B1{}, B0{}, B1{}, F_A{}, B0{}, B0{}, B0{}, no_loads);
-  // tile `it` in stage ST = it % 2 (compile-time: the loop runs over pairs
-  // of tiles). X: B(it-1, 1) | A(it, 1) | VALU(it, 0); then Y: B(it, 0) |
-  // A(it+1, 0) | VALU(it, 1) with the loads of col(it+1) and row(it+2)
-  auto tile_x = [&](auto fl, auto st_tag, int it) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
-    typedef std::integral_constant<int, ST ^ 1> SO;
-    step(B1{}, B1{}, B0{}, fl, SO{}, st_tag, st_tag, no_loads);
+  // Tile `it` lives in stage R = it % 3 (compile-time: the loop runs over
+  // three tiles at a time) from Y(it-1) to X(it+1):
+  //   X(it): B(it-1, 1) | A(it, 1) | VALU(it, 0)
+  //   Y(it): loads of tile it+2 into the stage of tile it-1 with the first
+  //          MFMA; B(it, 0) | A(it+1, 0) | VALU(it, 1)
+  auto tile_x = [&](auto fl, auto r_tag, int it) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_tag)::value;
+    typedef std::integral_constant<int, (R + 2) % 3> RP;
+    step(B1{}, B1{}, B0{}, fl, RP{}, r_tag, r_tag, no_loads);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  auto tile_y = [&](auto fl, auto st_tag, int it) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
-    typedef std::integral_constant<int, ST ^ 1> SO;
-    const Loads l = make_loads(it + 1 < ntl ? it + 1 : -1, it + 2 < ntl ? it + 2 : -1);
-    step(B0{}, B0{}, B1{}, fl, st_tag, SO{}, st_tag, [&](int j) { issue(SO{}, st_tag, l, j); });
+  auto tile_y = [&](auto fl, auto r_tag, int it) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_tag)::value;
+    typedef std::integral_constant<int, (R + 1) % 3> RN;
+    typedef std::integral_constant<int, (R + 2) % 3> RP;
+    const Loads l = make_loads(it + 2 < ntl ? it + 2 : -1);
+    step(B0{}, B0{}, B1{}, fl, r_tag, RN{}, r_tag, [&](int j) { issue(RP{}, l, j); });
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (wave == 0 && it + 1 < ntl) mask_cols(SO{}, it + 1);
+    if (wave == 0 && it + 2 < ntl) mask_rows(RP{}, it + 2);
     __syncthreads();
   };
-  // drain: B(last, 1) from the last tile's column stage
-  auto drain = [&](auto st_tag) __attribute__((always_inline)) {
-    step(B1{}, B0{}, B0{}, F_B{}, st_tag, B0{}, B0{}, no_loads);
+  // drain: B(last, 1)
+  auto drain = [&](auto r_tag) __attribute__((always_inline)) {
+    step(B1{}, B0{}, B0{}, F_B{}, r_tag, B0{}, B0{}, no_loads);
+  };
+  auto full = [&](auto r_tag, int it) __attribute__((always_inline)) {
+    tile_x(F_BAV{}, r_tag, it);
+    tile_y(F_BAV{}, r_tag, it);
+  };
+  auto last = [&](auto r_tag, int it) __attribute__((always_inline)) {
+    tile_x(F_BAV{}, r_tag, it);
+    tile_y(F_BV{}, r_tag, it);
+    drain(r_tag);
   };
   // first tile: nothing pending for B in X; last tile: no A(ntl, 0) in Y
   tile_x(F_AV{}, B0{}, 0);
@@ -619,23 +644,17 @@ __global__ __launch_bounds__(64 * DK_NW, 1) void softmax_bwd_dkdv_kernel(
   } else {
     tile_y(F_BAV{}, B0{}, 0);
     int it = 1;
-    for (; it + 2 < ntl; it += 2) {
-      tile_x(F_BAV{}, B1{}, it);
-      tile_y(F_BAV{}, B1{}, it);
-      tile_x(F_BAV{}, B0{}, it + 1);
-      tile_y(F_BAV{}, B0{}, it + 1);
+    for (; it + 2 <= ntl - 2; it += 3) {  // middle tiles 1 .. ntl-2
+      full(B1{}, it);
+      full(B2{}, it + 1);
+      full(B0{}, it + 2);
     }
-    if (it + 1 < ntl) {  // tiles it (odd) and the last, it + 1
-      tile_x(F_BAV{}, B1{}, it);
-      tile_y(F_BAV{}, B1{}, it);
-      tile_x(F_BAV{}, B0{}, it + 1);
-      tile_y(F_BV{}, B0{}, it + 1);
-      drain(B0{});
-    } else {  // the last tile, it (odd)
-      tile_x(F_BAV{}, B1{}, it);
-      tile_y(F_BV{}, B1{}, it);
-      drain(B1{});
-    }
+    if (it <= ntl - 2) full(B1{}, it++);
+    if (it <= ntl - 2) full(B2{}, it++);
+    const int rl = it % 3;  // it == ntl - 1
+    if (rl == 0) last(B0{}, it);
+    else if (rl == 1) last(B1{}, it);
+    else last(B2{}, it);
   }
   if (k_ok) {
     store_rows<D>(dk + hoff + my_k * D, acc_k, scale, half);
@@ -803,8 +822,7 @@ hipError_t launch_bwd_prep(const Geom& g, int dtype, const void* o, const void* 
 }
 
 hipError_t launch_softmax_bwd(const Geom& g, int dtype, int part, const void* q, const void* k,
-                              const void* v, const void* go, const bf16_t* q_t,
-                              const bf16_t* k_t, const bf16_t* g_t, const float* lse2,
+                              const void* v, const void* go, const float* lse2,
                               const float* delta, const int32_t* lohi, void* dq, void* dk,
                               void* dv, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)g.d);
@@ -821,12 +839,12 @@ hipError_t launch_softmax_bwd(const Geom& g, int dtype, int part, const void* q,
     if (part == 0)                                                                          \
       hipLaunchKernelGGL(softmax_bwd_dq_kernel<DD>, gq, dim3(64 * DQ_NW), 0, st,            \
                          (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,              \
-                         (const bf16_t*)go, k_t, lse2, delta, lohi, (bf16_t*)dq, g.F, g.S,  \
+                         (const bf16_t*)go, lse2, delta, lohi, (bf16_t*)dq, g.F, g.S,       \
                          g.chunk, g.nch, g.N, Np, tq, nq, scale_log2, scale);               \
     else                                                                                    \
       hipLaunchKernelGGL(softmax_bwd_dkdv_kernel<DD>, gk, dim3(64 * DK_NW), 0, st,          \
                          (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,              \
-                         (const bf16_t*)go, q_t, g_t, lse2, delta, lohi, (bf16_t*)dk,       \
+                         (const bf16_t*)go, lse2, delta, lohi, (bf16_t*)dk,                 \
                          (bf16_t*)dv, g.F, g.S, g.chunk, g.nch, g.N, Np, tk, nk,            \
                          scale_log2, scale);                                                \
   } while (0)

@@ -242,7 +242,7 @@ size_t hwa_text_state_workspace_bytes(int32_t text_tokens,
  *   p          batch, heads, head_dim, dtype, workspace (>= hwa_softmax_bwd_
  *              workspace_bytes), stage_events (NULL, or
  *              HWA_NUM_BWD_STAGE_EVENTS events recorded at [0] start, [1]
- *              after the window table, delta, lse scaling and transposes,
+ *              after the window table, delta and lse scaling,
  *              [2] after the dq kernel, [3] after the dk/dv kernel); the
  *              other fields are ignored
  * Returns HWA_OK, or an error status before anything is enqueued.
@@ -255,9 +255,9 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
                            int32_t chunk, int32_t radius, void* dq, void* dk,
                            void* dv, void* stream, const hwa_params* p);
 
-/* Workspace bytes hwa_softmax_bwd needs (0 on bad args): the window table,
- * delta and lse * log2(e) per query, and on bf16 transposed copies of q, k
- * and d_o (3 * B * H * d * roundup(N, 64) * 2 bytes). */
+/* Workspace bytes hwa_softmax_bwd needs (0 on bad args): the window table
+ * and delta and lse * log2(e) per query (2 * B * H * roundup(N, 64) * 4
+ * bytes, plus alignment). */
 size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
                                        int32_t chunk, const hwa_params* p);
 

@@ -245,7 +245,7 @@ def test_softmax_bwd_workspace_bytes():
         p = hwa.make_params(2, 3, 64, dt)
         n = L.hwa_softmax_bwd_workspace_bytes(10, 100, 5, ctypes.byref(p))
         Np = (10 * 100 + 63) // 64 * 64
-        # delta and lse2 per query, plus (bf16) three transposed bf16 copies
-        need = 2 * 6 * Np * 4 + (3 * 6 * 64 * Np * 2 if dt == 1 else 0)
-        assert need <= n <= need + 8 * 256
+        # the window table, delta and lse2 per query
+        need = 2 * 6 * Np * 4
+        assert need <= n <= need + 4 * 256
     assert L.hwa_softmax_bwd_workspace_bytes(0, 100, 5, ctypes.byref(p)) == 0
