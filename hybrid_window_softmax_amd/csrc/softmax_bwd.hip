@@ -35,7 +35,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BT = 64;  // rows (keys or queries) per streamed LDS tile
@@ -90,40 +89,6 @@ __device__ __forceinline__ bf16x8 row_op(const bf16_t* t, int blk, int kk, const
 // From a [D][64] tile: rows 32 * dblk + col, step j of the 64 columns.
 __device__ __forceinline__ bf16x8 col_op(const bf16_t* t, int dblk, int j, const int (&off)[4]) {
   return *(const bf16x8*)(t + dblk * (32 * BT) + off[j]);
-}
-
-// A operand with the contraction over the rows of a row tile, read with the
-// gfx950 LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes,
-// lane i receives element i % 4 of the 8-byte chunks that lanes i / 4 + 4 e
-// (e = 0..3) address. So if lane j of a group addresses row r0 + j / 4,
-// channels c0 + 4 (j % 4) .. + 3, lane i receives channel c0 + i of rows
-// r0 .. r0 + 3. For step j of a 64-row contraction (as op_chunk orders it)
-// and channel block dblk, lane (col, half) gets channel 32 dblk + col of the
-// logical rows 32 (j / 2) + 16 half + 8 (j % 2) + 0..7, two reads of four:
-// the rows that register block j holds in a permuted S / P block. Logical
-// row q sits in LDS row 32 (q / 32) + perm32^-1(q % 32) of the tile.
-__device__ __forceinline__ int inv_perm32(int x) {
-  return 8 * ((x >> 2) & 3) + 4 * (x >> 4) + (x & 3);
-}
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-template <int D>
-__device__ __forceinline__ bf16x8 tr_op(const bf16_t* t, int dblk, int j, int lane) {
-  const int grp = lane >> 4, i = lane & 15;
-  const int r0 = 32 * (j / 2) + 16 * (grp >> 1) + 8 * (j % 2) + (i >> 2);
-  const int ch = 32 * dblk + 16 * (grp & 1) + 4 * (i & 3);
-  i16x4 part[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int q = r0 + 4 * h;
-    const int m = 32 * (q >> 5) + inv_perm32(q & 31);
-    const int c = (ch & 63) >> 3;
-    const int off = (ch >> 6) * (BT * 64) + m * 64 + ((c ^ swz(m)) << 3) + (ch & 7);
-    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(t + off));
-  }
-  const i16x4 a = part[0], b = part[1];
-  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, ab);
 }
 
 // B operand of a row held in registers: row `row` of a row-major [*, D]
