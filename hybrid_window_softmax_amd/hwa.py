@@ -265,6 +265,36 @@ def softmax_bwd(q, k, v, o_sm, lse, d_o, frames: int, tokens_per_frame: int,
     return dq, dk, dv, workspace
 
 
+class WindowedSoftmaxAttention(torch.autograd.Function):
+    """The windowed softmax branch as an autograd function: the forward runs
+    hybrid_attn_fwd with FLAG_SOFTMAX_ONLY (saving o_sm and its log-sum-exp),
+    the backward runs hwa_softmax_bwd. Marshalling only: both passes are the
+    library's kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, frames, tokens_per_frame, chunk, radius):
+        B, H, N, d = q.shape
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        o, _ = hybrid_attn_fwd(q, k, v, None, None, None, None, None, None, frames,
+                               tokens_per_frame, chunk, radius, flags=FLAG_SOFTMAX_ONLY,
+                               softmax_lse=lse)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.geom = (frames, tokens_per_frame, chunk, radius)
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv, _ = softmax_bwd(q, k, v, o, lse, d_o.contiguous(), *ctx.geom)
+        return dq, dk, dv, None, None, None, None
+
+
+def windowed_softmax_attention(q, k, v, frames: int, tokens_per_frame: int, chunk: int = 5,
+                               radius: int = 1):
+    """o_sm of the windowed softmax branch, differentiable in q, k and v."""
+    return WindowedSoftmaxAttention.apply(q, k, v, frames, tokens_per_frame, chunk, radius)
+
+
 def text_state(k_txt, v_txt, beta_txt, workspace=None, out=None):
     """S_text [B, H, d, d] fp32 from text tokens (hwa_text_state)."""
     B, H, T, d = k_txt.shape

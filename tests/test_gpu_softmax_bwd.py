@@ -197,3 +197,28 @@ def test_forward_softmax_outputs(name):
     assert torch.equal(so, sm)
     assert torch.equal(lse, lse1)
     assert bool(torch.isfinite(lse).all())
+
+
+def test_autograd_function_small_bf16():
+    # hwa.windowed_softmax_attention through torch autograd: o_sm.backward(g)
+    # gives the library's dq, dk, dv, checked against the oracle gradient
+    inp = inputs.make("small-bf16-text")
+    c = inp.cfg
+    print("case small-bf16-text: autograd function", flush=True)
+    q, k, v = (to_dev(getattr(inp, n), True).requires_grad_() for n in ("q", "k", "v"))
+    g_host = inputs.grad_output(c)
+    o = hwa.windowed_softmax_attention(q, k, v, c["frames"], c["tokens_per_frame"], c["chunk"],
+                                       c["radius"])
+    o.backward(to_dev(g_host, True))
+    torch.cuda.synchronize()
+    lo, hi = oracle.window_bounds(c["frames"], c["chunk"], c["radius"])
+    S = c["tokens_per_frame"]
+    worst = 0.0
+    for h in (0, c["heads"] - 1):
+        ref = oracle.softmax_branch_grad(inp.f64("q", 0, h), inp.f64("k", 0, h),
+                                         inp.f64("v", 0, h), _g64(inp, g_host, 0, h), S, lo, hi)
+        for t, r in zip((q, k, v), ref):
+            worst = max(worst, oracle.rel_frobenius(
+                t.grad[0, h].float().cpu().numpy().astype(np.float64), r))
+    print(f"  rel err {worst:.2e}", flush=True)
+    assert worst <= TOL["bf16"]
