@@ -10,7 +10,8 @@ Source of the definition: the VDN-H3 article ("VDN-Minimax-H3", icman.com.cn
 news 81972), its sections on the far field, the five steps of the
 bidirectional linear branch, the update-rule table and the text state; and,
 for the backward pass of the windowed softmax branch, the chain rule through
-that softmax (``softmax_grad``).
+that softmax (``softmax_grad``), and for the linear branch's gradient the same
+steps in torch float64 under autograd (``linear_grad``).
 
 Every public function says which passage it follows and how it is pinned
 (see ``tests/test_oracle_*.py``). No function here is "parity unpinned".
@@ -41,3 +42,4 @@ from .softmax_grad import (  # noqa: F401
     softmax_branch_grad,
     softmax_grad_rows,
 )
+from .linear_grad import linear_branch_torch, linear_branch_grad  # noqa: F401
