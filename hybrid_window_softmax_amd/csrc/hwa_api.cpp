@@ -1,6 +1,6 @@
 // C ABI of libhwa: argument validation, workspace layouts and the launch
-// sequences of the hybrid attention forward and of the softmax branch's
-// backward. Declarations and semantics are
+// sequences of the hybrid attention forward and of the backward of both
+// branches. Declarations and semantics are
 // in include/hwa.h.
 
 #include <math.h>
@@ -394,6 +394,151 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
                                 dv, st) != hipSuccess)
       return HWA_ERR_HIP;
     if (mark(2 + part) != hipSuccess) return HWA_ERR_HIP;
+  }
+  return HWA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of hwa_linear_bwd (see hwa::LinBwdArgs for what each holds).
+struct LinBwdLayout {
+  size_t A, Bm, M, Pst, Qst, E, dSt, dXQ, dbank, lam0, gab, dal, dwpart, dkc, dvc, cpart;
+  size_t total;
+};
+
+LinBwdLayout lin_bwd_layout(const Geom& g) {
+  LinBwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t dd = (size_t)g.d * g.d * sizeof(float);
+  const size_t rowf = (size_t)g.d * sizeof(float);
+  L.A = take(bh * g.F * dd);
+  L.Bm = take(bh * g.F * dd);
+  L.M = take(bh * g.F * dd);
+  L.Pst = take(bh * (g.F + 1) * dd);
+  L.Qst = take(bh * (g.F + 1) * dd);
+  L.E = take(2 * bh * (g.F + 1) * g.d * sizeof(int32_t));
+  L.dSt = take(bh * g.F * dd);
+  L.dXQ = take(bh * g.F * dd);
+  L.dbank = take(2 * bh * (g.nch + 1) * dd);
+  L.lam0 = take(2 * bh * dd);
+  L.gab = take(2 * bh * g.F * rowf);
+  L.dal = take(bh * g.F * rowf);
+  L.dwpart = take(bh * g.F * rowf);
+  L.dkc = take(bh * (size_t)g.N * rowf);
+  L.dvc = take(bh * (size_t)g.N * rowf);
+  L.cpart = take(bh * g.F * 8 * rowf);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hwa_linear_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
+                                      int32_t chunk, const hwa_params* p) {
+  if (check_params(p) != HWA_OK) return 0;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, chunk, 0, p, g)) return 0;
+  return lin_bwd_layout(g).total;
+}
+
+hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const float* beta,
+                          const float* alpha, const void* gate, const float* text_state,
+                          const void* d_o, int32_t frames, int32_t tokens_per_frame,
+                          int32_t chunk, int32_t radius, int32_t rule, void* dq, void* dk,
+                          void* dv, float* dbeta, float* dalpha, void* dgate,
+                          float* dtext_state, float* dconv_k, float* dconv_v,
+                          float* drms_weight, void* stream, const hwa_params* p) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, chunk, radius, p, g)) return HWA_ERR_INVALID_ARG;
+  if (rule < HWA_RULE_VDN_SOLVE || rule > HWA_RULE_VDN_SCALED) return HWA_ERR_INVALID_ARG;
+  if (rule == HWA_RULE_SANA_SCALED) return HWA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !alpha || !gate || !d_o || !p->conv_k || !p->conv_v ||
+      !dq || !dk || !dv || !dbeta || !dalpha || !dgate || !dconv_k || !dconv_v)
+    return HWA_ERR_INVALID_ARG;
+  if (!isfinite(p->c) || !isfinite(p->text_scale) || !(p->rms_eps > 0.0f) ||
+      !isfinite(p->rms_eps))
+    return HWA_ERR_INVALID_ARG;
+  const size_t va = p->dtype == HWA_BF16 ? 16 : 4;
+  const void* io_ptrs[] = {q, k, v, gate, d_o, dq, dk, dv, dgate};
+  for (const void* x : io_ptrs)
+    if (!aligned(x, va)) return HWA_ERR_INVALID_ARG;
+  const void* f32_ptrs[] = {beta, alpha, text_state, p->conv_k, p->conv_v, p->rms_weight,
+                            dbeta, dalpha, dtext_state, dconv_k, dconv_v, drms_weight};
+  for (const void* x : f32_ptrs)
+    if (x && !aligned(x, 4)) return HWA_ERR_INVALID_ARG;
+  const LinBwdLayout L = lin_bwd_layout(g);
+  if (!p->workspace || p->workspace_bytes < L.total || !aligned(p->workspace, kAlign))
+    return HWA_ERR_WORKSPACE;
+
+  const size_t es = p->dtype == HWA_BF16 ? 2 : 4;
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t io_bytes = bh * (size_t)g.N * g.d * es;
+  const size_t tok_bytes = bh * (size_t)g.N * sizeof(float);
+  const size_t alpha_bytes = bh * (size_t)g.F * g.d * sizeof(float);
+  const size_t mat_bytes = bh * (size_t)g.d * g.d * sizeof(float);
+  const size_t conv_bytes = (size_t)g.H * g.d * 4 * sizeof(float);
+  const struct { const void* ptr; size_t n; } ins[] = {
+      {q, io_bytes}, {k, io_bytes}, {v, io_bytes}, {gate, io_bytes}, {d_o, io_bytes},
+      {beta, tok_bytes}, {alpha, alpha_bytes}, {text_state, mat_bytes},
+      {p->conv_k, conv_bytes}, {p->conv_v, conv_bytes},
+      {p->rms_weight, (size_t)g.d * sizeof(float)}, {p->workspace, p->workspace_bytes},
+  };
+  const struct { const void* ptr; size_t n; } outs[] = {
+      {dq, io_bytes}, {dk, io_bytes}, {dv, io_bytes}, {dgate, io_bytes},
+      {dbeta, tok_bytes}, {dalpha, alpha_bytes}, {dtext_state, mat_bytes},
+      {dconv_k, conv_bytes}, {dconv_v, conv_bytes},
+      {drms_weight, (size_t)g.d * sizeof(float)},
+  };
+  const int n_outs = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < n_outs; ++i) {
+    for (const auto& in : ins)
+      if (overlaps(outs[i].ptr, outs[i].n, in.ptr, in.n)) return HWA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i].ptr, outs[i].n, outs[j].ptr, outs[j].n)) return HWA_ERR_INVALID_ARG;
+  }
+
+  char* ws = (char*)p->workspace;
+  hwa::LinBwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.gate = gate; a.d_o = d_o;
+  a.beta = beta; a.alpha = alpha; a.text_state = text_state;
+  a.conv_k = p->conv_k; a.conv_v = p->conv_v; a.rms_w = p->rms_weight;
+  a.rule = rule; a.c = p->c; a.text_scale = p->text_scale; a.eps = p->rms_eps;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dgate = dgate;
+  a.dbeta = dbeta; a.dalpha = dalpha; a.dtext = dtext_state;
+  a.dconv_k = dconv_k; a.dconv_v = dconv_v; a.drms = drms_weight;
+  a.A = (float*)(ws + L.A); a.Bm = (float*)(ws + L.Bm); a.M = (float*)(ws + L.M);
+  a.Pst = (float*)(ws + L.Pst); a.Qst = (float*)(ws + L.Qst);
+  a.E = (int32_t*)(ws + L.E);
+  a.dSt = (float*)(ws + L.dSt);
+  a.dXP = a.dSt;  // dS_t is consumed by the gather before the prefix adjoint writes
+  a.dXQ = (float*)(ws + L.dXQ);
+  a.dbank = (float*)(ws + L.dbank); a.lam0 = (float*)(ws + L.lam0);
+  a.gab = (float*)(ws + L.gab); a.dal = (float*)(ws + L.dal);
+  a.dwpart = (float*)(ws + L.dwpart);
+  a.dkc = (float*)(ws + L.dkc); a.dvc = (float*)(ws + L.dvc);
+  a.cpart = (float*)(ws + L.cpart);
+
+  hipStream_t st = (hipStream_t)stream;
+  void* const* ev = p->stage_events;
+  auto mark = [&](int i) {
+    return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+  };
+  if (mark(0) != hipSuccess) return HWA_ERR_HIP;
+  for (int stage = 0; stage < 5; ++stage) {
+    if (hwa::launch_linear_bwd(g, p->dtype, stage, a, st) != hipSuccess) return HWA_ERR_HIP;
+    if (mark(stage + 1) != hipSuccess) return HWA_ERR_HIP;
   }
   return HWA_OK;
 }

@@ -1,0 +1,819 @@
+// Backward of the linear branch (VDN-H3 article, "Step 1" .. "Step 5" and
+// "Text state"; the gradients its "Training" section needs). For a loss L
+// with upstream gradient G = dL/dy of the branch output y, with the forward's
+// notation:
+//   q^ = L2(SiLU(q)), k^ = L2(SiLU(conv_k(k))), v^ = conv_v(v)
+//   A_f = sum_n beta_n k^_n k^_n^T,  B_f = sum_n beta_n v^_n k^_n^T
+//   M_f = (I + cc A_f)^-1, X = S diag(alpha_f) + c1 B_f, R_f(S) = X M_f
+//     (vdn_solve: cc = c1 = 1; vdn_scaled: cc = c^2, c1 = c)
+//   P_{-1} = Q_F = s0 = text_scale S_text, P_f = R_f(P_{f-1}), Q_f = R_f(Q_{f+1})
+//   S_t = P_{lo-1} diag(a_t) + Q_{hi+1} diag(b_t),
+//     a_t = prod_{l=lo..t} alpha_l, b_t = prod_{l=t..hi} alpha_l
+//   o = S_t q^, z = o / sqrt(mean(o^2) + eps), y = z * w * sigmoid(gate)
+// the reverse pass is:
+//   readout    dgate, dw, do = r (dz - z mean(dz z)), dq^ = S_t^T do,
+//              dS_t = sum_n do_n q^_n^T, dq through L2 and SiLU
+//   gather     dP_{lo-1} += dS_t diag(a_t), dQ_{hi+1} += dS_t diag(b_t),
+//              da_t = colsum(dS_t * P_{lo-1}), db_t = colsum(dS_t * Q_{hi+1})
+//   scans      (adjoint, opposite order) dX = lam M_f^T, lam <- dX diag(alpha_f)
+//              (+ the gather's bank gradients); dA_f = -cc P_f^T dX^P - cc
+//              Q_f^T dX^Q, dB_f = c1 (dX^P + dX^Q), dalpha_f = colsum(dX^P *
+//              P_{f-1} + dX^Q * Q_{f+1}); dS_text = text_scale (lam_P + lam_Q)
+//   statistics dk^ = beta (dA + dA^T) k^ + beta dB^T v^, dv^ = beta dB k^,
+//              dbeta = k^.(dA k^) + v^.(dB k^), then L2, SiLU and the convs
+// All arithmetic is fp32. The forward's states are recomputed first with its
+// own statistics, inverse and scan kernels (every frame kept: a scan with
+// chunk 1 stores one bank slot per frame). Every output element is one fixed
+// sum: no atomics, so repeated calls agree bit for bit.
+
+#include "hwa_internal.h"
+
+namespace hwa {
+
+namespace {
+
+// d/dx x sigmoid(x) = s (1 + x (1 - s))
+__device__ __forceinline__ float silu_grad(float x) {
+  const float s = sigmoid_f(x);
+  return s * fmaf(x, 1.0f - s, 1.0f);
+}
+
+// Gradient through x^ = u / max(||u||, 1e-12) given dx^, x^, inv = 1 / max(..),
+// dot = x^ . dx^ over the vector; a clamped norm passes dx^ * inv straight.
+__device__ __forceinline__ float l2_grad(float dxh, float xh, float inv, float dot,
+                                         bool clamped) {
+  return clamped ? dxh * inv : (dxh - xh * dot) * inv;
+}
+
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+constexpr int LB_TT = 32;  // readout backward: tokens per tile (8 lanes each)
+constexpr int SB_TT = 16;  // statistics backward: tokens per tile (16 lanes each)
+constexpr int AJ_R = 8;    // adjoint scan: state rows per workgroup
+
+}  // namespace
+
+// ---------------------------------------------------------------- exponents
+// The scan keeps row = stored * 2^e; fold e into the stored rows.
+__global__ __launch_bounds__(256) void fold_exp_kernel(float* __restrict__ Pst,
+                                                       float* __restrict__ Qst,
+                                                       const int32_t* __restrict__ E,
+                                                       long long rows, int D) {
+  const long long n = rows * D;
+  for (long long x = blockIdx.x * 256LL + threadIdx.x; x < 2 * n; x += (long long)gridDim.x * 256) {
+    const int dir = x >= n;
+    const long long y = x - dir * n;
+    const int e = E[dir * rows + y / D];
+    if (e != 0) {
+      float* p = (dir ? Qst : Pst) + y;
+      *p = ldexpf(*p, e);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- readout
+// One workgroup per (b, h, frame t): S_t in LDS; tokens 32 at a time, 8 lanes
+// per token, lane l owning channels l, l + 8, ...; dS_t accumulates in
+// registers, thread (ib, jb) owning rows ib + 16a and columns jb + 16b.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lin_readout_bwd_kernel(
+    const T* __restrict__ q, const T* __restrict__ gate, const T* __restrict__ gout,
+    const float* __restrict__ alpha, const float* __restrict__ Pst,
+    const float* __restrict__ Qst, const float* __restrict__ rms_w, float eps,
+    T* __restrict__ dq, T* __restrict__ dgate, float* __restrict__ dSt,
+    float* __restrict__ dwpart, int F, int S, int chunk, int radius, long long N) {
+  constexpr int LD = D + 1;
+  constexpr int TPT = 256 / LB_TT;
+  constexpr int CPT = D / TPT;
+  constexpr int BS = D / 16;
+  __shared__ float st_lds[D * LD];
+  __shared__ float qh_lds[LB_TT][D + 4];
+  __shared__ float do_lds[LB_TT][D + 4];
+  __shared__ float dec[2][D];
+
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const int bh = blockIdx.y;
+  int lo, hi;
+  window_of(t, F, chunk, radius, lo, hi);
+  for (int j = tid; j < D; j += 256) {
+    const float* al = alpha + (long long)bh * F * D + j;
+    float a = 1.0f, b = 1.0f;
+    for (int x = lo; x <= t; ++x) a *= al[(long long)x * D];
+    for (int x = t; x <= hi; ++x) b *= al[(long long)x * D];
+    dec[0][j] = a;
+    dec[1][j] = b;
+  }
+  __syncthreads();
+  const float* Pm = Pst + ((long long)bh * (F + 1) + lo) * D * D;      // P_{lo-1}
+  const float* Qm = Qst + ((long long)bh * (F + 1) + hi + 1) * D * D;  // Q_{hi+1}
+  for (int x = tid; x < D * D; x += 256) {
+    const int i = x / D, j = x % D;
+    st_lds[i * LD + j] = fmaf(Pm[x], dec[0][j], Qm[x] * dec[1][j]);
+  }
+
+  const int tt = tid / TPT, ln = tid % TPT;
+  const int ib = tid / 16, jb = tid % 16;
+  float wr[CPT], dw[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    wr[c] = rms_w ? rms_w[ln + TPT * c] : 1.0f;
+    dw[c] = 0.0f;
+  }
+  float acc[BS][BS];
+#pragma unroll
+  for (int a = 0; a < BS; ++a)
+#pragma unroll
+    for (int b = 0; b < BS; ++b) acc[a][b] = 0.0f;
+  const long long base = (long long)bh * N * D;
+  __syncthreads();
+
+  for (int s0 = 0; s0 < S; s0 += LB_TT) {
+    const int s = s0 + tt;
+    const bool valid = s < S;
+    const long long row = base + ((long long)t * S + s) * D + ln;
+    float qv[CPT], qh[CPT];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      qv[c] = valid ? ld_io<T>(q, row + TPT * c) : 0.0f;
+      qh[c] = silu_f(qv[c]);
+      ss = fmaf(qh[c], qh[c], ss);
+    }
+    ss = group_sum<TPT>(ss);
+    const float inv = inv_l2(ss);
+    const bool clamped = ss <= 1e-24f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      qh[c] *= inv;
+      qh_lds[tt][ln + TPT * c] = qh[c];
+    }
+    __syncthreads();
+    float o[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] = 0.0f;
+    for (int j = 0; j < D; ++j) {
+      const float x = qh_lds[tt][j];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] = fmaf(st_lds[(ln + TPT * c) * LD + j], x, o[c]);
+    }
+    float ms = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) ms = fmaf(o[c], o[c], ms);
+    ms = group_sum<TPT>(ms);
+    const float r = 1.0f / sqrtf(ms / D + eps);
+    float z[CPT], dz[CPT];
+    float dzz = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const long long ix = row + TPT * c;
+      const float gt = valid ? ld_io<T>(gate, ix) : 0.0f;
+      const float go = valid ? ld_io<T>(gout, ix) : 0.0f;
+      const float sg = sigmoid_f(gt);
+      z[c] = o[c] * r;
+      if (valid) st_io<T>(dgate, ix, go * z[c] * wr[c] * sg * (1.0f - sg));
+      dw[c] = fmaf(go * sg, z[c], dw[c]);
+      dz[c] = go * wr[c] * sg;
+      dzz = fmaf(dz[c], z[c], dzz);
+    }
+    const float mz = group_sum<TPT>(dzz) / D;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) do_lds[tt][ln + TPT * c] = r * (dz[c] - z[c] * mz);
+    __syncthreads();
+    float dqh[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) dqh[c] = 0.0f;
+    for (int i = 0; i < D; ++i) {
+      const float di = do_lds[tt][i];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) dqh[c] = fmaf(st_lds[i * LD + ln + TPT * c], di, dqh[c]);
+    }
+    float dot = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) dot = fmaf(qh[c], dqh[c], dot);
+    dot = group_sum<TPT>(dot);
+    if (valid) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+        st_io<T>(dq, row + TPT * c,
+                 l2_grad(dqh[c], qh[c], inv, dot, clamped) * silu_grad(qv[c]));
+    }
+    const int ntok = min(LB_TT, S - s0);
+    for (int x = 0; x < ntok; ++x) {
+      float dr[BS], qr[BS];
+#pragma unroll
+      for (int a = 0; a < BS; ++a) {
+        dr[a] = do_lds[x][ib + 16 * a];
+        qr[a] = qh_lds[x][jb + 16 * a];
+      }
+#pragma unroll
+      for (int a = 0; a < BS; ++a)
+#pragma unroll
+        for (int b = 0; b < BS; ++b) acc[a][b] = fmaf(dr[a], qr[b], acc[a][b]);
+    }
+    __syncthreads();
+  }
+  float* ds = dSt + ((long long)bh * F + t) * D * D;
+#pragma unroll
+  for (int a = 0; a < BS; ++a)
+#pragma unroll
+    for (int b = 0; b < BS; ++b) ds[(ib + 16 * a) * D + jb + 16 * b] = acc[a][b];
+  // dw partial of this frame: sum over the 32 token slots
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) qh_lds[tt][ln + TPT * c] = dw[c];
+  __syncthreads();
+  for (int j = tid; j < D; j += 256) {
+    float sum = 0.0f;
+    for (int x = 0; x < LB_TT; ++x) sum += qh_lds[x][j];
+    dwpart[((long long)bh * F + t) * D + j] = sum;
+  }
+}
+
+// ---------------------------------------------------------------- gather
+// One workgroup per (bank slot m, direction, b*h). Slot m stands for the
+// state P_{pos-1} (prefix) or Q_pos (suffix), pos = min(F, m chunk); it sums
+// dS_t diag(a_t) (or b_t) over the frames t that gather it and writes
+// da_t / db_t (column sums of dS_t times that state) of those frames.
+template <int D>
+__global__ __launch_bounds__(256) void lin_gather_bwd_kernel(
+    const float* __restrict__ dSt, const float* __restrict__ alpha,
+    const float* __restrict__ Pst, const float* __restrict__ Qst, float* __restrict__ dbank,
+    float* __restrict__ gab, int F, int chunk, int radius, int nch, int BH) {
+  constexpr int RG = 256 / D;  // row groups
+  constexpr int RPT = D / RG;  // rows per thread
+  __shared__ float red[RG][D];
+  const int tid = threadIdx.x;
+  const int m = blockIdx.x, dir = blockIdx.y, bh = blockIdx.z;
+  const int j = tid % D, rg = tid / D;
+  const int pos = min(F, m * chunk);
+  const float* X = (dir == 0 ? Pst : Qst) + ((long long)bh * (F + 1) + pos) * D * D;
+  float xs[RPT], acc[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    xs[k] = X[(rg + RG * k) * D + j];
+    acc[k] = 0.0f;
+  }
+  const float* al = alpha + (long long)bh * F * D + j;
+  for (int t = 0; t < F; ++t) {
+    int lo, hi;
+    window_of(t, F, chunk, radius, lo, hi);
+    if ((dir == 0 ? lo : hi + 1) != pos) continue;  // uniform over the workgroup
+    float coef = 1.0f;
+    const int x0 = dir == 0 ? lo : t, x1 = dir == 0 ? t : hi;
+    for (int x = x0; x <= x1; ++x) coef *= al[(long long)x * D];
+    const float* ds = dSt + ((long long)bh * F + t) * D * D;
+    float part = 0.0f;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const float v = ds[(rg + RG * k) * D + j];
+      acc[k] = fmaf(v, coef, acc[k]);
+      part = fmaf(v, xs[k], part);
+    }
+    red[rg][j] = part;
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) sum += red[g][tid];
+      gab[(((long long)dir * BH + bh) * F + t) * D + tid] = sum;
+    }
+    __syncthreads();
+  }
+  float* out = dbank + (((long long)dir * BH + bh) * (nch + 1) + m) * D * D;
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) out[(rg + RG * k) * D + j] = acc[k];
+}
+
+// ---------------------------------------------------------------- adjoint scans
+// The adjoint of each scan runs in the opposite frame order. The update
+// right-multiplies the state, so adjoint rows are independent as well: a
+// workgroup owns 8 rows of one (b*h, direction) chain, M_f staged in LDS.
+// Writes dX of every frame and the adjoint of s0.
+template <int D>
+__global__ __launch_bounds__(256) void lin_adjoint_kernel(
+    const float* __restrict__ Mi, const float* __restrict__ alpha,
+    const float* __restrict__ dbank, float* __restrict__ dXP, float* __restrict__ dXQ,
+    float* __restrict__ lam0, int F, int chunk, int nch, int BH) {
+  constexpr int TPR = D / 4;
+  __shared__ __attribute__((aligned(16))) float g_lds[D * D];
+  __shared__ float x_lds[AJ_R][D];
+  const int tid = threadIdx.x;
+  const int rb = blockIdx.x, dir = blockIdx.y, bh = blockIdx.z;
+  const int r = tid / TPR, j0 = (tid % TPR) * 4;
+  const bool active = r < AJ_R;
+  const int row = rb * AJ_R + r;
+  const float* db = dbank + ((long long)dir * BH + bh) * (nch + 1) * D * D;
+  float lam[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto inject = [&](int slot) {
+    if (!active) return;
+    const float4 v = *(const float4*)&db[((long long)slot * D + row) * D + j0];
+    lam[0] += v.x;
+    lam[1] += v.y;
+    lam[2] += v.z;
+    lam[3] += v.w;
+  };
+  inject(dir == 0 ? nch : 0);  // P_{F-1} / Q_0
+  float* dX = dir == 0 ? dXP : dXQ;
+  for (int i = 0; i < F; ++i) {
+    const int f = dir == 0 ? F - 1 - i : i;
+    const long long mo = ((long long)bh * F + f) * D * D;
+    for (int x = tid; x < D * D / 4; x += 256)
+      *(float4*)&g_lds[x * 4] = *(const float4*)&Mi[mo + (long long)x * 4];
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x_lds[r][j0 + u] = lam[u];
+    }
+    __syncthreads();
+    if (active) {
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      // dX = lam M_f^T = lam M_f (M_f is the inverse of a symmetric matrix)
+#pragma unroll 8
+      for (int kk = 0; kk < D; ++kk) {
+        const float xv = x_lds[r][kk];
+        const float4 gv = *(const float4*)&g_lds[kk * D + j0];
+        acc[0] = fmaf(xv, gv.x, acc[0]);
+        acc[1] = fmaf(xv, gv.y, acc[1]);
+        acc[2] = fmaf(xv, gv.z, acc[2]);
+        acc[3] = fmaf(xv, gv.w, acc[3]);
+      }
+      *(float4*)&dX[mo + (long long)row * D + j0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      const float4 a4 = *(const float4*)&alpha[((long long)bh * F + f) * D + j0];
+      lam[0] = acc[0] * a4.x;
+      lam[1] = acc[1] * a4.y;
+      lam[2] = acc[2] * a4.z;
+      lam[3] = acc[3] * a4.w;
+    }
+    if (dir == 0) {
+      if (f % chunk == 0) inject(f / chunk);  // P_{f-1} is bank slot f / chunk
+    } else {
+      if ((f + 1) % chunk == 0 || f + 1 == F) inject((f + chunk) / chunk);  // Q_{f+1}
+    }
+    __syncthreads();
+  }
+  if (active)
+    *(float4*)&lam0[(((long long)dir * BH + bh) * D + row) * D + j0] =
+        make_float4(lam[0], lam[1], lam[2], lam[3]);
+}
+
+// ---------------------------------------------------------------- frame gradients
+// One workgroup per (frame, b*h): dB_f, dA_f (into the buffers A_f, B_f had)
+// and the scans' part of dalpha_f.
+template <int D>
+__global__ __launch_bounds__(256) void lin_frame_grad_kernel(
+    const float* __restrict__ Pst, const float* __restrict__ Qst,
+    const float* __restrict__ dXP, const float* __restrict__ dXQ, float cc, float c1,
+    float* __restrict__ dA, float* __restrict__ dB, float* __restrict__ dal, int F) {
+  constexpr int BS = D / 16;
+  constexpr int KR = 16;
+  constexpr int RG = 256 / D, RPT = D / RG;
+  __shared__ float sp[KR][D + 4], sxp[KR][D + 4], sq[KR][D + 4], sxq[KR][D + 4];
+  __shared__ float red[RG][D];
+  const int tid = threadIdx.x;
+  const int f = blockIdx.x, bh = blockIdx.y;
+  const long long fo = ((long long)bh * F + f) * D * D;
+  const long long so = (long long)bh * (F + 1) * D * D;
+  const float* P0 = Pst + so + (long long)f * D * D;        // P_{f-1}
+  const float* P1 = Pst + so + (long long)(f + 1) * D * D;  // P_f
+  const float* Q0 = Qst + so + (long long)f * D * D;        // Q_f
+  const float* Q1 = Qst + so + (long long)(f + 1) * D * D;  // Q_{f+1}
+  const float* xp = dXP + fo;
+  const float* xq = dXQ + fo;
+  {
+    const int j = tid % D, rg = tid / D;
+    float part = 0.0f;
+#pragma unroll 4
+    for (int k = 0; k < RPT; ++k) {
+      const long long ix = (long long)(rg + RG * k) * D + j;
+      const float a = xp[ix], b = xq[ix];
+      dB[fo + ix] = c1 * (a + b);
+      part = fmaf(a, P0[ix], part);
+      part = fmaf(b, Q1[ix], part);
+    }
+    red[rg][j] = part;
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) sum += red[g][tid];
+      dal[((long long)bh * F + f) * D + tid] = sum;
+    }
+  }
+  const int ib = tid / 16, jb = tid % 16;
+  float acc[BS][BS];
+#pragma unroll
+  for (int a = 0; a < BS; ++a)
+#pragma unroll
+    for (int b = 0; b < BS; ++b) acc[a][b] = 0.0f;
+  for (int i0 = 0; i0 < D; i0 += KR) {
+    __syncthreads();
+    for (int x = tid; x < KR * D; x += 256) {
+      const int rr = x / D, col = x % D;
+      const long long ix = (long long)(i0 + rr) * D + col;
+      sp[rr][col] = P1[ix];
+      sxp[rr][col] = xp[ix];
+      sq[rr][col] = Q0[ix];
+      sxq[rr][col] = xq[ix];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int rr = 0; rr < KR; ++rr) {
+      float pa[BS], qa[BS], xa[BS], ya[BS];
+#pragma unroll
+      for (int a = 0; a < BS; ++a) {
+        pa[a] = sp[rr][ib + 16 * a];
+        qa[a] = sq[rr][ib + 16 * a];
+        xa[a] = sxp[rr][jb + 16 * a];
+        ya[a] = sxq[rr][jb + 16 * a];
+      }
+#pragma unroll
+      for (int a = 0; a < BS; ++a)
+#pragma unroll
+        for (int b = 0; b < BS; ++b) acc[a][b] = fmaf(pa[a], xa[b], fmaf(qa[a], ya[b], acc[a][b]));
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < BS; ++a)
+#pragma unroll
+    for (int b = 0; b < BS; ++b) dA[fo + (long long)(ib + 16 * a) * D + jb + 16 * b] = -cc * acc[a][b];
+}
+
+// ---------------------------------------------------------------- statistics
+// One workgroup per (frame, b*h): dA + dA^T and dB in LDS; tokens 16 at a
+// time, 16 lanes per token (channels l, l + 16, ...). Writes the gradients
+// before the convs (fp32) and dbeta.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lin_stats_bwd_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ conv_k, const float* __restrict__ conv_v,
+    const float* __restrict__ dA, const float* __restrict__ dB, float* __restrict__ dkc,
+    float* __restrict__ dvc, float* __restrict__ dbeta, int F, int S, int H, long long N) {
+  constexpr int LD = D + 1;
+  constexpr int TPT = 256 / SB_TT;
+  constexpr int CPT = D / TPT;
+  __shared__ float g_lds[D * LD];
+  __shared__ float b_lds[D * LD];
+  __shared__ float kh_lds[SB_TT][D + 4];
+  __shared__ float vh_lds[SB_TT][D + 4];
+  const int tid = threadIdx.x;
+  const int f = blockIdx.x, bh = blockIdx.y;
+  const int h = bh % H;
+  const long long fo = ((long long)bh * F + f) * D * D;
+  for (int x = tid; x < D * D; x += 256) {
+    const int i = x / D, j = x % D;
+    g_lds[i * LD + j] = dA[fo + x] + dA[fo + (long long)j * D + i];
+    b_lds[i * LD + j] = dB[fo + x];
+  }
+  const int tt = tid / TPT, ln = tid % TPT;
+  float wk[CPT][4], wv[CPT][4];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wk[c][j] = conv_k[((long long)h * D + ln + TPT * c) * 4 + j];
+      wv[c][j] = conv_v[((long long)h * D + ln + TPT * c) * 4 + j];
+    }
+  const long long base = (long long)bh * N * D;
+  __syncthreads();
+  for (int s0 = 0; s0 < S; s0 += SB_TT) {
+    const int s = s0 + tt;
+    const bool valid = s < S;
+    const long long n = (long long)f * S + s;
+    float kc[CPT], kh[CPT], vh[CPT];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      float ak = 0.0f, av = 0.0f;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (s - j >= 0) {
+            const long long ix = base + (n - j) * D + ln + TPT * c;
+            ak = fmaf(wk[c][j], ld_io<T>(k, ix), ak);
+            av = fmaf(wv[c][j], ld_io<T>(v, ix), av);
+          }
+      }
+      kc[c] = ak;
+      kh[c] = silu_f(ak);
+      vh[c] = av;
+      ss = fmaf(kh[c], kh[c], ss);
+    }
+    ss = group_sum<TPT>(ss);
+    const float inv = inv_l2(ss);
+    const bool clamped = ss <= 1e-24f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      kh[c] *= inv;
+      kh_lds[tt][ln + TPT * c] = kh[c];
+      vh_lds[tt][ln + TPT * c] = vh[c];
+    }
+    __syncthreads();
+    float gk[CPT], bk[CPT], bv[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) gk[c] = bk[c] = bv[c] = 0.0f;
+    for (int m = 0; m < D; ++m) {
+      const float km = kh_lds[tt][m], vm = vh_lds[tt][m];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int i = ln + TPT * c;
+        gk[c] = fmaf(g_lds[i * LD + m], km, gk[c]);
+        bk[c] = fmaf(b_lds[i * LD + m], km, bk[c]);
+        bv[c] = fmaf(b_lds[m * LD + i], vm, bv[c]);
+      }
+    }
+    const float bt = valid ? beta[(long long)bh * N + n] : 0.0f;
+    float db = 0.0f, dot = 0.0f;
+    float dkh[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      db = fmaf(kh[c], 0.5f * gk[c], db);
+      db = fmaf(vh[c], bk[c], db);
+      dkh[c] = bt * (gk[c] + bv[c]);
+      dot = fmaf(kh[c], dkh[c], dot);
+    }
+    db = group_sum<TPT>(db);
+    dot = group_sum<TPT>(dot);
+    if (valid) {
+      if (ln == 0) dbeta[(long long)bh * N + n] = db;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const long long ix = base + n * D + ln + TPT * c;
+        dkc[ix] = l2_grad(dkh[c], kh[c], inv, dot, clamped) * silu_grad(kc[c]);
+        dvc[ix] = bt * bk[c];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- convs
+// One workgroup per (frame, b*h): dk_s = sum_j w_j dkc_{s+j} inside the frame,
+// and the frame's part of the tap gradients sum_s dkc_s k_{s-j} (likewise v).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ conv_k,
+    const float* __restrict__ conv_v, const float* __restrict__ dkc,
+    const float* __restrict__ dvc, T* __restrict__ dk, T* __restrict__ dv,
+    float* __restrict__ cpart, int F, int S, int H, long long N) {
+  constexpr int G = 256 / D;
+  __shared__ float red[G][D][8];
+  const int tid = threadIdx.x;
+  const int f = blockIdx.x, bh = blockIdx.y;
+  const int h = bh % H;
+  const int c = tid % D, g0 = tid / D;
+  float wk[4], wv[4], pk[4], pv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    wk[j] = conv_k[((long long)h * D + c) * 4 + j];
+    wv[j] = conv_v[((long long)h * D + c) * 4 + j];
+    pk[j] = pv[j] = 0.0f;
+  }
+  const long long base = (long long)bh * N * D + (long long)f * S * D + c;
+  for (int s = g0; s < S; s += G) {
+    const long long ix = base + (long long)s * D;
+    const float gk = dkc[ix], gv = dvc[ix];
+    float ak = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (s + j < S) {
+        ak = fmaf(wk[j], dkc[ix + (long long)j * D], ak);
+        av = fmaf(wv[j], dvc[ix + (long long)j * D], av);
+      }
+      if (s - j >= 0) {
+        pk[j] = fmaf(gk, ld_io<T>(k, ix - (long long)j * D), pk[j]);
+        pv[j] = fmaf(gv, ld_io<T>(v, ix - (long long)j * D), pv[j]);
+      }
+    }
+    st_io<T>(dk, ix, ak);
+    st_io<T>(dv, ix, av);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    red[g0][c][j] = pk[j];
+    red[g0][c][4 + j] = pv[j];
+  }
+  __syncthreads();
+  for (int x = tid; x < D * 8; x += 256) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) sum += red[g][x / 8][x % 8];
+    cpart[((long long)bh * F + f) * D * 8 + x] = sum;
+  }
+}
+
+// ---------------------------------------------------------------- dalpha
+// dalpha_f = the scans' part + the gather's: a_t and b_t are products over
+// frames of the window, so frame f's factor gets da_t (db_t) times the
+// product of the other factors.
+template <int D>
+__global__ __launch_bounds__(256) void lin_alpha_grad_kernel(
+    const float* __restrict__ alpha, const float* __restrict__ gab,
+    const float* __restrict__ dal, float* __restrict__ dalpha, int F, int chunk, int radius,
+    int BH) {
+  const long long idx = blockIdx.x * 256LL + threadIdx.x;
+  if (idx >= (long long)BH * F * D) return;
+  const int j = (int)(idx % D);
+  const long long rf = idx / D;
+  const int f = (int)(rf % F);
+  const long long bh = rf / F;
+  const float* al = alpha + bh * F * D + j;
+  const float* ga = gab + bh * F * D + j;
+  const float* gb = gab + ((long long)BH + bh) * F * D + j;
+  float acc = dal[idx];
+  const long long W = min((long long)F, (2LL * radius + 2) * chunk);
+  const int t0 = (int)max(0LL, f - W), t1 = (int)min((long long)F - 1, f + W);
+  for (int t = t0; t <= t1; ++t) {
+    int lo, hi;
+    window_of(t, F, chunk, radius, lo, hi);
+    if (lo <= f && f <= t) {
+      float pr = 1.0f;
+      for (int x = lo; x <= t; ++x)
+        if (x != f) pr *= al[(long long)x * D];
+      acc = fmaf(ga[(long long)t * D], pr, acc);
+    }
+    if (t <= f && f <= hi) {
+      float pr = 1.0f;
+      for (int x = t; x <= hi; ++x)
+        if (x != f) pr *= al[(long long)x * D];
+      acc = fmaf(gb[(long long)t * D], pr, acc);
+    }
+  }
+  dalpha[idx] = acc;
+}
+
+// ---------------------------------------------------------------- parameters
+// Per-head conv taps (sum over batch and frames), the RMSNorm weight (sum over
+// everything) and dS_text = text_scale (lam_P + lam_Q); one thread per output.
+__global__ __launch_bounds__(256) void lin_param_grad_kernel(
+    const float* __restrict__ cpart, const float* __restrict__ dwpart,
+    const float* __restrict__ lam0, float* __restrict__ dconv_k, float* __restrict__ dconv_v,
+    float* __restrict__ drms, float* __restrict__ dtext, float text_scale, int B, int H,
+    int D, int F) {
+  const long long idx = blockIdx.x * 256LL + threadIdx.x;
+  const long long BH = (long long)B * H;
+  const long long n_conv = (long long)H * D * 8;
+  const long long n_text = BH * D * D;
+  if (idx < n_conv) {
+    const int h = (int)(idx / (D * 8));
+    const int x = (int)(idx % (D * 8));  // channel * 8 + tap (k: 0..3, v: 4..7)
+    float sum = 0.0f;
+    for (int b = 0; b < B; ++b)
+      for (int f = 0; f < F; ++f)
+        sum += cpart[(((long long)b * H + h) * F + f) * D * 8 + x];
+    const int ch = x / 8, tap = x % 8;
+    float* dst = tap < 4 ? dconv_k : dconv_v;
+    dst[((long long)h * D + ch) * 4 + (tap & 3)] = sum;
+  } else if (idx < n_conv + D) {
+    const int j = (int)(idx - n_conv);
+    float sum = 0.0f;
+    for (long long r = 0; r < BH * F; ++r) sum += dwpart[r * D + j];
+    if (drms) drms[j] = sum;
+  } else if (idx < n_conv + D + n_text) {
+    const long long x = idx - n_conv - D;
+    if (dtext) dtext[x] = text_scale * (lam0[x] + lam0[n_text + x]);
+  }
+}
+
+// ---------------------------------------------------------------- launch sequence
+#define LB_SWITCH_D(MACRO)          \
+  switch (g.d) {                    \
+    case 16: MACRO(16); break;      \
+    case 32: MACRO(32); break;      \
+    case 64: MACRO(64); break;      \
+    default: MACRO(128); break;     \
+  }
+
+hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdArgs& a,
+                             hipStream_t st) {
+  const int BH = g.B * g.H;
+  const float cc = a.rule == HWA_RULE_VDN_SCALED ? a.c * a.c : 1.0f;
+  const float c1 = a.rule == HWA_RULE_VDN_SCALED ? a.c : 1.0f;
+  const bool bf = dtype == HWA_BF16;
+  hipError_t e = hipSuccess;
+  switch (stage) {
+    case 0: {  // recompute: statistics, inverses, every frame's states
+      e = launch_stats(g, dtype, a.k, a.v, a.beta, a.conv_k, a.conv_v, true, a.A, a.Bm, st);
+      if (e != hipSuccess) return e;
+      e = launch_inverse(g, cc, a.A, a.M, st);
+      if (e != hipSuccess) return e;
+      Geom g1 = g;
+      g1.chunk = 1;
+      g1.nch = g.F;
+      e = launch_scan(g1, HWA_F32, a.rule, a.c, a.A, a.Bm, a.M, a.alpha, a.text_state,
+                      a.text_scale, a.Pst, a.Qst, a.E, st);
+      if (e != hipSuccess) return e;
+      const long long rows = (long long)BH * (g.F + 1) * g.d;
+      const long long work = 2 * rows * g.d;
+      const unsigned blocks = (unsigned)min(8192LL, (work + 255) / 256);
+      hipLaunchKernelGGL(fold_exp_kernel, dim3(blocks), dim3(256), 0, st, a.Pst, a.Qst, a.E,
+                         rows, g.d);
+      break;
+    }
+    case 1: {  // readout
+      dim3 grid(g.F, BH);
+#define RB(DD)                                                                           \
+  if (bf)                                                                                \
+    hipLaunchKernelGGL((lin_readout_bwd_kernel<bf16_t, DD>), grid, dim3(256), 0, st,      \
+                       (const bf16_t*)a.q, (const bf16_t*)a.gate, (const bf16_t*)a.d_o,   \
+                       a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (bf16_t*)a.dq,              \
+                       (bf16_t*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N); \
+  else                                                                                   \
+    hipLaunchKernelGGL((lin_readout_bwd_kernel<float, DD>), grid, dim3(256), 0, st,       \
+                       (const float*)a.q, (const float*)a.gate, (const float*)a.d_o,      \
+                       a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (float*)a.dq,               \
+                       (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N);
+      LB_SWITCH_D(RB)
+#undef RB
+      break;
+    }
+    case 2: {  // gather, adjoint scans, frame gradients
+      {
+        dim3 grid(g.nch + 1, 2, BH);
+#define GB(DD)                                                                       \
+  hipLaunchKernelGGL(lin_gather_bwd_kernel<DD>, grid, dim3(256), 0, st, a.dSt, a.alpha, \
+                     a.Pst, a.Qst, a.dbank, a.gab, g.F, g.chunk, g.radius, g.nch, BH);
+        LB_SWITCH_D(GB)
+#undef GB
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      {
+        dim3 grid(g.d / AJ_R, 2, BH);
+#define AJ(DD)                                                                          \
+  hipLaunchKernelGGL(lin_adjoint_kernel<DD>, grid, dim3(256), 0, st, a.M, a.alpha, a.dbank, \
+                     a.dXP, a.dXQ, a.lam0, g.F, g.chunk, g.nch, BH);
+        LB_SWITCH_D(AJ)
+#undef AJ
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      {
+        dim3 grid(g.F, BH);
+#define FG(DD)                                                                          \
+  hipLaunchKernelGGL(lin_frame_grad_kernel<DD>, grid, dim3(256), 0, st, a.Pst, a.Qst,    \
+                     a.dXP, a.dXQ, cc, c1, a.A, a.Bm, a.dal, g.F);
+        LB_SWITCH_D(FG)
+#undef FG
+      }
+      break;
+    }
+    case 3: {  // statistics and features
+      dim3 grid(g.F, BH);
+#define SB(DD)                                                                              \
+  if (bf)                                                                                   \
+    hipLaunchKernelGGL((lin_stats_bwd_kernel<bf16_t, DD>), grid, dim3(256), 0, st,          \
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, a.beta, a.conv_k, a.conv_v,   \
+                       a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);               \
+  else                                                                                      \
+    hipLaunchKernelGGL((lin_stats_bwd_kernel<float, DD>), grid, dim3(256), 0, st,           \
+                       (const float*)a.k, (const float*)a.v, a.beta, a.conv_k, a.conv_v,     \
+                       a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);
+      LB_SWITCH_D(SB)
+#undef SB
+      break;
+    }
+    case 4: {  // convs, dalpha, parameter sums
+      {
+        dim3 grid(g.F, BH);
+#define CB(DD)                                                                              \
+  if (bf)                                                                                   \
+    hipLaunchKernelGGL((lin_conv_bwd_kernel<bf16_t, DD>), grid, dim3(256), 0, st,           \
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, a.conv_k, a.conv_v, a.dkc,    \
+                       a.dvc, (bf16_t*)a.dk, (bf16_t*)a.dv, a.cpart, g.F, g.S, g.H, g.N);   \
+  else                                                                                      \
+    hipLaunchKernelGGL((lin_conv_bwd_kernel<float, DD>), grid, dim3(256), 0, st,            \
+                       (const float*)a.k, (const float*)a.v, a.conv_k, a.conv_v, a.dkc,     \
+                       a.dvc, (float*)a.dk, (float*)a.dv, a.cpart, g.F, g.S, g.H, g.N);
+        LB_SWITCH_D(CB)
+#undef CB
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      {
+        const long long n = (long long)BH * g.F * g.d;
+        dim3 grid((unsigned)((n + 255) / 256));
+#define AG(DD)                                                                            \
+  hipLaunchKernelGGL(lin_alpha_grad_kernel<DD>, grid, dim3(256), 0, st, a.alpha, a.gab,    \
+                     a.dal, a.dalpha, g.F, g.chunk, g.radius, BH);
+        LB_SWITCH_D(AG)
+#undef AG
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      {
+        const long long n = (long long)g.H * g.d * 8 + g.d + (long long)BH * g.d * g.d;
+        hipLaunchKernelGGL(lin_param_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, st, a.cpart, a.dwpart, a.lam0, a.dconv_k, a.dconv_v, a.drms,
+                           a.dtext, a.text_scale, g.B, g.H, g.d, g.F);
+      }
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+#undef LB_SWITCH_D
+
+}  // namespace hwa

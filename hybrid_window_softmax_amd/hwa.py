@@ -26,6 +26,11 @@ STAGES = ("window", "stats", "inverse", "scan", "decay+state", "vtranspose", "so
           "readout")
 NUM_BWD_STAGE_EVENTS = 4
 BWD_STAGES = ("prep", "dq", "dkdv")
+NUM_LIN_BWD_STAGE_EVENTS = 6
+LIN_BWD_STAGES = ("recompute", "readout", "scans", "stats", "convs")
+# gradients hwa_linear_bwd returns, in its argument order
+LIN_GRADS = ("q", "k", "v", "beta", "alpha", "gate", "text_state", "conv_k", "conv_v",
+             "rms_weight")
 
 HWA_OK = 0
 HWA_ERR_INVALID_ARG = 1
@@ -37,7 +42,8 @@ HWA_BF16 = 1
 
 EXPORTS = ("hybrid_attn_fwd", "hwa_workspace_bytes", "hwa_get_workspace_layout",
            "hwa_window_bounds", "hwa_text_state", "hwa_text_state_workspace_bytes",
-           "hwa_softmax_bwd", "hwa_softmax_bwd_workspace_bytes", "hwa_status_string")
+           "hwa_softmax_bwd", "hwa_softmax_bwd_workspace_bytes", "hwa_linear_bwd",
+           "hwa_linear_bwd_workspace_bytes", "hwa_status_string")
 
 
 class Params(ctypes.Structure):
@@ -105,6 +111,11 @@ def lib():
         L.hwa_softmax_bwd.restype = ctypes.c_int
         L.hwa_softmax_bwd_workspace_bytes.argtypes = [i32, i32, i32, PP]
         L.hwa_softmax_bwd_workspace_bytes.restype = sz
+        L.hwa_linear_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, PP]
+        L.hwa_linear_bwd.restype = ctypes.c_int
+        L.hwa_linear_bwd_workspace_bytes.argtypes = [i32, i32, i32, PP]
+        L.hwa_linear_bwd_workspace_bytes.restype = sz
         L.hwa_status_string.argtypes = [ctypes.c_int]
         L.hwa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -263,6 +274,63 @@ def softmax_bwd(q, k, v, o_sm, lse, d_o, frames: int, tokens_per_frame: int,
     if code != HWA_OK:
         raise HwaError(code)
     return dq, dk, dv, workspace
+
+
+def linear_bwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, d_o, frames: int,
+               tokens_per_frame: int, chunk: int = 5, radius: int = 1, rule="vdn_solve",
+               c: float = 0.5, text_scale: float = 0.5, rms_eps: float = 1e-6,
+               rms_weight=None, grads=None, workspace=None, stream=None,
+               stage_events=None):
+    """Gradients of the linear branch (hwa_linear_bwd) for upstream gradient
+    d_o, as a dict keyed by LIN_GRADS (``text_state`` and ``rms_weight``
+    always present: at the zero state / for unit weights when not given).
+
+    Tensors as for hybrid_attn_fwd, d_o like q. ``grads``: optional dict of
+    preallocated outputs. ``stage_events``: optional ctypes array of
+    NUM_LIN_BWD_STAGE_EVENTS hipEvent_t. Returns (grads, workspace).
+    """
+    B, H, N, d = q.shape
+    F = frames
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("d_o", d_o)):
+        _check(t, name, q.dtype, (B, H, N, d), dev)
+    _check(beta, "beta", torch.float32, (B, H, N), dev)
+    _check(alpha, "alpha", torch.float32, (B, H, F, d), dev)
+    _check(text_state, "text_state", torch.float32, (B, H, d, d), dev)
+    _check(conv_k, "conv_k", torch.float32, (H, d, 4), dev)
+    _check(conv_v, "conv_v", torch.float32, (H, d, 4), dev)
+    _check(rms_weight, "rms_weight", torch.float32, (d,), dev)
+    p = make_params(B, H, d, q.dtype, c, text_scale, rms_eps, conv_k, conv_v, rms_weight)
+    need = int(lib().hwa_linear_bwd_workspace_bytes(frames, tokens_per_frame, chunk,
+                                                    ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if stage_events is not None:
+        p.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
+    shapes = dict(q=(q.dtype, (B, H, N, d)), k=(q.dtype, (B, H, N, d)),
+                  v=(q.dtype, (B, H, N, d)), gate=(q.dtype, (B, H, N, d)),
+                  beta=(torch.float32, (B, H, N)), alpha=(torch.float32, (B, H, F, d)),
+                  text_state=(torch.float32, (B, H, d, d)),
+                  conv_k=(torch.float32, (H, d, 4)), conv_v=(torch.float32, (H, d, 4)),
+                  rms_weight=(torch.float32, (d,)))
+    g = dict(grads or {})
+    for name, (dt, shp) in shapes.items():
+        if g.get(name) is None:
+            g[name] = torch.empty(shp, dtype=dt, device=dev)
+        _check(g[name], "d" + name, dt, shp, dev)
+    st = _stream(dev) if stream is None else ctypes.c_void_p(stream)
+    code = lib().hwa_linear_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(gate), _ptr(text_state),
+        _ptr(d_o), frames, tokens_per_frame, chunk, radius,
+        RULES[rule] if isinstance(rule, str) else rule, _ptr(g["q"]), _ptr(g["k"]),
+        _ptr(g["v"]), _ptr(g["beta"]), _ptr(g["alpha"]), _ptr(g["gate"]),
+        _ptr(g["text_state"]), _ptr(g["conv_k"]), _ptr(g["conv_v"]), _ptr(g["rms_weight"]),
+        st, ctypes.byref(p))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return g, workspace
 
 
 class WindowedSoftmaxAttention(torch.autograd.Function):

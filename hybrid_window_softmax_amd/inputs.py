@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TID = dict(q=0, k=1, v=2, gate=3, beta=4, alpha=5, k_txt=6, v_txt=7,
-           beta_txt=8, conv_k=9, conv_v=10, rms_weight=11, d_out=12)
+           beta_txt=8, conv_k=9, conv_v=10, rms_weight=11, d_out=12, state=13)
 
 # The five workloads, by name. Token counts per frame follow 832x480 (52x30
 # latent grid) and 1024x1024 (64x64) canvases at 16x spatial compression.
@@ -213,4 +213,17 @@ def grad_output(cfg) -> np.ndarray:
         for h in range(H):
             x = _draw(cfg["seed"], "d_out", b, h, (N, d), "normal")
             out[b, h] = f32_to_bf16_bits(x) if bf16 else x
+    return out
+
+
+def state_matrix(cfg) -> np.ndarray:
+    """A text state S_text [B, H, d, d] float32 drawn directly, N(0, 1 / d)
+    (the gradient tests feed the same matrix to both sides)."""
+    if not isinstance(cfg, dict):
+        cfg = WORKLOADS[cfg]
+    B, H, d = cfg["batch"], cfg["heads"], cfg["head_dim"]
+    out = np.empty((B, H, d, d), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = _draw(cfg["seed"], "state", b, h, (d, d), "normal", std=d ** -0.5)
     return out

@@ -261,6 +261,56 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
 size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
                                        int32_t chunk, const hwa_params* p);
 
+/*
+ * hwa_linear_bwd -- gradient of the linear branch y (article, "Step 1:
+ * NoPE features" .. "Step 5", "Text state"; needed to train the hybrid
+ * attention as its "Training" section does) for a loss L with upstream
+ * gradient d_o = dL/dy. With the forward's definitions (features q^, k^, v^;
+ * statistics A_f, B_f; the update rule's scans P, Q from s0 = text_scale *
+ * text_state; S_t gathered with the bridge decays; y = RMSNorm(S_t q^) *
+ * w * sigmoid(gate)), the call writes dL/d(every input):
+ *
+ *   q, k, v, gate, d_o [B, H, N, d] dtype  as for hybrid_attn_fwd (the raw q:
+ *                                          the branch never reads q_rope)
+ *   beta [B, H, N], alpha [B, H, F, d], text_state [B, H, d, d] or NULL
+ *                                          fp32, as for hybrid_attn_fwd
+ *   frames .. rule                         as for hybrid_attn_fwd; rule
+ *                                          HWA_RULE_SANA_SCALED returns
+ *                                          HWA_ERR_UNSUPPORTED
+ *   dq, dk, dv, dgate [B, H, N, d] dtype   written (bf16: rounded from fp32)
+ *   dbeta [B, H, N], dalpha [B, H, F, d]   fp32, written
+ *   dtext_state [B, H, d, d] fp32 or NULL  dL/dtext_state (with a NULL
+ *                                          text_state: at the zero state)
+ *   dconv_k, dconv_v [H, d, 4] fp32        summed over the batch
+ *   drms_weight [d] fp32 or NULL           summed over batch and heads
+ *   p   batch, heads, head_dim, dtype, c, text_scale, rms_eps, conv_k, conv_v,
+ *       rms_weight (NULL => ones), workspace (>= hwa_linear_bwd_workspace_
+ *       bytes), stage_events (NULL, or HWA_NUM_LIN_BWD_STAGE_EVENTS events
+ *       recorded at [0] start, [1] after recomputing the statistics, inverses
+ *       and every frame's scan states, [2] after the readout, [3] after the
+ *       gather, adjoint scans and per-frame gradients, [4] after the
+ *       statistics and features, [5] after the convs and parameter sums)
+ * Outputs must not overlap each other, an input or the workspace. All
+ * arithmetic is fp32. Returns HWA_OK, or an error status before anything is
+ * enqueued.
+ */
+#define HWA_NUM_LIN_BWD_STAGE_EVENTS 6
+
+hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const float* beta,
+                          const float* alpha, const void* gate, const float* text_state,
+                          const void* d_o, int32_t frames, int32_t tokens_per_frame,
+                          int32_t chunk, int32_t radius, int32_t rule, void* dq, void* dk,
+                          void* dv, float* dbeta, float* dalpha, void* dgate,
+                          float* dtext_state, float* dconv_k, float* dconv_v,
+                          float* drms_weight, void* stream, const hwa_params* p);
+
+/* Workspace bytes hwa_linear_bwd needs (0 on bad args): per (b, h) seven
+ * fp32 d x d matrices per frame (statistics, inverses, both scans' states,
+ * their adjoints), the bank gradients, and two fp32 [N, d] arrays (the
+ * feature gradients before the convs), plus alignment. */
+size_t hwa_linear_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
+                                      int32_t chunk, const hwa_params* p);
+
 /* Static English text of a status. */
 const char* hwa_status_string(hwa_status s);
 

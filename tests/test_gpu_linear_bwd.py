@@ -1,0 +1,126 @@
+"""GPU parity of the linear branch's backward (hwa_linear_bwd) with the fp64
+oracle gradient (torch autograd of the branch, pinned by finite differences
+of the numpy oracle), through the C ABI.
+
+Every gradient is compared per (b, h) slice by relative Frobenius error;
+the conv taps (per head) are compared summed over the batch and the RMSNorm
+weight summed over batch and heads, as the library returns them. Without a
+text state the library returns dL/dS_text at the zero state, which the
+oracle gives for S_text = 0. Bar: 1e-5 (fp32) / 5e-3 (bf16: dq, dk, dv and
+dgate are rounded to bf16, the fp32 outputs see the bf16 inputs only).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hybrid_window_softmax_amd import hwa, inputs
+from harness import TOL, to_dev
+
+pytestmark = pytest.mark.gpu
+
+PER_HEAD = ("q", "k", "v", "beta", "alpha", "gate", "text_state")
+
+
+def _gpu_grads(inp, rule, st_host, g_host):
+    c = inp.cfg
+    bf = c["dtype"] == "bf16"
+    t = {n: to_dev(getattr(inp, n), bf) for n in
+         ("q", "k", "v", "gate", "beta", "alpha", "conv_k", "conv_v", "rms_weight")}
+    d_o = to_dev(g_host, bf)
+    S_t = None if st_host is None else to_dev(st_host, False)
+    grads, _ = hwa.linear_bwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"], S_t,
+                              t["conv_k"], t["conv_v"], d_o, c["frames"], c["tokens_per_frame"],
+                              c["chunk"], c["radius"], rule, c["c"], 0.5, 1e-6, t["rms_weight"])
+    torch.cuda.synchronize()
+    return {n: x.float().cpu().numpy().astype(np.float64) for n, x in grads.items()}
+
+
+def _f64(inp, x):
+    if inp.cfg["dtype"] == "bf16" and x.dtype == np.uint16:
+        return inputs.bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, np.float64)
+
+
+def check(inp, rule="vdn_solve", text=True):
+    c = inp.cfg
+    print(f"case {c['name']} {c['dtype']} B{c['batch']} H{c['heads']} d{c['head_dim']} "
+          f"F{c['frames']} S{c['tokens_per_frame']} chunk {c['chunk']} r {c['radius']} "
+          f"{rule} text {text}", flush=True)
+    g_host = inputs.grad_output(c)
+    st_host = inputs.state_matrix(c) if text else None
+    got = _gpu_grads(inp, rule, st_host, g_host)
+    B, H, d = c["batch"], c["heads"], c["head_dim"]
+    worst = dict.fromkeys(PER_HEAD, 0.0)
+    conv_k = np.zeros((H, d, 4))
+    conv_v = np.zeros((H, d, 4))
+    w = np.zeros(d)
+    for b in range(B):
+        for h in range(H):
+            S_text = st_host[b, h] if text else np.zeros((d, d))
+            ref = oracle.linear_branch_grad(
+                inp.f64("q", b, h), inp.f64("k", b, h), inp.f64("v", b, h), inp.beta[b, h],
+                inp.alpha[b, h], inp.f64("gate", b, h), S_text, inp.conv_k[h], inp.conv_v[h],
+                inp.rms_weight, _f64(inp, g_host[b, h]), c["tokens_per_frame"], c["chunk"],
+                c["radius"], rule, c["c"], 0.5, 1e-6)
+            for n in PER_HEAD:
+                r = ref["S_text" if n == "text_state" else n]
+                worst[n] = max(worst[n], oracle.rel_frobenius(got[n][b, h], r))
+            conv_k[h] += ref["conv_k"]
+            conv_v[h] += ref["conv_v"]
+            w += ref["w"]
+    worst["conv_k"] = oracle.rel_frobenius(got["conv_k"], conv_k)
+    worst["conv_v"] = oracle.rel_frobenius(got["conv_v"], conv_v)
+    worst["rms_weight"] = oracle.rel_frobenius(got["rms_weight"], w)
+    print("  rel err " + " ".join(f"d{n} {e:.2e}" for n, e in worst.items()), flush=True)
+    tol = TOL[c["dtype"]]
+    assert max(worst.values()) <= tol, worst
+
+
+def test_tiny_fp32_160tok():
+    check(inputs.make("tiny-f32"))
+
+
+@pytest.mark.parametrize("kw,rule,text", [
+    (dict(frames=17, head_dim=32, tokens_per_frame=37), "vdn_scaled", True),   # partial chunk
+    (dict(frames=12, head_dim=64, tokens_per_frame=20, batch=2, heads=2, radius=0),
+     "vdn_solve", False),
+    (dict(frames=14, head_dim=128, tokens_per_frame=24, chunk=3), "vdn_solve", True),
+    (dict(frames=6, head_dim=16, tokens_per_frame=3, chunk=1), "vdn_scaled", True),  # S < taps
+])
+def test_small_fp32(kw, rule, text):
+    check(inputs.make(inputs.tiny_config(text_tokens=0, seed=400, **kw),
+                      random_rms_weight=True), rule, text)
+
+
+def test_small_bf16_5120tok():
+    check(inputs.make("small-bf16-text", random_rms_weight=True))
+
+
+@pytest.mark.parametrize("kw,rule", [
+    (dict(frames=11, head_dim=128, tokens_per_frame=45, heads=2), "vdn_scaled"),
+    (dict(frames=1, head_dim=64, tokens_per_frame=1), "vdn_solve"),             # one token
+])
+def test_bf16_shapes(kw, rule):
+    check(inputs.make(inputs.tiny_config(text_tokens=0, dtype="bf16", seed=401, **kw)), rule)
+
+
+def test_repeat_bit_exact():
+    # no atomics: every output element is one fixed sum
+    inp = inputs.make("small-bf16-text")
+    c = inp.cfg
+    print("case small-bf16-text: two calls agree bit for bit", flush=True)
+    g_host = inputs.grad_output(c)
+    st = inputs.state_matrix(c)
+    a = _gpu_grads(inp, "vdn_solve", st, g_host)
+    b = _gpu_grads(inp, "vdn_solve", st, g_host)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_sana_scaled_unsupported():
+    inp = inputs.make("tiny-f32")
+    with pytest.raises(hwa.HwaError) as e:
+        _gpu_grads(inp, "sana_scaled", None, inputs.grad_output(inp.cfg))
+    assert e.value.code == hwa.HWA_ERR_UNSUPPORTED
