@@ -118,4 +118,7 @@ def linear_branch_grad(q, k, v, beta, alpha, gate, S_text, conv_k, conv_v, w, g,
     y = linear_branch_torch(*(ts[n] for n in NAMES), S, chunk, radius, rule, c, text_scale,
                             eps)
     (y * torch.tensor(np.asarray(g, np.float64), dtype=_T)).sum().backward()
-    return {n: t.grad.numpy() for n, t in ts.items() if t is not None}
+    # an input y does not depend on (k, v, beta and the convs when every
+    # window spans all frames) has gradient zero; autograd leaves it unset
+    return {n: (t.grad.numpy() if t.grad is not None else np.zeros(tuple(t.shape)))
+            for n, t in ts.items() if t is not None}
