@@ -14,7 +14,8 @@ timed on a bounded sample of the same workload.
 With --softmax-bwd it instead times the backward of the windowed softmax
 branch (hwa_softmax_bwd: dq, dk, dv from q, k, v, the branch output, its
 log-sum-exp and the upstream gradient) on the same workload and prints that
-line.
+line; with --linear-bwd, the backward of the linear branch (hwa_linear_bwd:
+every input's gradient, fp32 arithmetic).
 """
 
 from __future__ import annotations
@@ -276,6 +277,130 @@ def bench_softmax_bwd(args, cfg, inp, up):
     }
 
 
+def linear_bwd_cpu_baseline(inp, g_host, st_host, rule, heads_run=1):
+    """The oracle's linear-branch gradient (fp64 autograd) on `heads_run`
+    whole heads, scaled to the whole job's tokens/s."""
+    import numpy as np
+    import torch
+    import oracle
+    from hybrid_window_softmax_amd import inputs
+    cfg = inp.cfg
+    S = cfg["tokens_per_frame"]
+    t0 = time.perf_counter()
+    for h in range(heads_run):
+        g = inputs.bf16_bits_to_f32(g_host[0, h]) if g_host.dtype == np.uint16 else g_host[0, h]
+        oracle.linear_branch_grad(inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h),
+                                  inp.beta[0, h], inp.alpha[0, h], inp.f64("gate", 0, h),
+                                  st_host[0, h], inp.conv_k[h], inp.conv_v[h], inp.rms_weight,
+                                  g.astype(np.float64), S, cfg["chunk"], cfg["radius"], rule,
+                                  cfg["c"], 0.5, 1e-6)
+    dt = time.perf_counter() - t0
+    N = cfg["frames"] * S
+    total_s = dt * cfg["heads"] * cfg["batch"] / heads_run
+    return {"value": N * cfg["batch"] / total_s, "unit": "tokens/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{heads_run} of {cfg['heads']} heads (all {N} tokens of each), "
+                      f"{dt:.1f} s wall, scaled by heads"}
+
+
+def bench_linear_bwd(args, cfg, inp, up):
+    """One step = one hwa_linear_bwd over the whole workload (every input and
+    the upstream gradient resident in HBM)."""
+    import torch
+    from hybrid_window_softmax_amd import hwa, inputs
+    g_host = inputs.grad_output(cfg)
+    st_host = inputs.state_matrix(cfg)
+    t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
+                                          "conv_v", "rms_weight")}
+    g = up(g_host)
+    text = up(st_host)
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+    B, H, N, d = t["q"].shape
+    grads = None
+
+    def call(events=None, ws=None):
+        nonlocal grads
+        grads, ws = hwa.linear_bwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"], text,
+                                   t["conv_k"], t["conv_v"], g, F, S, cfg["chunk"], cfg["radius"],
+                                   args.rule, cfg["c"], 0.5, 1e-6, t["rms_weight"], grads=grads,
+                                   workspace=ws, stage_events=events)
+        return ws
+
+    log("bench: linear-branch backward warmup")
+    ws = call()
+    for _ in range(max(0, args.warmup - 1)):
+        call(ws=ws)
+    torch.cuda.synchronize()
+    timer = hwa.StageTimer(args.steps, hwa.NUM_LIN_BWD_STAGE_EVENTS, hwa.LIN_BWD_STAGES)
+    log(f"bench: timing {args.steps} linear backward steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(events=timer.sets[i], ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage = timer.stage_ms()
+    timer.close()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    log("bench: stage ms " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()))
+    io = 2 if cfg["dtype"] == "bf16" else 4
+    tok = B * H * N
+    # fp32 products per token: readout S_t q^, S_t^T do, do q^^T (3 x 2 d^2);
+    # statistics (dA + dA^T) k^, dB k^, dB^T v^ (3 x 2 d^2)
+    work = {
+        "readout": dict(flops=6 * d * d * tok, bytes=0),
+        "stats": dict(flops=6 * d * d * tok, bytes=0),
+        # read the fp32 gradients before the convs and k, v; write dk, dv
+        "convs": dict(flops=0, bytes=tok * d * (2 * 4 + 4 * io)),
+    }
+    kernels = {}
+    for name in hwa.LIN_BWD_STAGES:
+        rec = {"ms": round(stage[name], 4)}
+        w = work.get(name)
+        if w:
+            sec = stage[name] / 1000.0
+            if w["flops"]:
+                rec["TFLOPs"] = round(w["flops"] / sec / 1e12, 2)
+                rec["frac"] = round(w["flops"] / sec / 1e12 / PEAK_FP32_TFLOPS, 4)
+            if w["bytes"]:
+                rec["hbm_GBs"] = round(w["bytes"] / sec / 1e9, 1)
+                rec["hbm_frac"] = round(w["bytes"] / sec / 1e9 / PEAK_HBM_GBS, 4)
+        kernels[name] = rec
+    dom = max(("readout", "stats"), key=lambda n: stage[n])
+    achieved = work[dom]["flops"] / (stage[dom] / 1000.0) / 1e12
+    roofline = {"kernel": f"lin_{dom}_bwd_kernel", "bound": "alu",
+                "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": work[dom]["flops"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle's linear-branch gradient on a sample")
+        del t, g, text, grads, ws
+        torch.cuda.empty_cache()
+        cpu = linear_bwd_cpu_baseline(inp, g_host, st_host, args.rule, args.cpu_heads)
+    return {
+        "metric": "linear-branch backward (dq, dk, dv, dbeta, dalpha, dgate, dS_text, dconv, "
+                  "dw) tokens/s",
+        "value": round(B * N / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: B{B} H{H} d{d} F{F} x S{S} = {N} tokens, "
+                               f"chunk {cfg['chunk']} radius {cfg['radius']}, {args.rule}, "
+                               f"{cfg['dtype']} I/O, linear branch backward",
+                   "tokens": N, "heads": H, "head_dim": d},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +414,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (three times), the "
                          "reference kernel for scaling HBM byte counters")
+    ap.add_argument("--linear-bwd", action="store_true",
+                    help="time the linear branch's backward (hwa_linear_bwd) instead")
     ap.add_argument("--softmax-bwd", action="store_true",
                     help="time the windowed-softmax backward (hwa_softmax_bwd) instead")
     ap.add_argument("--gemm-ceiling", action="store_true",
@@ -350,6 +477,9 @@ def main():
 
     if args.softmax_bwd:
         print(json.dumps(bench_softmax_bwd(args, cfg, inp, up)), flush=True)
+        return
+    if args.linear_bwd:
+        print(json.dumps(bench_linear_bwd(args, cfg, inp, up)), flush=True)
         return
 
     t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",

@@ -124,3 +124,29 @@ def test_sana_scaled_unsupported():
     with pytest.raises(hwa.HwaError) as e:
         _gpu_grads(inp, "sana_scaled", None, inputs.grad_output(inp.cfg))
     assert e.value.code == hwa.HWA_ERR_UNSUPPORTED
+
+
+def test_long_clip_132600tok_one_head():
+    # the full workload (24 heads, 85 frames of 1560 tokens) on the GPU; every
+    # gradient of head 5 against the oracle (the batch is 1, so that head's
+    # conv-tap gradients are the library's; the RMSNorm weight's sums over
+    # all heads and is covered by the smaller cases)
+    name = "long-clip-832x480-85f"
+    inp = inputs.make(name)
+    c = inp.cfg
+    h = 5
+    print(f"case {name}: all heads on the GPU, head {h} against the oracle", flush=True)
+    g_host = inputs.grad_output(c)
+    st_host = inputs.state_matrix(c)
+    got = _gpu_grads(inp, "vdn_solve", st_host, g_host)
+    ref = oracle.linear_branch_grad(
+        inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h), inp.beta[0, h],
+        inp.alpha[0, h], inp.f64("gate", 0, h), st_host[0, h], inp.conv_k[h], inp.conv_v[h],
+        inp.rms_weight, _f64(inp, g_host[0, h]), c["tokens_per_frame"], c["chunk"],
+        c["radius"], "vdn_solve", c["c"], 0.5, 1e-6)
+    errs = {n: oracle.rel_frobenius(got[n][0, h], ref["S_text" if n == "text_state" else n])
+            for n in PER_HEAD}
+    errs["conv_k"] = oracle.rel_frobenius(got["conv_k"][h], ref["conv_k"])
+    errs["conv_v"] = oracle.rel_frobenius(got["conv_v"][h], ref["conv_v"])
+    print("  rel err " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert max(errs.values()) <= TOL["bf16"], errs
