@@ -605,6 +605,404 @@ __global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------- MFMA variants
+// The per-token products of the readout and of the statistics are dense
+// contractions of a 16-token tile with the frame's d x d matrices, so for
+// d = 64 and 128 they run on fp32 MFMA (v_mfma_f32_16x16x4_f32: fp32 operands
+// and accumulation, the VALU kernels' precision). Operand layout of one MFMA:
+// A[i][k] from lane i + 16 k, B[k][j] from lane j + 16 k; lane j + 16 g holds
+// D[4 g + r][j] in register r. Wave w owns output channels 32 w .. 32 w + 31
+// (two 16-column blocks); per-token sums over the channels combine the 16
+// lanes of a row group and then the waves through LDS.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ f32x4_t mfma16(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int MT = 16;  // tokens per MFMA tile
+
+// sum over the 16 lanes of a row group
+__device__ __forceinline__ float row_sum16(float x) { return group_sum<16>(x); }
+
+}  // namespace
+
+// Statistics backward on MFMA: gk = (dA + dA^T) k^, bk = dB k^, bv = dB^T v^
+// for the 16 tokens of a tile; features staged in LDS by all threads.
+template <typename T, int D>
+__global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ conv_k, const float* __restrict__ conv_v,
+    const float* __restrict__ dA, const float* __restrict__ dB, float* __restrict__ dkc,
+    float* __restrict__ dvc, float* __restrict__ dbeta, int F, int S, int H, long long N) {
+  constexpr int NT = 2 * D;
+  constexpr int NW = D / 32;
+  constexpr int LD = D + 1;
+  constexpr int LT = D + 4;
+  constexpr int TPT = NT / MT;
+  constexpr int CPT = D / TPT;
+  __shared__ float g_lds[D * LD];
+  __shared__ float b_lds[D * LD];
+  __shared__ float kh_lds[MT * LT];
+  __shared__ float vh_lds[MT * LT];
+  __shared__ float sg_lds[MT * LT];
+  __shared__ float red[NW][MT][2];
+  __shared__ float tok_inv[MT];
+  __shared__ int tok_clamped[MT];
+  const int tid = threadIdx.x;
+  const int f = blockIdx.x, bh = blockIdx.y;
+  const int h = bh % H;
+  const long long fo = ((long long)bh * F + f) * D * D;
+  for (int x = tid; x < D * D; x += NT) {
+    const int i = x / D, j = x % D;
+    g_lds[i * LD + j] = dA[fo + x] + dA[fo + (long long)j * D + i];
+    b_lds[i * LD + j] = dB[fo + x];
+  }
+  const int tt = tid / TPT, ln = tid % TPT;
+  float wk[CPT][4], wv[CPT][4];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wk[c][j] = conv_k[((long long)h * D + ln + TPT * c) * 4 + j];
+      wv[c][j] = conv_v[((long long)h * D + ln + TPT * c) * 4 + j];
+    }
+  const int lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const long long base = (long long)bh * N * D;
+  __syncthreads();
+  for (int s0 = 0; s0 < S; s0 += MT) {
+    {  // features of the tile
+      const int s = s0 + tt;
+      const bool valid = s < S;
+      const long long n = (long long)f * S + s;
+      float kc[CPT], kh[CPT], vh[CPT];
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        float ak = 0.0f, av = 0.0f;
+        if (valid) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (s - j >= 0) {
+              const long long ix = base + (n - j) * D + ln + TPT * c;
+              ak = fmaf(wk[c][j], ld_io<T>(k, ix), ak);
+              av = fmaf(wv[c][j], ld_io<T>(v, ix), av);
+            }
+        }
+        kc[c] = ak;
+        kh[c] = silu_f(ak);
+        vh[c] = av;
+        ss = fmaf(kh[c], kh[c], ss);
+      }
+      ss = group_sum<TPT>(ss);
+      const float inv = inv_l2(ss);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int o = tt * LT + ln + TPT * c;
+        kh_lds[o] = kh[c] * inv;
+        vh_lds[o] = vh[c];
+        sg_lds[o] = silu_grad(kc[c]);
+      }
+      if (ln == 0) {
+        tok_inv[tt] = inv;
+        tok_clamped[tt] = ss <= 1e-24f;
+      }
+    }
+    __syncthreads();
+    f32x4_t gk[2], bk[2], bv[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) gk[b] = bk[b] = bv[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int m0 = 0; m0 < D; m0 += 4) {
+      const int m = m0 + lq;
+      const float ak = kh_lds[lr * LT + m];
+      const float av = vh_lds[lr * LT + m];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int j = 32 * w + 16 * b + lr;
+        gk[b] = mfma16(ak, g_lds[m * LD + j], gk[b]);  // (dA + dA^T) symmetric
+        bk[b] = mfma16(ak, b_lds[j * LD + m], bk[b]);  // dB[j][m]
+        bv[b] = mfma16(av, b_lds[m * LD + j], bv[b]);  // dB[m][j]
+      }
+    }
+    float db[4], dot[4], dkh[2][4], bt[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * lq + r;
+      const int s = s0 + tk;
+      bt[r] = s < S ? beta[(long long)bh * N + (long long)f * S + s] : 0.0f;
+      db[r] = dot[r] = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int o = tk * LT + 32 * w + 16 * b + lr;
+        const float khv = kh_lds[o], vhv = vh_lds[o];
+        db[r] = fmaf(khv, 0.5f * gk[b][r], db[r]);
+        db[r] = fmaf(vhv, bk[b][r], db[r]);
+        dkh[b][r] = bt[r] * (gk[b][r] + bv[b][r]);
+        dot[r] = fmaf(khv, dkh[b][r], dot[r]);
+      }
+      db[r] = row_sum16(db[r]);
+      dot[r] = row_sum16(dot[r]);
+      if (lr == 0) {
+        red[w][tk][0] = db[r];
+        red[w][tk][1] = dot[r];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * lq + r;
+      const int s = s0 + tk;
+      if (s >= S) continue;
+      float dbt = 0.0f, dt = 0.0f;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) {
+        dbt += red[x][tk][0];
+        dt += red[x][tk][1];
+      }
+      const long long n = (long long)f * S + s;
+      if (w == 0 && lr == 0) dbeta[(long long)bh * N + n] = dbt;
+      const float inv = tok_inv[tk];
+      const bool clamped = tok_clamped[tk] != 0;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int ch = 32 * w + 16 * b + lr;
+        const int o = tk * LT + ch;
+        const long long ix = base + n * D + ch;
+        dkc[ix] = l2_grad(dkh[b][r], kh_lds[o], inv, dt, clamped) * sg_lds[o];
+        dvc[ix] = bt[r] * bk[b][r];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Readout backward on MFMA, per 16-token tile: o = S_t q^ (A: q^ tile, B:
+// S_t^T), do from the RMSNorm and gate, dq^ = S_t^T do (A: do tile, B: S_t),
+// dS_t += do^T q^ (A: do^T, B: q^; wave w owns rows 32 w .. 32 w + 31 of
+// dS_t, all columns, in registers for the whole frame).
+template <typename T, int D>
+__global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
+    const T* __restrict__ q, const T* __restrict__ gate, const T* __restrict__ gout,
+    const float* __restrict__ alpha, const float* __restrict__ Pst,
+    const float* __restrict__ Qst, const float* __restrict__ rms_w, float eps,
+    T* __restrict__ dq, T* __restrict__ dgate, float* __restrict__ dSt,
+    float* __restrict__ dwpart, int F, int S, int chunk, int radius, long long N) {
+  constexpr int NT = 2 * D;
+  constexpr int NW = D / 32;
+  constexpr int NB = D / 16;  // 16-column blocks of dS_t
+  constexpr int LD = D + 1;
+  constexpr int LT = D + 16;
+  constexpr int TPT = NT / MT;
+  constexpr int CPT = D / TPT;
+  __shared__ float st_lds[D * LD];
+  __shared__ float qh_lds[MT * LT];
+  __shared__ float do_lds[MT * LT];
+  __shared__ float sg_lds[MT * LT];
+  __shared__ float red[3][NW][MT];
+  __shared__ float tok_inv[MT];
+  __shared__ int tok_clamped[MT];
+  __shared__ float dec[2][D];
+
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const int bh = blockIdx.y;
+  int lo, hi;
+  window_of(t, F, chunk, radius, lo, hi);
+  for (int j = tid; j < D; j += NT) {
+    const float* al = alpha + (long long)bh * F * D + j;
+    float a = 1.0f, b = 1.0f;
+    for (int x = lo; x <= t; ++x) a *= al[(long long)x * D];
+    for (int x = t; x <= hi; ++x) b *= al[(long long)x * D];
+    dec[0][j] = a;
+    dec[1][j] = b;
+  }
+  __syncthreads();
+  const float* Pm = Pst + ((long long)bh * (F + 1) + lo) * D * D;      // P_{lo-1}
+  const float* Qm = Qst + ((long long)bh * (F + 1) + hi + 1) * D * D;  // Q_{hi+1}
+  for (int x = tid; x < D * D; x += NT) {
+    const int i = x / D, j = x % D;
+    st_lds[i * LD + j] = fmaf(Pm[x], dec[0][j], Qm[x] * dec[1][j]);
+  }
+  const int tt = tid / TPT, ln = tid % TPT;
+  const int lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  float wr[2], dw[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    wr[b] = rms_w ? rms_w[32 * w + 16 * b + lr] : 1.0f;
+    dw[b] = 0.0f;
+  }
+  f32x4_t acc[2][NB];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) acc[bi][bj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const long long base = (long long)bh * N * D;
+  __syncthreads();
+
+  for (int s0 = 0; s0 < S; s0 += MT) {
+    {  // features of the tile
+      const int s = s0 + tt;
+      const bool valid = s < S;
+      const long long row = base + ((long long)t * S + s) * D + ln;
+      float qv[CPT], u[CPT];
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        qv[c] = valid ? ld_io<T>(q, row + TPT * c) : 0.0f;
+        u[c] = silu_f(qv[c]);
+        ss = fmaf(u[c], u[c], ss);
+      }
+      ss = group_sum<TPT>(ss);
+      const float inv = inv_l2(ss);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int o = tt * LT + ln + TPT * c;
+        qh_lds[o] = u[c] * inv;
+        sg_lds[o] = silu_grad(qv[c]);
+      }
+      if (ln == 0) {
+        tok_inv[tt] = inv;
+        tok_clamped[tt] = ss <= 1e-24f;
+      }
+    }
+    __syncthreads();
+    // o = S_t q^
+    f32x4_t o[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) o[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int m0 = 0; m0 < D; m0 += 4) {
+      const int m = m0 + lq;
+      const float a = qh_lds[lr * LT + m];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) o[b] = mfma16(a, st_lds[(32 * w + 16 * b + lr) * LD + m], o[b]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float ms = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) ms = fmaf(o[b][r], o[b][r], ms);
+      ms = row_sum16(ms);
+      if (lr == 0) red[0][w][4 * lq + r] = ms;
+    }
+    __syncthreads();
+    float rinv[4], z[2][4], dz[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * lq + r;
+      const int s = s0 + tk;
+      const bool valid = s < S;
+      float ms = 0.0f;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) ms += red[0][x][tk];
+      rinv[r] = 1.0f / sqrtf(ms / D + eps);
+      float dzz = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const long long ix = base + ((long long)t * S + s) * D + 32 * w + 16 * b + lr;
+        const float gt = valid ? ld_io<T>(gate, ix) : 0.0f;
+        const float go = valid ? ld_io<T>(gout, ix) : 0.0f;
+        const float sg = sigmoid_f(gt);
+        z[b][r] = o[b][r] * rinv[r];
+        if (valid) st_io<T>(dgate, ix, go * z[b][r] * wr[b] * sg * (1.0f - sg));
+        dw[b] = fmaf(go * sg, z[b][r], dw[b]);
+        dz[b][r] = go * wr[b] * sg;
+        dzz = fmaf(dz[b][r], z[b][r], dzz);
+      }
+      dzz = row_sum16(dzz);
+      if (lr == 0) red[1][w][tk] = dzz;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * lq + r;
+      float mz = 0.0f;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) mz += red[1][x][tk];
+      mz /= D;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        do_lds[tk * LT + 32 * w + 16 * b + lr] = rinv[r] * (dz[b][r] - z[b][r] * mz);
+    }
+    __syncthreads();
+    // dq^ = S_t^T do
+    f32x4_t g[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) g[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int i0 = 0; i0 < D; i0 += 4) {
+      const int i = i0 + lq;
+      const float a = do_lds[lr * LT + i];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) g[b] = mfma16(a, st_lds[i * LD + 32 * w + 16 * b + lr], g[b]);
+    }
+    // dS_t += do^T q^ over the tile's tokens
+#pragma unroll
+    for (int k0 = 0; k0 < MT; k0 += 4) {
+      const int tk = k0 + lq;
+      float a[2], bq[NB];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) a[bi] = do_lds[tk * LT + 32 * w + 16 * bi + lr];
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj) bq[bj] = qh_lds[tk * LT + 16 * bj + lr];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) acc[bi][bj] = mfma16(a[bi], bq[bj], acc[bi][bj]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * lq + r;
+      float dt = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) dt = fmaf(qh_lds[tk * LT + 32 * w + 16 * b + lr], g[b][r], dt);
+      dt = row_sum16(dt);
+      if (lr == 0) red[2][w][tk] = dt;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * lq + r;
+      const int s = s0 + tk;
+      if (s >= S) continue;
+      float dt = 0.0f;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) dt += red[2][x][tk];
+      const float inv = tok_inv[tk];
+      const bool clamped = tok_clamped[tk] != 0;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int ch = 32 * w + 16 * b + lr;
+        const int o2 = tk * LT + ch;
+        st_io<T>(dq, base + ((long long)t * S + s) * D + ch,
+                 l2_grad(g[b][r], qh_lds[o2], inv, dt, clamped) * sg_lds[o2]);
+      }
+    }
+    __syncthreads();
+  }
+  float* ds = dSt + ((long long)bh * F + t) * D * D;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ds[(32 * w + 16 * bi + 4 * lq + r) * D + 16 * bj + lr] = acc[bi][bj][r];
+  // dw partial of this frame: the four row groups of each column
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float x = dw[b];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (lq == 0) dwpart[((long long)bh * F + t) * D + 32 * w + 16 * b + lr] = x;
+  }
+}
+
 // ---------------------------------------------------------------- dalpha
 // dalpha_f = the scans' part + the gather's: a_t and b_t are products over
 // frames of the window, so frame f's factor gets da_t (db_t) times the
@@ -726,7 +1124,24 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
                        (const float*)a.q, (const float*)a.gate, (const float*)a.d_o,      \
                        a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (float*)a.dq,               \
                        (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N);
-      LB_SWITCH_D(RB)
+#define RBM(DD)                                                                          \
+  if (bf)                                                                                \
+    hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<bf16_t, DD>), grid, dim3(2 * DD), 0, st, \
+                       (const bf16_t*)a.q, (const bf16_t*)a.gate, (const bf16_t*)a.d_o,   \
+                       a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (bf16_t*)a.dq,              \
+                       (bf16_t*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N); \
+  else                                                                                   \
+    hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<float, DD>), grid, dim3(2 * DD), 0, st, \
+                       (const float*)a.q, (const float*)a.gate, (const float*)a.d_o,      \
+                       a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (float*)a.dq,               \
+                       (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N);
+      switch (g.d) {
+        case 16: RB(16); break;
+        case 32: RB(32); break;
+        case 64: RBM(64); break;
+        default: RBM(128); break;
+      }
+#undef RBM
 #undef RB
       break;
     }
@@ -770,7 +1185,22 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
     hipLaunchKernelGGL((lin_stats_bwd_kernel<float, DD>), grid, dim3(256), 0, st,           \
                        (const float*)a.k, (const float*)a.v, a.beta, a.conv_k, a.conv_v,     \
                        a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);
-      LB_SWITCH_D(SB)
+#define SBM(DD)                                                                             \
+  if (bf)                                                                                   \
+    hipLaunchKernelGGL((lin_stats_bwd_mfma_kernel<bf16_t, DD>), grid, dim3(2 * DD), 0, st,  \
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, a.beta, a.conv_k, a.conv_v,   \
+                       a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);               \
+  else                                                                                      \
+    hipLaunchKernelGGL((lin_stats_bwd_mfma_kernel<float, DD>), grid, dim3(2 * DD), 0, st,   \
+                       (const float*)a.k, (const float*)a.v, a.beta, a.conv_k, a.conv_v,     \
+                       a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);
+      switch (g.d) {
+        case 16: SB(16); break;
+        case 32: SB(32); break;
+        case 64: SBM(64); break;
+        default: SBM(128); break;
+      }
+#undef SBM
 #undef SB
       break;
     }
