@@ -367,7 +367,11 @@ def bench_linear_bwd(args, cfg, inp, up):
         kernels[name] = rec
     dom = max(("readout", "stats"), key=lambda n: stage[n])
     achieved = work[dom]["flops"] / (stage[dom] / 1000.0) / 1e12
-    roofline = {"kernel": f"lin_{dom}_bwd_kernel", "bound": "alu",
+    # d = 64, 128: fp32 MFMA kernels (peak = the fp32 MFMA rate, the same
+    # figure as the fp32 vector rate); d = 16, 32: fp32 VALU kernels
+    mfma = d in (64, 128)
+    roofline = {"kernel": f"lin_{dom}_bwd{'_mfma' if mfma else ''}_kernel",
+                "bound": "mfma" if mfma else "alu",
                 "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None,
                 "algorithmic_flops_per_launch": work[dom]["flops"]}

@@ -470,6 +470,7 @@ hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const flo
   if (!isfinite(p->c) || !isfinite(p->text_scale) || !(p->rms_eps > 0.0f) ||
       !isfinite(p->rms_eps))
     return HWA_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)HWA_FLAG_ACCUMULATE) return HWA_ERR_INVALID_ARG;
   const size_t va = p->dtype == HWA_BF16 ? 16 : 4;
   const void* io_ptrs[] = {q, k, v, gate, d_o, dq, dk, dv, dgate};
   for (const void* x : io_ptrs)
@@ -515,6 +516,7 @@ hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const flo
   a.beta = beta; a.alpha = alpha; a.text_state = text_state;
   a.conv_k = p->conv_k; a.conv_v = p->conv_v; a.rms_w = p->rms_weight;
   a.rule = rule; a.c = p->c; a.text_scale = p->text_scale; a.eps = p->rms_eps;
+  a.acc = (p->flags & HWA_FLAG_ACCUMULATE) ? 1 : 0;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dgate = dgate;
   a.dbeta = dbeta; a.dalpha = dalpha; a.dtext = dtext_state;
   a.dconv_k = dconv_k; a.dconv_v = dconv_v; a.drms = drms_weight;

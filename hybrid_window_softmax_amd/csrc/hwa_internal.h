@@ -182,6 +182,7 @@ struct LinBwdArgs {
   const void *q, *k, *v, *gate, *d_o;
   const float *beta, *alpha, *text_state, *conv_k, *conv_v, *rms_w;
   int rule;
+  int acc;  // add dq, dk, dv to the buffers' contents
   float c, text_scale, eps;
   void *dq, *dk, *dv, *dgate;
   float *dbeta, *dalpha, *dtext, *dconv_k, *dconv_v, *drms;

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void lin_readout_bwd_kernel(
     const float* __restrict__ alpha, const float* __restrict__ Pst,
     const float* __restrict__ Qst, const float* __restrict__ rms_w, float eps,
     T* __restrict__ dq, T* __restrict__ dgate, float* __restrict__ dSt,
-    float* __restrict__ dwpart, int F, int S, int chunk, int radius, long long N) {
+    float* __restrict__ dwpart, int F, int S, int chunk, int radius, long long N, int accum) {
   constexpr int LD = D + 1;
   constexpr int TPT = 256 / LB_TT;
   constexpr int CPT = D / TPT;
@@ -201,7 +201,8 @@ __global__ __launch_bounds__(256) void lin_readout_bwd_kernel(
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
         st_io<T>(dq, row + TPT * c,
-                 l2_grad(dqh[c], qh[c], inv, dot, clamped) * silu_grad(qv[c]));
+                 l2_grad(dqh[c], qh[c], inv, dot, clamped) * silu_grad(qv[c]) +
+                     (accum ? ld_io<T>(dq, row + TPT * c) : 0.0f));
     }
     const int ntok = min(LB_TT, S - s0);
     for (int x = 0; x < ntok; ++x) {
@@ -558,7 +559,7 @@ __global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ conv_k,
     const float* __restrict__ conv_v, const float* __restrict__ dkc,
     const float* __restrict__ dvc, T* __restrict__ dk, T* __restrict__ dv,
-    float* __restrict__ cpart, int F, int S, int H, long long N) {
+    float* __restrict__ cpart, int F, int S, int H, long long N, int accum) {
   constexpr int G = 256 / D;
   __shared__ float red[G][D][8];
   const int tid = threadIdx.x;
@@ -587,6 +588,10 @@ __global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
         pk[j] = fmaf(gk, ld_io<T>(k, ix - (long long)j * D), pk[j]);
         pv[j] = fmaf(gv, ld_io<T>(v, ix - (long long)j * D), pv[j]);
       }
+    }
+    if (accum) {
+      ak += ld_io<T>(dk, ix);
+      av += ld_io<T>(dv, ix);
     }
     st_io<T>(dk, ix, ak);
     st_io<T>(dv, ix, av);
@@ -790,7 +795,7 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
     const float* __restrict__ alpha, const float* __restrict__ Pst,
     const float* __restrict__ Qst, const float* __restrict__ rms_w, float eps,
     T* __restrict__ dq, T* __restrict__ dgate, float* __restrict__ dSt,
-    float* __restrict__ dwpart, int F, int S, int chunk, int radius, long long N) {
+    float* __restrict__ dwpart, int F, int S, int chunk, int radius, long long N, int accum) {
   constexpr int NT = 2 * D;
   constexpr int NW = D / 32;
   constexpr int NB = D / 16;  // 16-column blocks of dS_t
@@ -979,8 +984,10 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
       for (int b = 0; b < 2; ++b) {
         const int ch = 32 * w + 16 * b + lr;
         const int o2 = tk * LT + ch;
-        st_io<T>(dq, base + ((long long)t * S + s) * D + ch,
-                 l2_grad(g[b][r], qh_lds[o2], inv, dt, clamped) * sg_lds[o2]);
+        const long long ix = base + ((long long)t * S + s) * D + ch;
+        st_io<T>(dq, ix,
+                 l2_grad(g[b][r], qh_lds[o2], inv, dt, clamped) * sg_lds[o2] +
+                     (accum ? ld_io<T>(dq, ix) : 0.0f));
       }
     }
     __syncthreads();
@@ -1118,23 +1125,23 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
     hipLaunchKernelGGL((lin_readout_bwd_kernel<bf16_t, DD>), grid, dim3(256), 0, st,      \
                        (const bf16_t*)a.q, (const bf16_t*)a.gate, (const bf16_t*)a.d_o,   \
                        a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (bf16_t*)a.dq,              \
-                       (bf16_t*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N); \
+                       (bf16_t*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N, a.acc); \
   else                                                                                   \
     hipLaunchKernelGGL((lin_readout_bwd_kernel<float, DD>), grid, dim3(256), 0, st,       \
                        (const float*)a.q, (const float*)a.gate, (const float*)a.d_o,      \
                        a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (float*)a.dq,               \
-                       (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N);
+                       (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N, a.acc);
 #define RBM(DD)                                                                          \
   if (bf)                                                                                \
     hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<bf16_t, DD>), grid, dim3(2 * DD), 0, st, \
                        (const bf16_t*)a.q, (const bf16_t*)a.gate, (const bf16_t*)a.d_o,   \
                        a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (bf16_t*)a.dq,              \
-                       (bf16_t*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N); \
+                       (bf16_t*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N, a.acc); \
   else                                                                                   \
     hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<float, DD>), grid, dim3(2 * DD), 0, st, \
                        (const float*)a.q, (const float*)a.gate, (const float*)a.d_o,      \
                        a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (float*)a.dq,               \
-                       (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N);
+                       (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N, a.acc);
       switch (g.d) {
         case 16: RB(16); break;
         case 32: RB(32); break;
@@ -1211,11 +1218,11 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
   if (bf)                                                                                   \
     hipLaunchKernelGGL((lin_conv_bwd_kernel<bf16_t, DD>), grid, dim3(256), 0, st,           \
                        (const bf16_t*)a.k, (const bf16_t*)a.v, a.conv_k, a.conv_v, a.dkc,    \
-                       a.dvc, (bf16_t*)a.dk, (bf16_t*)a.dv, a.cpart, g.F, g.S, g.H, g.N);   \
+                       a.dvc, (bf16_t*)a.dk, (bf16_t*)a.dv, a.cpart, g.F, g.S, g.H, g.N, a.acc);   \
   else                                                                                      \
     hipLaunchKernelGGL((lin_conv_bwd_kernel<float, DD>), grid, dim3(256), 0, st,            \
                        (const float*)a.k, (const float*)a.v, a.conv_k, a.conv_v, a.dkc,     \
-                       a.dvc, (float*)a.dk, (float*)a.dv, a.cpart, g.F, g.S, g.H, g.N);
+                       a.dvc, (float*)a.dk, (float*)a.dv, a.cpart, g.F, g.S, g.H, g.N, a.acc);
         LB_SWITCH_D(CB)
 #undef CB
       }

@@ -21,6 +21,7 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 FLAG_SOFTMAX_ONLY = 1
 FLAG_LINEAR_ONLY = 2
 FLAG_KEEP_INTERMEDIATES = 4
+FLAG_ACCUMULATE = 8
 NUM_STAGE_EVENTS = 9
 STAGES = ("window", "stats", "inverse", "scan", "decay+state", "vtranspose", "softmax",
           "readout")
@@ -280,14 +281,15 @@ def linear_bwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, d_o, fram
                tokens_per_frame: int, chunk: int = 5, radius: int = 1, rule="vdn_solve",
                c: float = 0.5, text_scale: float = 0.5, rms_eps: float = 1e-6,
                rms_weight=None, grads=None, workspace=None, stream=None,
-               stage_events=None):
+               stage_events=None, accumulate=False):
     """Gradients of the linear branch (hwa_linear_bwd) for upstream gradient
     d_o, as a dict keyed by LIN_GRADS (``text_state`` and ``rms_weight``
     always present: at the zero state / for unit weights when not given).
 
     Tensors as for hybrid_attn_fwd, d_o like q. ``grads``: optional dict of
     preallocated outputs. ``stage_events``: optional ctypes array of
-    NUM_LIN_BWD_STAGE_EVENTS hipEvent_t. Returns (grads, workspace).
+    NUM_LIN_BWD_STAGE_EVENTS hipEvent_t. ``accumulate``: add dq, dk, dv to
+    the tensors given in ``grads`` (FLAG_ACCUMULATE). Returns (grads, workspace).
     """
     B, H, N, d = q.shape
     F = frames
@@ -300,7 +302,10 @@ def linear_bwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, d_o, fram
     _check(conv_k, "conv_k", torch.float32, (H, d, 4), dev)
     _check(conv_v, "conv_v", torch.float32, (H, d, 4), dev)
     _check(rms_weight, "rms_weight", torch.float32, (d,), dev)
-    p = make_params(B, H, d, q.dtype, c, text_scale, rms_eps, conv_k, conv_v, rms_weight)
+    p = make_params(B, H, d, q.dtype, c, text_scale, rms_eps, conv_k, conv_v, rms_weight,
+                    flags=FLAG_ACCUMULATE if accumulate else 0)
+    if accumulate and any((grads or {}).get(n) is None for n in ("q", "k", "v")):
+        raise ValueError("accumulate needs dq, dk and dv in grads")
     need = int(lib().hwa_linear_bwd_workspace_bytes(frames, tokens_per_frame, chunk,
                                                     ctypes.byref(p)))
     if workspace is None:
@@ -355,6 +360,56 @@ class WindowedSoftmaxAttention(torch.autograd.Function):
         q, k, v, o, lse = ctx.saved_tensors
         dq, dk, dv, _ = softmax_bwd(q, k, v, o, lse, d_o.contiguous(), *ctx.geom)
         return dq, dk, dv, None, None, None, None
+
+
+class HybridAttention(torch.autograd.Function):
+    """out = o_sm + y of the hybrid attention as an autograd function: the
+    forward is hybrid_attn_fwd (also saving o_sm and its log-sum-exp), the
+    backward is hwa_softmax_bwd for dq, dk, dv of the softmax branch and then
+    hwa_linear_bwd with FLAG_ACCUMULATE, which adds the linear branch's dq,
+    dk, dv and writes the gradients of every other input. Marshalling only."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, rms_weight,
+                frames, tokens_per_frame, chunk, radius, rule, c, text_scale, rms_eps):
+        B, H, N, d = q.shape
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        o_sm = torch.empty_like(q)
+        out, _ = hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
+                                 frames, tokens_per_frame, chunk, radius, rule, c, text_scale,
+                                 rms_eps, rms_weight, softmax_lse=lse, softmax_out=o_sm)
+        ctx.save_for_backward(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
+                              rms_weight, o_sm, lse)
+        ctx.geom = (frames, tokens_per_frame, chunk, radius, rule, c, text_scale, rms_eps)
+        ctx.has_text = text_state is not None
+        ctx.has_w = rms_weight is not None
+        return out
+
+    @staticmethod
+    def backward(ctx, d_out):
+        (q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, rms_weight, o_sm,
+         lse) = ctx.saved_tensors
+        F, S, chunk, radius, rule, c, text_scale, rms_eps = ctx.geom
+        d_out = d_out.contiguous()
+        dq, dk, dv, _ = softmax_bwd(q, k, v, o_sm, lse, d_out, F, S, chunk, radius)
+        g, _ = linear_bwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, d_out, F, S,
+                          chunk, radius, rule, c, text_scale, rms_eps, rms_weight,
+                          grads=dict(q=dq, k=dk, v=dv), accumulate=True)
+        return (g["q"], g["k"], g["v"], g["beta"], g["alpha"], g["gate"],
+                g["text_state"] if ctx.has_text else None, g["conv_k"], g["conv_v"],
+                g["rms_weight"] if ctx.has_w else None,
+                None, None, None, None, None, None, None, None)
+
+
+def hybrid_attention(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, frames: int,
+                     tokens_per_frame: int, chunk: int = 5, radius: int = 1,
+                     rule="vdn_solve", c: float = 0.5, text_scale: float = 0.5,
+                     rms_eps: float = 1e-6, rms_weight=None):
+    """out = o_sm + y, differentiable in every tensor input (the update rules
+    vdn_solve and vdn_scaled; no q_rope / k_rope)."""
+    return HybridAttention.apply(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
+                                 rms_weight, frames, tokens_per_frame, chunk, radius, rule, c,
+                                 text_scale, rms_eps)
 
 
 def windowed_softmax_attention(q, k, v, frames: int, tokens_per_frame: int, chunk: int = 5,

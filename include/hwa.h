@@ -66,10 +66,13 @@ typedef enum { HWA_F32 = 0, HWA_BF16 = 1 } hwa_dtype;
 enum {
   HWA_FLAG_SOFTMAX_ONLY = 1,      /* out = o_sm (linear branch skipped)      */
   HWA_FLAG_LINEAR_ONLY = 2,       /* out = y (softmax branch skipped)        */
-  HWA_FLAG_KEEP_INTERMEDIATES = 4 /* accepted for compatibility: the         */
-                                  /* intermediates are always left in the   */
-                                  /* workspace at hwa_workspace_layout's     */
-                                  /* offsets                                 */
+  HWA_FLAG_KEEP_INTERMEDIATES = 4, /* accepted for compatibility: the        */
+                                   /* intermediates are always left in the  */
+                                   /* workspace at hwa_workspace_layout's    */
+                                   /* offsets                                */
+  HWA_FLAG_ACCUMULATE = 8          /* hwa_linear_bwd only: add dq, dk, dv to */
+                                   /* what those buffers hold (the softmax   */
+                                   /* branch's gradient, for out = o_sm + y) */
 };
 
 typedef struct {
@@ -290,6 +293,10 @@ size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
  *       and every frame's scan states, [2] after the readout, [3] after the
  *       gather, adjoint scans and per-frame gradients, [4] after the
  *       statistics and features, [5] after the convs and parameter sums)
+ * p->flags: 0, or HWA_FLAG_ACCUMULATE to add dq, dk, dv to the contents of
+ * those buffers (one fp32 sum, then the rounding to dtype) -- with
+ * hwa_softmax_bwd's output there, the sum is the gradient of out = o_sm + y
+ * with respect to q, k and v (when the forward used no q_rope / k_rope).
  * Outputs must not overlap each other, an input or the workspace. All
  * arithmetic is fp32. Returns HWA_OK, or an error status before anything is
  * enqueued.

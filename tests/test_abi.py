@@ -249,3 +249,69 @@ def test_softmax_bwd_workspace_bytes():
         need = 2 * 6 * Np * 4
         assert need <= n <= need + 4 * 256
     assert L.hwa_softmax_bwd_workspace_bytes(0, 100, 5, ctypes.byref(p)) == 0
+
+
+_LIN = ("q", "k", "v", "beta", "alpha", "gate", "text", "g", "dq", "dk", "dv", "dbeta",
+        "dalpha", "dgate", "dtext", "dconv_k", "dconv_v", "drms")
+
+
+def _lin_call(p, F=10, S=16, chunk=5, radius=1, rule=0, **ptrs):
+    d = {n: BASE + ((13 + i) << 36) for i, n in enumerate(_LIN)}
+    d.update(ptrs)
+    vp = ctypes.c_void_p
+    a = [vp(d[n]) for n in _LIN]
+    return hwa.lib().hwa_linear_bwd(*a[:8], F, S, chunk, radius, rule, *a[8:], None,
+                                    ctypes.byref(p))
+
+
+def _lin_ws(p, F=10, S=16, chunk=5, extra=0):
+    n = hwa.lib().hwa_linear_bwd_workspace_bytes(F, S, chunk, ctypes.byref(p))
+    assert n > 0
+    p.workspace = BASE + (10 << 36)
+    p.workspace_bytes = n + extra
+    return p
+
+
+@no_gpu
+def test_linear_bwd_validation():
+    E = hwa
+    p = _lin_ws(_params())
+    for name in _LIN:
+        if name in ("text", "dtext", "drms"):  # optional
+            continue
+        assert _lin_call(p, **{name: None}) == E.HWA_ERR_INVALID_ARG, name
+    assert _lin_call(_lin_ws(_params(conv_k=None))) == E.HWA_ERR_INVALID_ARG
+    assert _lin_call(p, rule=1) == E.HWA_ERR_UNSUPPORTED                 # sana_scaled
+    assert _lin_call(p, rule=3) == E.HWA_ERR_INVALID_ARG
+    assert _lin_call(p, F=0) == E.HWA_ERR_INVALID_ARG
+    assert _lin_call(p, radius=-1) == E.HWA_ERR_INVALID_ARG
+    assert _lin_call(p, q=BASE + 8) == E.HWA_ERR_INVALID_ARG              # misaligned bf16
+    assert _lin_call(p, dbeta=BASE + 2) == E.HWA_ERR_INVALID_ARG          # misaligned fp32
+    assert _lin_call(p, dk=BASE + (21 << 36)) == E.HWA_ERR_INVALID_ARG    # dk aliases dq
+    assert _lin_call(p, dbeta=BASE + (16 << 36)) == E.HWA_ERR_INVALID_ARG  # dbeta aliases beta
+    assert _lin_call(p, dalpha=p.workspace) == E.HWA_ERR_INVALID_ARG      # in the workspace
+    assert _lin_call(p, drms=BASE + (28 << 36)) == E.HWA_ERR_INVALID_ARG  # drms aliases dconv_k
+    assert _lin_call(_lin_ws(_params(), extra=-256)) == E.HWA_ERR_WORKSPACE
+    assert _lin_call(_params()) == E.HWA_ERR_WORKSPACE
+    assert _lin_call(_lin_ws(_params(rms_eps=0.0))) == E.HWA_ERR_INVALID_ARG
+    assert _lin_call(_lin_ws(_params(flags=1))) == E.HWA_ERR_INVALID_ARG  # forward-only flag
+    assert _lin_call(_params(head_dim=16, dtype=1)) == E.HWA_ERR_UNSUPPORTED
+
+
+def test_linear_bwd_workspace_bytes():
+    L = hwa.lib()
+    B, H, d, F, S, chunk = 2, 3, 64, 12, 100, 5
+    nch = (F + chunk - 1) // chunk
+    bh, dd, N = B * H, d * d * 4, F * S
+    for dt in (0, 1):
+        p = hwa.make_params(B, H, d, dt)
+        n = L.hwa_linear_bwd_workspace_bytes(F, S, chunk, ctypes.byref(p))
+        # statistics, inverses, dS_t, the suffix adjoint (F each), both scans'
+        # states (F + 1 each), their exponents, the bank gradients, the
+        # adjoints of s0, per-frame vectors (gather 2, dalpha, dw), the fp32
+        # gradients before the convs, the per-frame tap gradients
+        need = (bh * (5 * F + 2 * (F + 1)) * dd + 2 * bh * (F + 1) * d * 4
+                + 2 * bh * (nch + 1) * dd + 2 * bh * dd + 4 * bh * F * d * 4
+                + 2 * bh * N * d * 4 + bh * F * d * 8 * 4)
+        assert need <= n <= need + 16 * 256
+    assert L.hwa_linear_bwd_workspace_bytes(0, 100, 5, ctypes.byref(p)) == 0

@@ -150,3 +150,57 @@ def test_long_clip_132600tok_one_head():
     errs["conv_v"] = oracle.rel_frobenius(got["conv_v"][h], ref["conv_v"])
     print("  rel err " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()), flush=True)
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("cfg,rule", [
+    ("small-bf16-text", "vdn_solve"),
+    (inputs.tiny_config(frames=17, head_dim=32, tokens_per_frame=37, text_tokens=0, seed=402),
+     "vdn_scaled"),
+])
+def test_hybrid_autograd(cfg, rule):
+    # hwa.hybrid_attention through torch autograd: out.backward(g) runs
+    # hwa_softmax_bwd, then hwa_linear_bwd accumulating into dq, dk, dv; every
+    # gradient against the oracle (softmax-branch gradient + linear-branch
+    # gradient for q, k, v)
+    inp = inputs.make(cfg, random_rms_weight=True)
+    c = inp.cfg
+    bf = c["dtype"] == "bf16"
+    print(f"case {c['name']} {c['dtype']}: hybrid attention autograd, {rule}", flush=True)
+    t = {n: to_dev(getattr(inp, n), bf).requires_grad_() for n in
+         ("q", "k", "v", "gate", "beta", "alpha", "conv_k", "conv_v", "rms_weight")}
+    st_host = inputs.state_matrix(c)
+    text = to_dev(st_host, False).requires_grad_()
+    g_host = inputs.grad_output(c)
+    F, S, ch, r = c["frames"], c["tokens_per_frame"], c["chunk"], c["radius"]
+    out = hwa.hybrid_attention(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"], text,
+                               t["conv_k"], t["conv_v"], F, S, ch, r, rule, c["c"], 0.5, 1e-6,
+                               t["rms_weight"])
+    out.backward(to_dev(g_host, bf))
+    torch.cuda.synchronize()
+    got = {n: x.grad.float().cpu().numpy().astype(np.float64) for n, x in t.items()}
+    got["text_state"] = text.grad.cpu().numpy().astype(np.float64)
+    lo, hi = oracle.window_bounds(F, ch, r)
+    B, H, d = c["batch"], c["heads"], c["head_dim"]
+    worst = dict.fromkeys(PER_HEAD, 0.0)
+    conv_k, conv_v, w = np.zeros((H, d, 4)), np.zeros((H, d, 4)), np.zeros(d)
+    for b in range(B):
+        for h in range(H):
+            q, k, v = (inp.f64(n, b, h) for n in ("q", "k", "v"))
+            g = _f64(inp, g_host[b, h])
+            ref = oracle.linear_branch_grad(
+                q, k, v, inp.beta[b, h], inp.alpha[b, h], inp.f64("gate", b, h), st_host[b, h],
+                inp.conv_k[h], inp.conv_v[h], inp.rms_weight, g, S, ch, r, rule, c["c"], 0.5,
+                1e-6)
+            sq, sk, sv = oracle.softmax_branch_grad(q, k, v, g, S, lo, hi)
+            ref["q"], ref["k"], ref["v"] = ref["q"] + sq, ref["k"] + sk, ref["v"] + sv
+            for n in PER_HEAD:
+                rr = ref["S_text" if n == "text_state" else n]
+                worst[n] = max(worst[n], oracle.rel_frobenius(got[n][b, h], rr))
+            conv_k[h] += ref["conv_k"]
+            conv_v[h] += ref["conv_v"]
+            w += ref["w"]
+    worst["conv_k"] = oracle.rel_frobenius(got["conv_k"], conv_k)
+    worst["conv_v"] = oracle.rel_frobenius(got["conv_v"], conv_v)
+    worst["rms_weight"] = oracle.rel_frobenius(got["rms_weight"], w)
+    print("  rel err " + " ".join(f"d{n} {e:.2e}" for n, e in worst.items()), flush=True)
+    assert max(worst.values()) <= TOL[c["dtype"]], worst

@@ -107,3 +107,52 @@ def test_softmax_bwd_repeat_and_graph_replay_bit_exact(name):
         _say(f"  replay {rep}: {mism} elements differ from the eager call")
         assert mism == 0
     del graph
+
+
+@pytest.mark.parametrize("name", ["small-bf16-text", "tiny-f32"])
+def test_linear_bwd_graph_replay_bit_exact(name):
+    # hwa_linear_bwd enqueues only kernels (no memsets, no atomics): a captured
+    # call replays to the eager result bit for bit
+    from hybrid_window_softmax_amd import hwa
+    from harness import to_dev
+    cfg = inputs.WORKLOADS[name]
+    _say(f"case {name}: linear backward, eager call, then a graph replayed three times")
+    inp = inputs.make(cfg)
+    bf = cfg["dtype"] == "bf16"
+    t = {n: to_dev(getattr(inp, n), bf) for n in
+         ("q", "k", "v", "gate", "beta", "alpha", "conv_k", "conv_v", "rms_weight")}
+    g = to_dev(inputs.grad_output(cfg), bf)
+    st = to_dev(inputs.state_matrix(cfg), False)
+    F, S, ch, r = cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"], cfg["radius"]
+
+    def call(grads=None, ws=None):
+        return hwa.linear_bwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"], st,
+                              t["conv_k"], t["conv_v"], g, F, S, ch, r, "vdn_solve", cfg["c"],
+                              0.5, 1e-6, t["rms_weight"], grads=grads, workspace=ws)
+
+    ref, ws = call()
+    ref = {n: x.clone() for n, x in ref.items()}
+    outs = {n: torch.empty_like(x) for n, x in ref.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(outs, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(outs, ws)
+
+    def bits(x):
+        return x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+
+    for rep in range(3):
+        for x in outs.values():
+            x.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        mism = sum(int((bits(outs[n]) != bits(ref[n])).sum()) for n in ref)
+        _say(f"  replay {rep}: {mism} elements differ from the eager call")
+        assert mism == 0
+    del graph
