@@ -632,6 +632,29 @@ constexpr int MT = 16;  // tokens per MFMA tile
 // sum over the 16 lanes of a row group
 __device__ __forceinline__ float row_sum16(float x) { return group_sum<16>(x); }
 
+// Eight consecutive channels of one token row: one 16-byte load for bf16
+// (rows and the channel offset are 16-byte aligned), eight loads for fp32.
+template <typename T>
+struct Row8;
+template <>
+struct Row8<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *(const uint4*)p; }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <>
+struct Row8<float> {
+  float x[8];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = p[i];
+  }
+  __device__ __forceinline__ float get(int i) const { return x[i]; }
+};
+
 }  // namespace
 
 // Statistics backward on MFMA: gk = (dA + dA^T) k^, bk = dB k^, bv = dB^T v^
@@ -646,15 +669,16 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
   constexpr int NW = D / 32;
   constexpr int LD = D + 1;
   constexpr int LT = D + 4;
-  constexpr int TPT = NT / MT;
-  constexpr int CPT = D / TPT;
+  constexpr int TPT = NT / MT;  // threads per token: 8 consecutive channels each
+  static_assert(TPT * 8 == D, "feature mapping");
   __shared__ float g_lds[D * LD];
   __shared__ float b_lds[D * LD];
-  __shared__ float kh_lds[MT * LT];
-  __shared__ float vh_lds[MT * LT];
-  __shared__ float sg_lds[MT * LT];
+  __shared__ __attribute__((aligned(16))) float kh_lds[MT * LT];
+  __shared__ __attribute__((aligned(16))) float vh_lds[MT * LT];
+  __shared__ __attribute__((aligned(16))) float sg_lds[MT * LT];
   __shared__ float red[NW][MT][2];
   __shared__ float tok_inv[MT];
+  __shared__ float tok_beta[MT];
   __shared__ int tok_clamped[MT];
   const int tid = threadIdx.x;
   const int f = blockIdx.x, bh = blockIdx.y;
@@ -666,35 +690,49 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
     b_lds[i * LD + j] = dB[fo + x];
   }
   const int tt = tid / TPT, ln = tid % TPT;
-  float wk[CPT][4], wv[CPT][4];
+  const int ch0 = 8 * ln;
+  float wk[8][4], wv[8][4];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      wk[c][j] = conv_k[((long long)h * D + ln + TPT * c) * 4 + j];
-      wv[c][j] = conv_v[((long long)h * D + ln + TPT * c) * 4 + j];
+      wk[c][j] = conv_k[((long long)h * D + ch0 + c) * 4 + j];
+      wv[c][j] = conv_v[((long long)h * D + ch0 + c) * 4 + j];
     }
   const int lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const long long base = (long long)bh * N * D;
+  // raw k, v rows of the conv taps of this thread's token, fetched a tile
+  // ahead so their latency overlaps the previous tile's MFMAs
+  Row8<T> rk[4], rv[4];
+  auto fetch = [&](int s0_) {
+    const int s = s0_ + tt;
+    if (s >= S) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s - j >= 0) {
+        const long long ix = base + ((long long)f * S + s - j) * D + ch0;
+        rk[j].load(k + ix);
+        rv[j].load(v + ix);
+      }
+  };
+  fetch(0);
   __syncthreads();
   for (int s0 = 0; s0 < S; s0 += MT) {
     {  // features of the tile
       const int s = s0 + tt;
       const bool valid = s < S;
-      const long long n = (long long)f * S + s;
-      float kc[CPT], kh[CPT], vh[CPT];
+      float kc[8], kh[8], vh[8];
       float ss = 0.0f;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
+      for (int c = 0; c < 8; ++c) {
         float ak = 0.0f, av = 0.0f;
         if (valid) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (s - j >= 0) {
-              const long long ix = base + (n - j) * D + ln + TPT * c;
-              ak = fmaf(wk[c][j], ld_io<T>(k, ix), ak);
-              av = fmaf(wv[c][j], ld_io<T>(v, ix), av);
+              ak = fmaf(wk[c][j], rk[j].get(c), ak);
+              av = fmaf(wv[c][j], rv[j].get(c), av);
             }
         }
         kc[c] = ak;
@@ -704,19 +742,23 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
       }
       ss = group_sum<TPT>(ss);
       const float inv = inv_l2(ss);
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int o = tt * LT + ln + TPT * c;
-        kh_lds[o] = kh[c] * inv;
-        vh_lds[o] = vh[c];
-        sg_lds[o] = silu_grad(kc[c]);
-      }
+      const int o = tt * LT + ch0;
+      *(float4*)&kh_lds[o] = make_float4(kh[0] * inv, kh[1] * inv, kh[2] * inv, kh[3] * inv);
+      *(float4*)&kh_lds[o + 4] = make_float4(kh[4] * inv, kh[5] * inv, kh[6] * inv, kh[7] * inv);
+      *(float4*)&vh_lds[o] = make_float4(vh[0], vh[1], vh[2], vh[3]);
+      *(float4*)&vh_lds[o + 4] = make_float4(vh[4], vh[5], vh[6], vh[7]);
+      *(float4*)&sg_lds[o] = make_float4(silu_grad(kc[0]), silu_grad(kc[1]), silu_grad(kc[2]),
+                                         silu_grad(kc[3]));
+      *(float4*)&sg_lds[o + 4] = make_float4(silu_grad(kc[4]), silu_grad(kc[5]),
+                                             silu_grad(kc[6]), silu_grad(kc[7]));
       if (ln == 0) {
         tok_inv[tt] = inv;
         tok_clamped[tt] = ss <= 1e-24f;
+        tok_beta[tt] = valid ? beta[(long long)bh * N + (long long)f * S + s] : 0.0f;
       }
     }
     __syncthreads();
+    if (s0 + MT < S) fetch(s0 + MT);
     f32x4_t gk[2], bk[2], bv[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) gk[b] = bk[b] = bv[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -737,8 +779,7 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tk = 4 * lq + r;
-      const int s = s0 + tk;
-      bt[r] = s < S ? beta[(long long)bh * N + (long long)f * S + s] : 0.0f;
+      bt[r] = tok_beta[tk];
       db[r] = dot[r] = 0.0f;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -801,12 +842,12 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
   constexpr int NB = D / 16;  // 16-column blocks of dS_t
   constexpr int LD = D + 1;
   constexpr int LT = D + 16;
-  constexpr int TPT = NT / MT;
-  constexpr int CPT = D / TPT;
+  constexpr int TPT = NT / MT;  // threads per token: 8 consecutive channels each
+  static_assert(TPT * 8 == D, "feature mapping");
   __shared__ float st_lds[D * LD];
-  __shared__ float qh_lds[MT * LT];
+  __shared__ __attribute__((aligned(16))) float qh_lds[MT * LT];
   __shared__ float do_lds[MT * LT];
-  __shared__ float sg_lds[MT * LT];
+  __shared__ __attribute__((aligned(16))) float sg_lds[MT * LT];
   __shared__ float red[3][NW][MT];
   __shared__ float tok_inv[MT];
   __shared__ int tok_clamped[MT];
@@ -847,35 +888,57 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
 #pragma unroll
     for (int bj = 0; bj < NB; ++bj) acc[bi][bj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const long long base = (long long)bh * N * D;
+  const int ch0 = 8 * ln;
+  // this thread's 8 channels of its token's q row, fetched a tile ahead
+  Row8<T> rq;
+  auto fetch = [&](int s0_) {
+    const int s = s0_ + tt;
+    if (s < S) rq.load(q + base + ((long long)t * S + s) * D + ch0);
+  };
+  fetch(0);
   __syncthreads();
 
   for (int s0 = 0; s0 < S; s0 += MT) {
     {  // features of the tile
       const int s = s0 + tt;
       const bool valid = s < S;
-      const long long row = base + ((long long)t * S + s) * D + ln;
-      float qv[CPT], u[CPT];
+      float qv[8], u[8];
       float ss = 0.0f;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        qv[c] = valid ? ld_io<T>(q, row + TPT * c) : 0.0f;
+      for (int c = 0; c < 8; ++c) {
+        qv[c] = valid ? rq.get(c) : 0.0f;
         u[c] = silu_f(qv[c]);
         ss = fmaf(u[c], u[c], ss);
       }
       ss = group_sum<TPT>(ss);
       const float inv = inv_l2(ss);
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int o = tt * LT + ln + TPT * c;
-        qh_lds[o] = u[c] * inv;
-        sg_lds[o] = silu_grad(qv[c]);
-      }
+      const int o = tt * LT + ch0;
+      *(float4*)&qh_lds[o] = make_float4(u[0] * inv, u[1] * inv, u[2] * inv, u[3] * inv);
+      *(float4*)&qh_lds[o + 4] = make_float4(u[4] * inv, u[5] * inv, u[6] * inv, u[7] * inv);
+      *(float4*)&sg_lds[o] = make_float4(silu_grad(qv[0]), silu_grad(qv[1]), silu_grad(qv[2]),
+                                         silu_grad(qv[3]));
+      *(float4*)&sg_lds[o + 4] = make_float4(silu_grad(qv[4]), silu_grad(qv[5]),
+                                             silu_grad(qv[6]), silu_grad(qv[7]));
       if (ln == 0) {
         tok_inv[tt] = inv;
         tok_clamped[tt] = ss <= 1e-24f;
       }
     }
     __syncthreads();
+    // the gate and upstream gradient of this lane's output elements, issued
+    // before the next tile's q so the first product hides their latency
+    float gtv[2][4], gov[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = s0 + 4 * lq + r;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const long long ix = base + ((long long)t * S + s) * D + 32 * w + 16 * b + lr;
+        gtv[b][r] = s < S ? ld_io<T>(gate, ix) : 0.0f;
+        gov[b][r] = s < S ? ld_io<T>(gout, ix) : 0.0f;
+      }
+    }
+    if (s0 + MT < S) fetch(s0 + MT);
     // o = S_t q^
     f32x4_t o[2];
 #pragma unroll
@@ -910,9 +973,8 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const long long ix = base + ((long long)t * S + s) * D + 32 * w + 16 * b + lr;
-        const float gt = valid ? ld_io<T>(gate, ix) : 0.0f;
-        const float go = valid ? ld_io<T>(gout, ix) : 0.0f;
-        const float sg = sigmoid_f(gt);
+        const float go = gov[b][r];
+        const float sg = sigmoid_f(gtv[b][r]);
         z[b][r] = o[b][r] * rinv[r];
         if (valid) st_io<T>(dgate, ix, go * z[b][r] * wr[b] * sg * (1.0f - sg));
         dw[b] = fmaf(go * sg, z[b][r], dw[b]);
