@@ -554,13 +554,18 @@ __global__ __launch_bounds__(256) void lin_stats_bwd_kernel(
 // ---------------------------------------------------------------- convs
 // One workgroup per (frame, b*h): dk_s = sum_j w_j dkc_{s+j} inside the frame,
 // and the frame's part of the tap gradients sum_s dkc_s k_{s-j} (likewise v).
+// A thread owns one channel of a contiguous token range and slides two
+// four-entry windows along it (dkc_{s..s+3}, k_{s-3..s}): two loads per tensor
+// and token.
+constexpr int CV_NT = 512;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
+__global__ __launch_bounds__(CV_NT) void lin_conv_bwd_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ conv_k,
     const float* __restrict__ conv_v, const float* __restrict__ dkc,
     const float* __restrict__ dvc, T* __restrict__ dk, T* __restrict__ dv,
     float* __restrict__ cpart, int F, int S, int H, long long N, int accum) {
-  constexpr int G = 256 / D;
+  constexpr int G = CV_NT / D;
   __shared__ float red[G][D][8];
   const int tid = threadIdx.x;
   const int f = blockIdx.x, bh = blockIdx.y;
@@ -573,21 +578,29 @@ __global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
     wv[j] = conv_v[((long long)h * D + c) * 4 + j];
     pk[j] = pv[j] = 0.0f;
   }
+  const int len = (S + G - 1) / G;
+  const int sb = min(S, g0 * len), se = min(S, sb + len);
   const long long base = (long long)bh * N * D + (long long)f * S * D + c;
-  for (int s = g0; s < S; s += G) {
+  float gk[4], gv[4], xk[4], xv[4];  // gk[j] = dkc_{s+j}; xk[j] = k_{s-j}
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool fwd = sb + j < S, back = j > 0 && sb - j >= 0;
+    gk[j] = fwd ? dkc[base + (long long)(sb + j) * D] : 0.0f;
+    gv[j] = fwd ? dvc[base + (long long)(sb + j) * D] : 0.0f;
+    xk[j] = back ? ld_io<T>(k, base + (long long)(sb - j) * D) : 0.0f;
+    xv[j] = back ? ld_io<T>(v, base + (long long)(sb - j) * D) : 0.0f;
+  }
+  for (int s = sb; s < se; ++s) {
     const long long ix = base + (long long)s * D;
-    const float gk = dkc[ix], gv = dvc[ix];
+    xk[0] = ld_io<T>(k, ix);
+    xv[0] = ld_io<T>(v, ix);
     float ak = 0.0f, av = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (s + j < S) {
-        ak = fmaf(wk[j], dkc[ix + (long long)j * D], ak);
-        av = fmaf(wv[j], dvc[ix + (long long)j * D], av);
-      }
-      if (s - j >= 0) {
-        pk[j] = fmaf(gk, ld_io<T>(k, ix - (long long)j * D), pk[j]);
-        pv[j] = fmaf(gv, ld_io<T>(v, ix - (long long)j * D), pv[j]);
-      }
+      ak = fmaf(wk[j], gk[j], ak);
+      av = fmaf(wv[j], gv[j], av);
+      pk[j] = fmaf(gk[0], xk[j], pk[j]);
+      pv[j] = fmaf(gv[0], xv[j], pv[j]);
     }
     if (accum) {
       ak += ld_io<T>(dk, ix);
@@ -595,6 +608,18 @@ __global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
     }
     st_io<T>(dk, ix, ak);
     st_io<T>(dv, ix, av);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      gk[j] = gk[j + 1];
+      gv[j] = gv[j + 1];
+    }
+    gk[3] = s + 4 < S ? dkc[ix + 4LL * D] : 0.0f;
+    gv[3] = s + 4 < S ? dvc[ix + 4LL * D] : 0.0f;
+#pragma unroll
+    for (int j = 3; j > 0; --j) {
+      xk[j] = xk[j - 1];
+      xv[j] = xv[j - 1];
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -602,12 +627,30 @@ __global__ __launch_bounds__(256) void lin_conv_bwd_kernel(
     red[g0][c][4 + j] = pv[j];
   }
   __syncthreads();
-  for (int x = tid; x < D * 8; x += 256) {
+  for (int x = tid; x < D * 8; x += CV_NT) {
     float sum = 0.0f;
 #pragma unroll
     for (int g = 0; g < G; ++g) sum += red[g][x / 8][x % 8];
     cpart[((long long)bh * F + f) * D * 8 + x] = sum;
   }
+}
+
+// Sum of the RMSNorm weight's per-frame partials over every (b, h, frame):
+// one workgroup per channel block, a fixed-order tree per channel.
+__global__ __launch_bounds__(256) void lin_rms_grad_kernel(const float* __restrict__ dwpart,
+                                                           float* __restrict__ drms, int D,
+                                                           long long rows) {
+  __shared__ float red[256];
+  const int j = blockIdx.x;
+  float sum = 0.0f;
+  for (long long r = threadIdx.x; r < rows; r += 256) sum += dwpart[r * D + j];
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) drms[j] = red[0];
 }
 
 // ---------------------------------------------------------------- MFMA variants
@@ -1113,13 +1156,12 @@ __global__ __launch_bounds__(256) void lin_alpha_grad_kernel(
 }
 
 // ---------------------------------------------------------------- parameters
-// Per-head conv taps (sum over batch and frames), the RMSNorm weight (sum over
-// everything) and dS_text = text_scale (lam_P + lam_Q); one thread per output.
+// Per-head conv taps (sum over batch and frames) and dS_text = text_scale
+// (lam_P + lam_Q); one thread per output.
 __global__ __launch_bounds__(256) void lin_param_grad_kernel(
-    const float* __restrict__ cpart, const float* __restrict__ dwpart,
-    const float* __restrict__ lam0, float* __restrict__ dconv_k, float* __restrict__ dconv_v,
-    float* __restrict__ drms, float* __restrict__ dtext, float text_scale, int B, int H,
-    int D, int F) {
+    const float* __restrict__ cpart, const float* __restrict__ lam0, float* __restrict__ dconv_k,
+    float* __restrict__ dconv_v, float* __restrict__ dtext, float text_scale, int B, int H, int D,
+    int F) {
   const long long idx = blockIdx.x * 256LL + threadIdx.x;
   const long long BH = (long long)B * H;
   const long long n_conv = (long long)H * D * 8;
@@ -1134,13 +1176,8 @@ __global__ __launch_bounds__(256) void lin_param_grad_kernel(
     const int ch = x / 8, tap = x % 8;
     float* dst = tap < 4 ? dconv_k : dconv_v;
     dst[((long long)h * D + ch) * 4 + (tap & 3)] = sum;
-  } else if (idx < n_conv + D) {
-    const int j = (int)(idx - n_conv);
-    float sum = 0.0f;
-    for (long long r = 0; r < BH * F; ++r) sum += dwpart[r * D + j];
-    if (drms) drms[j] = sum;
-  } else if (idx < n_conv + D + n_text) {
-    const long long x = idx - n_conv - D;
+  } else if (idx < n_conv + n_text) {
+    const long long x = idx - n_conv;
     if (dtext) dtext[x] = text_scale * (lam0[x] + lam0[n_text + x]);
   }
 }
@@ -1278,11 +1315,11 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
         dim3 grid(g.F, BH);
 #define CB(DD)                                                                              \
   if (bf)                                                                                   \
-    hipLaunchKernelGGL((lin_conv_bwd_kernel<bf16_t, DD>), grid, dim3(256), 0, st,           \
+    hipLaunchKernelGGL((lin_conv_bwd_kernel<bf16_t, DD>), grid, dim3(CV_NT), 0, st,           \
                        (const bf16_t*)a.k, (const bf16_t*)a.v, a.conv_k, a.conv_v, a.dkc,    \
                        a.dvc, (bf16_t*)a.dk, (bf16_t*)a.dv, a.cpart, g.F, g.S, g.H, g.N, a.acc);   \
   else                                                                                      \
-    hipLaunchKernelGGL((lin_conv_bwd_kernel<float, DD>), grid, dim3(256), 0, st,            \
+    hipLaunchKernelGGL((lin_conv_bwd_kernel<float, DD>), grid, dim3(CV_NT), 0, st,            \
                        (const float*)a.k, (const float*)a.v, a.conv_k, a.conv_v, a.dkc,     \
                        a.dvc, (float*)a.dk, (float*)a.dv, a.cpart, g.F, g.S, g.H, g.N, a.acc);
         LB_SWITCH_D(CB)
@@ -1300,10 +1337,15 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
       {
-        const long long n = (long long)g.H * g.d * 8 + g.d + (long long)BH * g.d * g.d;
+        const long long n = (long long)g.H * g.d * 8 + (long long)BH * g.d * g.d;
         hipLaunchKernelGGL(lin_param_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
-                           0, st, a.cpart, a.dwpart, a.lam0, a.dconv_k, a.dconv_v, a.drms,
-                           a.dtext, a.text_scale, g.B, g.H, g.d, g.F);
+                           0, st, a.cpart, a.lam0, a.dconv_k, a.dconv_v, a.dtext, a.text_scale,
+                           g.B, g.H, g.d, g.F);
+        if (a.drms) {
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+          hipLaunchKernelGGL(lin_rms_grad_kernel, dim3(g.d), dim3(256), 0, st, a.dwpart, a.drms,
+                             g.d, (long long)BH * g.F);
+        }
       }
       break;
     }
