@@ -872,29 +872,33 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
 // Readout backward on MFMA, per 16-token tile: o = S_t q^ (A: q^ tile, B:
 // S_t^T), do from the RMSNorm and gate, dq^ = S_t^T do (A: do tile, B: S_t),
 // dS_t += do^T q^ (A: do^T, B: q^; wave w owns rows 32 w .. 32 w + 31 of
-// dS_t, all columns, in registers for the whole frame).
+// dS_t, all columns, in registers for the whole frame). Two wave groups share
+// S_t and take a 16-token tile each per step, so every SIMD holds two waves;
+// their dS_t partials are added at the end.
 template <typename T, int D>
-__global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
+__global__ __launch_bounds__(4 * D) void lin_readout_bwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ gate, const T* __restrict__ gout,
     const float* __restrict__ alpha, const float* __restrict__ Pst,
     const float* __restrict__ Qst, const float* __restrict__ rms_w, float eps,
     T* __restrict__ dq, T* __restrict__ dgate, float* __restrict__ dSt,
     float* __restrict__ dwpart, int F, int S, int chunk, int radius, long long N, int accum) {
-  constexpr int NT = 2 * D;
-  constexpr int NW = D / 32;
+  constexpr int GR = 2;  // wave groups, one token tile each
+  constexpr int NT = 2 * D * GR;
+  constexpr int NW = D / 32;  // waves per group
   constexpr int NB = D / 16;  // 16-column blocks of dS_t
   constexpr int LD = D + 1;
   constexpr int LT = D + 16;
-  constexpr int TPT = NT / MT;  // threads per token: 8 consecutive channels each
+  constexpr int TPT = NT / (MT * GR);  // threads per token: 8 consecutive channels each
   static_assert(TPT * 8 == D, "feature mapping");
   __shared__ float st_lds[D * LD];
-  __shared__ __attribute__((aligned(16))) float qh_lds[MT * LT];
-  __shared__ float do_lds[MT * LT];
-  __shared__ __attribute__((aligned(16))) float sg_lds[MT * LT];
-  __shared__ float red[3][NW][MT];
-  __shared__ float tok_inv[MT];
-  __shared__ int tok_clamped[MT];
+  __shared__ __attribute__((aligned(16))) float qh_lds[GR * MT * LT];
+  __shared__ float do_lds[GR * MT * LT];
+  __shared__ __attribute__((aligned(16))) float sg_lds[GR * MT * LT];
+  __shared__ float red[GR][3][NW][MT];
+  __shared__ float tok_inv[GR * MT];
+  __shared__ int tok_clamped[GR * MT];
   __shared__ float dec[2][D];
+  __shared__ float dwx[D];
 
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
@@ -917,8 +921,12 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
     st_lds[i * LD + j] = fmaf(Pm[x], dec[0][j], Qm[x] * dec[1][j]);
   }
   const int tt = tid / TPT, ln = tid % TPT;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int grp = (tid >> 6) / NW, w = (tid >> 6) % NW;  // group, wave within it
   const int lr = lane & 15, lq = lane >> 4;
+  float* const qh = qh_lds + grp * MT * LT;
+  float* const dob = do_lds + grp * MT * LT;
+  float* const sgb = sg_lds + grp * MT * LT;
   float wr[2], dw[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -941,8 +949,9 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
   fetch(0);
   __syncthreads();
 
-  for (int s0 = 0; s0 < S; s0 += MT) {
-    {  // features of the tile
+  for (int s0 = 0; s0 < S; s0 += MT * GR) {
+    const int sg0 = s0 + MT * grp;  // this group's tile
+    {  // features of both tiles
       const int s = s0 + tt;
       const bool valid = s < S;
       float qv[8], u[8];
@@ -973,7 +982,7 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
     float gtv[2][4], gov[2][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int s = s0 + 4 * lq + r;
+      const int s = sg0 + 4 * lq + r;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const long long ix = base + ((long long)t * S + s) * D + 32 * w + 16 * b + lr;
@@ -981,7 +990,7 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
         gov[b][r] = s < S ? ld_io<T>(gout, ix) : 0.0f;
       }
     }
-    if (s0 + MT < S) fetch(s0 + MT);
+    if (s0 + MT * GR < S) fetch(s0 + MT * GR);
     // o = S_t q^
     f32x4_t o[2];
 #pragma unroll
@@ -989,7 +998,7 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
 #pragma unroll 4
     for (int m0 = 0; m0 < D; m0 += 4) {
       const int m = m0 + lq;
-      const float a = qh_lds[lr * LT + m];
+      const float a = qh[lr * LT + m];
 #pragma unroll
       for (int b = 0; b < 2; ++b) o[b] = mfma16(a, st_lds[(32 * w + 16 * b + lr) * LD + m], o[b]);
     }
@@ -999,18 +1008,18 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
 #pragma unroll
       for (int b = 0; b < 2; ++b) ms = fmaf(o[b][r], o[b][r], ms);
       ms = row_sum16(ms);
-      if (lr == 0) red[0][w][4 * lq + r] = ms;
+      if (lr == 0) red[grp][0][w][4 * lq + r] = ms;
     }
     __syncthreads();
     float rinv[4], z[2][4], dz[2][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tk = 4 * lq + r;
-      const int s = s0 + tk;
+      const int s = sg0 + tk;
       const bool valid = s < S;
       float ms = 0.0f;
 #pragma unroll
-      for (int x = 0; x < NW; ++x) ms += red[0][x][tk];
+      for (int x = 0; x < NW; ++x) ms += red[grp][0][x][tk];
       rinv[r] = 1.0f / sqrtf(ms / D + eps);
       float dzz = 0.0f;
 #pragma unroll
@@ -1025,7 +1034,7 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
         dzz = fmaf(dz[b][r], z[b][r], dzz);
       }
       dzz = row_sum16(dzz);
-      if (lr == 0) red[1][w][tk] = dzz;
+      if (lr == 0) red[grp][1][w][tk] = dzz;
     }
     __syncthreads();
 #pragma unroll
@@ -1033,11 +1042,11 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
       const int tk = 4 * lq + r;
       float mz = 0.0f;
 #pragma unroll
-      for (int x = 0; x < NW; ++x) mz += red[1][x][tk];
+      for (int x = 0; x < NW; ++x) mz += red[grp][1][x][tk];
       mz /= D;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-        do_lds[tk * LT + 32 * w + 16 * b + lr] = rinv[r] * (dz[b][r] - z[b][r] * mz);
+        dob[tk * LT + 32 * w + 16 * b + lr] = rinv[r] * (dz[b][r] - z[b][r] * mz);
     }
     __syncthreads();
     // dq^ = S_t^T do
@@ -1047,7 +1056,7 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
 #pragma unroll 4
     for (int i0 = 0; i0 < D; i0 += 4) {
       const int i = i0 + lq;
-      const float a = do_lds[lr * LT + i];
+      const float a = dob[lr * LT + i];
 #pragma unroll
       for (int b = 0; b < 2; ++b) g[b] = mfma16(a, st_lds[i * LD + 32 * w + 16 * b + lr], g[b]);
     }
@@ -1057,9 +1066,9 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
       const int tk = k0 + lq;
       float a[2], bq[NB];
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi) a[bi] = do_lds[tk * LT + 32 * w + 16 * bi + lr];
+      for (int bi = 0; bi < 2; ++bi) a[bi] = dob[tk * LT + 32 * w + 16 * bi + lr];
 #pragma unroll
-      for (int bj = 0; bj < NB; ++bj) bq[bj] = qh_lds[tk * LT + 16 * bj + lr];
+      for (int bj = 0; bj < NB; ++bj) bq[bj] = qh[tk * LT + 16 * bj + lr];
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -1070,48 +1079,72 @@ __global__ __launch_bounds__(2 * D) void lin_readout_bwd_mfma_kernel(
       const int tk = 4 * lq + r;
       float dt = 0.0f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) dt = fmaf(qh_lds[tk * LT + 32 * w + 16 * b + lr], g[b][r], dt);
+      for (int b = 0; b < 2; ++b) dt = fmaf(qh[tk * LT + 32 * w + 16 * b + lr], g[b][r], dt);
       dt = row_sum16(dt);
-      if (lr == 0) red[2][w][tk] = dt;
+      if (lr == 0) red[grp][2][w][tk] = dt;
     }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tk = 4 * lq + r;
-      const int s = s0 + tk;
+      const int s = sg0 + tk;
       if (s >= S) continue;
       float dt = 0.0f;
 #pragma unroll
-      for (int x = 0; x < NW; ++x) dt += red[2][x][tk];
-      const float inv = tok_inv[tk];
-      const bool clamped = tok_clamped[tk] != 0;
+      for (int x = 0; x < NW; ++x) dt += red[grp][2][x][tk];
+      const float inv = tok_inv[grp * MT + tk];
+      const bool clamped = tok_clamped[grp * MT + tk] != 0;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int ch = 32 * w + 16 * b + lr;
         const int o2 = tk * LT + ch;
         const long long ix = base + ((long long)t * S + s) * D + ch;
         st_io<T>(dq, ix,
-                 l2_grad(g[b][r], qh_lds[o2], inv, dt, clamped) * sg_lds[o2] +
+                 l2_grad(g[b][r], qh[o2], inv, dt, clamped) * sgb[o2] +
                      (accum ? ld_io<T>(dq, ix) : 0.0f));
       }
     }
     __syncthreads();
   }
-  float* ds = dSt + ((long long)bh * F + t) * D * D;
-#pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-    for (int bj = 0; bj < NB; ++bj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        ds[(32 * w + 16 * bi + 4 * lq + r) * D + 16 * bj + lr] = acc[bi][bj][r];
-  // dw partial of this frame: the four row groups of each column
+  // group 1 hands its dS_t and dw partials to group 0 through LDS (S_t is no
+  // longer read after the loop's last barrier)
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    float x = dw[b];
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    if (lq == 0) dwpart[((long long)bh * F + t) * D + 32 * w + 16 * b + lr] = x;
+    dw[b] += __shfl_xor(dw[b], 16);
+    dw[b] += __shfl_xor(dw[b], 32);
+  }
+  if (grp == 1) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          st_lds[(32 * w + 16 * bi + 4 * lq + r) * D + 16 * bj + lr] = acc[bi][bj][r];
+    if (lq == 0) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) dwx[32 * w + 16 * b + lr] = dw[b];
+    }
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float* ds = dSt + ((long long)bh * F + t) * D * D;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int o = (32 * w + 16 * bi + 4 * lq + r) * D + 16 * bj + lr;
+          ds[o] = acc[bi][bj][r] + st_lds[o];
+        }
+    if (lq == 0) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int ch = 32 * w + 16 * b + lr;
+        dwpart[((long long)bh * F + t) * D + ch] = dw[b] + dwx[ch];
+      }
+    }
   }
 }
 
@@ -1232,12 +1265,12 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
                        (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N, a.acc);
 #define RBM(DD)                                                                          \
   if (bf)                                                                                \
-    hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<bf16_t, DD>), grid, dim3(2 * DD), 0, st, \
+    hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<bf16_t, DD>), grid, dim3(4 * DD), 0, st, \
                        (const bf16_t*)a.q, (const bf16_t*)a.gate, (const bf16_t*)a.d_o,   \
                        a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (bf16_t*)a.dq,              \
                        (bf16_t*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N, a.acc); \
   else                                                                                   \
-    hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<float, DD>), grid, dim3(2 * DD), 0, st, \
+    hipLaunchKernelGGL((lin_readout_bwd_mfma_kernel<float, DD>), grid, dim3(4 * DD), 0, st, \
                        (const float*)a.q, (const float*)a.gate, (const float*)a.d_o,      \
                        a.alpha, a.Pst, a.Qst, a.rms_w, a.eps, (float*)a.dq,               \
                        (float*)a.dgate, a.dSt, a.dwpart, g.F, g.S, g.chunk, g.radius, g.N, a.acc);
