@@ -701,18 +701,21 @@ struct Row8<float> {
 }  // namespace
 
 // Statistics backward on MFMA: gk = (dA + dA^T) k^, bk = dB k^, bv = dB^T v^
-// for the 16 tokens of a tile; features staged in LDS by all threads.
+// for the 16 tokens of a tile; features staged in LDS by the first half of
+// the threads. d / 16 waves (two per SIMD), wave w owning the 16 output
+// channels 16 w .. 16 w + 15 of all three products.
 template <typename T, int D>
-__global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
+__global__ __launch_bounds__(4 * D) void lin_stats_bwd_mfma_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
     const float* __restrict__ conv_k, const float* __restrict__ conv_v,
     const float* __restrict__ dA, const float* __restrict__ dB, float* __restrict__ dkc,
     float* __restrict__ dvc, float* __restrict__ dbeta, int F, int S, int H, long long N) {
-  constexpr int NT = 2 * D;
-  constexpr int NW = D / 32;
+  constexpr int NT = 4 * D;
+  constexpr int NW = D / 16;  // waves, one 16-channel block each
   constexpr int LD = D + 1;
   constexpr int LT = D + 4;
-  constexpr int TPT = NT / MT;  // threads per token: 8 consecutive channels each
+  constexpr int NF = NT / 2;    // feature threads
+  constexpr int TPT = NF / MT;  // threads per token: 8 consecutive channels each
   static_assert(TPT * 8 == D, "feature mapping");
   __shared__ float g_lds[D * LD];
   __shared__ float b_lds[D * LD];
@@ -732,7 +735,8 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
     g_lds[i * LD + j] = dA[fo + x] + dA[fo + (long long)j * D + i];
     b_lds[i * LD + j] = dB[fo + x];
   }
-  const int tt = tid / TPT, ln = tid % TPT;
+  const bool feat = tid < NF;
+  const int tt = (tid % NF) / TPT, ln = tid % TPT;
   const int ch0 = 8 * ln;
   float wk[8][4], wv[8][4];
 #pragma unroll
@@ -750,7 +754,7 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
   Row8<T> rk[4], rv[4];
   auto fetch = [&](int s0_) {
     const int s = s0_ + tt;
-    if (s >= S) return;
+    if (!feat || s >= S) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (s - j >= 0) {
@@ -762,7 +766,7 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
   fetch(0);
   __syncthreads();
   for (int s0 = 0; s0 < S; s0 += MT) {
-    {  // features of the tile
+    if (feat) {  // features of the tile
       const int s = s0 + tt;
       const bool valid = s < S;
       float kc[8], kh[8], vh[8];
@@ -802,31 +806,32 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
     }
     __syncthreads();
     if (s0 + MT < S) fetch(s0 + MT);
-    f32x4_t gk[2], bk[2], bv[2];
+    constexpr int NBW = 1;  // 16-channel blocks per wave
+    f32x4_t gk[NBW], bk[NBW], bv[NBW];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) gk[b] = bk[b] = bv[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
+    for (int b = 0; b < NBW; ++b) gk[b] = bk[b] = bv[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
     for (int m0 = 0; m0 < D; m0 += 4) {
       const int m = m0 + lq;
       const float ak = kh_lds[lr * LT + m];
       const float av = vh_lds[lr * LT + m];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int j = 32 * w + 16 * b + lr;
+      for (int b = 0; b < NBW; ++b) {
+        const int j = 16 * w + lr;
         gk[b] = mfma16(ak, g_lds[m * LD + j], gk[b]);  // (dA + dA^T) symmetric
         bk[b] = mfma16(ak, b_lds[j * LD + m], bk[b]);  // dB[j][m]
         bv[b] = mfma16(av, b_lds[m * LD + j], bv[b]);  // dB[m][j]
       }
     }
-    float db[4], dot[4], dkh[2][4], bt[4];
+    float db[4], dot[4], dkh[NBW][4], bt[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tk = 4 * lq + r;
       bt[r] = tok_beta[tk];
       db[r] = dot[r] = 0.0f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int o = tk * LT + 32 * w + 16 * b + lr;
+      for (int b = 0; b < NBW; ++b) {
+        const int o = tk * LT + 16 * w + lr;
         const float khv = kh_lds[o], vhv = vh_lds[o];
         db[r] = fmaf(khv, 0.5f * gk[b][r], db[r]);
         db[r] = fmaf(vhv, bk[b][r], db[r]);
@@ -857,8 +862,8 @@ __global__ __launch_bounds__(2 * D) void lin_stats_bwd_mfma_kernel(
       const float inv = tok_inv[tk];
       const bool clamped = tok_clamped[tk] != 0;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int ch = 32 * w + 16 * b + lr;
+      for (int b = 0; b < NBW; ++b) {
+        const int ch = 16 * w + lr;
         const int o = tk * LT + ch;
         const long long ix = base + n * D + ch;
         dkc[ix] = l2_grad(dkh[b][r], kh_lds[o], inv, dt, clamped) * sg_lds[o];
@@ -1326,11 +1331,11 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
                        a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);
 #define SBM(DD)                                                                             \
   if (bf)                                                                                   \
-    hipLaunchKernelGGL((lin_stats_bwd_mfma_kernel<bf16_t, DD>), grid, dim3(2 * DD), 0, st,  \
+    hipLaunchKernelGGL((lin_stats_bwd_mfma_kernel<bf16_t, DD>), grid, dim3(4 * DD), 0, st,  \
                        (const bf16_t*)a.k, (const bf16_t*)a.v, a.beta, a.conv_k, a.conv_v,   \
                        a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);               \
   else                                                                                      \
-    hipLaunchKernelGGL((lin_stats_bwd_mfma_kernel<float, DD>), grid, dim3(2 * DD), 0, st,   \
+    hipLaunchKernelGGL((lin_stats_bwd_mfma_kernel<float, DD>), grid, dim3(4 * DD), 0, st,   \
                        (const float*)a.k, (const float*)a.v, a.beta, a.conv_k, a.conv_v,     \
                        a.A, a.Bm, a.dkc, a.dvc, a.dbeta, g.F, g.S, g.H, g.N);
       switch (g.d) {
