@@ -43,6 +43,9 @@ SOFTMAX_SRCS = [os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", n)
 # the backward kernels' sources
 SOFTMAX_BWD_SRCS = [os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", n)
                     for n in ("softmax_bwd.hip", "attn_tile.h", "hwa_internal.h")]
+LIN_BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "linear_bwd_traffic.json")
+LIN_BWD_SRCS = [os.path.join(ROOT, "hybrid_window_softmax_amd", "csrc", n)
+                for n in ("linear_bwd.hip", "linear_bwd.h", "hwa_internal.h")]
 
 
 def log(*a):
@@ -119,6 +122,21 @@ def recorded_traffic(path=TRAFFIC_FILE, srcs=None):
 
 def softmax_traffic():
     return recorded_traffic(TRAFFIC_FILE, SOFTMAX_SRCS)
+
+
+def linear_bwd_traffic(kernel):
+    """HBM bytes per launch of one linear-backward kernel from the committed
+    counter summary (which covers several kernels), or None when the sources
+    changed since the counters were taken."""
+    try:
+        with open(LIN_BWD_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        sha = sources_sha256(LIN_BWD_SRCS)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
 def cpu_baseline(inp, rule, heads_run=1):
@@ -368,12 +386,15 @@ def bench_linear_bwd(args, cfg, inp, up):
     dom = max(("readout", "stats"), key=lambda n: stage[n])
     achieved = work[dom]["flops"] / (stage[dom] / 1000.0) / 1e12
     # d = 64, 128: fp32 MFMA kernels (peak = the fp32 MFMA rate, the same
-    # figure as the fp32 vector rate); d = 16, 32: fp32 VALU kernels
+    # figure as the fp32 vector rate); d = 16, 32: fp32 VALU kernels. traffic:
+    # the counters were taken on the 132,600-token clip only
     mfma = d in (64, 128)
-    roofline = {"kernel": f"lin_{dom}_bwd{'_mfma' if mfma else ''}_kernel",
-                "bound": "mfma" if mfma else "alu",
+    kname = f"lin_{dom}_bwd{'_mfma' if mfma else ''}_kernel"
+    roofline = {"kernel": kname, "bound": "mfma" if mfma else "alu",
                 "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                "traffic": linear_bwd_traffic(kname) if cfg["name"] == "long-clip-832x480-85f"
+                else None,
                 "algorithmic_flops_per_launch": work[dom]["flops"]}
     cpu = None
     if not args.no_cpu_baseline:

@@ -7,7 +7,7 @@
 #include <stddef.h>
 #include <string.h>
 
-#include "hwa_internal.h"
+#include "linear_bwd.h"
 
 using hwa::bf16_t;
 using hwa::Geom;

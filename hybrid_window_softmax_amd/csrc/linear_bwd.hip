@@ -26,7 +26,7 @@
 // chunk 1 stores one bank slot per frame). Every output element is one fixed
 // sum: no atomics, so repeated calls agree bit for bit.
 
-#include "hwa_internal.h"
+#include "linear_bwd.h"
 
 namespace hwa {
 
