@@ -21,7 +21,8 @@
 //              P_{f-1} + dX^Q * Q_{f+1}); dS_text = text_scale (lam_P + lam_Q)
 //   statistics dk^ = beta (dA + dA^T) k^ + beta dB^T v^, dv^ = beta dB k^,
 //              dbeta = k^.(dA k^) + v^.(dB k^), then L2, SiLU and the convs
-// All arithmetic is fp32. The forward's states are recomputed first with its
+// All arithmetic is fp32 (bf16 calls: the recomputed scan is the forward's
+// split-bf16 MFMA scan). The forward's states are recomputed first with its
 // own statistics, inverse and scan kernels (every frame kept: a scan with
 // chunk 1 stores one bank slot per frame). Every output element is one fixed
 // sum: no atomics, so repeated calls agree bit for bit.
@@ -1245,7 +1246,9 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
       Geom g1 = g;
       g1.chunk = 1;
       g1.nch = g.F;
-      e = launch_scan(g1, HWA_F32, a.rule, a.c, a.A, a.Bm, a.M, a.alpha, a.text_state,
+      // the forward's own scan for the call's dtype (bf16: split-bf16 MFMA,
+      // about 16 significant bits per product; fp32: fp32)
+      e = launch_scan(g1, dtype, a.rule, a.c, a.A, a.Bm, a.M, a.alpha, a.text_state,
                       a.text_scale, a.Pst, a.Qst, a.E, st);
       if (e != hipSuccess) return e;
       const long long rows = (long long)BH * (g.F + 1) * g.d;
