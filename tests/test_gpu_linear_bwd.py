@@ -204,3 +204,27 @@ def test_hybrid_autograd(cfg, rule):
     worst["rms_weight"] = oracle.rel_frobenius(got["rms_weight"], w)
     print("  rel err " + " ".join(f"d{n} {e:.2e}" for n, e in worst.items()), flush=True)
     assert max(worst.values()) <= TOL[c["dtype"]], worst
+
+
+@pytest.mark.parametrize("name,h", [("clip-832x480-31f", 23), ("canvas-1024x1024-64f", 11)])
+def test_full_size_one_head(name, h):
+    # the other full-size workloads: every head on the GPU, one head against
+    # the oracle in full (batch 1: that head's conv-tap gradients are the
+    # library's)
+    inp = inputs.make(name)
+    c = inp.cfg
+    print(f"case {name}: all heads on the GPU, head {h} against the oracle", flush=True)
+    g_host = inputs.grad_output(c)
+    st_host = inputs.state_matrix(c)
+    got = _gpu_grads(inp, "vdn_solve", st_host, g_host)
+    ref = oracle.linear_branch_grad(
+        inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h), inp.beta[0, h],
+        inp.alpha[0, h], inp.f64("gate", 0, h), st_host[0, h], inp.conv_k[h], inp.conv_v[h],
+        inp.rms_weight, _f64(inp, g_host[0, h]), c["tokens_per_frame"], c["chunk"],
+        c["radius"], "vdn_solve", c["c"], 0.5, 1e-6)
+    errs = {n: oracle.rel_frobenius(got[n][0, h], ref["S_text" if n == "text_state" else n])
+            for n in PER_HEAD}
+    errs["conv_k"] = oracle.rel_frobenius(got["conv_k"][h], ref["conv_k"])
+    errs["conv_v"] = oracle.rel_frobenius(got["conv_v"][h], ref["conv_v"])
+    print("  rel err " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert max(errs.values()) <= TOL["bf16"], errs
