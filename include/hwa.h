@@ -298,8 +298,9 @@ size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
  * hwa_softmax_bwd's output there, the sum is the gradient of out = o_sm + y
  * with respect to q, k and v (when the forward used no q_rope / k_rope).
  * Outputs must not overlap each other, an input or the workspace. All
- * arithmetic is fp32. Returns HWA_OK, or an error status before anything is
- * enqueued.
+ * arithmetic is fp32, except that bf16 calls recompute the scan states with
+ * the forward's split-bf16 MFMA scan (about 16 significant bits per product).
+ * Returns HWA_OK, or an error status before anything is enqueued.
  */
 #define HWA_NUM_LIN_BWD_STAGE_EVENTS 6
 
