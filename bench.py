@@ -15,7 +15,8 @@ With --softmax-bwd it instead times the backward of the windowed softmax
 branch (hwa_softmax_bwd: dq, dk, dv from q, k, v, the branch output, its
 log-sum-exp and the upstream gradient) on the same workload and prints that
 line; with --linear-bwd, the backward of the linear branch (hwa_linear_bwd:
-every input's gradient, fp32 arithmetic).
+every input's gradient, fp32 arithmetic); with --train-step, the forward
+followed by both backward passes (every input's gradient of the output).
 """
 
 from __future__ import annotations
@@ -426,6 +427,114 @@ def bench_linear_bwd(args, cfg, inp, up):
     }
 
 
+def bench_train_step(args, cfg, inp, up):
+    """One step = the forward (keeping o_sm and its log-sum-exp), the softmax
+    branch's backward, then the linear branch's backward adding its dq, dk, dv
+    to the softmax branch's: every input's gradient of out = o_sm + y."""
+    import torch
+    from hybrid_window_softmax_amd import hwa, inputs
+    g_host = inputs.grad_output(cfg)
+    t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
+                                          "conv_v", "rms_weight", "k_txt", "v_txt",
+                                          "beta_txt")}
+    text = hwa.text_state(t["k_txt"], t["v_txt"], t["beta_txt"]) if t["k_txt"] is not None \
+        else None
+    g = up(g_host)
+    F, S, ch, r = cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"], cfg["radius"]
+    q = t["q"]
+    B, H, N, d = q.shape
+    out, o_sm = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    st = {"wf": None, "ws": None, "wl": None, "grads": None}
+
+    def step(ev=None, sev=None):
+        if ev:
+            ev[0].record()
+        _, st["wf"] = hwa.hybrid_attn_fwd(q, t["k"], t["v"], t["beta"], t["alpha"], t["gate"], text,
+                                          t["conv_k"], t["conv_v"], F, S, ch, r, args.rule,
+                                          cfg["c"], 0.5, 1e-6, t["rms_weight"], out=out,
+                                          workspace=st["wf"], softmax_lse=lse, softmax_out=o_sm)
+        if ev:
+            ev[1].record()
+        st["ws"] = hwa.softmax_bwd(q, t["k"], t["v"], o_sm, lse, g, F, S, ch, r, dq=dq, dk=dk,
+                                   dv=dv, workspace=st["ws"], stage_events=sev)[3]
+        if ev:
+            ev[2].record()
+        grads = dict(st["grads"] or {}, q=dq, k=dk, v=dv)
+        st["grads"], st["wl"] = hwa.linear_bwd(q, t["k"], t["v"], t["beta"], t["alpha"], t["gate"],
+                                               text, t["conv_k"], t["conv_v"], g, F, S, ch, r,
+                                               args.rule, cfg["c"], 0.5, 1e-6, t["rms_weight"],
+                                               grads=grads, workspace=st["wl"], accumulate=True)
+        if ev:
+            ev[3].record()
+
+    log("bench: training step warmup")
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    timer = hwa.StageTimer(args.steps, hwa.NUM_BWD_STAGE_EVENTS, hwa.BWD_STAGES)
+    log(f"bench: timing {args.steps} training steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i], timer.sets[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    phases = {}
+    for j, name in enumerate(("forward", "softmax_bwd", "linear_bwd")):
+        phases[name] = {"ms": round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps, 4)}
+    stage = timer.stage_ms()
+    timer.close()
+    log("bench: phase ms " + ", ".join(f"{k} {v['ms']:.3f}" for k, v in phases.items()))
+    pairs = window_pairs(cfg) * B * H
+    dkdv_flops = 8 * d * pairs
+    achieved = dkdv_flops / (stage["dkdv"] / 1000.0) / 1e12
+    roofline = {"kernel": "softmax_bwd_dkdv_kernel", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(BWD_TRAFFIC_FILE, SOFTMAX_BWD_SRCS)
+                if cfg["name"] == "long-clip-832x480-85f" else None,
+                "algorithmic_flops_per_launch": dkdv_flops}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle's forward and gradients on a sample")
+        del t, g, text, out, o_sm, lse, dq, dk, dv, st
+        torch.cuda.empty_cache()
+        g_host_st = inputs.state_matrix(cfg)
+        parts = [cpu_baseline(inp, args.rule, args.cpu_heads),
+                 softmax_bwd_cpu_baseline(inp, g_host, args.cpu_heads),
+                 linear_bwd_cpu_baseline(inp, g_host, g_host_st, args.rule, args.cpu_heads)]
+        tok = B * N
+        total_s = sum(tok / p["value"] for p in parts)
+        cpu = {"value": tok / total_s, "unit": "tokens/s", "cores": parts[0]["cores"],
+               "kind": "oracle",
+               "sample": f"{args.cpu_heads} of {H} heads (all {N} tokens of each) of the forward, "
+                         "the softmax gradient and the linear-branch gradient, each scaled by heads"}
+    return {
+        "metric": "hybrid attention training step (forward + backward, every input's gradient) "
+                  "tokens/s",
+        "value": round(B * N / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: B{B} H{H} d{d} F{F} x S{S} = {N} tokens, "
+                               f"chunk {ch} radius {r}, {args.rule}, forward + backward",
+                   "tokens": N, "heads": H, "head_dim": d},
+        "roofline": roofline,
+        "phases": phases,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,6 +548,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (three times), the "
                          "reference kernel for scaling HBM byte counters")
+    ap.add_argument("--train-step", action="store_true",
+                    help="time forward + both backward passes (every input's gradient) instead")
     ap.add_argument("--linear-bwd", action="store_true",
                     help="time the linear branch's backward (hwa_linear_bwd) instead")
     ap.add_argument("--softmax-bwd", action="store_true",
@@ -505,6 +616,9 @@ def main():
         return
     if args.linear_bwd:
         print(json.dumps(bench_linear_bwd(args, cfg, inp, up)), flush=True)
+        return
+    if args.train_step:
+        print(json.dumps(bench_train_step(args, cfg, inp, up)), flush=True)
         return
 
     t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
