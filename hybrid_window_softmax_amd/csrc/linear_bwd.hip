@@ -59,6 +59,8 @@ constexpr int AJ_R = 8;    // adjoint scan: state rows per workgroup
 
 }  // namespace
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------- exponents
 // The scan keeps row = stored * 2^e; fold e into the stored rows.
 __global__ __launch_bounds__(256) void fold_exp_kernel(float* __restrict__ Pst,
@@ -321,16 +323,33 @@ __global__ __launch_bounds__(256) void lin_adjoint_kernel(
   };
   inject(dir == 0 ? nch : 0);  // P_{F-1} / Q_0
   float* dX = dir == 0 ? dXP : dXQ;
+  // M_f of the next step is fetched into registers while this step computes
+  constexpr int NV = D * D / 4;  // 16-byte pieces of one M_f
+  constexpr int MV = NV >= 256 ? NV / 256 : 1;
+  f32x4_t mreg[MV];
+  {
+    const f32x4_t* src = (const f32x4_t*)&Mi[((long long)bh * F + (dir == 0 ? F - 1 : 0)) * D * D];
+#pragma unroll
+    for (int u = 0; u < MV; ++u) mreg[u] = (NV >= 256 || tid < NV) ? src[tid + 256 * u] : f32x4_t{};
+  }
   for (int i = 0; i < F; ++i) {
     const int f = dir == 0 ? F - 1 - i : i;
     const long long mo = ((long long)bh * F + f) * D * D;
-    for (int x = tid; x < D * D / 4; x += 256)
-      *(float4*)&g_lds[x * 4] = *(const float4*)&Mi[mo + (long long)x * 4];
+#pragma unroll
+    for (int u = 0; u < MV; ++u)
+      if (NV >= 256 || tid < NV) *(f32x4_t*)&g_lds[(tid + 256 * u) * 4] = mreg[u];
     if (active) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) x_lds[r][j0 + u] = lam[u];
     }
     __syncthreads();
+    if (i + 1 < F) {
+      const f32x4_t* src =
+          (const f32x4_t*)&Mi[((long long)bh * F + (dir == 0 ? f - 1 : f + 1)) * D * D];
+#pragma unroll
+      for (int u = 0; u < MV; ++u)
+        mreg[u] = (NV >= 256 || tid < NV) ? src[tid + 256 * u] : f32x4_t{};
+    }
     if (active) {
       float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       // dX = lam M_f^T = lam M_f (M_f is the inverse of a symmetric matrix)
@@ -663,8 +682,6 @@ __global__ __launch_bounds__(256) void lin_rms_grad_kernel(const float* __restri
 // D[4 g + r][j] in register r. Wave w owns output channels 32 w .. 32 w + 31
 // (two 16-column blocks); per-token sums over the channels combine the 16
 // lanes of a row group and then the waves through LDS.
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 namespace {
 
 __device__ __forceinline__ f32x4_t mfma16(float a, float b, f32x4_t c) {
