@@ -39,6 +39,7 @@ from .hybrid_attn import (  # noqa: F401
 )
 from .softmax_grad import (  # noqa: F401
     softmax_lse,
+    softmax_lse_rows,
     softmax_branch_grad,
     softmax_grad_rows,
 )

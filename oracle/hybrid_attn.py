@@ -32,7 +32,6 @@ Tokens are frame-major: token n belongs to frame n // S.
 from __future__ import annotations
 
 import math
-from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -80,7 +79,7 @@ def _softmax_block(qs, ks, vs):
     return p @ vs
 
 
-def softmax_branch(q, k, v, S: int, lo, hi, row_block: int = 512):
+def softmax_branch(q, k, v, S: int, lo, hi, row_block: int = 512, frames=None):
     """Windowed softmax output for one (batch, head) slice.
 
     q, k, v: [N, d] (the softmax branch's q/k, i.e. RoPE'd ones if the caller
@@ -90,6 +89,9 @@ def softmax_branch(q, k, v, S: int, lo, hi, row_block: int = 512):
     is"). Query rows are processed ``row_block`` at a time only to bound
     memory; each row's arithmetic is the plain definition.
 
+    ``frames``: optional (t0, t1); then only the query frames t0..t1-1 are
+    computed and the result holds their rows, [(t1 - t0) * S, d].
+
     Pinned by: a brute-force N x N masked softmax, textbook full attention
     (radius covering all chunks) and chunk-block-diagonal attention (radius 0).
     """
@@ -97,13 +99,13 @@ def softmax_branch(q, k, v, S: int, lo, hi, row_block: int = 512):
     k = np.asarray(k, _F64)
     v = np.asarray(v, _F64)
     N, d = q.shape
-    F = N // S
-    out = np.empty((N, v.shape[1]), dtype=_F64)
-    for t in range(F):
+    t0, t1 = (0, N // S) if frames is None else frames
+    out = np.empty(((t1 - t0) * S, v.shape[1]), dtype=_F64)
+    for t in range(t0, t1):
         k0, k1 = int(lo[t]) * S, (int(hi[t]) + 1) * S
         for r0 in range(t * S, (t + 1) * S, row_block):
             r1 = min((t + 1) * S, r0 + row_block)
-            out[r0:r1] = _softmax_block(q[r0:r1], k[k0:k1], v[k0:k1])
+            out[r0 - t0 * S:r1 - t0 * S] = _softmax_block(q[r0:r1], k[k0:k1], v[k0:k1])
     return out
 
 
@@ -381,6 +383,38 @@ def hybrid_attn_head(q, k, v, beta, alpha, gate, S_text, conv_k, conv_v, w,
     return o_sm + y, o_sm, y, inter
 
 
+# Arguments of the whole-call tasks, set in the parent before the worker
+# processes are forked (so the arrays are not pickled) and read by them.
+_TASKS = {}
+
+
+def _task(job):
+    """One task of :func:`hybrid_attn`: ("sm", b, h, t0, t1) is the softmax
+    branch of query frames t0..t1-1 of slice (b, h), ("lin", b, h) its whole
+    linear branch. Returns (job, rows)."""
+    a = _TASKS
+    b, h = job[1], job[2]
+    if job[0] == "sm":
+        qs = a["q"] if a["q_rope"] is None else a["q_rope"]
+        ks = a["k"] if a["k_rope"] is None else a["k_rope"]
+        return job, softmax_branch(qs[b, h], ks[b, h], a["v"][b, h], a["S"], a["lo"], a["hi"],
+                                   frames=(job[3], job[4]))
+    st = None if a["text_state"] is None else a["text_state"][b, h]
+    y, _ = linear_branch(a["q"][b, h], a["k"][b, h], a["v"][b, h], a["beta"][b, h],
+                         a["alpha"][b, h], a["gate"][b, h], st, a["conv_k"][h], a["conv_v"][h],
+                         a["w"], a["S"], a["chunk"], a["radius"], a["rule"], a["c"],
+                         a["text_scale"], a["eps"])
+    return job, y
+
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
 def hybrid_attn(q, k, v, beta, alpha, gate, text_state_, conv_k, conv_v, w,
                 frames: int, S: int, chunk: int = 5, radius: int = 1,
                 rule: str = "vdn_solve", c: float = 0.5,
@@ -389,35 +423,55 @@ def hybrid_attn(q, k, v, beta, alpha, gate, text_state_, conv_k, conv_v, w,
     """Whole call over [B, H, N, d] inputs; returns (out, o_sm, y) in fp64.
 
     alpha: [B, H, F, d]; beta: [B, H, N]; text_state_: [B, H, d, d] or None;
-    conv_k, conv_v: [H, d, 4]; w: [d] or None (ones). (b, h) slices are
-    independent and may be spread over ``workers`` threads.
+    conv_k, conv_v: [H, d, 4]; w: [d] or None (ones). Every (b, h) slice is
+    the one-slice definition (:func:`hybrid_attn_head`), so out = o_sm + y
+    ("Why video models are stuck on attention"). The work is cut into
+    independent tasks: the softmax branch per (b, h, query chunk) -- the query
+    frames of a chunk share one key range -- and the linear branch per (b, h).
+    With ``workers`` > 1 the tasks run in that many forked processes, each
+    with one BLAS thread; the arithmetic of a row does not depend on it.
+
+    Pinned by: equality with :func:`hybrid_attn_head` slice by slice on a
+    batch-2, two-head case with per-head conv taps, text states and alpha, in
+    one process and in a pool.
     """
     Bn, H, N, d = np.shape(q)
-    assert N == frames * S
+    if N != frames * S:
+        raise ValueError("N must equal frames * S")
     if w is None:
         w = np.ones(d)
-    out = np.empty((Bn, H, N, d), dtype=_F64)
-    o_sm = np.empty_like(out)
-    y = np.empty_like(out)
+    lo, hi = window_bounds(frames, chunk, radius)
+    _TASKS.clear()
+    _TASKS.update(q=q, k=k, v=v, beta=beta, alpha=alpha, gate=gate, text_state=text_state_,
+                  conv_k=conv_k, conv_v=conv_v, w=w, S=S, chunk=chunk, radius=radius,
+                  rule=rule, c=c, text_scale=text_scale, eps=eps, q_rope=q_rope,
+                  k_rope=k_rope, lo=lo, hi=hi)
+    jobs = [("sm", b, h, t0, min(frames, t0 + chunk))
+            for b in range(Bn) for h in range(H) for t0 in range(0, frames, chunk)]
+    jobs += [("lin", b, h) for b in range(Bn) for h in range(H)]
+    o_sm = np.empty((Bn, H, N, d), dtype=_F64)
+    y = np.empty_like(o_sm)
 
-    def one(bh):
-        b, h = bh
-        st = None if text_state_ is None else text_state_[b, h]
-        qr = None if q_rope is None else q_rope[b, h]
-        kr = None if k_rope is None else k_rope[b, h]
-        r = hybrid_attn_head(q[b, h], k[b, h], v[b, h], beta[b, h], alpha[b, h],
-                             gate[b, h], st, conv_k[h], conv_v[h], w, S, chunk,
-                             radius, rule, c, text_scale, eps, qr, kr)
-        out[b, h], o_sm[b, h], y[b, h] = r[0], r[1], r[2]
+    def put(job, rows):
+        if job[0] == "sm":
+            o_sm[job[1], job[2], job[3] * S:job[4] * S] = rows
+        else:
+            y[job[1], job[2]] = rows
 
-    jobs = [(b, h) for b in range(Bn) for h in range(H)]
-    if workers > 1:
-        with ThreadPoolExecutor(workers) as ex:
-            list(ex.map(one, jobs))
-    else:
-        for j in jobs:
-            one(j)
-    return out, o_sm, y
+    try:
+        if workers > 1:
+            import multiprocessing as mp
+            from concurrent.futures import ProcessPoolExecutor
+            with ProcessPoolExecutor(workers, mp_context=mp.get_context("fork"),
+                                     initializer=_one_blas_thread) as ex:
+                for job, rows in ex.map(_task, jobs):
+                    put(job, rows)
+        else:
+            for job in jobs:
+                put(*_task(job))
+    finally:
+        _TASKS.clear()
+    return o_sm + y, o_sm, y
 
 
 def text_state(k_txt, v_txt, beta_txt):

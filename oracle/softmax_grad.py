@@ -64,6 +64,20 @@ def softmax_lse(q, k, S: int, lo, hi, row_block: int = 512):
     return lse
 
 
+def softmax_lse_rows(q, k, S: int, lo, hi, rows):
+    """lse_n of :func:`softmax_lse` for the selected query ``rows`` only, one
+    row at a time (sampled checks at full size)."""
+    q = np.asarray(q)
+    d = q.shape[1]
+    out = np.empty(len(rows), dtype=_F64)
+    for i, n in enumerate(np.asarray(rows, dtype=np.int64)):
+        k0, k1 = _window_keys(int(n) // S, S, lo, hi)
+        s = np.asarray(k[k0:k1], _F64) @ np.asarray(q[n], _F64) / math.sqrt(d)
+        m = s.max()
+        out[i] = m + np.log(np.exp(s - m).sum())
+    return out
+
+
 def _block_grad(qs, ks, vs, gs):
     """Gradients of one block of query rows against their common window."""
     d = qs.shape[1]

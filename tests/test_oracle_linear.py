@@ -75,6 +75,39 @@ def test_features_unit_norm_and_raw_q():
     assert np.abs(vh2 - 2.0 * vh).max() < 1e-13
 
 
+def test_l2_clamp_zero_and_tiny_rows():
+    # "Step 1" L2 with the epsilon reading x / max(||x||, 1e-12): a zero row
+    # stays zero (no 0/0), a row of norm 5e-13 is divided by 1e-12, not by its
+    # norm, and a row of norm exactly 1e-12 by that norm (both sides agree)
+    x = np.array([[0.0, 0.0, 0.0],
+                  [3e-13, 4e-13, 0.0],
+                  [6e-13, 0.0, 8e-13],
+                  [3.0, 0.0, 4.0]])
+    got = oracle.l2_normalize(x)
+    assert np.array_equal(got[0], np.zeros(3))
+    assert np.allclose(got[1], [0.3, 0.4, 0.0], rtol=1e-12, atol=0)
+    assert np.allclose(got[2], [0.6, 0.0, 0.8], rtol=1e-12, atol=0)
+    assert np.allclose(got[3], [0.6, 0.0, 0.8], rtol=1e-15, atol=0)
+    # a different eps moves only the clamped rows
+    got2 = oracle.l2_normalize(x, eps=1e-13)
+    assert np.allclose(got2[1], [0.6, 0.8, 0.0], rtol=1e-12, atol=0)
+    assert np.array_equal(got2[3], got[3])
+    # the features of an all-zero k row (SiLU(0) = 0) are zero, so such a
+    # token adds nothing to A and B whatever its beta
+    S, d = 4, 5
+    k = RNG.standard_normal((S, d))
+    k[2] = 0.0
+    taps = np.zeros((d, 4))
+    taps[:, 0] = 1.0
+    _, kh, vh = oracle.features(k, k, k, taps, taps, S)
+    assert np.array_equal(kh[2], np.zeros(d))
+    A, B = oracle.frame_statistics(kh, vh, np.array([0.5, 0.7, 1e6, 0.2]), S)
+    keep = [0, 1, 3]
+    A2, B2 = oracle.frame_statistics(kh[keep], vh[keep], np.array([0.5, 0.7, 0.2]), 3)
+    assert np.allclose(A, A2, rtol=1e-13, atol=1e-15)
+    assert np.allclose(B, B2, rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- statistics
 def test_statistics_invariants_and_bruteforce():
     S, d, F = 9, 6, 3

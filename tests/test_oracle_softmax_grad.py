@@ -115,11 +115,16 @@ def test_lse_matches_logsumexp_and_output():
     lo, hi = oracle.window_bounds(F, 3, 1)
     lse = oracle.softmax_lse(q, k, S, lo, hi, row_block=4)
     o = oracle.softmax_branch(q, k, v, S, lo, hi)
+    rows = np.array([0, 7, 23, 47])
+    lse_rows = oracle.softmax_lse_rows(q, k, S, lo, hi, rows)
     for n in range(F * S):
         t = n // S
         k0, k1 = lo[t] * S, (hi[t] + 1) * S
         s = q[n] @ k[k0:k1].T / math.sqrt(d)
         assert lse[n] == pytest.approx(scipy.special.logsumexp(s), rel=1e-14)
+        if n in rows:
+            i = int(np.nonzero(rows == n)[0][0])
+            assert lse_rows[i] == pytest.approx(scipy.special.logsumexp(s), rel=1e-14)
         np.testing.assert_allclose(np.exp(s - lse[n]) @ v[k0:k1], o[n], rtol=1e-12, atol=1e-14)
 
 

@@ -76,3 +76,51 @@ def test_rel_frobenius_semantics():
     assert abs(oracle.rel_frobenius(1.5 * a, a) - 0.5) < 1e-15
     assert oracle.rel_frobenius(np.zeros(3), np.zeros(3)) == 0.0
     assert oracle.rel_frobenius(np.array([1e-30, 0, 0]), np.zeros(3)) == float("inf")
+
+
+@pytest.mark.parametrize("workers", [1, 3])
+def test_whole_call_wrapper_is_the_slice_definition(workers):
+    # the [B, H] wrapper (task split over (b, h, query chunk) and (b, h), run
+    # in one process or a pool) equals the one-slice definition for every
+    # (b, h): per-head conv taps, per-slice text states and alpha, a partial
+    # last chunk, and separate softmax-branch q/k for the softmax tasks
+    cfg = inputs.tiny_config(frames=12, text_tokens=8, head_dim=16, tokens_per_frame=10,
+                             heads=2, batch=2, chunk=5, seed=301)
+    inp = inputs.make(cfg, random_rms_weight=True)
+    other = inputs.make({**cfg, "seed": 302})
+    B, H, F, S = cfg["batch"], cfg["heads"], cfg["frames"], cfg["tokens_per_frame"]
+    f64 = lambda name, src=inp: src.f32(name).astype(np.float64)  # noqa: E731
+    st = np.stack([np.stack([oracle.text_state(inp.f64("k_txt", b, h), inp.f64("v_txt", b, h),
+                                               inp.beta_txt[b, h]) for h in range(H)])
+                   for b in range(B)])
+    assert not np.allclose(inp.conv_k[0], inp.conv_k[1])
+    assert not np.allclose(st[0, 0], st[1, 1]) and not np.allclose(inp.alpha[0, 1], inp.alpha[1, 1])
+    for rope in (False, True):
+        qr = f64("q", other) if rope else None
+        kr = f64("k", other) if rope else None
+        out, o_sm, y = oracle.hybrid_attn(
+            f64("q"), f64("k"), f64("v"), inp.beta.astype(np.float64),
+            inp.alpha.astype(np.float64), f64("gate"), st, inp.conv_k, inp.conv_v,
+            inp.rms_weight, F, S, cfg["chunk"], cfg["radius"], "vdn_scaled", 0.5, 0.5, 1e-6,
+            q_rope=qr, k_rope=kr, workers=workers)
+        for b in range(B):
+            for h in range(H):
+                ref = oracle.hybrid_attn_head(
+                    inp.f64("q", b, h), inp.f64("k", b, h), inp.f64("v", b, h),
+                    inp.beta[b, h], inp.alpha[b, h], inp.f64("gate", b, h), st[b, h],
+                    inp.conv_k[h], inp.conv_v[h], inp.rms_weight, S, cfg["chunk"],
+                    cfg["radius"], "vdn_scaled", 0.5, 0.5, 1e-6,
+                    q_rope=None if qr is None else qr[b, h],
+                    k_rope=None if kr is None else kr[b, h])
+                for got, r in ((out, ref[0]), (o_sm, ref[1]), (y, ref[2])):
+                    assert np.allclose(got[b, h], r, rtol=1e-12, atol=1e-15), (rope, b, h)
+        assert np.any(y) and np.array_equal(out, o_sm + y)
+    # without a text state and with the default (unit) RMSNorm weight
+    out, o_sm, y = oracle.hybrid_attn(
+        f64("q"), f64("k"), f64("v"), inp.beta.astype(np.float64),
+        inp.alpha.astype(np.float64), f64("gate"), None, inp.conv_k, inp.conv_v, None, F, S,
+        workers=workers)
+    ref = oracle.hybrid_attn_head(inp.f64("q", 1, 0), inp.f64("k", 1, 0), inp.f64("v", 1, 0),
+                                  inp.beta[1, 0], inp.alpha[1, 0], inp.f64("gate", 1, 0), None,
+                                  inp.conv_k[0], inp.conv_v[0], np.ones(16), S)
+    assert np.allclose(out[1, 0], ref[0], rtol=1e-12, atol=1e-15)
