@@ -36,6 +36,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector, packed) / fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_traffic.json")
+# the workload the softmax kernel's HBM counters were taken on
+TRAFFIC_WORKLOAD = "long-clip-832x480-85f"
+# the full-size workloads the metric spans (48k to 262k tokens)
+RANGE_WORKLOADS = ("clip-832x480-31f", "long-clip-832x480-85f", "canvas-1024x1024-64f")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_bwd_traffic.json")
 # the softmax kernel's sources (the kernel, the readout epilogue and the tile
 # helpers it includes)
@@ -140,36 +144,80 @@ def linear_bwd_traffic(kernel):
     return rec.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
-def cpu_baseline(inp, rule, heads_run=1):
-    """The fp64 oracle as it stands, on `heads_run` whole heads of the same
-    workload (softmax branch, linear branch and text state), scaled to the
-    whole job's tokens/s."""
+def host_info():
+    """CPU model and the numpy / BLAS build this process uses."""
     import numpy as np
-    import oracle
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')})"
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        pass
+    return {"cpu_model": model, "numpy": np.__version__, "blas": blas}
+
+
+def cpu_workers():
+    """Worker processes for the oracle: the host cores this process may run
+    on, at most 16 (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(inp, rule, heads_run=None, workers=None):
+    """The fp64 oracle as it stands (oracle.hybrid_attn: softmax branch per
+    (batch, head, query chunk), linear branch per (batch, head), text states)
+    on the first `heads_run` heads of the same workload, run by a pool of
+    `workers` processes with one BLAS thread each, scaled to the whole job's
+    tokens/s. Call it before the GPU is touched: the pool forks."""
+    import math
+
+    import numpy as np
+    import oracle
     cfg = inp.cfg
-    S = cfg["tokens_per_frame"]
+    W = workers or cpu_workers()
+    F, S, ch = cfg["frames"], cfg["tokens_per_frame"], cfg["chunk"]
+    nch = -(-F // ch)
+    if heads_run is None:  # enough tasks for six per worker (about 10-20 s)
+        heads_run = max(1, math.ceil(6 * W / (nch + 1)))
+    hr = min(heads_run, cfg["heads"])
+    B = cfg["batch"]
+    from hybrid_window_softmax_amd import inputs
+
+    def f32(name):  # exact upcast of the first hr heads of an I/O tensor
+        a = np.ascontiguousarray(getattr(inp, name)[:, :hr])
+        return inputs.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+    q, k, v, gate = f32("q"), f32("k"), f32("v"), f32("gate")
     t0 = time.perf_counter()
-    for h in range(heads_run):
-        st = None
-        if inp.k_txt is not None:
-            st = oracle.text_state(inp.f64("k_txt", 0, h), inp.f64("v_txt", 0, h),
-                                   inp.beta_txt[0, h].astype(np.float64))
-        oracle.hybrid_attn_head(inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h),
-                                inp.beta[0, h], inp.alpha[0, h], inp.f64("gate", 0, h), st,
-                                inp.conv_k[h], inp.conv_v[h], inp.rms_weight, S,
-                                cfg["chunk"], cfg["radius"], rule, cfg["c"], 0.5, 1e-6)
+    st = None
+    if inp.k_txt is not None:
+        st = np.stack([np.stack([oracle.text_state(inp.f64("k_txt", b, h),
+                                                   inp.f64("v_txt", b, h),
+                                                   inp.beta_txt[b, h].astype(np.float64))
+                                 for h in range(hr)]) for b in range(B)])
+    oracle.hybrid_attn(q, k, v, inp.beta[:, :hr], inp.alpha[:, :hr], gate, st,
+                       inp.conv_k[:hr], inp.conv_v[:hr], inp.rms_weight, F, S, ch,
+                       cfg["radius"], rule, cfg["c"], 0.5, 1e-6, workers=W)
     dt = time.perf_counter() - t0
-    N = cfg["frames"] * S
-    total_s = dt * cfg["heads"] * cfg["batch"] / heads_run
-    return {"value": N * cfg["batch"] / total_s, "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{heads_run} of {cfg['heads']} heads (all {N} tokens of each), "
-                      f"{dt:.1f} s wall, scaled by heads"}
+    N = F * S
+    total_s = dt * cfg["heads"] / hr
+    return {"value": N * B / total_s, "unit": "tokens/s", "cores": W, "kind": "oracle",
+            "sample": f"{hr} of {cfg['heads']} heads (all {N} tokens of each; "
+                      f"{B * hr * (nch + 1)} tasks: softmax per (batch, head, query chunk), "
+                      f"linear branch per (batch, head), plus the text states) on {W} worker "
+                      f"processes with one BLAS thread each, {dt:.1f} s wall, scaled by heads",
+            **host_info()}
 
 
 def softmax_bwd_cpu_baseline(inp, g_host, heads_run=1):
@@ -270,7 +318,7 @@ def bench_softmax_bwd(args, cfg, inp, up):
         log("bench: timing the CPU oracle's gradient on a sample")
         del q, k, v, g, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
-        cpu = softmax_bwd_cpu_baseline(inp, g_host, args.cpu_heads)
+        cpu = softmax_bwd_cpu_baseline(inp, g_host, args.cpu_heads or 1)
     return {
         "metric": "windowed-softmax backward (dq, dk, dv) tokens/s",
         "value": round(B * N / (ms / 1000.0), 1),
@@ -402,7 +450,7 @@ def bench_linear_bwd(args, cfg, inp, up):
         log("bench: timing the CPU oracle's linear-branch gradient on a sample")
         del t, g, text, grads, ws
         torch.cuda.empty_cache()
-        cpu = linear_bwd_cpu_baseline(inp, g_host, st_host, args.rule, args.cpu_heads)
+        cpu = linear_bwd_cpu_baseline(inp, g_host, st_host, args.rule, args.cpu_heads or 1)
     return {
         "metric": "linear-branch backward (dq, dk, dv, dbeta, dalpha, dgate, dS_text, dconv, "
                   "dw) tokens/s",
@@ -434,6 +482,22 @@ def bench_train_step(args, cfg, inp, up):
     import torch
     from hybrid_window_softmax_amd import hwa, inputs
     g_host = inputs.grad_output(cfg)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle's forward and gradients on a sample")
+        g_host_st = inputs.state_matrix(cfg)
+        hr = args.cpu_heads or 1
+        parts = [cpu_baseline(inp, args.rule, hr),
+                 softmax_bwd_cpu_baseline(inp, g_host, hr),
+                 linear_bwd_cpu_baseline(inp, g_host, g_host_st, args.rule, hr)]
+        tok = cfg["batch"] * cfg["frames"] * cfg["tokens_per_frame"]
+        total_s = sum(tok / p["value"] for p in parts)
+        cpu = {"value": tok / total_s, "unit": "tokens/s", "cores": parts[0]["cores"],
+               "kind": "oracle",
+               "sample": f"{hr} of {cfg['heads']} heads (all tokens of each) of the forward "
+                         "(worker pool), the softmax gradient and the linear-branch gradient "
+                         "(BLAS threads), each scaled by heads",
+               **host_info()}
     t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
                                           "conv_v", "rms_weight", "k_txt", "v_txt",
                                           "beta_txt")}
@@ -497,21 +561,6 @@ def bench_train_step(args, cfg, inp, up):
                 "traffic": recorded_traffic(BWD_TRAFFIC_FILE, SOFTMAX_BWD_SRCS)
                 if cfg["name"] == "long-clip-832x480-85f" else None,
                 "algorithmic_flops_per_launch": dkdv_flops}
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle's forward and gradients on a sample")
-        del t, g, text, out, o_sm, lse, dq, dk, dv, st
-        torch.cuda.empty_cache()
-        g_host_st = inputs.state_matrix(cfg)
-        parts = [cpu_baseline(inp, args.rule, args.cpu_heads),
-                 softmax_bwd_cpu_baseline(inp, g_host, args.cpu_heads),
-                 linear_bwd_cpu_baseline(inp, g_host, g_host_st, args.rule, args.cpu_heads)]
-        tok = B * N
-        total_s = sum(tok / p["value"] for p in parts)
-        cpu = {"value": tok / total_s, "unit": "tokens/s", "cores": parts[0]["cores"],
-               "kind": "oracle",
-               "sample": f"{args.cpu_heads} of {H} heads (all {N} tokens of each) of the forward, "
-                         "the softmax gradient and the linear-branch gradient, each scaled by heads"}
     return {
         "metric": "hybrid attention training step (forward + backward, every input's gradient) "
                   "tokens/s",
@@ -543,8 +592,12 @@ def main():
     ap.add_argument("--workload", default="long-clip-832x480-85f",
                     help="a name in hybrid_window_softmax_amd.inputs.WORKLOADS")
     ap.add_argument("--rule", default="vdn_solve")
-    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="heads of the CPU oracle's sample (default: two tasks per worker)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-range", action="store_true",
+                    help="skip the other rules and full-size workloads of the metric's range")
+    ap.add_argument("--range-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (three times), the "
                          "reference kernel for scaling HBM byte counters")
@@ -621,6 +674,85 @@ def main():
         print(json.dumps(bench_train_step(args, cfg, inp, up)), flush=True)
         return
 
+    cpu = None
+    if not args.no_cpu_baseline:
+        # first, while no GPU state exists in this process: the pool forks
+        log("bench: timing the CPU oracle on a sample")
+        cpu = cpu_baseline(inp, args.rule, args.cpu_heads)
+    res = time_forward(cfg, inp, args.rule, args.steps, args.warmup, up)
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+    tokens = cfg["batch"] * F * S
+    ms = res["ms"]
+    rng = None
+    if not args.no_range:
+        # the rest of the metric's range: the other rules on this workload and
+        # the other full-size workloads, each timed the same way
+        rng = {}
+        cases = [(cfg["name"], r) for r in cfg["rules"] if r != args.rule]
+        cases += [(n, "vdn_solve") for n in RANGE_WORKLOADS if n != cfg["name"]]
+        for name, rule in cases:
+            c2 = inputs.WORKLOADS[name]
+            log(f"bench: range entry {name} {rule}")
+            inp2 = inp if name == cfg["name"] else inputs.make(c2)
+            r2 = time_forward(c2, inp2, rule, args.range_steps, 2, make_up(c2))
+            rng[f"{name} {rule}"] = {
+                "tokens": c2["batch"] * c2["frames"] * c2["tokens_per_frame"],
+                "ms_per_step": round(r2["ms"], 4),
+                "tokens_per_s": round(c2["batch"] * c2["frames"] * c2["tokens_per_frame"]
+                                      / (r2["ms"] / 1000.0), 1),
+                "softmax_frac": r2["roofline"]["frac"],
+                "hbm_frac": {k: v["hbm_frac"] for k, v in r2["kernels"].items()
+                             if k != "softmax"},
+            }
+            del inp2
+    rec = {
+        "metric": "hybrid-attn fwd tokens/s at 48k-262k tokens; % of MFMA / HBM roofline",
+        "value": round(tokens / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: B{cfg['batch']} H{cfg['heads']} "
+                               f"d{cfg['head_dim']} F{F} x S{S} = {F * S} tokens, "
+                               f"chunk {cfg['chunk']} radius {cfg['radius']}, "
+                               f"{args.rule}, text state from {cfg['text_tokens']} tokens",
+                   "tokens": F * S, "heads": cfg["heads"], "head_dim": cfg["head_dim"],
+                   "rule": args.rule},
+        "roofline": res["roofline"],
+        "kernels": res["kernels"],
+        "range": rng,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def make_up(cfg):
+    """Host array -> device tensor for a workload (bf16 bits become bf16)."""
+    import torch
+    dev = torch.device("cuda:0")
+    bf = cfg["dtype"] == "bf16"
+
+    def up(a):
+        if a is None:
+            return None
+        if bf and a.dtype.name == "uint16":
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    return up
+
+
+def time_forward(cfg, inp, rule, steps, warmup, up):
+    """Time `steps` hybrid_attn_fwd calls on a workload (after `warmup`
+    untimed ones): wall time per call, every stage's hipEvent time and rates,
+    and the softmax kernel's roofline. Frees its device memory."""
+    import torch
+    from hybrid_window_softmax_amd import hwa
     t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
                                           "conv_v", "rms_weight", "k_txt", "v_txt",
                                           "beta_txt")}
@@ -633,29 +765,29 @@ def main():
     def call(events=None, ws=None):
         return hwa.hybrid_attn_fwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"],
                                    text, t["conv_k"], t["conv_v"], F, S, cfg["chunk"],
-                                   cfg["radius"], args.rule, cfg["c"], 0.5, 1e-6,
+                                   cfg["radius"], rule, cfg["c"], 0.5, 1e-6,
                                    t["rms_weight"], out=out, workspace=ws,
                                    stage_events=events)[1]
 
-    log("bench: warmup")
+    log(f"bench: {cfg['name']} {rule}: warmup")
     ws = call()
-    for _ in range(max(0, args.warmup - 1)):
+    for _ in range(max(0, warmup - 1)):
         call(ws=ws)
     torch.cuda.synchronize()
-    timer = hwa.StageTimer(args.steps)
-    log(f"bench: timing {args.steps} steps")
+    timer = hwa.StageTimer(steps)
+    log(f"bench: {cfg['name']} {rule}: timing {steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         call(events=timer.sets[i], ws=ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     stage = timer.stage_ms()
     timer.close()
-    ms = (t1 - t0) * 1000.0 / args.steps
-    tokens = cfg["batch"] * F * S
+    ms = (t1 - t0) * 1000.0 / steps
     log("bench: stage ms " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()))
 
+    bf = cfg["dtype"] == "bf16"
     work = algorithmic_work(cfg)
     fused = bf  # the library fuses the readout into the softmax on bf16 (no q_rope)
     if fused:
@@ -680,40 +812,11 @@ def main():
                 "bound": "mfma",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": softmax_traffic(),
+                "traffic": softmax_traffic() if cfg["name"] == TRAFFIC_WORKLOAD else None,
                 "algorithmic_flops_per_launch": sm_flops}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle on a sample")
-        del t, out, ws
-        torch.cuda.empty_cache()
-        cpu = cpu_baseline(inp, args.rule, args.cpu_heads)
-
-    rec = {
-        "metric": "hybrid-attn fwd tokens/s at 48k-262k tokens; % of MFMA / HBM roofline",
-        "value": round(tokens / (ms / 1000.0), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg["dtype"],
-        "data": "synthetic",
-        "config": {"workload": f"{cfg['name']}: B{cfg['batch']} H{cfg['heads']} "
-                               f"d{cfg['head_dim']} F{F} x S{S} = {F * S} tokens, "
-                               f"chunk {cfg['chunk']} radius {cfg['radius']}, "
-                               f"{args.rule}, text state from {cfg['text_tokens']} tokens",
-                   "tokens": F * S, "heads": cfg["heads"], "head_dim": cfg["head_dim"],
-                   "rule": args.rule},
-        "roofline": roofline,
-        "kernels": kernels,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(rec), flush=True)
+    del t, text, out, ws
+    torch.cuda.empty_cache()
+    return {"ms": ms, "stage": stage, "kernels": kernels, "roofline": roofline}
 
 
 if __name__ == "__main__":

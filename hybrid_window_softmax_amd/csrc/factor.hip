@@ -7,6 +7,10 @@
 // multiplies by M_f. (sana_scaled, S -> (S D)(I - c^2 A) + c B, needs no
 // inverse.)
 //
+// bf16 calls take M in the operand order of the bf16 scan, split into hi and
+// lo bf16 parts (launch_update_packed; for sana_scaled the same kernel writes
+// I - c^2 A without inverting).
+//
 // Inversion is the in-place Gauss-Jordan sweep without pivoting. It is
 // stable here because I + c~^2 A >= I: every pivot is a Schur complement of
 // an SPD matrix >= I, hence >= 1. A workgroup of 256 threads inverts one
@@ -19,9 +23,22 @@
 
 namespace hwa {
 
-template <int D>
+// Element (r, c) of a d x d matrix in the bf16 scan's operand order: the
+// B operand of wave w = r / 32 (output columns 32w .. 32w+31) at step
+// kk = c / 16 is one contiguous 1 KB block, lane (c % 16) / 8 * 32 + r % 32
+// holding the 8 consecutive elements c - c % 8 .. (the scan multiplies by M
+// from the right and M is symmetric, so row r of M is column r).
+__host__ __device__ constexpr long long packed_index(int D, int r, int c) {
+  return ((((long long)(r / 32) * (D / 16) + c / 16) * 64) + ((c % 16) / 8) * 32 + r % 32) * 8 +
+         c % 8;
+}
+
+// PACK: write M as two bf16 matrices, hi = bf16(M) then lo = bf16(M - hi), in
+// the order of packed_index (2 * d * d elements per matrix), for the bf16
+// scan. INVERT == false: M = I - c2 A itself (sana_scaled's update matrix).
+template <int D, bool PACK, bool INVERT>
 __global__ __launch_bounds__(256) void inverse_kernel(
-    const float* __restrict__ A, float* __restrict__ M, float c2) {
+    const float* __restrict__ A, void* __restrict__ Mout, float c2) {
   constexpr int BS = D / 16;
   __shared__ float rowbuf[2][D];
   __shared__ float colbuf[2][D];
@@ -30,16 +47,17 @@ __global__ __launch_bounds__(256) void inverse_kernel(
   const int ib = tid / 16, jb = tid % 16;
   const long long mo = (long long)blockIdx.x * D * D;
   float m[BS][BS];
+  const float sgn = INVERT ? 1.0f : -1.0f;
 #pragma unroll
   for (int a = 0; a < BS; ++a)
 #pragma unroll
     for (int b = 0; b < BS; ++b) {
       const int i = ib * BS + a, j = jb * BS + b;
-      m[a][b] = (i == j ? 1.0f : 0.0f) + c2 * A[mo + (long long)i * D + j];
+      m[a][b] = (i == j ? 1.0f : 0.0f) + sgn * c2 * A[mo + (long long)i * D + j];
     }
 
   // pivot k = kb * BS + kr; kr is unrolled so register indices are static
-  for (int kb = 0; kb < 16; ++kb) {
+  for (int kb = 0; kb < (INVERT ? 16 : 0); ++kb) {
 #pragma unroll
     for (int kr = 0; kr < BS; ++kr) {
       const int k = kb * BS + kr;
@@ -77,11 +95,40 @@ __global__ __launch_bounds__(256) void inverse_kernel(
       }
     }
   }
+  if constexpr (PACK) {
+    // a thread's BS consecutive columns of a row are one 2 * BS-byte run
+    bf16_t* P = (bf16_t*)Mout + (long long)blockIdx.x * 2 * D * D;
 #pragma unroll
-  for (int a = 0; a < BS; ++a)
+    for (int a = 0; a < BS; ++a) {
+      const int r = ib * BS + a;
+      uint32_t hw[BS / 2], lw[BS / 2];
 #pragma unroll
-    for (int b = 0; b < BS; ++b)
-      M[mo + (long long)(ib * BS + a) * D + jb * BS + b] = m[a][b];
+      for (int b = 0; b < BS; b += 2) {
+        __bf16 h0, l0, h1, l1;
+        split_bf16(m[a][b], h0, l0);
+        split_bf16(m[a][b + 1], h1, l1);
+        hw[b / 2] = (uint32_t)__builtin_bit_cast(bf16_t, h0) |
+                    ((uint32_t)__builtin_bit_cast(bf16_t, h1) << 16);
+        lw[b / 2] = (uint32_t)__builtin_bit_cast(bf16_t, l0) |
+                    ((uint32_t)__builtin_bit_cast(bf16_t, l1) << 16);
+      }
+      const long long o = packed_index(D, r, jb * BS);
+      if constexpr (BS == 8) {
+        *(uint4*)(P + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *(uint4*)(P + D * D + o) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      } else if constexpr (BS == 4) {
+        *(uint2*)(P + o) = make_uint2(hw[0], hw[1]);
+        *(uint2*)(P + D * D + o) = make_uint2(lw[0], lw[1]);
+      }
+    }
+  } else {
+    float* M = (float*)Mout;
+#pragma unroll
+    for (int a = 0; a < BS; ++a)
+#pragma unroll
+      for (int b = 0; b < BS; ++b)
+        M[mo + (long long)(ib * BS + a) * D + jb * BS + b] = m[a][b];
+  }
 }
 
 // C = B M for every matrix (text state: S_text = B (I + A)^-1).
@@ -123,7 +170,7 @@ hipError_t launch_inverse(const Geom& g, float c2, const float* A, float* M,
                           hipStream_t st) {
   dim3 grid((unsigned)((long long)g.B * g.H * g.F));
 #define INV_LAUNCH(DD) \
-  hipLaunchKernelGGL(inverse_kernel<DD>, grid, dim3(256), 0, st, A, M, c2)
+  hipLaunchKernelGGL((inverse_kernel<DD, false, true>), grid, dim3(256), 0, st, A, M, c2)
   switch (g.d) {
     case 16: INV_LAUNCH(16); break;
     case 32: INV_LAUNCH(32); break;
@@ -131,6 +178,27 @@ hipError_t launch_inverse(const Geom& g, float c2, const float* A, float* M,
     default: INV_LAUNCH(128); break;
   }
 #undef INV_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_update_packed(const Geom& g, bool invert, float c2, const float* A,
+                                bf16_t* packed, hipStream_t st) {
+  dim3 grid((unsigned)((long long)g.B * g.H * g.F));
+  if (g.d == 128) {
+    if (invert)
+      hipLaunchKernelGGL((inverse_kernel<128, true, true>), grid, dim3(256), 0, st, A,
+                         (void*)packed, c2);
+    else
+      hipLaunchKernelGGL((inverse_kernel<128, true, false>), grid, dim3(256), 0, st, A,
+                         (void*)packed, c2);
+  } else {
+    if (invert)
+      hipLaunchKernelGGL((inverse_kernel<64, true, true>), grid, dim3(256), 0, st, A,
+                         (void*)packed, c2);
+    else
+      hipLaunchKernelGGL((inverse_kernel<64, true, false>), grid, dim3(256), 0, st, A,
+                         (void*)packed, c2);
+  }
   return hipGetLastError();
 }
 

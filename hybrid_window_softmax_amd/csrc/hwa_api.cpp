@@ -171,7 +171,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                            const void* gate, const float* text_state,
                            int32_t frames, int32_t tokens_per_frame,
                            int32_t chunk, int32_t radius, int32_t rule,
-                           void* out, void* stream, const hwa_params* p) {
+                           void* out, hipStream_t stream, const hwa_params* p) {
   hwa_status s = check_params(p);
   if (s != HWA_OK) return s;
   Geom g;
@@ -179,8 +179,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
     return HWA_ERR_INVALID_ARG;
   if (rule < HWA_RULE_VDN_SOLVE || rule > HWA_RULE_VDN_SCALED)
     return HWA_ERR_INVALID_ARG;
-  const uint32_t known = HWA_FLAG_SOFTMAX_ONLY | HWA_FLAG_LINEAR_ONLY |
-                         HWA_FLAG_KEEP_INTERMEDIATES;
+  const uint32_t known = HWA_FLAG_SOFTMAX_ONLY | HWA_FLAG_LINEAR_ONLY;
   if (p->flags & ~known) return HWA_ERR_INVALID_ARG;
   const bool do_sm = !(p->flags & HWA_FLAG_LINEAR_ONLY);
   const bool do_lin = !(p->flags & HWA_FLAG_SOFTMAX_ONLY);
@@ -236,7 +235,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
       overlaps(lse_out, lse_bytes, sm_out, io_bytes))
     return HWA_ERR_INVALID_ARG;
 
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = stream;
   char* ws = (char*)p->workspace;
   int32_t* lohi = (int32_t*)(ws + L.lohi);
   float* A = (float*)(ws + L.stat_a);
@@ -265,15 +264,27 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                   p->conv_v, true, A, Bm, st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(2) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && rule != HWA_RULE_SANA_SCALED) {
+  const bool bf = p->dtype == HWA_BF16;
+  if (do_lin && bf) {
+    // M_f = (I + c~^2 A_f)^-1, or I - c^2 A_f for sana_scaled, written as the
+    // bf16 scan's packed (hi, lo) operands into the map_m region
+    const bool sana = rule == HWA_RULE_SANA_SCALED;
+    const float cc = rule == HWA_RULE_VDN_SOLVE ? 1.0f : p->c * p->c;
+    if (hwa::launch_update_packed(g, !sana, cc, A, (bf16_t*)M, st) != hipSuccess)
+      return HWA_ERR_HIP;
+  } else if (do_lin && rule != HWA_RULE_SANA_SCALED) {
     const float cc = rule == HWA_RULE_VDN_SCALED ? p->c : 1.0f;
     if (hwa::launch_inverse(g, cc * cc, A, M, st) != hipSuccess)
       return HWA_ERR_HIP;
   }
   if (mark(3) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && hwa::launch_scan(g, p->dtype, rule, p->c, A, Bm, M, alpha,
-                                 text_state, p->text_scale, bank_p, bank_q,
-                                 bank_e, st) != hipSuccess)
+  if (do_lin && bf &&
+      hwa::launch_scan_packed(g, rule, p->c, (const bf16_t*)M, Bm, alpha, text_state,
+                              p->text_scale, bank_p, bank_q, bank_e, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (do_lin && !bf &&
+      hwa::launch_scan(g, p->dtype, rule, p->c, A, Bm, M, alpha, text_state, p->text_scale,
+                       bank_p, bank_q, bank_e, st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(4) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && hwa::launch_decay(g, alpha, lohi, decay, st) != hipSuccess)
@@ -344,7 +355,7 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
                            const void* o_sm, const float* lse, const void* d_o,
                            int32_t frames, int32_t tokens_per_frame,
                            int32_t chunk, int32_t radius, void* dq, void* dk,
-                           void* dv, void* stream, const hwa_params* p) {
+                           void* dv, hipStream_t stream, const hwa_params* p) {
   hwa_status s = check_params(p);
   if (s != HWA_OK) return s;
   Geom g;
@@ -375,7 +386,7 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
       if (overlaps(outs[i], io_bytes, outs[j], io_bytes)) return HWA_ERR_INVALID_ARG;
   }
 
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = stream;
   char* ws = (char*)p->workspace;
   int32_t* lohi = (int32_t*)(ws + L.lohi);
   float* delta = (float*)(ws + L.delta);
@@ -457,7 +468,7 @@ hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const flo
                           int32_t chunk, int32_t radius, int32_t rule, void* dq, void* dk,
                           void* dv, float* dbeta, float* dalpha, void* dgate,
                           float* dtext_state, float* dconv_k, float* dconv_v,
-                          float* drms_weight, void* stream, const hwa_params* p) {
+                          float* drms_weight, hipStream_t stream, const hwa_params* p) {
   hwa_status s = check_params(p);
   if (s != HWA_OK) return s;
   Geom g;
@@ -532,7 +543,7 @@ hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const flo
   a.dkc = (float*)(ws + L.dkc); a.dvc = (float*)(ws + L.dvc);
   a.cpart = (float*)(ws + L.cpart);
 
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = stream;
   void* const* ev = p->stage_events;
   auto mark = [&](int i) {
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
@@ -555,7 +566,7 @@ size_t hwa_text_state_workspace_bytes(int32_t text_tokens,
 
 hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
                           const float* beta_txt, int32_t text_tokens,
-                          float* state_out, void* stream,
+                          float* state_out, hipStream_t stream,
                           const hwa_params* p) {
   hwa_status s = check_params(p);
   if (s != HWA_OK) return s;
@@ -576,10 +587,13 @@ hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
       overlaps(state_out, st_bytes, beta_txt, bh * text_tokens * sizeof(float)) ||
       overlaps(state_out, st_bytes, p->workspace, p->workspace_bytes))
     return HWA_ERR_INVALID_ARG;
-  const size_t va = p->dtype == HWA_BF16 ? 2 : 4;
-  if (!aligned(k_txt, va) || !aligned(v_txt, va) || !aligned(state_out, 16))
+  // the forward's rules: 16 bytes for bf16 token rows (the statistics kernel
+  // reads them 8 bytes at a time), 4 bytes for fp32 arrays
+  const size_t va = p->dtype == HWA_BF16 ? 16 : 4;
+  if (!aligned(k_txt, va) || !aligned(v_txt, va) || !aligned(beta_txt, 4) ||
+      !aligned(state_out, 16))
     return HWA_ERR_INVALID_ARG;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = stream;
   float* A = (float*)p->workspace;
   float* Bm = (float*)((char*)p->workspace + need / 3);
   float* M = (float*)((char*)p->workspace + 2 * (need / 3));
@@ -588,6 +602,34 @@ hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
     return HWA_ERR_HIP;
   if (hwa::launch_inverse(g, 1.0f, A, M, st) != hipSuccess) return HWA_ERR_HIP;
   if (hwa::launch_matmul_bm(g, Bm, M, state_out, st) != hipSuccess)
+    return HWA_ERR_HIP;
+  return HWA_OK;
+}
+
+hwa_status hwa_frame_alpha(const void* k, const float* w, const float* bias,
+                           const float* a_log, int32_t frames, int32_t tokens_per_frame,
+                           float* alpha, hipStream_t stream, const hwa_params* p) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, 1, 0, p, g)) return HWA_ERR_INVALID_ARG;
+  if (!k || !w || !bias || !a_log || !alpha) return HWA_ERR_INVALID_ARG;
+  // 16-byte row loads of k; fp32 arrays on 4 bytes
+  if (!aligned(k, 16) || !aligned(w, 4) || !aligned(bias, 4) || !aligned(a_log, 4) ||
+      !aligned(alpha, 4))
+    return HWA_ERR_INVALID_ARG;
+  const size_t es = p->dtype == HWA_BF16 ? 2 : 4;
+  const size_t bh = (size_t)g.B * g.H;
+  const size_t a_bytes = bh * (size_t)g.F * g.d * sizeof(float);
+  const struct { const void* ptr; size_t n; } ins[] = {
+      {k, bh * (size_t)g.N * g.d * es},
+      {w, (size_t)g.H * g.d * g.d * sizeof(float)},
+      {bias, (size_t)g.H * g.d * sizeof(float)},
+      {a_log, (size_t)g.H * g.d * sizeof(float)},
+  };
+  for (const auto& in : ins)
+    if (overlaps(alpha, a_bytes, in.ptr, in.n)) return HWA_ERR_INVALID_ARG;
+  if (hwa::launch_frame_alpha(g, p->dtype, k, w, bias, a_log, alpha, stream) != hipSuccess)
     return HWA_ERR_HIP;
   return HWA_OK;
 }

@@ -130,6 +130,12 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
 hipError_t launch_inverse(const Geom& g, float c2, const float* A, float* M,
                           hipStream_t st);
 
+// bf16 calls: M_f = (I + c2 A_f)^-1 (invert) or M_f = I - c2 A_f (not invert),
+// as hi and lo bf16 matrices in the bf16 scan's operand order, [B*H*F][2][d*d]
+// (d = 64 or 128).
+hipError_t launch_update_packed(const Geom& g, bool invert, float c2, const float* A,
+                                bf16_t* packed, hipStream_t st);
+
 // C = B M for every (b, h, f).
 hipError_t launch_matmul_bm(const Geom& g, const float* Bm, const float* M,
                             float* C, hipStream_t st);
@@ -140,6 +146,18 @@ hipError_t launch_scan(const Geom& g, int dtype, int rule, float c,
                        const float* alpha, const float* text_state,
                        float text_scale, float* bank_p, float* bank_q,
                        int32_t* bank_e, hipStream_t st);
+
+// Per-frame forget gate alpha [B*H, F, d] = exp(-exp(a_log) softplus(mean_f(k) W + bias))
+// (W: [H, d, d], input channel x output channel; bias, a_log: [H, d]).
+hipError_t launch_frame_alpha(const Geom& g, int dtype, const void* k, const float* w,
+                              const float* bias, const float* a_log, float* alpha,
+                              hipStream_t st);
+
+// The forward's bf16 scan on packed update matrices (launch_update_packed).
+hipError_t launch_scan_packed(const Geom& g, int rule, float c, const bf16_t* Mp,
+                              const float* Bm, const float* alpha, const float* text_state,
+                              float text_scale, float* bank_p, float* bank_q,
+                              int32_t* bank_e, hipStream_t st);
 
 // Bridge decays of every (b, h, t): prod_{j=lo..t} alpha_j, prod_{j=t..hi}.
 hipError_t launch_decay(const Geom& g, const float* alpha, const int32_t* lohi,

@@ -313,6 +313,180 @@ __global__ __launch_bounds__(2 * D) void scan_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bf16 path,
+// update matrices packed by launch_update_packed
+// The forward's bf16 scan. M_f (or I - c^2 A_f for sana_scaled) arrives as
+// hi and lo bf16 matrices already in MFMA operand order: wave w's B operand
+// of step kk is one contiguous 1 KB block per part, which every lane loads
+// straight into registers (16 bytes each), one frame ahead. Only X goes
+// through LDS. Per frame:
+//   X = S diag(alpha) + c1 2^-e B (own 32 x 32 block) -> split to bf16 (hi,
+//   lo) -> LDS (double buffered); one barrier;
+//   S = X M (+ c2 2^-e B): A operand = rows of X from LDS, B operand = the
+//   registers; the three split products (hi*hi, hi*lo, lo*hi) on separate
+//   accumulators.
+// A write of X buffer b in frame i + 2 cannot overtake a read of it in frame
+// i: every wave passes frame i + 1's barrier after its frame-i reads.
+// Row exponents (SANA, the diverging rule): as in scan_mfma_kernel.
+template <int D, bool SANA>
+__global__ __launch_bounds__(2 * D) void scan_packed_kernel(
+    const bf16_t* __restrict__ Mp, const float* __restrict__ Bm,
+    const float* __restrict__ alpha, float c1, float c2,
+    const float* __restrict__ text_state, float text_scale,
+    float* __restrict__ bank_p, float* __restrict__ bank_q,
+    int32_t* __restrict__ bank_e, int F, int chunk, int nch, int BH) {
+  constexpr int XP = D + 8;    // padded X row (bf16)
+  constexpr int KK = D / 16;   // MFMA steps over the contraction
+  __shared__ __attribute__((aligned(16))) bf16_t x_hi[2][32 * XP];
+  __shared__ __attribute__((aligned(16))) bf16_t x_lo[2][32 * XP];
+  __shared__ unsigned rmax[2][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int rb = blockIdx.x;   // 32-row block
+  const int dir = blockIdx.y;  // 0 prefix, 1 suffix
+  const int bh = blockIdx.z;
+  const int n = wave * 32 + col;  // this lane's state column
+  auto rowof = [&](int r) { return 8 * (r / 4) + 4 * half + (r % 4); };
+
+  float sv[16];
+  int e[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = rb * 32 + rowof(r);
+    sv[r] = text_state ? text_scale * text_state[((long long)bh * D + row) * D + n] : 0.0f;
+    e[r] = 0;
+  }
+  if (SANA && tid < 32) rmax[0][tid] = rmax[1][tid] = 0u;  // published by the first barrier
+  float* bank = dir == 0 ? bank_p : bank_q;
+  int32_t* be = bank_e + (long long)dir * BH * (nch + 1) * D;
+  auto store = [&](int slot) {
+    float* dst = bank + ((long long)bh * (nch + 1) + slot) * D * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[(long long)(rb * 32 + rowof(r)) * D + n] = sv[r];
+    if (wave == 0 && col == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        be[((long long)bh * (nch + 1) + slot) * D + rb * 32 + rowof(r)] = e[r];
+    }
+  };
+  store(dir == 0 ? 0 : nch);
+
+  // the next frame, read ahead: this wave's B operands (hi, lo), this
+  // block's B rows, alpha of this column
+  u32x4_t mnext[2][KK];
+  float braw[16], anext;
+  auto fetch = [&](int f) {
+    const u32x4_t* m4 = (const u32x4_t*)(Mp + ((long long)bh * F + f) * 2 * D * D);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      mnext[0][kk] = m4[(wave * KK + kk) * 64 + lane];
+      mnext[1][kk] = m4[D * D / 8 + (wave * KK + kk) * 64 + lane];
+    }
+    const long long mo = ((long long)bh * F + f) * D * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) braw[r] = Bm[mo + (long long)(rb * 32 + rowof(r)) * D + n];
+    anext = alpha[((long long)bh * F + f) * D + n];
+  };
+  fetch(dir == 0 ? 0 : F - 1);
+
+  for (int i = 0; i < F; ++i) {
+    const int f = dir == 0 ? i : F - 1 - i;
+    const int buf = i & 1;
+    // ---- X = S diag(alpha) + c1 2^-e B (own block) -> LDS (hi, lo)
+    float bcur[16];
+    const float acur = anext;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      bcur[r] = ldexpf(braw[r], -e[r]);
+      const float x = fmaf(c1, bcur[r], sv[r] * acur);
+      __bf16 h, l;
+      split_bf16(x, h, l);
+      x_hi[buf][rowof(r) * XP + n] = __builtin_bit_cast(bf16_t, h);
+      x_lo[buf][rowof(r) * XP + n] = __builtin_bit_cast(bf16_t, l);
+    }
+    u32x4_t mcur[2][KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      mcur[0][kk] = mnext[0][kk];
+      mcur[1][kk] = mnext[1][kk];
+    }
+    if (i + 1 < F) fetch(dir == 0 ? f + 1 : f - 1);
+    __syncthreads();
+    // ---- S = X M (+ c2 2^-e B)
+    f32x16_t acc, acc1, acc2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[r] = c2 * bcur[r];
+      acc1[r] = 0.0f;
+      acc2[r] = 0.0f;
+    }
+    const bf16_t* xh = &x_hi[buf][col * XP + half * 8];
+    const bf16_t* xl = &x_lo[buf][col * XP + half * 8];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8_t ah = *(const bf16x8_t*)(xh + kk * 16);
+      const bf16x8_t al = *(const bf16x8_t*)(xl + kk * 16);
+      const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, mcur[0][kk]);
+      const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, mcur[1][kk]);
+      acc = mfma32(ah, bh, acc);
+      acc1 = mfma32(ah, bl, acc1);
+      acc2 = mfma32(al, bh, acc2);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = acc[r] + (acc1[r] + acc2[r]);
+    if (SANA) {
+      // row max |S| over all columns: 32 lanes of a half, then the waves
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float m = fabsf(sv[r]);
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (col == 0) atomicMax(&rmax[buf][rowof(r)], __float_as_uint(m));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float m = __uint_as_float(rmax[buf][rowof(r)]);
+        if (m > 0x1p64f) {
+          int ex;
+          frexpf(m, &ex);
+          sv[r] = ldexpf(sv[r], -ex);
+          e[r] += ex;
+        }
+      }
+      if (tid < 32) rmax[buf ^ 1][tid] = 0u;  // cleared for the next frame
+    }
+    if (dir == 0) {
+      if ((f + 1) % chunk == 0 || f + 1 == F) store((f + chunk) / chunk);
+    } else {
+      if (f % chunk == 0) store(f / chunk);
+    }
+  }
+}
+
+hipError_t launch_scan_packed(const Geom& g, int rule, float c, const bf16_t* Mp,
+                              const float* Bm, const float* alpha, const float* text_state,
+                              float text_scale, float* bank_p, float* bank_q,
+                              int32_t* bank_e, hipStream_t st) {
+  const bool sana = rule == HWA_RULE_SANA_SCALED;
+  const float c1 = sana ? 0.0f : (rule == HWA_RULE_VDN_SCALED ? c : 1.0f);
+  const float c2 = sana ? c : 0.0f;
+  dim3 grid(g.d / 32, 2, g.B * g.H);
+#define SP_SCAN(DD, SN)                                                                 \
+  hipLaunchKernelGGL((scan_packed_kernel<DD, SN>), grid, dim3(2 * DD), 0, st, Mp, Bm, alpha, \
+                     c1, c2, text_state, text_scale, bank_p, bank_q, bank_e, g.F, g.chunk,   \
+                     g.nch, g.B * g.H)
+  if (g.d == 128) {
+    if (sana) SP_SCAN(128, true); else SP_SCAN(128, false);
+  } else {
+    if (sana) SP_SCAN(64, true); else SP_SCAN(64, false);
+  }
+#undef SP_SCAN
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const Geom& g, int dtype, int rule, float c,
                        const float* A, const float* Bm, const float* M,
                        const float* alpha, const float* text_state,

@@ -7,6 +7,10 @@
 // One workgroup per (b, h, frame). Tokens stream through LDS 32 at a time;
 // every thread owns a (d/16) x (d/16) block of A and of B in registers.
 // Text mode (conv == false) forms k^ = L2(SiLU(k)) and v^ = v.
+// fp32 calls use the VALU kernel (fp32 arithmetic throughout). bf16 calls use
+// the MFMA kernel below, whose operands carry sqrt(beta); it is exact only
+// for beta >= 0, so after it the VALU kernel recomputes, in fp32, the frames
+// that hold a negative beta (the others exit after reading their betas).
 
 #include "hwa_internal.h"
 
@@ -19,7 +23,7 @@ __global__ __launch_bounds__(256) void stats_kernel(
     const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ conv_k,
     const float* __restrict__ conv_v, int conv, float* __restrict__ A,
-    float* __restrict__ Bm, int F, int S, int H, long long N) {
+    float* __restrict__ Bm, int F, int S, int H, long long N, int neg_only) {
   constexpr int TPT = 256 / ST_TT;  // threads per token (8)
   constexpr int CPT = D / TPT;      // channels per thread
   constexpr int BS = D / 16;        // accumulator block edge
@@ -35,6 +39,11 @@ __global__ __launch_bounds__(256) void stats_kernel(
   const T* vp = v + (long long)bh * N * D;
   const float* bp = beta + (long long)bh * N;
   const long long n0 = (long long)f * S;
+  if (neg_only) {  // only frames that hold a negative beta
+    int cnt = 0;
+    for (int s = tid; s < S; s += 256) cnt += bp[n0 + s] < 0.0f ? 1 : 0;
+    if (__syncthreads_or(cnt) == 0) return;
+  }
 
   // conv taps of this thread's channels
   const int tt = tid / TPT;
@@ -127,7 +136,9 @@ __global__ __launch_bounds__(256) void stats_kernel(
 // ---------------------------------------------------------------- bf16 MFMA
 // bf16 I/O: the two contractions over a frame's tokens run on MFMA
 // (v_mfma_f32_32x32x16_bf16) as split-bf16 products. With
-// k' = sqrt(beta) k^ and v' = sqrt(beta) v^:  A = K'^T K',  B = V'^T K'.
+// k' = sqrt(beta) k^ and v' = sqrt(beta) v^:  A = K'^T K',  B = V'^T K'
+// (for beta >= 0; a frame with a negative beta is overwritten afterwards by
+// the fp32 kernel above).
 // Waves in two roles per (b, h, frame), so that the feature VALU work and
 // the MFMAs overlap:
 //  - SX_PW(d) producer waves turn 64-token tiles into features (thread = 4
@@ -352,7 +363,7 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
 #define STATS_LAUNCH(TT, DD)                                                  \
   hipLaunchKernelGGL((stats_kernel<TT, DD>), grid, dim3(256), 0, st,          \
                      (const TT*)k, (const TT*)v, beta, conv_k, conv_v,        \
-                     (int)conv, A, Bm, g.F, g.S, g.H, g.N)
+                     (int)conv, A, Bm, g.F, g.S, g.H, g.N, NEG_ONLY)
 #define STATS_D(TT)                        \
   switch (g.d) {                           \
     case 16: STATS_LAUNCH(TT, 16); break;  \
@@ -368,8 +379,14 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
     if (g.d == 128) SX_LAUNCH(128);
     else SX_LAUNCH(64);
 #undef SX_LAUNCH
+    // frames with a negative beta again, exactly
+#define NEG_ONLY 1
+    STATS_D(bf16_t)
+#undef NEG_ONLY
   } else {
+#define NEG_ONLY 0
     STATS_D(float)
+#undef NEG_ONLY
   }
 #undef STATS_D
 #undef STATS_LAUNCH

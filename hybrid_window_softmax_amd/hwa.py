@@ -20,7 +20,6 @@ RULES = {"vdn_solve": 0, "sana_scaled": 1, "vdn_scaled": 2}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 FLAG_SOFTMAX_ONLY = 1
 FLAG_LINEAR_ONLY = 2
-FLAG_KEEP_INTERMEDIATES = 4
 FLAG_ACCUMULATE = 8
 NUM_STAGE_EVENTS = 9
 STAGES = ("window", "stats", "inverse", "scan", "decay+state", "vtranspose", "softmax",
@@ -44,7 +43,7 @@ HWA_BF16 = 1
 EXPORTS = ("hybrid_attn_fwd", "hwa_workspace_bytes", "hwa_get_workspace_layout",
            "hwa_window_bounds", "hwa_text_state", "hwa_text_state_workspace_bytes",
            "hwa_softmax_bwd", "hwa_softmax_bwd_workspace_bytes", "hwa_linear_bwd",
-           "hwa_linear_bwd_workspace_bytes", "hwa_status_string")
+           "hwa_linear_bwd_workspace_bytes", "hwa_frame_alpha", "hwa_status_string")
 
 
 class Params(ctypes.Structure):
@@ -117,6 +116,8 @@ def lib():
         L.hwa_linear_bwd.restype = ctypes.c_int
         L.hwa_linear_bwd_workspace_bytes.argtypes = [i32, i32, i32, PP]
         L.hwa_linear_bwd_workspace_bytes.restype = sz
+        L.hwa_frame_alpha.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, PP]
+        L.hwa_frame_alpha.restype = ctypes.c_int
         L.hwa_status_string.argtypes = [ctypes.c_int]
         L.hwa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -434,6 +435,29 @@ def text_state(k_txt, v_txt, beta_txt, workspace=None, out=None):
         out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     code = lib().hwa_text_state(_ptr(k_txt), _ptr(v_txt), _ptr(beta_txt), T, _ptr(out),
                                 _stream(dev), ctypes.byref(p))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return out
+
+
+def frame_alpha(k, w, bias, a_log, frames: int, tokens_per_frame: int, out=None,
+                stream=None):
+    """alpha [B, H, F, d] fp32 = exp(-exp(a_log) softplus(mean_frame(k) w + bias))
+    (hwa_frame_alpha). k: [B, H, N, d] bf16 or fp32; w: [H, d, d]; bias,
+    a_log: [H, d] fp32."""
+    B, H, N, d = k.shape
+    dev = k.device
+    _check(k, "k", k.dtype, (B, H, N, d), dev)
+    _check(w, "w", torch.float32, (H, d, d), dev)
+    _check(bias, "bias", torch.float32, (H, d), dev)
+    _check(a_log, "a_log", torch.float32, (H, d), dev)
+    if out is None:
+        out = torch.empty((B, H, frames, d), dtype=torch.float32, device=dev)
+    _check(out, "alpha", torch.float32, (B, H, frames, d), dev)
+    p = make_params(B, H, d, k.dtype)
+    st = _stream(dev) if stream is None else ctypes.c_void_p(stream)
+    code = lib().hwa_frame_alpha(_ptr(k), _ptr(w), _ptr(bias), _ptr(a_log), frames,
+                                 tokens_per_frame, _ptr(out), st, ctypes.byref(p))
     if code != HWA_OK:
         raise HwaError(code)
     return out

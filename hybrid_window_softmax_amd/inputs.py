@@ -13,8 +13,9 @@ the softmax branch 12 (:func:`grad_output`, for the backward pass).
 Distributions (the workloads of the hybrid attention on video-DiT latents):
 q, k, v, gate ~ N(0, 1); beta ~ U(0, 1) per (head, token); alpha ~ U(lo, hi)
 per (head, frame, key channel); conv taps ~ N(0, 1/4); RMSNorm weight = 1;
-text tokens k, v ~ N(0, 1), beta ~ U(0, 1). bf16 tensors are the fp32 draws
-rounded to nearest-even.
+text tokens k, v ~ N(0, 1), beta ~ U(0, 1) (a workload's "beta" range, if it
+gives one, replaces U(0, 1) for video and text tokens). bf16 tensors are the
+fp32 draws rounded to nearest-even.
 """
 
 from __future__ import annotations
@@ -26,7 +27,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TID = dict(q=0, k=1, v=2, gate=3, beta=4, alpha=5, k_txt=6, v_txt=7,
-           beta_txt=8, conv_k=9, conv_v=10, rms_weight=11, d_out=12, state=13)
+           beta_txt=8, conv_k=9, conv_v=10, rms_weight=11, d_out=12, state=13,
+           alpha_w=14, alpha_b=15, alpha_a=16)
 
 # The five workloads, by name. Token counts per frame follow 832x480 (52x30
 # latent grid) and 1024x1024 (64x64) canvases at 16x spatial compression.
@@ -56,13 +58,14 @@ WORKLOADS = {
 
 def tiny_config(frames=17, radius=1, text_tokens=16, rule="vdn_solve",
                 head_dim=16, tokens_per_frame=16, heads=1, dtype="f32",
-                seed=100, alpha=(0.8, 1.0), chunk=5, batch=1):
-    """Extra small cases: partial last chunk, text state on/off, radius 0."""
+                seed=100, alpha=(0.8, 1.0), chunk=5, batch=1, beta=(0.0, 1.0)):
+    """Extra small cases: partial last chunk, text state on/off, radius 0;
+    ``beta``: the range of the uniform beta draws (video and text tokens)."""
     return dict(name=f"tiny-F{frames}-r{radius}-T{text_tokens}-{rule}",
                 batch=batch, heads=heads, head_dim=head_dim, frames=frames,
                 tokens_per_frame=tokens_per_frame, dtype=dtype, chunk=chunk,
                 radius=radius, rules=(rule,), c=0.5, text_tokens=text_tokens,
-                alpha=alpha, seed=seed)
+                alpha=alpha, seed=seed, beta=beta)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -166,14 +169,15 @@ def make(cfg, *, beta_zero=False, alpha_one=False, identity_conv=False,
         b, h = bh
         for name, arr in (("q", q), ("k", k), ("v", v), ("gate", gate)):
             arr[b, h] = io(_draw(seed, name, b, h, (N, d), "normal"))
-        beta[b, h] = 0.0 if beta_zero else _draw(seed, "beta", b, h, (N,), "uniform")
+        b_lo, b_hi = cfg.get("beta", (0.0, 1.0))
+        beta[b, h] = 0.0 if beta_zero else _draw(seed, "beta", b, h, (N,), "uniform", b_lo, b_hi)
         a_lo, a_hi = cfg["alpha"]
         alpha[b, h] = 1.0 if alpha_one else _draw(seed, "alpha", b, h, (F, d),
                                                    "uniform", a_lo, a_hi)
         if T > 0:
             k_txt[b, h] = io(_draw(seed, "k_txt", b, h, (T, d), "normal"))
             v_txt[b, h] = io(_draw(seed, "v_txt", b, h, (T, d), "normal"))
-            beta_txt[b, h] = _draw(seed, "beta_txt", b, h, (T,), "uniform")
+            beta_txt[b, h] = _draw(seed, "beta_txt", b, h, (T,), "uniform", b_lo, b_hi)
 
     jobs = [(b, h) for b in range(B) for h in range(H)]
     if workers > 1 and len(jobs) > 1:
@@ -227,3 +231,19 @@ def state_matrix(cfg) -> np.ndarray:
         for h in range(H):
             out[b, h] = _draw(cfg["seed"], "state", b, h, (d, d), "normal", std=d ** -0.5)
     return out
+
+
+def alpha_weights(cfg):
+    """Synthetic weights of the per-frame forget-gate producer, per head:
+    W [H, d, d] ~ N(0, 1/d), bias [H, d] ~ N(0, 1/4), a_log [H, d] =
+    ln(0.05) + N(0, 1/25), float32 (with N(0, 1) keys the gates fall in
+    about 0.90 .. 0.99, the range of the workloads' alpha draws)."""
+    if not isinstance(cfg, dict):
+        cfg = WORKLOADS[cfg]
+    H, d, seed = cfg["heads"], cfg["head_dim"], cfg["seed"]
+    w = np.stack([_draw(seed, "alpha_w", 0, h, (d, d), "normal", std=d ** -0.5)
+                  for h in range(H)])
+    b = np.stack([_draw(seed, "alpha_b", 0, h, (d,), "normal", std=0.5) for h in range(H)])
+    a = np.stack([np.float32(np.log(0.05)) + _draw(seed, "alpha_a", 0, h, (d,), "normal",
+                                                   std=0.2) for h in range(H)])
+    return w.astype(np.float32), b.astype(np.float32), a.astype(np.float32)

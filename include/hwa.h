@@ -45,6 +45,12 @@
 extern "C" {
 #endif
 
+/* HIP's stream handle, declared as HIP's own headers declare it (an opaque
+ * pointer; the identical typedef may appear again when hip_runtime.h is
+ * included too). */
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
 typedef enum {
   HWA_OK = 0,
   HWA_ERR_INVALID_ARG = 1, /* NULL pointer, size <= 0, bad enum, aliasing  */
@@ -63,13 +69,13 @@ typedef enum {
 /* Element type of q, k, v, gate, out (and of the text tokens). */
 typedef enum { HWA_F32 = 0, HWA_BF16 = 1 } hwa_dtype;
 
+/* Flags. Every hybrid_attn_fwd call leaves its intermediates (window table,
+ * A, B, M, the state banks, S_t) in the workspace at the offsets
+ * hwa_get_workspace_layout reports, so no flag asks for them; bit 4 is
+ * unused and, like any unknown bit, rejected with HWA_ERR_INVALID_ARG. */
 enum {
   HWA_FLAG_SOFTMAX_ONLY = 1,      /* out = o_sm (linear branch skipped)      */
   HWA_FLAG_LINEAR_ONLY = 2,       /* out = y (softmax branch skipped)        */
-  HWA_FLAG_KEEP_INTERMEDIATES = 4, /* accepted for compatibility: the        */
-                                   /* intermediates are always left in the  */
-                                   /* workspace at hwa_workspace_layout's    */
-                                   /* offsets                                */
   HWA_FLAG_ACCUMULATE = 8          /* hwa_linear_bwd only: add dq, dk, dv to */
                                    /* what those buffers hold (the softmax   */
                                    /* branch's gradient, for out = o_sm + y) */
@@ -79,7 +85,8 @@ typedef struct {
   uint32_t struct_size;  /* = sizeof(hwa_params)                              */
   int32_t batch;         /* B >= 1                                            */
   int32_t heads;         /* H >= 1                                            */
-  int32_t head_dim;      /* d: 16, 32, 64 or 128 (bf16: 64 or 128)             */
+  int32_t head_dim;      /* d: 16, 32, 64 or 128 with fp32; 64 or 128 with     */
+                         /* bf16 (other values: HWA_ERR_UNSUPPORTED)           */
   int32_t dtype;         /* hwa_dtype                                          */
   float c;               /* scale c of sana_scaled / vdn_scaled (ignored by    */
                          /* vdn_solve)                                         */
@@ -123,9 +130,14 @@ typedef struct {
  *   lohi     int32 [2, F]         window bounds lo then hi (inclusive frames)
  *   stat_a   [B, H, F, d, d]      A_f
  *   stat_b   [B, H, F, d, d]      B_f (d_v x d_k)
- *   map_m    [B, H, F, d, d]      M_f = (I + c~^2 A_f)^-1 (c~ = 1 for vdn_solve,
- *                                 c for vdn_scaled; not written for
- *                                 sana_scaled)
+ *   map_m    [B, H, F, d, d]      fp32 calls: M_f = (I + c~^2 A_f)^-1 (c~ = 1 for
+ *                                 vdn_solve, c for vdn_scaled; not written for
+ *                                 sana_scaled). bf16 calls: the same bytes hold
+ *                                 per frame two bf16 d x d matrices, hi =
+ *                                 bf16(M_f) and lo = bf16(M_f - hi), with M_f =
+ *                                 I - c^2 A_f for sana_scaled, element (r, c)
+ *                                 at ((((r/32)*(d/16) + c/16)*64 + (c%16)/8*32
+ *                                 + r%32)*8 + c%8 (the scan's operand order)
  *   bank_p   [B, H, n_ch+1, d, d] prefix states, slot m = P_{min(F, m*chunk)-1}
  *   bank_q   [B, H, n_ch+1, d, d] suffix states, slot m = Q_{min(F, m*chunk)}
  *   decay    [B, H, F, 2, d]      bridge decays prod_{lo..t} alpha, prod_{t..hi} alpha
@@ -152,7 +164,10 @@ typedef struct {
  *
  *   q, k, v    [B, H, N, d]  dtype  raw (pre-RoPE) q/k and v, shared by both
  *                                   branches (article: one QKV projection)
- *   beta       [B, H, N]     fp32   per-token write strength
+ *   beta       [B, H, N]     fp32   per-token write strength, any sign (with
+ *                                   beta < 0, I + c~^2 A_f must stay positive
+ *                                   definite: the inverse takes its pivots in
+ *                                   order, without exchanges)
  *   alpha      [B, H, F, d]  fp32   per-frame, per-key-channel forget gate
  *   gate       [B, H, N, d]  dtype  output-gate pre-activation (sigmoid)
  *   text_state [B, H, d, d]  fp32   S_text (d_v x d_k) or NULL (zero start)
@@ -171,7 +186,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                            const void* gate, const float* text_state,
                            int32_t frames, int32_t tokens_per_frame,
                            int32_t chunk, int32_t radius, int32_t rule,
-                           void* out, void* stream, const hwa_params* p);
+                           void* out, hipStream_t stream, const hwa_params* p);
 
 /*
  * softmax_lse and softmax_out (when not NULL) are written by calls that run
@@ -214,7 +229,7 @@ hwa_status hwa_window_bounds(int32_t frames, int32_t chunk, int32_t radius,
  */
 hwa_status hwa_text_state(const void* k_txt, const void* v_txt,
                           const float* beta_txt, int32_t text_tokens,
-                          float* state_out, void* stream,
+                          float* state_out, hipStream_t stream,
                           const hwa_params* p);
 
 size_t hwa_text_state_workspace_bytes(int32_t text_tokens,
@@ -256,7 +271,7 @@ hwa_status hwa_softmax_bwd(const void* q, const void* k, const void* v,
                            const void* o_sm, const float* lse, const void* d_o,
                            int32_t frames, int32_t tokens_per_frame,
                            int32_t chunk, int32_t radius, void* dq, void* dk,
-                           void* dv, void* stream, const hwa_params* p);
+                           void* dv, hipStream_t stream, const hwa_params* p);
 
 /* Workspace bytes hwa_softmax_bwd needs (0 on bad args): the window table
  * and delta and lse * log2(e) per query (2 * B * H * roundup(N, 64) * 4
@@ -310,7 +325,7 @@ hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const flo
                           int32_t chunk, int32_t radius, int32_t rule, void* dq, void* dk,
                           void* dv, float* dbeta, float* dalpha, void* dgate,
                           float* dtext_state, float* dconv_k, float* dconv_v,
-                          float* drms_weight, void* stream, const hwa_params* p);
+                          float* drms_weight, hipStream_t stream, const hwa_params* p);
 
 /* Workspace bytes hwa_linear_bwd needs (0 on bad args): per (b, h) seven
  * fp32 d x d matrices per frame (statistics, inverses, both scans' states,
@@ -318,6 +333,27 @@ hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const flo
  * feature gradients before the convs), plus alignment. */
 size_t hwa_linear_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
                                       int32_t chunk, const hwa_params* p);
+
+/*
+ * hwa_frame_alpha -- the per-frame, per-key-channel forget gate alpha that
+ * hybrid_attn_fwd takes (article, "Step 3": D = diag(alpha), a gate in (0, 1)
+ * produced by the model's FrameKDAAlpha layer). The article gives no formula
+ * or weights for that layer; this entry point computes the stated form
+ *   m_f = mean_{n in frame f} k_n,  z_f = m_f W_h + b_h,
+ *   alpha_f = exp(-exp(a_h) * softplus(z_f)),  softplus(z) = log(1 + e^z)
+ * per (batch, head h, frame f), in fp32:
+ *   k      [B, H, N, d]  dtype  the raw k of the linear branch (16-byte aligned)
+ *   w      [H, d, d]     fp32   W_h[i][j]: input channel i, output channel j
+ *   bias   [H, d]        fp32
+ *   a_log  [H, d]        fp32   log decay rate a_h
+ *   frames, tokens_per_frame    F >= 1, S >= 1
+ *   alpha  [B, H, F, d]  fp32   written; must not overlap an input
+ * Uses p->batch, heads, head_dim, dtype and ignores the other fields (no
+ * workspace). Returns HWA_OK, or an error status before anything is enqueued.
+ */
+hwa_status hwa_frame_alpha(const void* k, const float* w, const float* bias,
+                           const float* a_log, int32_t frames, int32_t tokens_per_frame,
+                           float* alpha, hipStream_t stream, const hwa_params* p);
 
 /* Static English text of a status. */
 const char* hwa_status_string(hwa_status s);

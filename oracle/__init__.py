@@ -28,6 +28,7 @@ from .hybrid_attn import (  # noqa: F401
     features,
     frame_statistics,
     rule_step,
+    frame_alpha,
     scan,
     gathered_state,
     readout,

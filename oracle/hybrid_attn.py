@@ -245,6 +245,36 @@ def rule_step(S_in, A, B, alpha, rule: str = "vdn_solve", c: float = 1.0):
     return np.linalg.solve(M.T, rhs.T).T
 
 
+def frame_alpha(k, w, bias, a_log, S: int):
+    """Per-frame, per-key-channel forget gate alpha_f in (0, 1) ("Step 3":
+    D = diag(alpha) is a per-channel forget gate with values between 0 and 1,
+    produced by a layer the article calls FrameKDAAlpha).
+
+    The article names the producer but gives neither its formula nor its
+    weights. Reading (a gate of the kind "KDA" delta-rule layers use, taken
+    once per frame): pool the frame's raw k rows, project, and map through a
+    decay rate,
+        m_f = mean_{n in f} k_n          (d)
+        z_f = m_f W + b                  (W: d x d, input channel i, output j)
+        alpha_f = exp(-exp(a) * softplus(z_f)),  softplus(z) = log(1 + e^z),
+    so alpha lies in (0, 1), tends to 1 where z -> -inf and falls as z grows.
+    k: [N, d] (one (batch, head) slice); w: [d, d]; bias, a_log: [d].
+    Returns [F, d].
+
+    Pinned by: W = 0, b = 0 giving 2^(-exp(a)) exactly (softplus(0) = ln 2),
+    a scalar brute force with an unsymmetric W (catches a transposed W), the
+    range (0, 1) and monotonicity in z, and invariance to the token order
+    inside a frame.
+    """
+    k = np.asarray(k, _F64)
+    N, d = k.shape
+    F = N // S
+    m = k.reshape(F, S, d).mean(axis=1)
+    z = m @ np.asarray(w, _F64) + np.asarray(bias, _F64)[None, :]
+    softplus = np.logaddexp(0.0, z)
+    return np.exp(-np.exp(np.asarray(a_log, _F64))[None, :] * softplus)
+
+
 # --------------------------------------------------------------------------
 # Step 4: bidirectional scan and boundary gather
 # --------------------------------------------------------------------------

@@ -122,3 +122,41 @@ def oracle_softmax_rows(inp, b, h, rows):
     lo, hi = oracle.window_bounds(c["frames"], c["chunk"], c["radius"])
     return oracle.softmax_rows(inp.f32("q", b, h), inp.f32("k", b, h), inp.f32("v", b, h),
                                c["tokens_per_frame"], lo, hi, rows)
+
+
+# ---------------------------------------------------------------- guard bands
+GUARD = 4096  # elements (bytes for the workspace) of poison around a buffer
+
+
+def poisoned(shape, dtype, dev="cuda", guard=GUARD):
+    """An output buffer pre-filled with NaN and surrounded by `guard` NaN
+    elements on each side. Returns (view, flat): the view is what the library
+    writes, flat holds the guard bands for :func:`check_poisoned`."""
+    n = int(np.prod(shape))
+    flat = torch.full((n + 2 * guard,), float("nan"), dtype=dtype, device=dev)
+    return flat[guard:guard + n].view(*shape), flat
+
+
+def check_poisoned(view, flat, name, guard=GUARD):
+    """Every element the call should write is finite, and both guard bands
+    still hold the exact NaN bit pattern they were filled with."""
+    n = view.numel()
+    bits = torch.int16 if flat.element_size() == 2 else torch.int32
+    pat = torch.full((1,), float("nan"), dtype=flat.dtype, device=flat.device).view(bits)
+    fb = flat.view(bits)
+    assert torch.equal(fb[:guard], pat.expand(guard)), f"{name}: guard before the buffer written"
+    assert torch.equal(fb[guard + n:], pat.expand(guard)), f"{name}: guard after the buffer written"
+    bad = (~torch.isfinite(view.float())).sum().item()
+    assert bad == 0, f"{name}: {bad} elements left unwritten (NaN) or non-finite"
+
+
+def guarded_workspace(nbytes, dev="cuda", guard=GUARD):
+    """A workspace of exactly `nbytes` (256-byte aligned) with `guard` bytes of
+    0xA5 before and after it. Returns (view, flat)."""
+    flat = torch.full((nbytes + 2 * guard,), 0xA5, dtype=torch.uint8, device=dev)
+    return flat[guard:guard + nbytes], flat
+
+
+def check_workspace_guard(flat, nbytes, name, guard=GUARD):
+    assert bool((flat[:guard] == 0xA5).all()), f"{name}: bytes before the workspace written"
+    assert bool((flat[guard + nbytes:] == 0xA5).all()), f"{name}: bytes after the workspace written"

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "hwa.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(hwa_[a-z_]+|hybrid_attn_fwd)\s*\(", src))
+    return set(re.findall(r"\b(hwa_[a-z_]+|hybrid_attn_fwd[a-z_]*)\s*\(", src))
 
 
 def test_exports_every_declared_symbol():
@@ -115,6 +115,8 @@ def test_argument_validation_codes():
     assert _call(p, out=p.workspace) == E.HWA_ERR_INVALID_ARG      # out aliases workspace
     pf = _with_ws(_params(flags=hwa.FLAG_SOFTMAX_ONLY | hwa.FLAG_LINEAR_ONLY))
     assert _call(pf) == E.HWA_ERR_INVALID_ARG
+    pf = _with_ws(_params(flags=4))  # no flag asks for the intermediates: bit 4 is unused
+    assert _call(pf) == E.HWA_ERR_INVALID_ARG
     pf = _with_ws(_params(flags=64))
     assert _call(pf) == E.HWA_ERR_INVALID_ARG
     assert _call(_with_ws(_params(rms_eps=0.0))) == E.HWA_ERR_INVALID_ARG
@@ -172,6 +174,27 @@ def test_text_state_validation():
     assert L.hwa_text_state(vp(BASE), vp(BASE + (1 << 36)), vp(BASE + (2 << 36)), 16,
                             vp(BASE + (3 << 36)), None, ctypes.byref(p)) == E.HWA_ERR_WORKSPACE
     assert L.hwa_text_state_workspace_bytes(16, ctypes.byref(p)) > 0
+
+
+@no_gpu
+def test_text_state_alignment():
+    # the forward's alignment rules: bf16 token rows on 16 bytes, fp32 arrays
+    # (beta_txt) on 4; a misaligned slice is rejected before any launch
+    E = hwa
+    vp = ctypes.c_void_p
+    L = hwa.lib()
+    p = _params()  # bf16, d 64
+    p.workspace = BASE + (10 << 36)
+    p.workspace_bytes = L.hwa_text_state_workspace_bytes(16, ctypes.byref(p))
+    k, v, b, st = BASE, BASE + (1 << 36), BASE + (2 << 36), BASE + (3 << 36)
+    for kk, vv, bb in ((k + 8, v, b), (k, v + 2, b), (k, v, b + 2)):
+        assert L.hwa_text_state(vp(kk), vp(vv), vp(bb), 16, vp(st), None,
+                                ctypes.byref(p)) == E.HWA_ERR_INVALID_ARG
+    pf = _params(dtype=0)  # fp32 rows on 4 bytes
+    pf.workspace = BASE + (10 << 36)
+    pf.workspace_bytes = L.hwa_text_state_workspace_bytes(16, ctypes.byref(pf))
+    assert L.hwa_text_state(vp(k + 2), vp(v), vp(b), 16, vp(st), None,
+                            ctypes.byref(pf)) == E.HWA_ERR_INVALID_ARG
 
 
 @no_gpu
@@ -315,3 +338,28 @@ def test_linear_bwd_workspace_bytes():
                 + 2 * bh * N * d * 4 + bh * F * d * 8 * 4)
         assert need <= n <= need + 16 * 256
     assert L.hwa_linear_bwd_workspace_bytes(0, 100, 5, ctypes.byref(p)) == 0
+
+
+@no_gpu
+def test_frame_alpha_validation():
+    E = hwa
+    vp = ctypes.c_void_p
+    fn = hwa.lib().hwa_frame_alpha
+    k, w, b, a, out = (BASE + (i << 36) for i in range(1, 6))
+
+    def call(p, F=10, S=16, **kw):
+        d = dict(k=k, w=w, b=b, a=a, out=out)
+        d.update(kw)
+        return fn(vp(d["k"]), vp(d["w"]), vp(d["b"]), vp(d["a"]), F, S, vp(d["out"]), None,
+                  ctypes.byref(p))
+
+    p = _params()
+    assert call(p, k=None) == E.HWA_ERR_INVALID_ARG
+    assert call(p, out=None) == E.HWA_ERR_INVALID_ARG
+    assert call(p, F=0) == E.HWA_ERR_INVALID_ARG
+    assert call(p, S=0) == E.HWA_ERR_INVALID_ARG
+    assert call(p, k=k + 8) == E.HWA_ERR_INVALID_ARG      # k rows on 16 bytes
+    assert call(p, a=a + 2) == E.HWA_ERR_INVALID_ARG      # fp32 on 4 bytes
+    assert call(p, out=w) == E.HWA_ERR_INVALID_ARG        # alpha overlaps W
+    assert call(p, out=k + 64) == E.HWA_ERR_INVALID_ARG   # alpha inside k
+    assert call(_params(head_dim=48)) == E.HWA_ERR_UNSUPPORTED

@@ -10,30 +10,58 @@ oracle gives for S_text = 0. Bar: 1e-5 (fp32) / 5e-3 (bf16: dq, dk, dv and
 dgate are rounded to bf16, the fp32 outputs see the bf16 inputs only).
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from hybrid_window_softmax_amd import hwa, inputs
-from harness import TOL, to_dev
+from harness import (TOL, check_poisoned, check_workspace_guard, guarded_workspace,
+                     poisoned, to_dev)
 
 pytestmark = pytest.mark.gpu
 
 PER_HEAD = ("q", "k", "v", "beta", "alpha", "gate", "text_state")
 
 
-def _gpu_grads(inp, rule, st_host, g_host):
+def _gpu_grads(inp, rule, st_host, g_host, guard=False):
+    """hwa_linear_bwd's gradients as float64 host arrays. ``guard``: every
+    output pre-filled with NaN inside NaN guard bands and the workspace inside
+    0xA5 bands, checked after the call."""
     c = inp.cfg
     bf = c["dtype"] == "bf16"
     t = {n: to_dev(getattr(inp, n), bf) for n in
          ("q", "k", "v", "gate", "beta", "alpha", "conv_k", "conv_v", "rms_weight")}
     d_o = to_dev(g_host, bf)
     S_t = None if st_host is None else to_dev(st_host, False)
+    grads = ws = None
+    if guard:
+        B, H, N, d = t["q"].shape
+        F = c["frames"]
+        io = t["q"].dtype
+        shapes = dict(q=((B, H, N, d), io), k=((B, H, N, d), io), v=((B, H, N, d), io),
+                      gate=((B, H, N, d), io), beta=((B, H, N), torch.float32),
+                      alpha=((B, H, F, d), torch.float32),
+                      text_state=((B, H, d, d), torch.float32),
+                      conv_k=((H, d, 4), torch.float32), conv_v=((H, d, 4), torch.float32),
+                      rms_weight=((d,), torch.float32))
+        bufs = {n: poisoned(shp, dt) for n, (shp, dt) in shapes.items()}
+        grads = {n: b[0] for n, b in bufs.items()}
+        p = hwa.make_params(B, H, d, io)
+        need = int(hwa.lib().hwa_linear_bwd_workspace_bytes(F, c["tokens_per_frame"],
+                                                            c["chunk"], ctypes.byref(p)))
+        ws, ws_flat = guarded_workspace(need)
     grads, _ = hwa.linear_bwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"], S_t,
                               t["conv_k"], t["conv_v"], d_o, c["frames"], c["tokens_per_frame"],
-                              c["chunk"], c["radius"], rule, c["c"], 0.5, 1e-6, t["rms_weight"])
+                              c["chunk"], c["radius"], rule, c["c"], 0.5, 1e-6, t["rms_weight"],
+                              grads=grads, workspace=ws)
     torch.cuda.synchronize()
+    if guard:
+        for n, (view, flat) in bufs.items():
+            check_poisoned(view, flat, f"{c['name']} d{n}")
+        check_workspace_guard(ws_flat, need, f"{c['name']} linear backward")
     return {n: x.float().cpu().numpy().astype(np.float64) for n, x in grads.items()}
 
 
@@ -135,10 +163,11 @@ def test_long_clip_132600tok_one_head():
     inp = inputs.make(name)
     c = inp.cfg
     h = 5
-    print(f"case {name}: all heads on the GPU, head {h} against the oracle", flush=True)
+    print(f"case {name}: all heads on the GPU (outputs poisoned and guarded), head {h} "
+          "against the oracle", flush=True)
     g_host = inputs.grad_output(c)
     st_host = inputs.state_matrix(c)
-    got = _gpu_grads(inp, "vdn_solve", st_host, g_host)
+    got = _gpu_grads(inp, "vdn_solve", st_host, g_host, guard=True)
     ref = oracle.linear_branch_grad(
         inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h), inp.beta[0, h],
         inp.alpha[0, h], inp.f64("gate", 0, h), st_host[0, h], inp.conv_k[h], inp.conv_v[h],
@@ -213,10 +242,11 @@ def test_full_size_one_head(name, h):
     # library's)
     inp = inputs.make(name)
     c = inp.cfg
-    print(f"case {name}: all heads on the GPU, head {h} against the oracle", flush=True)
+    print(f"case {name}: all heads on the GPU (outputs poisoned and guarded), head {h} "
+          "against the oracle", flush=True)
     g_host = inputs.grad_output(c)
     st_host = inputs.state_matrix(c)
-    got = _gpu_grads(inp, "vdn_solve", st_host, g_host)
+    got = _gpu_grads(inp, "vdn_solve", st_host, g_host, guard=True)
     ref = oracle.linear_branch_grad(
         inp.f64("q", 0, h), inp.f64("k", 0, h), inp.f64("v", 0, h), inp.beta[0, h],
         inp.alpha[0, h], inp.f64("gate", 0, h), st_host[0, h], inp.conv_k[h], inp.conv_v[h],
@@ -228,3 +258,14 @@ def test_full_size_one_head(name, h):
     errs["conv_v"] = oracle.rel_frobenius(got["conv_v"][h], ref["conv_v"])
     print("  rel err " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()), flush=True)
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 128)])
+def test_negative_beta(dtype, d):
+    # beta ~ U(-0.5, 1): negative writes in the statistics (on bf16 calls the
+    # frames that hold one are recomputed by the fp32 statistics kernel); with
+    # and without a text state
+    for text in (True, False):
+        check(inputs.make(inputs.tiny_config(frames=12, text_tokens=0, head_dim=d,
+                                             tokens_per_frame=40, dtype=dtype, heads=2,
+                                             seed=403, beta=(-0.5, 1.0))), "vdn_solve", text)

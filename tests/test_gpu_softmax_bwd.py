@@ -9,20 +9,27 @@ rounding points -- bf16 p and ds operands, fp32 accumulation, bf16 outputs --
 predicts 2.3e-3 to 2.4e-3 at d = 64 and 128).
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from hybrid_window_softmax_amd import hwa, inputs
-from harness import TOL, GpuCase, sample_rows, to_dev
+from harness import (TOL, GpuCase, check_poisoned, check_workspace_guard,
+                     guarded_workspace, poisoned, sample_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
 LSE_TOL = {"f32": 2e-5, "bf16": 4e-3}  # absolute, natural-log units
 
 
-def _run(inp, g_host):
+def _run(inp, g_host, guard=False):
+    """Forward (softmax only, for the lse) then hwa_softmax_bwd. ``guard``:
+    dq, dk, dv pre-filled with NaN inside NaN guard bands and the workspace
+    inside 0xA5 bands; checked after the call (every element written, no
+    byte past a buffer)."""
     c = inp.cfg
     bf = c["dtype"] == "bf16"
     q, k, v = (to_dev(getattr(inp, n), bf) for n in ("q", "k", "v"))
@@ -32,7 +39,19 @@ def _run(inp, g_host):
     F, S = c["frames"], c["tokens_per_frame"]
     o, _ = hwa.hybrid_attn_fwd(q, k, v, None, None, None, None, None, None, F, S, c["chunk"],
                                c["radius"], flags=hwa.FLAG_SOFTMAX_ONLY, softmax_lse=lse)
-    dq, dk, dv, _ = hwa.softmax_bwd(q, k, v, o, lse, g, F, S, c["chunk"], c["radius"])
+    if guard:
+        bufs = [poisoned((B, H, N, d), q.dtype) for _ in range(3)]
+        p = hwa.make_params(B, H, d, q.dtype)
+        need = int(hwa.lib().hwa_softmax_bwd_workspace_bytes(F, S, c["chunk"], ctypes.byref(p)))
+        ws, ws_flat = guarded_workspace(need)
+        dq, dk, dv, _ = hwa.softmax_bwd(q, k, v, o, lse, g, F, S, c["chunk"], c["radius"],
+                                        dq=bufs[0][0], dk=bufs[1][0], dv=bufs[2][0], workspace=ws)
+        torch.cuda.synchronize()
+        for (view, flat), nm in zip(bufs, ("dq", "dk", "dv")):
+            check_poisoned(view, flat, f"{c['name']} {nm}")
+        check_workspace_guard(ws_flat, need, f"{c['name']} softmax backward")
+    else:
+        dq, dk, dv, _ = hwa.softmax_bwd(q, k, v, o, lse, g, F, S, c["chunk"], c["radius"])
     torch.cuda.synchronize()
     # float32 host copies (exact for both dtypes); heads are widened one at a time
     return (lse.cpu().numpy().astype(np.float64),
@@ -129,9 +148,10 @@ def _key_rows(cfg, chunks, seed):
 def _check_sampled(name, heads, chunks=3):
     inp = inputs.make(name)
     c = inp.cfg
-    print(f"case {name}: sampled rows of heads {heads} + sums over every head", flush=True)
+    print(f"case {name}: sampled rows of heads {heads} + sums over every head, outputs "
+          "poisoned and guarded", flush=True)
     g_host = inputs.grad_output(c)
-    lse, dq, dk, dv = _run(inp, g_host)
+    lse, dq, dk, dv = _run(inp, g_host, guard=True)
     F, S = c["frames"], c["tokens_per_frame"]
     nch = (F + c["chunk"] - 1) // c["chunk"]
     lo, hi = oracle.window_bounds(F, c["chunk"], c["radius"])

@@ -9,6 +9,7 @@ rational arithmetic.
 """
 
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -382,3 +383,42 @@ def test_text_state_single_token_closed_form():
     kh = oracle.l2_normalize(oracle.silu(k))[0]
     # Sherman-Morrison with a unit key: B (I + A)^-1 = beta/(1+beta) v k^T
     assert np.abs(got - 0.6 / 1.6 * np.outer(v[0], kh)).max() < 1e-14
+
+
+# ---------------------------------------------------------------- alpha producer
+def test_frame_alpha_closed_forms_and_bruteforce():
+    # the gate reading alpha_f = exp(-exp(a) softplus(mean_f(k) W + b))
+    S, d, F = 7, 5, 4
+    k = RNG.standard_normal((F * S, d))
+    a_log = RNG.standard_normal(d) * 0.5
+    # W = 0, b = 0: softplus(0) = ln 2, so alpha = 2^(-exp(a)) for every frame
+    got = oracle.frame_alpha(k, np.zeros((d, d)), np.zeros(d), a_log, S)
+    assert np.allclose(got, np.broadcast_to(2.0 ** -np.exp(a_log), (F, d)), rtol=1e-14, atol=0)
+    # exp(a) = 1 and z = 0: alpha = 1/2 exactly
+    half = oracle.frame_alpha(k, np.zeros((d, d)), np.zeros(d), np.zeros(d), S)
+    assert np.allclose(half, 0.5, rtol=1e-15, atol=0)
+    # scalar brute force with an unsymmetric W (input channel i, output j)
+    w = RNG.standard_normal((d, d))
+    assert not np.allclose(w, w.T)
+    b = RNG.standard_normal(d)
+    got = oracle.frame_alpha(k, w, b, a_log, S)
+    for f in range(F):
+        m = [sum(k[f * S + s, i] for s in range(S)) / S for i in range(d)]
+        for j in range(d):
+            z = sum(m[i] * w[i, j] for i in range(d)) + b[j]
+            sp = max(z, 0.0) + math.log1p(math.exp(-abs(z)))
+            ref = math.exp(-math.exp(a_log[j]) * sp)
+            assert abs(got[f, j] - ref) <= 1e-13 * ref
+    # range and monotonicity: a larger pre-activation gives a smaller gate
+    assert np.all((got > 0) & (got < 1))
+    up = oracle.frame_alpha(k, w, b + 1.0, a_log, S)
+    assert np.all(up < got)
+    far = oracle.frame_alpha(k, w, b - 60.0, a_log, S)
+    assert np.all(1.0 - far < 1e-20) and np.all(far <= 1.0)
+    # the order of tokens inside a frame does not matter; frames are separate
+    perm = np.concatenate([f * S + RNG.permutation(S) for f in range(F)])
+    assert np.allclose(oracle.frame_alpha(k[perm], w, b, a_log, S), got, rtol=1e-13, atol=0)
+    k2 = k.copy()
+    k2[S:2 * S] += 1.0
+    got2 = oracle.frame_alpha(k2, w, b, a_log, S)
+    assert np.array_equal(got2[[0, 2, 3]], got[[0, 2, 3]]) and not np.allclose(got2[1], got[1])
