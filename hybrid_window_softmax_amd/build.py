@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhwa.so")
 
 SOURCES = ["hwa_api.cpp", "softmax.hip", "softmax_bwd.hip", "stats.hip", "factor.hip",
-           "scan.hip", "readout.hip", "linear_bwd.hip", "alpha.hip"]
+           "scan.hip", "readout.hip", "linear_bwd.hip", "noalloc.hip",
+           "alpha.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

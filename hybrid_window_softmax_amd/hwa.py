@@ -40,7 +40,7 @@ HWA_ERR_HIP = 4
 HWA_F32 = 0
 HWA_BF16 = 1
 
-EXPORTS = ("hybrid_attn_fwd", "hwa_workspace_bytes", "hwa_get_workspace_layout",
+EXPORTS = ("hybrid_attn_fwd", "hybrid_attn_fwd_noalloc", "hwa_workspace_bytes", "hwa_get_workspace_layout",
            "hwa_window_bounds", "hwa_text_state", "hwa_text_state_workspace_bytes",
            "hwa_softmax_bwd", "hwa_softmax_bwd_workspace_bytes", "hwa_linear_bwd",
            "hwa_linear_bwd_workspace_bytes", "hwa_frame_alpha", "hwa_status_string")
@@ -95,6 +95,8 @@ def lib():
         L.hybrid_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       i32, vp, vp, PP]
         L.hybrid_attn_fwd.restype = ctypes.c_int
+        L.hybrid_attn_fwd_noalloc.argtypes = L.hybrid_attn_fwd.argtypes
+        L.hybrid_attn_fwd_noalloc.restype = ctypes.c_int
         L.hwa_workspace_bytes.argtypes = [i32, i32, i32, PP]
         L.hwa_workspace_bytes.restype = sz
         L.hwa_get_workspace_layout.argtypes = [i32, i32, i32, PP, ctypes.POINTER(Layout)]
@@ -193,8 +195,13 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
                     text_scale: float = 0.5, rms_eps: float = 1e-6,
                     rms_weight=None, q_rope=None, k_rope=None, flags: int = 0,
                     out=None, workspace=None, stream=None, stage_events=None,
-                    softmax_lse=None, softmax_out=None):
+                    softmax_lse=None, softmax_out=None, noalloc=False):
     """out = windowed softmax + delta-rule linear branch (see include/hwa.h).
+
+    ``noalloc``: call hybrid_attn_fwd_noalloc instead, which uses the
+    library's own fixed scratch array (HWA_NOALLOC_SCRATCH_BYTES per GPU) and
+    allocates nothing; no workspace is allocated here either (the returned
+    workspace is None).
 
     q, k, v, gate: [B, H, N, d] bf16 or fp32 CUDA tensors; beta [B, H, N],
     alpha [B, H, F, d], text_state [B, H, d, d] (or None), conv_k/conv_v
@@ -222,20 +229,23 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
                     q_rope, k_rope, None, flags)
     p.softmax_lse = None if softmax_lse is None else softmax_lse.data_ptr()
     p.softmax_out = None if softmax_out is None else softmax_out.data_ptr()
-    need = workspace_bytes(frames, tokens_per_frame, chunk, p)
-    if workspace is None:
-        workspace = alloc_workspace(need, dev)
-    p.workspace = workspace.data_ptr()
-    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if noalloc:
+        workspace = None
+    else:
+        need = workspace_bytes(frames, tokens_per_frame, chunk, p)
+        if workspace is None:
+            workspace = alloc_workspace(need, dev)
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
     if stage_events is not None:
         p.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
     if out is None:
         out = torch.empty_like(q)
     st = _stream(dev) if stream is None else ctypes.c_void_p(stream)
-    code = lib().hybrid_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
-                                 _ptr(gate), _ptr(text_state), frames, tokens_per_frame,
-                                 chunk, radius, RULES[rule] if isinstance(rule, str) else rule,
-                                 _ptr(out), st, ctypes.byref(p))
+    fn = lib().hybrid_attn_fwd_noalloc if noalloc else lib().hybrid_attn_fwd
+    code = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(gate), _ptr(text_state),
+              frames, tokens_per_frame, chunk, radius,
+              RULES[rule] if isinstance(rule, str) else rule, _ptr(out), st, ctypes.byref(p))
     if code != HWA_OK:
         raise HwaError(code)
     return out, workspace

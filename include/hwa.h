@@ -189,6 +189,33 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                            void* out, hipStream_t stream, const hwa_params* p);
 
 /*
+ * hybrid_attn_fwd_noalloc -- hybrid_attn_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, semantics and kernels as
+ * hybrid_attn_fwd, except that p->workspace and p->workspace_bytes are
+ * ignored: the scratch is a device array inside the library, one per GPU, of
+ * HWA_NOALLOC_SCRATCH_BYTES bytes, which each GPU the library runs on holds
+ * until the process ends. The call never allocates or frees memory. Its
+ * first call on a device looks up that device's copy of the array (the
+ * current device, which must be the one `stream` belongs to).
+ *   Returns HWA_ERR_WORKSPACE when hwa_workspace_bytes() for these sizes
+ *   exceeds HWA_NOALLOC_SCRATCH_BYTES (nothing is enqueued), HWA_ERR_HIP if
+ *   the array's address cannot be obtained, otherwise what hybrid_attn_fwd
+ *   returns. The array keeps the last call's contents (every value a call
+ *   reads from it is written by that call first). Calls on one GPU share the
+ *   array: calls that overlap in time on one GPU (different streams, or
+ *   threads) race and must be serialised by the caller.
+ */
+#define HWA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+hwa_status hybrid_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* beta, const float* alpha,
+                                   const void* gate, const float* text_state,
+                                   int32_t frames, int32_t tokens_per_frame,
+                                   int32_t chunk, int32_t radius, int32_t rule,
+                                   void* out, hipStream_t stream, const hwa_params* p);
+
+/*
  * softmax_lse and softmax_out (when not NULL) are written by calls that run
  * the softmax branch; they must not overlap each other, out, an input or the
  * workspace. With HWA_FLAG_LINEAR_ONLY they must be NULL.

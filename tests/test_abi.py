@@ -341,6 +341,37 @@ def test_linear_bwd_workspace_bytes():
 
 
 @no_gpu
+def test_noalloc_rejects_before_any_launch():
+    # hybrid_attn_fwd_noalloc: sizes whose workspace exceeds the library's
+    # fixed scratch array are rejected with HWA_ERR_WORKSPACE, bad arguments
+    # with the forward's own codes, all before anything is enqueued
+    E = hwa
+    vp = ctypes.c_void_p
+    fn = hwa.lib().hybrid_attn_fwd_noalloc
+
+    def call(p, F, S, chunk=5, radius=1, **ptrs):
+        d = dict(q=BASE + (3 << 36), k=BASE + (4 << 36), v=BASE + (5 << 36),
+                 beta=BASE + (6 << 36), alpha=BASE + (7 << 36), gate=BASE + (8 << 36),
+                 out=BASE + (9 << 36))
+        d.update(ptrs)
+        return fn(vp(d["q"]), vp(d["k"]), vp(d["v"]), vp(d["beta"]), vp(d["alpha"]),
+                  vp(d["gate"]), None, F, S, chunk, radius, 0, vp(d["out"]), None,
+                  ctypes.byref(p))
+
+    cap = 64 << 20
+    p = _params(heads=24, head_dim=128)
+    assert hwa.workspace_bytes(31, 1560, 5, p) > cap
+    assert call(p, 31, 1560) == E.HWA_ERR_WORKSPACE
+    assert call(_params(), 0, 16) == E.HWA_ERR_INVALID_ARG
+    assert call(_params(head_dim=48), 10, 16) == E.HWA_ERR_UNSUPPORTED
+    assert call(_params(), 10, 16, radius=-1) == E.HWA_ERR_INVALID_ARG
+    assert call(_params(), 10, 16, q=None) == E.HWA_ERR_INVALID_ARG
+    short = _params()
+    short.struct_size = hwa.Params.softmax_lse.offset - 1
+    assert call(short, 10, 16) == E.HWA_ERR_INVALID_ARG
+
+
+@no_gpu
 def test_frame_alpha_validation():
     E = hwa
     vp = ctypes.c_void_p
