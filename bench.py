@@ -40,6 +40,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_traffic.json")
 TRAFFIC_WORKLOAD = "long-clip-832x480-85f"
 # the full-size workloads the metric spans (48k to 262k tokens)
 RANGE_WORKLOADS = ("clip-832x480-31f", "long-clip-832x480-85f", "canvas-1024x1024-64f")
+# latent grid width of the workloads' frames (832x480: 52 x 30; 1024x1024: 64 x 64)
+BLOCK_GRID_W = {1560: 52, 4096: 64, 256: 16, 16: 4}
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_bwd_traffic.json")
 # the softmax kernel's sources (the kernel, the readout epilogue and the tile
 # helpers it includes)
@@ -475,6 +477,107 @@ def bench_linear_bwd(args, cfg, inp, up):
     }
 
 
+def bench_block(args, cfg, inp, up):
+    """One step = one hwa_block_fwd over the workload: the QKV projection of a
+    block input x [B, N, H d] (with the 3D RoPE in its epilogue), the hybrid
+    attention of every head, the output projection."""
+    import numpy as np
+    import torch
+    from hybrid_window_softmax_amd import hwa, inputs
+    B, H, d = cfg["batch"], cfg["heads"], cfg["head_dim"]
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+    N, D = F * S, H * d
+    grid_w = BLOCK_GRID_W.get(S, S)
+    xb, wqb, wob = inputs.block_inputs(cfg)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # first, while no GPU state exists in this process: the pool forks
+        log("bench: timing the CPU oracle on a sample")
+        att = cpu_baseline(inp, args.rule, args.cpu_heads)
+        ns = min(N, 2048)
+        x64 = inputs.bf16_bits_to_f32(xb[0, :ns]).astype(np.float64)
+        wq64 = inputs.bf16_bits_to_f32(wqb).astype(np.float64)
+        wo64 = inputs.bf16_bits_to_f32(wob).astype(np.float64)
+        t0 = time.perf_counter()
+        x64 @ wq64.T
+        x64 @ wo64.T  # the output projection has the same shape as x @ W_o^T
+        dt = time.perf_counter() - t0
+        proj_s = dt * (B * N) / ns
+        tok = B * N
+        total_s = tok / att["value"] + proj_s
+        cpu = dict(att, value=tok / total_s,
+                   sample=att["sample"] + f"; the two projections (fp64 numpy matmuls, BLAS "
+                   f"threads) timed on {ns} tokens ({dt:.2f} s) and scaled by tokens")
+    t = {n: up(getattr(inp, n)) for n in ("beta", "alpha", "gate", "conv_k", "conv_v",
+                                          "rms_weight", "k_txt", "v_txt", "beta_txt")}
+    text = hwa.text_state(t["k_txt"], t["v_txt"], t["beta_txt"]) if t["k_txt"] is not None \
+        else None
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)  # noqa: E731
+    x, wq, wo = to(xb), to(wqb), to(wob)
+    y = torch.empty_like(x)
+
+    def call(events=None, ws=None):
+        return hwa.block_fwd(x, wq, wo, t["beta"], t["alpha"], t["gate"], text, t["conv_k"],
+                             t["conv_v"], H, F, S, grid_w, 10000.0, cfg["chunk"], cfg["radius"],
+                             args.rule, cfg["c"], 0.5, 1e-6, t["rms_weight"], y=y, workspace=ws,
+                             stage_events=events)[1]
+
+    log("bench: block warmup")
+    ws = call()
+    for _ in range(max(0, args.warmup - 1)):
+        call(ws=ws)
+    torch.cuda.synchronize()
+    timer = hwa.StageTimer(args.steps, hwa.NUM_BLOCK_STAGE_EVENTS, hwa.BLOCK_STAGES)
+    log(f"bench: timing {args.steps} block steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(events=timer.sets[i], ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage = timer.stage_ms()
+    timer.close()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    log("bench: stage ms " + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()))
+    M = B * N
+    flops = {"qkv": 2 * M * D * 3 * D, "out_proj": 2 * M * D * D}
+    kernels = {}
+    for name in hwa.BLOCK_STAGES:
+        rec = {"ms": round(stage[name], 4)}
+        if name in flops:
+            tf = flops[name] / (stage[name] / 1000.0) / 1e12
+            rec["TFLOPs"] = round(tf, 2)
+            rec["frac"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        kernels[name] = rec
+    achieved = flops["qkv"] / (stage["qkv"] / 1000.0) / 1e12
+    roofline = {"kernel": "gemm_nt_kernel (QKV projection, RoPE epilogue)", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": flops["qkv"]}
+    return {
+        "metric": "hybrid attention block (QKV projection + 3D RoPE, hybrid attention, output "
+                  "projection) tokens/s",
+        "value": round(B * N / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: B{B} H{H} d{d} F{F} x S{S} = {N} tokens, "
+                               f"D {D}, latent grid {grid_w} wide, chunk {cfg['chunk']} radius "
+                               f"{cfg['radius']}, {args.rule}, attention block",
+                   "tokens": N, "heads": H, "head_dim": d},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+
+
 def bench_train_step(args, cfg, inp, up):
     """One step = the forward (keeping o_sm and its log-sum-exp), the softmax
     branch's backward, then the linear branch's backward adding its dq, dk, dv
@@ -598,6 +701,10 @@ def main():
     ap.add_argument("--no-range", action="store_true",
                     help="skip the other rules and full-size workloads of the metric's range")
     ap.add_argument("--range-steps", type=int, default=10)
+    ap.add_argument("--route-tau", type=float, default=1.5,
+                    help="also time the block-sparse routed softmax at this threshold "
+                         "(approximate; reported under 'routed')")
+    ap.add_argument("--no-routed", dest="route_tau", action="store_const", const=None)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (three times), the "
                          "reference kernel for scaling HBM byte counters")
@@ -605,6 +712,9 @@ def main():
                     help="time forward + both backward passes (every input's gradient) instead")
     ap.add_argument("--linear-bwd", action="store_true",
                     help="time the linear branch's backward (hwa_linear_bwd) instead")
+    ap.add_argument("--block", action="store_true",
+                    help="time the attention block (hwa_block_fwd: projections + RoPE + hybrid "
+                         "attention) instead")
     ap.add_argument("--softmax-bwd", action="store_true",
                     help="time the windowed-softmax backward (hwa_softmax_bwd) instead")
     ap.add_argument("--gemm-ceiling", action="store_true",
@@ -667,6 +777,9 @@ def main():
     if args.softmax_bwd:
         print(json.dumps(bench_softmax_bwd(args, cfg, inp, up)), flush=True)
         return
+    if args.block:
+        print(json.dumps(bench_block(args, cfg, inp, up)), flush=True)
+        return
     if args.linear_bwd:
         print(json.dumps(bench_linear_bwd(args, cfg, inp, up)), flush=True)
         return
@@ -683,6 +796,9 @@ def main():
     F, S = cfg["frames"], cfg["tokens_per_frame"]
     tokens = cfg["batch"] * F * S
     ms = res["ms"]
+    routed = None
+    if args.route_tau is not None:
+        routed = time_routed(cfg, inp, args.rule, args.route_tau, args.range_steps, up, ms)
     rng = None
     if not args.no_range:
         # the rest of the metric's range: the other rules on this workload and
@@ -727,6 +843,7 @@ def main():
         "roofline": res["roofline"],
         "kernels": res["kernels"],
         "range": rng,
+        "routed": routed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -745,6 +862,83 @@ def make_up(cfg):
             return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
     return up
+
+
+def time_routed(cfg, inp, rule, tau, steps, up, dense_ms):
+    """The block-sparse routed forward (HWA_FLAG_ROUTED) on the same workload:
+    time per call, the kept fraction of the window's key blocks, and the
+    routed o_sm's relative Frobenius error against the dense o_sm (both from
+    softmax-only calls, every head)."""
+    import math
+
+    import torch
+    from hybrid_window_softmax_amd import hwa
+    t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",
+                                          "conv_v", "rms_weight", "k_txt", "v_txt",
+                                          "beta_txt")}
+    text = hwa.text_state(t["k_txt"], t["v_txt"], t["beta_txt"]) if t["k_txt"] is not None \
+        else None
+    out = torch.empty_like(t["q"])
+    F, S = cfg["frames"], cfg["tokens_per_frame"]
+
+    def call(tau_, flags=0, ws=None, o=out, events=None):
+        return hwa.hybrid_attn_fwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"],
+                                   text, t["conv_k"], t["conv_v"], F, S, cfg["chunk"],
+                                   cfg["radius"], rule, cfg["c"], 0.5, 1e-6, t["rms_weight"],
+                                   flags=flags, out=o, workspace=ws, route_tau=tau_,
+                                   stage_events=events)[1]
+
+    log(f"bench: routed softmax, tau {tau}")
+    ws = call(tau)
+    for _ in range(2):
+        call(tau, ws=ws)
+    torch.cuda.synchronize()
+    timer = hwa.StageTimer(steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(tau, ws=ws, events=timer.sets[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    stage = timer.stage_ms()
+    timer.close()
+    B, H = cfg["batch"], cfg["heads"]
+    p = hwa.make_params(B, H, cfg["head_dim"], torch.bfloat16, flags=hwa.FLAG_ROUTED)
+    L = hwa.route_layout(F, S, cfg["chunk"], p)
+    nch = -(-F // cfg["chunk"])
+    tpc = L["tiles_per_chunk"]
+    cnt = ws[L["count"]:L["count"] + B * H * nch * tpc * 4].view(torch.int32).view(
+        B * H, nch, tpc).to(torch.float64)
+    # blocks of each chunk's window (every tile of a chunk sees the same window)
+    lo, hi = [], []
+    for c in range(nch):
+        f0 = c * cfg["chunk"]
+        lo.append(max(0, (c - cfg["radius"]) * cfg["chunk"]) * S)
+        hi.append((min(F - 1, (c + cfg["radius"] + 1) * cfg["chunk"] - 1) + 1) * S)
+        del f0
+    nkb = torch.tensor([(h_ - 1) // 128 - l_ // 128 + 1 for l_, h_ in zip(lo, hi)],
+                       dtype=torch.float64, device=cnt.device)
+    ntq = torch.tensor([-(-(min(F, (c + 1) * cfg["chunk"]) - c * cfg["chunk"]) * S // 256)
+                        for c in range(nch)], device=cnt.device)
+    valid = torch.arange(tpc, device=cnt.device)[None, :] < ntq[:, None]
+    kept = float((cnt * valid).sum())
+    total = float((valid * nkb[:, None]).sum() * B * H)
+    dense_sm = torch.empty_like(out)
+    routed_sm = torch.empty_like(out)
+    call(None, hwa.FLAG_SOFTMAX_ONLY, None, dense_sm)
+    call(tau, hwa.FLAG_SOFTMAX_ONLY, ws, routed_sm)
+    torch.cuda.synchronize()
+    a = routed_sm.float().view(B * H, -1)
+    r = dense_sm.float().view(B * H, -1)
+    err = float(((a - r).norm(dim=1) / r.norm(dim=1)).max())
+    del t, text, out, ws, dense_sm, routed_sm, a, r
+    torch.cuda.empty_cache()
+    return {"tau": tau, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(B * F * S / (ms / 1000.0), 1),
+            "speedup_vs_dense": round(dense_ms / ms, 3),
+            "softmax_ms": round(stage["softmax"], 4),
+            "routing_and_vtranspose_ms": round(stage["vtranspose"], 4),
+            "kept_block_fraction": round(kept / total, 4),
+            "o_sm_rel_err_vs_dense": round(err, 4)}
 
 
 def time_forward(cfg, inp, rule, steps, warmup, up):

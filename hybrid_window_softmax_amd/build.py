@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libhwa.so")
 
 SOURCES = ["hwa_api.cpp", "softmax.hip", "softmax_bwd.hip", "stats.hip", "factor.hip",
            "scan.hip", "readout.hip", "linear_bwd.hip", "noalloc.hip",
-           "alpha.hip"]
+           "alpha.hip", "block.hip", "route.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -37,6 +37,9 @@ float* lse_out_of(const hwa_params* p) {
 void* sm_out_of(const hwa_params* p) {
   return field_or_null(p, &hwa_params::softmax_out, offsetof(hwa_params, softmax_out));
 }
+bool has_route_tau(const hwa_params* p) {
+  return p->struct_size >= offsetof(hwa_params, route_tau) + sizeof(float);
+}
 
 // Basic checks on the params struct shared by every entry point.
 hwa_status check_params(const hwa_params* p) {
@@ -77,9 +80,11 @@ bool make_geom(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
 // counters (internal, the last region inside L.total).
 struct Internal {
   size_t st16 = 0, st_eps = 0, sched = 0;
+  size_t rq = 0, rk = 0, rcount = 0, rlist = 0;  // routing (HWA_FLAG_ROUTED)
 };
 
-hwa_workspace_layout compute_layout(const Geom& g, int dtype, Internal* in = nullptr) {
+hwa_workspace_layout compute_layout(const Geom& g, int dtype, Internal* in = nullptr,
+                                    bool routed = false) {
   hwa_workspace_layout L;
   const size_t bh = (size_t)g.B * g.H;
   const size_t dd = (size_t)g.d * g.d;
@@ -103,6 +108,14 @@ hwa_workspace_layout compute_layout(const Geom& g, int dtype, Internal* in = nul
   x.st16 = L.st16 = take(dtype == HWA_BF16 ? bh * g.F * dd * sizeof(_Float16) : 0);
   x.st_eps = L.st_eps = take(dtype == HWA_BF16 ? bh * g.F * sizeof(float) : 0);
   x.sched = take(hwa::HWA_SCHED_WORDS * sizeof(unsigned));
+  if (routed) {
+    const size_t units = bh * g.nch;
+    const size_t nt = (size_t)hwa::route_tiles(g);
+    x.rq = take(units * nt * g.d * sizeof(float));
+    x.rk = take(units * (size_t)hwa::route_pieces(g) * g.d * sizeof(float));
+    x.rcount = take(units * nt * sizeof(int32_t));
+    x.rlist = take(units * nt * (size_t)hwa::route_blocks_max(g) * sizeof(uint16_t));
+  }
   if (in) *in = x;
   L.total = off;
   return L;
@@ -154,7 +167,26 @@ hwa_status hwa_get_workspace_layout(int32_t frames, int32_t tokens_per_frame,
   Geom g;
   if (!layout || !make_geom(frames, tokens_per_frame, chunk, 0, p, g))
     return HWA_ERR_INVALID_ARG;
-  *layout = compute_layout(g, p->dtype);
+  *layout = compute_layout(g, p->dtype, nullptr, (p->flags & HWA_FLAG_ROUTED) != 0);
+  return HWA_OK;
+}
+
+hwa_status hwa_get_route_layout(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
+                                const hwa_params* p, size_t* count_offset,
+                                size_t* list_offset, int32_t* tiles_per_chunk,
+                                int32_t* list_stride) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  Geom g;
+  if (!count_offset || !list_offset || !tiles_per_chunk || !list_stride ||
+      !make_geom(frames, tokens_per_frame, chunk, 0, p, g))
+    return HWA_ERR_INVALID_ARG;
+  Internal X;
+  compute_layout(g, p->dtype, &X, true);
+  *count_offset = X.rcount;
+  *list_offset = X.rlist;
+  *tiles_per_chunk = hwa::route_tiles(g);
+  *list_stride = hwa::route_blocks_max(g);
   return HWA_OK;
 }
 
@@ -179,11 +211,19 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
     return HWA_ERR_INVALID_ARG;
   if (rule < HWA_RULE_VDN_SOLVE || rule > HWA_RULE_VDN_SCALED)
     return HWA_ERR_INVALID_ARG;
-  const uint32_t known = HWA_FLAG_SOFTMAX_ONLY | HWA_FLAG_LINEAR_ONLY;
+  const uint32_t known = HWA_FLAG_SOFTMAX_ONLY | HWA_FLAG_LINEAR_ONLY | HWA_FLAG_ROUTED;
   if (p->flags & ~known) return HWA_ERR_INVALID_ARG;
   const bool do_sm = !(p->flags & HWA_FLAG_LINEAR_ONLY);
   const bool do_lin = !(p->flags & HWA_FLAG_SOFTMAX_ONLY);
   if (!do_sm && !do_lin) return HWA_ERR_INVALID_ARG;
+  const bool routed = (p->flags & HWA_FLAG_ROUTED) != 0;
+  if (routed) {
+    if (!do_sm || !has_route_tau(p) || isnan(p->route_tau)) return HWA_ERR_INVALID_ARG;
+    if (p->dtype != HWA_BF16) return HWA_ERR_UNSUPPORTED;
+    // the softmax kernel's list of kept 64-key tiles holds at most 4096
+    const long long wkeys = (2LL * radius + 1) * chunk * (long long)tokens_per_frame;
+    if (wkeys / 64 + 4 > 4096) return HWA_ERR_UNSUPPORTED;
+  }
   if (!q || !k || !v || !out) return HWA_ERR_INVALID_ARG;
   if (do_lin && (!beta || !alpha || !gate || !p->conv_k || !p->conv_v))
     return HWA_ERR_INVALID_ARG;
@@ -208,7 +248,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
     return HWA_ERR_INVALID_ARG;
 
   Internal X;
-  const hwa_workspace_layout L = compute_layout(g, p->dtype, &X);
+  const hwa_workspace_layout L = compute_layout(g, p->dtype, &X, routed);
   if (!p->workspace || p->workspace_bytes < L.total ||
       !aligned(p->workspace, kAlign))
     return HWA_ERR_WORKSPACE;
@@ -255,8 +295,9 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
   };
   // the linear branch first, so that on bf16 the softmax kernel can add its
-  // readout in the epilogue (raw q only: no RoPE'd q on that path)
-  const bool fuse = do_sm && do_lin && p->dtype == HWA_BF16 && qs == q;
+  // readout in the epilogue (reading the raw q itself when the softmax runs
+  // on q_rope)
+  const bool fuse = do_sm && do_lin && p->dtype == HWA_BF16;
   if (mark(0) != hipSuccess) return HWA_ERR_HIP;
   if (hwa::launch_window_table(g, lohi, st, sched) != hipSuccess) return HWA_ERR_HIP;
   if (mark(1) != hipSuccess) return HWA_ERR_HIP;
@@ -297,10 +338,19 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   if (do_sm && p->dtype == HWA_BF16 &&
       hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
     return HWA_ERR_HIP;
+  hwa::RouteArgs rt{(const int*)(ws + X.rcount), (const uint16_t*)(ws + X.rlist),
+                    hwa::route_blocks_max(g)};
+  if (routed &&
+      hwa::launch_route(g, (const bf16_t*)qs, (const bf16_t*)ks, lohi, p->route_tau,
+                        (float*)(ws + X.rq), (float*)(ws + X.rk), (int*)(ws + X.rcount),
+                        (uint16_t*)(ws + X.rlist), rt.nkb_max, st) != hipSuccess)
+    return HWA_ERR_HIP;
   if (mark(6) != hipSuccess) return HWA_ERR_HIP;
-  const hwa::ReadoutArgs ra{(const bf16_t*)gate, st16, st_eps, p->rms_weight, g.F};
+  const hwa::ReadoutArgs ra{(const bf16_t*)gate, st16, st_eps, p->rms_weight, g.F,
+                            qs == q ? nullptr : (const bf16_t*)q};
   if (do_sm && hwa::launch_softmax(g, p->dtype, qs, ks, v, v_t, lohi, out, st,
-                                   fuse ? &ra : nullptr, sched, lse_out, sm_out) != hipSuccess)
+                                   fuse ? &ra : nullptr, sched, lse_out, sm_out,
+                                   routed ? &rt : nullptr) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(7) != hipSuccess) return HWA_ERR_HIP;
   if (do_lin && !fuse &&
@@ -631,6 +681,100 @@ hwa_status hwa_frame_alpha(const void* k, const float* w, const float* bias,
     if (overlaps(alpha, a_bytes, in.ptr, in.n)) return HWA_ERR_INVALID_ARG;
   if (hwa::launch_frame_alpha(g, p->dtype, k, w, bias, a_log, alpha, stream) != hipSuccess)
     return HWA_ERR_HIP;
+  return HWA_OK;
+}
+
+namespace {
+
+// The block's own regions (q, k, v, q_rope, k_rope, the attention output)
+// before the attention's workspace.
+size_t block_io_bytes(const Geom& g) {
+  return align_up((size_t)g.B * g.H * g.N * g.d * sizeof(bf16_t));
+}
+
+}  // namespace
+
+size_t hwa_block_workspace_bytes(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
+                                 const hwa_params* p) {
+  if (check_params(p) != HWA_OK || p->dtype != HWA_BF16) return 0;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, chunk, 0, p, g)) return 0;
+  const size_t att = hwa_workspace_bytes(frames, tokens_per_frame, chunk, p);
+  return att ? 6 * block_io_bytes(g) + att : 0;
+}
+
+hwa_status hwa_block_fwd(const void* x, const void* w_qkv, const void* w_o, const float* beta,
+                         const float* alpha, const void* gate, const float* text_state,
+                         int32_t frames, int32_t tokens_per_frame, int32_t grid_w,
+                         float rope_theta, int32_t chunk, int32_t radius, int32_t rule, void* y,
+                         hipStream_t stream, const hwa_params* p) {
+  hwa_status s = check_params(p);
+  if (s != HWA_OK) return s;
+  if (p->dtype != HWA_BF16) return HWA_ERR_UNSUPPORTED;
+  Geom g;
+  if (!make_geom(frames, tokens_per_frame, chunk, radius, p, g)) return HWA_ERR_INVALID_ARG;
+  if (!x || !w_qkv || !w_o || !y || grid_w < 1 || tokens_per_frame % grid_w != 0 ||
+      !(rope_theta > 0.0f) || !isfinite(rope_theta))
+    return HWA_ERR_INVALID_ARG;
+  if (p->flags || p->q_rope || p->k_rope || lse_out_of(p) || sm_out_of(p))
+    return HWA_ERR_INVALID_ARG;
+  const size_t D = (size_t)g.H * g.d;
+  const size_t M = (size_t)g.B * g.N;
+  // 32-bit byte offsets of the projections' direct loads
+  if (M * D * 2 >= (1ull << 31)) return HWA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(y, 16))
+    return HWA_ERR_INVALID_ARG;
+  const size_t need = hwa_block_workspace_bytes(frames, tokens_per_frame, chunk, p);
+  if (!need || !p->workspace || p->workspace_bytes < need || !aligned(p->workspace, kAlign))
+    return HWA_ERR_WORKSPACE;
+  const size_t io = M * D * sizeof(bf16_t);
+  const struct { const void* ptr; size_t n; } ins[] = {
+      {x, io}, {w_qkv, 3 * D * D * sizeof(bf16_t)}, {w_o, D * D * sizeof(bf16_t)},
+      {p->workspace, p->workspace_bytes},
+  };
+  for (const auto& in : ins)
+    if (overlaps(y, io, in.ptr, in.n)) return HWA_ERR_INVALID_ARG;
+
+  char* ws = (char*)p->workspace;
+  const size_t r = block_io_bytes(g);
+  bf16_t* q = (bf16_t*)ws;
+  bf16_t* k = (bf16_t*)(ws + r);
+  bf16_t* v = (bf16_t*)(ws + 2 * r);
+  bf16_t* qr = (bf16_t*)(ws + 3 * r);
+  bf16_t* kr = (bf16_t*)(ws + 4 * r);
+  bf16_t* att = (bf16_t*)(ws + 5 * r);
+  hwa_params pa = *p;
+  pa.q_rope = qr;
+  pa.k_rope = kr;
+  pa.workspace = ws + 6 * r;
+  pa.workspace_bytes = p->workspace_bytes - 6 * r;
+  pa.stage_events = nullptr;
+  // the attention's own checks, before anything is enqueued: with a NULL
+  // workspace it stops at the workspace check (HWA_ERR_WORKSPACE) when every
+  // other argument is valid
+  {
+    hwa_params pv = pa;
+    pv.workspace = nullptr;
+    pv.workspace_bytes = 0;
+    const hwa_status sv = hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, frames,
+                                          tokens_per_frame, chunk, radius, rule, att, stream, &pv);
+    if (sv != HWA_ERR_WORKSPACE) return sv;
+  }
+  void* const* ev = p->stage_events;
+  auto mark = [&](int i) { return ev ? hipEventRecord((hipEvent_t)ev[i], stream) : hipSuccess; };
+  if (mark(0) != hipSuccess) return HWA_ERR_HIP;
+  if (hwa::launch_gemm_qkv((const bf16_t*)x, (const bf16_t*)w_qkv, (int)M, (int)g.N, g.H, g.d,
+                           g.S, grid_w, rope_theta, q, k, v, qr, kr, stream) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(1) != hipSuccess) return HWA_ERR_HIP;
+  s = hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, frames, tokens_per_frame, chunk,
+                      radius, rule, att, stream, &pa);
+  if (s != HWA_OK) return s;
+  if (mark(2) != hipSuccess) return HWA_ERR_HIP;
+  if (hwa::launch_gemm_out(att, (const bf16_t*)w_o, (int)M, (int)g.N, g.H, g.d, (bf16_t*)y,
+                           stream) != hipSuccess)
+    return HWA_ERR_HIP;
+  if (mark(3) != hipSuccess) return HWA_ERR_HIP;
   return HWA_OK;
 }
 

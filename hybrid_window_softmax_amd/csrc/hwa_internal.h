@@ -95,6 +95,7 @@ struct ReadoutArgs {
   const float* st_eps;   // [B*H, F] RMSNorm eps at that scale
   const float* rms_w;    // [d] or null (ones)
   int F;
+  const bf16_t* q_raw;   // raw q when the softmax branch runs on a rotated q, else null
 };
 
 // S_t = P_{lo-1} diag(a_t) + Q_{hi+1} diag(b_t) of every (b, h, t) for the
@@ -106,16 +107,37 @@ hipError_t launch_state(const Geom& g, const float* decay, const float* bank_p,
                         _Float16* st, float* st_eps, hipStream_t st_stream);
 
 // fuse != null (bf16 only): the softmax kernel also adds the linear-branch
-// readout y = RMSNorm(S_t q^) * sigmoid(gate) of its queries (q must then be
-// the raw q) before it writes out. sched (bf16 only): HWA_SCHED_WORDS
+// readout y = RMSNorm(S_t q^) * sigmoid(gate) of its queries before it writes
+// out (q^ from the softmax's own q, or from fuse->q_raw when that is set: the
+// softmax then runs on a rotated q). sched (bf16 only): HWA_SCHED_WORDS
 // counters, zero at launch (the kernel leaves them non-zero). lse (or null):
 // [B*H, N] fp32 log-sum-exp of each query's scaled scores; sm_out (or null):
 // o_sm alone, in the I/O dtype.
+// Kept 128-key blocks of every (b, h, chunk, 256-query tile) for the routed
+// softmax: count [B*H, nch, tiles], list [B*H, nch, tiles, nkb_max] (block
+// indices relative to the window's first block, increasing).
+struct RouteArgs {
+  const int* count;
+  const uint16_t* list;
+  int nkb_max;
+};
+
+// route (bf16 only) != null: the block-sparse variant, on route's lists.
 hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
                           const int32_t* lohi, void* out, hipStream_t st,
                           const ReadoutArgs* fuse, unsigned* sched, float* lse,
-                          void* sm_out);
+                          void* sm_out, const RouteArgs* route = nullptr);
+
+// Block means and kept-block lists of the routed softmax (route.hip), from
+// the softmax branch's q, k (bf16); qmean [B*H, nch, tiles, d] and ksum
+// [B*H, nch, pieces, d] fp32 are scratch.
+hipError_t launch_route(const Geom& g, const bf16_t* q, const bf16_t* k, const int32_t* lohi,
+                        float tau, float* qmean, float* ksum, int* sel_count,
+                        uint16_t* sel_list, int nkb_max, hipStream_t st);
+int route_tiles(const Geom& g);    // 256-query tiles per chunk
+int route_pieces(const Geom& g);   // 128-key pieces per chunk
+int route_blocks_max(const Geom& g);  // key blocks of a window, at most
 
 hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
                              hipStream_t st);
@@ -158,6 +180,17 @@ hipError_t launch_scan_packed(const Geom& g, int rule, float c, const bf16_t* Mp
                               const float* Bm, const float* alpha, const float* text_state,
                               float text_scale, float* bank_p, float* bank_q,
                               int32_t* bank_e, hipStream_t st);
+
+// The attention block's projections (bf16 MFMA). QKV: x [M = B*T, H*d] times
+// W_qkv [3*H*d, H*d]^T into q, k, v [B, H, T, d] and the 3D-rotated qr, kr
+// (S tokens per frame, grid_w latent columns, base theta). Output: the
+// attention output att [B, H, T, d] read as [M, H*d], times W_o [H*d, H*d]^T
+// into y [M, H*d]. M * H * d * 2 < 2^31.
+hipError_t launch_gemm_qkv(const bf16_t* x, const bf16_t* w_qkv, int M, int T, int H, int d,
+                           int S, int grid_w, float theta, bf16_t* q, bf16_t* k, bf16_t* v,
+                           bf16_t* qr, bf16_t* kr, hipStream_t st);
+hipError_t launch_gemm_out(const bf16_t* att, const bf16_t* w_o, int M, int T, int H, int d,
+                           bf16_t* y, hipStream_t st);
 
 // Bridge decays of every (b, h, t): prod_{j=lo..t} alpha_j, prod_{j=t..hi}.
 hipError_t launch_decay(const Geom& g, const float* alpha, const int32_t* lohi,

@@ -46,6 +46,8 @@ constexpr int SM_SPARE = 128;
 #ifndef SM_PREFETCH
 #define SM_PREFETCH 2
 #endif
+constexpr int SM_RB = 128;             // key block of the routed variant
+constexpr int SM_ROUTE_TILES = 4096;   // kept tiles per window, at most
 
 // ---------------------------------------------------------------- window table
 __global__ void window_table_kernel(int F, int chunk, int radius,
@@ -135,14 +137,17 @@ hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
 // that stage indices are compile-time. Eight waves (256 queries) share every
 // tile; one workgroup per CU (two waves per SIMD).
 
-template <int D>
+// ROUTED: the block-sparse variant -- the workgroup streams only the 64-key
+// tiles of the 128-key blocks its query tile kept (route.hip's lists), in
+// increasing order; with every block kept it visits exactly the dense tiles.
+template <int D, bool ROUTED>
 __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ vt, const int32_t* __restrict__ lohi,
     bf16_t* __restrict__ out, int F, int S, int chunk, int nch, long long N,
     long long Np, int tiles_per_chunk, float scale_log2, ReadoutArgs ra, int fuse,
     unsigned* __restrict__ sched, int ntiles_total, float* __restrict__ lse_out,
-    bf16_t* __restrict__ sm_out) {
+    bf16_t* __restrict__ sm_out, RouteArgs rt) {
   // the body uses device-only lambdas; the host pass needs only the stub
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KC = D / 8;          // 16-byte chunks per key
@@ -313,13 +318,43 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   };
 
   const long long kt_first = k_begin / SM_KT * SM_KT;
-  const int ntiles = (int)((k_end - kt_first + SM_KT - 1) / SM_KT);
+  int ntiles = (int)((k_end - kt_first + SM_KT - 1) / SM_KT);
+  // routed: the kept tiles (offsets from kt_first in tiles); the halves of a
+  // kept block that lie outside the window are left out
+  __shared__ uint16_t tlist[ROUTED ? SM_ROUTE_TILES : 1];
+  __shared__ int tlist_n;
+  if constexpr (ROUTED) {
+    if (tid == 0) {
+      const long long slot = ((long long)bh * nch + c) * tiles_per_chunk + tile;
+      const int cnt = rt.count[slot];
+      const uint16_t* lst = rt.list + slot * rt.nkb_max;
+      const long long jfirst = k_begin / SM_RB;
+      int n = 0;
+      for (int i = 0; i < cnt; ++i) {
+        const long long key0 = (jfirst + lst[i]) * SM_RB;
+        for (int h = 0; h < SM_RB / SM_KT; ++h) {
+          const long long tk = key0 + (long long)h * SM_KT;
+          if (tk + SM_KT > k_begin && tk < k_end && n < SM_ROUTE_TILES)
+            tlist[n++] = (uint16_t)((tk - kt_first) / SM_KT);
+        }
+      }
+      tlist_n = n;
+    }
+    __syncthreads();
+    ntiles = __builtin_amdgcn_readfirstlane(tlist_n);
+  }
+  // first key of tile `it` of this workgroup's sequence
+  auto tile_key = [&] __device__(int it) __attribute__((always_inline)) -> long long {
+    if constexpr (ROUTED) return kt_first + (long long)tlist[it] * SM_KT;
+    else return kt_first + (long long)it * SM_KT;
+  };
 
   // keys of tile `it` outside [k_begin, k_end) score -inf (first and last
   // tile only); returns whether the tile needed it
   auto mask = [&] __device__(int it, f32x16 (&sv)[2]) __attribute__((always_inline)) {
-    const int lo_rel = (int)(k_begin - kt_first) - it * SM_KT;  // keys before lo_rel and
-    const int hi_rel = (int)(k_end - kt_first) - it * SM_KT;    // from hi_rel on are out
+    const long long kt = tile_key(it);
+    const int lo_rel = (int)(k_begin - kt);  // keys before lo_rel and
+    const int hi_rel = (int)(k_end - kt);    // from hi_rel on are out
     if (lo_rel <= 0 && hi_rel >= SM_KT) return false;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -371,7 +406,10 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
                    __attribute__((always_inline)) {
     constexpr int SI = decltype(si_tag)::value;
     constexpr int SO = SI ^ 1;  // K(i+1) and V(i-1)
-    const long long kt0 = kt_first + (long long)it * SM_KT;
+    // K(i+2) (past the last tile: the last one again, which nothing reads)
+    // and V(i)
+    const long long kt0 = tile_key(it);
+    const long long kt2 = ROUTED ? tile_key(min(it + 2, ntiles - 1)) : kt0 + 2 * SM_KT;
     const bf16_t* ks = &k_lds[SO][0];
     const bf16_t* vs = &v_lds[SO][0];
     const float mb = m_run * scale_log2;
@@ -397,7 +435,7 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
       // (K(i+2) past the last tile loads rows that nothing reads)
       if (g == 0 || g == NG / 2) {
         if ((wave < SM_NW / 2) == (g == 0)) {
-          dma_k(kt0 + 2 * SM_KT, SI);
+          dma_k(kt2, SI);
           dma_v(kt0, SI);
         }
       }
@@ -465,8 +503,8 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   const int t_first = (int)(q_tile0 / S);
   StateChunks<D, SM_THREADS> stc;  // S_t of a frame, global -> registers -> LDS
   if (fuse) stc.load(ra.st + ((long long)bh * ra.F + t_first) * D * D, tid);
-  dma_k(kt_first, 0);
-  if (ntiles > 1) dma_k(kt_first + SM_KT, 1);
+  dma_k(tile_key(0), 0);
+  if (ntiles > 1) dma_k(tile_key(1), 1);
   if (fuse) {
     load_weight<D, SM_THREADS>(rl, ra.rms_w, tid);
     stc.store(rl, tid);
@@ -509,8 +547,8 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
     // the same loads and barriers as a step of the active waves
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
-      const long long kt0 = kt_first + (long long)it * SM_KT;
-      dma_k(kt0 + 2 * SM_KT, it & 1);
+      const long long kt0 = tile_key(it);
+      dma_k(ROUTED ? tile_key(min(it + 2, ntiles - 1)) : kt0 + 2 * SM_KT, it & 1);
       dma_v(kt0, it & 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -557,9 +595,10 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
 
   // ---- fused linear-branch readout: out = o_sm + y, frame by frame (a tile
   // of SM_QT queries spans at most two frames when S >= SM_QT; in general
-  // every frame from the first query's to the last's). qreg holds raw q
-  // (no RoPE on this path) in the chunk order of the QK operand; S_t's
-  // columns are read in the same order.
+  // every frame from the first query's to the last's). q^ comes from the raw
+  // q in the chunk order of the QK operand: qreg itself, or, when the softmax
+  // ran on a rotated q, the raw rows loaded here in that order; S_t's columns
+  // are read in the same order.
   // chunk kk of the lane half: channels 8 * (8 * (kk / 4) + op_chunk(kk % 4, half)),
   // a lane part 16 * half plus a compile-time part
   struct KOff {
@@ -567,8 +606,17 @@ __global__ __launch_bounds__(SM_THREADS, 1) void softmax_bf16_kernel(
   };
   const int qlane = 16 * half;
   u32x4 qraw[D / 16];
+  if (ra.q_raw) {
+    const bf16_t* qrow = ra.q_raw + (long long)bh * N * D + my_q * D;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) qraw[kk] = __builtin_bit_cast(u32x4, qreg[kk]);
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int dc = 8 * (kk / 4) + op_chunk(kk % 4, half);
+      qraw[kk] = my_q < N ? *(const u32x4*)(qrow + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qraw[kk] = __builtin_bit_cast(u32x4, qreg[kk]);
+  }
   const long long q_last = min(q_tile0 + SM_QT, q_end) - 1;
   const int t_last = (int)(q_last / S);
   const int my_t = my_q < q_end ? (int)(my_q / S) : -1;
@@ -709,7 +757,7 @@ hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
                           const void* k, const void* v, const bf16_t* v_t,
                           const int32_t* lohi, void* out, hipStream_t st,
                           const ReadoutArgs* fuse, unsigned* sched, float* lse,
-                          void* sm_out) {
+                          void* sm_out, const RouteArgs* route) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)g.d);
   const int qpc = g.chunk * g.S;  // queries of a full chunk
   if (dtype == HWA_BF16) {
@@ -719,14 +767,18 @@ hipError_t launch_softmax(const Geom& g, int dtype, const void* q,
     dim3 grid(ntiles + 8 * SM_SPARE);
     const long long Np = round_up64(g.N);
     const ReadoutArgs ra = fuse ? *fuse : ReadoutArgs{};
-#define SM_LAUNCH(DD)                                                        \
-  hipLaunchKernelGGL(softmax_bf16_kernel<DD>, grid, dim3(SM_THREADS), 0, st, \
-                     (const bf16_t*)q, (const bf16_t*)k, v_t, lohi,          \
-                     (bf16_t*)out, g.F, g.S, g.chunk, g.nch, g.N, Np, tpc,   \
-                     scale_log2, ra, fuse ? 1 : 0, sched, ntiles, lse,       \
-                     (bf16_t*)sm_out)
-    if (g.d == 128) SM_LAUNCH(128);
-    else SM_LAUNCH(64);
+    const RouteArgs rt = route ? *route : RouteArgs{};
+#define SM_LAUNCH(DD, RR)                                                        \
+  hipLaunchKernelGGL((softmax_bf16_kernel<DD, RR>), grid, dim3(SM_THREADS), 0, st, \
+                     (const bf16_t*)q, (const bf16_t*)k, v_t, lohi,              \
+                     (bf16_t*)out, g.F, g.S, g.chunk, g.nch, g.N, Np, tpc,       \
+                     scale_log2, ra, fuse ? 1 : 0, sched, ntiles, lse,           \
+                     (bf16_t*)sm_out, rt)
+    if (g.d == 128) {
+      if (route) SM_LAUNCH(128, true); else SM_LAUNCH(128, false);
+    } else {
+      if (route) SM_LAUNCH(64, true); else SM_LAUNCH(64, false);
+    }
 #undef SM_LAUNCH
   } else {
     const int tpc = (qpc + 127) / 128;

@@ -21,12 +21,15 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 FLAG_SOFTMAX_ONLY = 1
 FLAG_LINEAR_ONLY = 2
 FLAG_ACCUMULATE = 8
+FLAG_ROUTED = 16
 NUM_STAGE_EVENTS = 9
 STAGES = ("window", "stats", "inverse", "scan", "decay+state", "vtranspose", "softmax",
           "readout")
 NUM_BWD_STAGE_EVENTS = 4
 BWD_STAGES = ("prep", "dq", "dkdv")
 NUM_LIN_BWD_STAGE_EVENTS = 6
+NUM_BLOCK_STAGE_EVENTS = 4
+BLOCK_STAGES = ("qkv", "attention", "out_proj")
 LIN_BWD_STAGES = ("recompute", "readout", "scans", "stats", "convs")
 # gradients hwa_linear_bwd returns, in its argument order
 LIN_GRADS = ("q", "k", "v", "beta", "alpha", "gate", "text_state", "conv_k", "conv_v",
@@ -43,7 +46,8 @@ HWA_BF16 = 1
 EXPORTS = ("hybrid_attn_fwd", "hybrid_attn_fwd_noalloc", "hwa_workspace_bytes", "hwa_get_workspace_layout",
            "hwa_window_bounds", "hwa_text_state", "hwa_text_state_workspace_bytes",
            "hwa_softmax_bwd", "hwa_softmax_bwd_workspace_bytes", "hwa_linear_bwd",
-           "hwa_linear_bwd_workspace_bytes", "hwa_frame_alpha", "hwa_status_string")
+           "hwa_linear_bwd_workspace_bytes", "hwa_frame_alpha", "hwa_block_fwd",
+           "hwa_block_workspace_bytes", "hwa_get_route_layout", "hwa_status_string")
 
 
 class Params(ctypes.Structure):
@@ -67,6 +71,7 @@ class Params(ctypes.Structure):
         ("stage_events", ctypes.c_void_p),
         ("softmax_lse", ctypes.c_void_p),
         ("softmax_out", ctypes.c_void_p),
+        ("route_tau", ctypes.c_float),
     ]
 
 
@@ -120,6 +125,15 @@ def lib():
         L.hwa_linear_bwd_workspace_bytes.restype = sz
         L.hwa_frame_alpha.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, PP]
         L.hwa_frame_alpha.restype = ctypes.c_int
+        L.hwa_block_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float,
+                                    i32, i32, i32, vp, vp, PP]
+        L.hwa_block_fwd.restype = ctypes.c_int
+        L.hwa_block_workspace_bytes.argtypes = [i32, i32, i32, PP]
+        L.hwa_block_workspace_bytes.restype = sz
+        L.hwa_get_route_layout.argtypes = [i32, i32, i32, PP, ctypes.POINTER(sz),
+                                           ctypes.POINTER(sz), ctypes.POINTER(i32),
+                                           ctypes.POINTER(i32)]
+        L.hwa_get_route_layout.restype = ctypes.c_int
         L.hwa_status_string.argtypes = [ctypes.c_int]
         L.hwa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -175,6 +189,19 @@ def workspace_layout(frames, tokens_per_frame, chunk, p: Params) -> dict:
     return {n: getattr(L, n) for n, _ in Layout._fields_}
 
 
+def route_layout(frames, tokens_per_frame, chunk, p: Params) -> dict:
+    """Where the routed softmax's kept-block lists sit in the workspace."""
+    co, lo = ctypes.c_size_t(), ctypes.c_size_t()
+    tpc, stride = ctypes.c_int32(), ctypes.c_int32()
+    code = lib().hwa_get_route_layout(frames, tokens_per_frame, chunk, ctypes.byref(p),
+                                      ctypes.byref(co), ctypes.byref(lo), ctypes.byref(tpc),
+                                      ctypes.byref(stride))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return {"count": co.value, "list": lo.value, "tiles_per_chunk": tpc.value,
+            "stride": stride.value}
+
+
 def _check(t, name, dtype, shape, device):
     if t is None:
         return
@@ -195,8 +222,11 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
                     text_scale: float = 0.5, rms_eps: float = 1e-6,
                     rms_weight=None, q_rope=None, k_rope=None, flags: int = 0,
                     out=None, workspace=None, stream=None, stage_events=None,
-                    softmax_lse=None, softmax_out=None, noalloc=False):
+                    softmax_lse=None, softmax_out=None, noalloc=False, route_tau=None):
     """out = windowed softmax + delta-rule linear branch (see include/hwa.h).
+
+    ``route_tau``: run the softmax branch block-sparse (FLAG_ROUTED) with this
+    keep threshold (-inf keeps every block).
 
     ``noalloc``: call hybrid_attn_fwd_noalloc instead, which uses the
     library's own fixed scratch array (HWA_NOALLOC_SCRATCH_BYTES per GPU) and
@@ -225,8 +255,12 @@ def hybrid_attn_fwd(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
     _check(rms_weight, "rms_weight", torch.float32, (d,), dev)
     _check(softmax_lse, "softmax_lse", torch.float32, (B, H, N), dev)
     _check(softmax_out, "softmax_out", q.dtype, (B, H, N, d), dev)
+    if route_tau is not None:
+        flags |= FLAG_ROUTED
     p = make_params(B, H, d, q.dtype, c, text_scale, rms_eps, conv_k, conv_v, rms_weight,
                     q_rope, k_rope, None, flags)
+    if route_tau is not None:
+        p.route_tau = route_tau
     p.softmax_lse = None if softmax_lse is None else softmax_lse.data_ptr()
     p.softmax_out = None if softmax_out is None else softmax_out.data_ptr()
     if noalloc:
@@ -471,6 +505,51 @@ def frame_alpha(k, w, bias, a_log, frames: int, tokens_per_frame: int, out=None,
     if code != HWA_OK:
         raise HwaError(code)
     return out
+
+
+def block_fwd(x, w_qkv, w_o, beta, alpha, gate, text_state, conv_k, conv_v, heads: int,
+              frames: int, tokens_per_frame: int, grid_w: int, rope_theta: float = 10000.0,
+              chunk: int = 5, radius: int = 1, rule="vdn_solve", c: float = 0.5,
+              text_scale: float = 0.5, rms_eps: float = 1e-6, rms_weight=None, y=None,
+              workspace=None, stream=None, stage_events=None):
+    """The attention block (hwa_block_fwd): y = concat_h(hybrid attention of
+    the projected, 3D-rotated heads) W_o^T. x [B, N, D] bf16 with D = heads *
+    d; w_qkv [3 D, D], w_o [D, D] bf16; beta [B, H, N], alpha [B, H, F, d],
+    gate [B, H, N, d] (bf16), text_state [B, H, d, d] or None, conv taps
+    [H, d, 4], rms_weight [d] or None. Returns (y, workspace)."""
+    B, N, D = x.shape
+    H = heads
+    d = D // H
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (B, N, D), dev)
+    _check(w_qkv, "w_qkv", torch.bfloat16, (3 * D, D), dev)
+    _check(w_o, "w_o", torch.bfloat16, (D, D), dev)
+    _check(beta, "beta", torch.float32, (B, H, N), dev)
+    _check(alpha, "alpha", torch.float32, (B, H, frames, d), dev)
+    _check(gate, "gate", torch.bfloat16, (B, H, N, d), dev)
+    _check(text_state, "text_state", torch.float32, (B, H, d, d), dev)
+    _check(conv_k, "conv_k", torch.float32, (H, d, 4), dev)
+    _check(conv_v, "conv_v", torch.float32, (H, d, 4), dev)
+    _check(rms_weight, "rms_weight", torch.float32, (d,), dev)
+    p = make_params(B, H, d, torch.bfloat16, c, text_scale, rms_eps, conv_k, conv_v, rms_weight)
+    need = int(lib().hwa_block_workspace_bytes(frames, tokens_per_frame, chunk, ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if stage_events is not None:
+        p.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
+    if y is None:
+        y = torch.empty_like(x)
+    st = _stream(dev) if stream is None else ctypes.c_void_p(stream)
+    code = lib().hwa_block_fwd(_ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(beta), _ptr(alpha),
+                               _ptr(gate), _ptr(text_state), frames, tokens_per_frame, grid_w,
+                               rope_theta, chunk, radius,
+                               RULES[rule] if isinstance(rule, str) else rule, _ptr(y), st,
+                               ctypes.byref(p))
+    if code != HWA_OK:
+        raise HwaError(code)
+    return y, workspace
 
 
 class StageTimer:

@@ -28,7 +28,7 @@ import numpy as np
 
 TID = dict(q=0, k=1, v=2, gate=3, beta=4, alpha=5, k_txt=6, v_txt=7,
            beta_txt=8, conv_k=9, conv_v=10, rms_weight=11, d_out=12, state=13,
-           alpha_w=14, alpha_b=15, alpha_a=16)
+           alpha_w=14, alpha_b=15, alpha_a=16, x=17, w_qkv=18, w_o=19)
 
 # The five workloads, by name. Token counts per frame follow 832x480 (52x30
 # latent grid) and 1024x1024 (64x64) canvases at 16x spatial compression.
@@ -247,3 +247,19 @@ def alpha_weights(cfg):
     a = np.stack([np.float32(np.log(0.05)) + _draw(seed, "alpha_a", 0, h, (d,), "normal",
                                                    std=0.2) for h in range(H)])
     return w.astype(np.float32), b.astype(np.float32), a.astype(np.float32)
+
+
+def block_inputs(cfg):
+    """Block input x [B, N, D] ~ N(0, 1) and the projections' synthetic
+    weights W_qkv [3 D, D], W_o [D, D] ~ N(0, 1/D) (so q, k, v ~ N(0, 1) as in
+    the attention workloads), D = heads * head_dim; bf16 bits (uint16).
+    x of batch element b is drawn as slice (b, 0)."""
+    if not isinstance(cfg, dict):
+        cfg = WORKLOADS[cfg]
+    B, H, d, seed = cfg["batch"], cfg["heads"], cfg["head_dim"], cfg["seed"]
+    D = H * d
+    N = cfg["frames"] * cfg["tokens_per_frame"]
+    x = np.stack([f32_to_bf16_bits(_draw(seed, "x", b, 0, (N, D), "normal")) for b in range(B)])
+    wq = f32_to_bf16_bits(_draw(seed, "w_qkv", 0, 0, (3 * D, D), "normal", std=D ** -0.5))
+    wo = f32_to_bf16_bits(_draw(seed, "w_o", 0, 0, (D, D), "normal", std=D ** -0.5))
+    return x, wq, wo

@@ -76,9 +76,12 @@ typedef enum { HWA_F32 = 0, HWA_BF16 = 1 } hwa_dtype;
 enum {
   HWA_FLAG_SOFTMAX_ONLY = 1,      /* out = o_sm (linear branch skipped)      */
   HWA_FLAG_LINEAR_ONLY = 2,       /* out = y (softmax branch skipped)        */
-  HWA_FLAG_ACCUMULATE = 8          /* hwa_linear_bwd only: add dq, dk, dv to */
+  HWA_FLAG_ACCUMULATE = 8,         /* hwa_linear_bwd only: add dq, dk, dv to */
                                    /* what those buffers hold (the softmax   */
                                    /* branch's gradient, for out = o_sm + y) */
+  HWA_FLAG_ROUTED = 16             /* hybrid_attn_fwd, bf16: block-sparse    */
+                                   /* softmax branch (hwa_params.route_tau;  */
+                                   /* see below)                             */
 };
 
 typedef struct {
@@ -107,9 +110,10 @@ typedef struct {
                          /* timing: [0] start, then after [1] window table,   */
                          /* [2] statistics, [3] inverses, [4] scan, [5] decay */
                          /* products and (bf16) S_t of every frame, [6] V    */
-                         /* transpose, [7] softmax (with the                  */
+                         /* transpose (and the routing of HWA_FLAG_ROUTED),   */
+                         /* [7] softmax (with the                             */
                          /* linear-branch readout fused in, on bf16 calls     */
-                         /* without q_rope that run both branches), [8]       */
+                         /* that run both branches), [8]                      */
                          /* separate readout (a skipped stage records its     */
                          /* event with the previous one)                      */
   /* Fields below were added later; a caller whose struct_size ends before   */
@@ -120,7 +124,34 @@ typedef struct {
                          /* for hwa_softmax_bwd)                               */
   void* softmax_out;     /* NULL, or [B,H,N,d] dtype: hybrid_attn_fwd also     */
                          /* writes o_sm alone there (for hwa_softmax_bwd)      */
+  float route_tau;       /* HWA_FLAG_ROUTED: keep threshold mean + tau * std   */
+                         /* (-INFINITY keeps every block; NaN is rejected)     */
 } hwa_params;
+
+/*
+ * Block-sparse routing of the softmax branch (HWA_FLAG_ROUTED), an
+ * approximation of the windowed softmax after the H3 acceleration report
+ * (section 9.7.3, "Sol-Attn": 128-token blocks, block means of Q and K,
+ * trial scores q_mean . k_mean, keep the blocks above mean + tau * std,
+ * exact attention on the kept blocks). Per (batch, head) and chunk, with the
+ * chunk's key window [kb, ke):
+ *   query tiles: 256 queries from the chunk's first one; key blocks: the
+ *   global 128-token blocks [128 j, 128 j + 128) cut to the window;
+ *   q_mean, k_mean: means over the tile's queries / the block's window keys
+ *   (of the softmax branch's q and k); s_j = q_mean . k_mean_j / sqrt(d);
+ *   block j is kept when s_j >= mean_j s + tau * std_j s (population
+ *   standard deviation over the window's blocks), and so is the first block
+ *   of largest s; every query of the tile then attends to the keys of its
+ *   kept blocks only (fp32 scores, so a block within rounding of the
+ *   threshold may go either way).
+ * bf16 only; the window may span at most 4096 64-key tiles
+ * (HWA_ERR_UNSUPPORTED otherwise). The kept blocks stay in the workspace at
+ * the offsets hwa_get_route_layout reports.
+ */
+hwa_status hwa_get_route_layout(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
+                                const hwa_params* p, size_t* count_offset,
+                                size_t* list_offset, int32_t* tiles_per_chunk,
+                                int32_t* list_stride);
 
 #define HWA_NUM_STAGE_EVENTS 9
 
@@ -150,6 +181,10 @@ typedef struct {
  *   st16     fp16 [B, H, F, d, d] (bf16 only) S_t = P_{lo-1} diag(a_t) +
  *                                 Q_{hi+1} diag(b_t) of every frame, times 2^-m
  *   st_eps   [B, H, F]            (bf16 only) rms_eps * 2^-2m, the same m
+ * With HWA_FLAG_ROUTED the workspace also holds the routing's block means and
+ * kept-block lists (hwa_get_route_layout): count int32 [B, H, n_ch, tiles]
+ * and list uint16 [B, H, n_ch, tiles, stride], block indices relative to the
+ * window's first 128-token block, in increasing order.
  * n_ch = ceil(F / chunk). The last 256 bytes before `total` hold the softmax
  * kernel's work-queue counters (internal; each call zeroes them itself).
  */
@@ -381,6 +416,54 @@ size_t hwa_linear_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
 hwa_status hwa_frame_alpha(const void* k, const float* w, const float* bias,
                            const float* a_log, int32_t frames, int32_t tokens_per_frame,
                            float* alpha, hipStream_t stream, const hwa_params* p);
+
+/*
+ * hwa_block_fwd -- the attention block around the hybrid attention (article,
+ * "Why video models are stuck on attention": one QKV projection feeds both
+ * branches and their outputs are summed; "Step 1": the softmax branch uses
+ * RoPE'd q and k, the linear branch unrotated ones). The article defines
+ * neither the projections' layout nor the RoPE; this entry point computes,
+ * per batch element, with D = H * d:
+ *   [q | k | v] = x W_qkv^T            (q, k, v rounded to bf16)
+ *   q_rope, k_rope = RoPE3D(q), RoPE3D(k)
+ *   out_h = hybrid_attn_fwd(q, k, v, ..., q_rope, k_rope) of every head h
+ *   y = [out_0 | ... | out_{H-1}] W_o^T
+ * RoPE3D: token n of frame t = n / S sits at row r = (n % S) / grid_w and
+ * column (n % S) % grid_w of the latent grid; its d / 2 channel pairs
+ * (2i, 2i + 1) are split into p_t = d/2 - 2 floor(d/6) time pairs, then
+ * p_h = floor(d/6) row pairs, then p_w = floor(d/6) column pairs, and pair u
+ * of an axis with P pairs is turned by the angle pos * rope_theta^(-u / P)
+ * (pos = t, r or the column): (a, b) -> (a cos - b sin, a sin + b cos).
+ *   x      [B, N, D]   bf16   block input (tokens frame-major, N = F * S)
+ *   w_qkv  [3 D, D]    bf16   rows = output features: q (head h at rows
+ *                             h d .. h d + d - 1), then k, then v
+ *   w_o    [D, D]      bf16   rows = output features
+ *   beta, alpha, gate, text_state, chunk, radius, rule: as hybrid_attn_fwd
+ *                             (per head, [B, H, ...])
+ *   grid_w                    latent grid columns, >= 1, dividing S
+ *   rope_theta                RoPE base (> 0; 10000 is the usual one)
+ *   y      [B, N, D]   bf16   written; must not overlap an input or the
+ *                             workspace
+ * bf16 only (HWA_ERR_UNSUPPORTED for fp32), d = 64 or 128, and B * N * D * 2 <
+ * 2^31. p: batch, heads, head_dim, dtype, c, text_scale, rms_eps, conv_k,
+ * conv_v, rms_weight as for hybrid_attn_fwd; workspace >=
+ * hwa_block_workspace_bytes (q, k, v, their rotations and the attention
+ * output, then the attention's own workspace); stage_events (NULL or
+ * HWA_NUM_BLOCK_STAGE_EVENTS events: [0] start, [1] after the QKV
+ * projection, [2] after the hybrid attention, [3] after the output
+ * projection); flags, q_rope, k_rope, softmax_lse and softmax_out must be 0 /
+ * NULL. Returns HWA_OK, or an error status before anything is enqueued.
+ */
+#define HWA_NUM_BLOCK_STAGE_EVENTS 4
+
+hwa_status hwa_block_fwd(const void* x, const void* w_qkv, const void* w_o, const float* beta,
+                         const float* alpha, const void* gate, const float* text_state,
+                         int32_t frames, int32_t tokens_per_frame, int32_t grid_w,
+                         float rope_theta, int32_t chunk, int32_t radius, int32_t rule, void* y,
+                         hipStream_t stream, const hwa_params* p);
+
+size_t hwa_block_workspace_bytes(int32_t frames, int32_t tokens_per_frame, int32_t chunk,
+                                 const hwa_params* p);
 
 /* Static English text of a status. */
 const char* hwa_status_string(hwa_status s);

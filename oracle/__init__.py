@@ -45,3 +45,5 @@ from .softmax_grad import (  # noqa: F401
     softmax_grad_rows,
 )
 from .linear_grad import linear_branch_torch, linear_branch_grad  # noqa: F401
+from .block import rope_pairs, rope_angles, rope3d, block_fwd  # noqa: F401
+from .routing import route_scores, route_keep, routed_softmax  # noqa: F401

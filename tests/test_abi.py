@@ -394,3 +394,26 @@ def test_frame_alpha_validation():
     assert call(p, out=w) == E.HWA_ERR_INVALID_ARG        # alpha overlaps W
     assert call(p, out=k + 64) == E.HWA_ERR_INVALID_ARG   # alpha inside k
     assert call(_params(head_dim=48)) == E.HWA_ERR_UNSUPPORTED
+
+
+@no_gpu
+def test_routed_flag_validation():
+    E = hwa
+    R = hwa.FLAG_ROUTED
+    p = _with_ws(_params(flags=R))
+    p.route_tau = float("nan")
+    assert _call(p) == E.HWA_ERR_INVALID_ARG                       # NaN threshold
+    p = _with_ws(_params(flags=R | hwa.FLAG_LINEAR_ONLY))
+    assert _call(p) == E.HWA_ERR_INVALID_ARG                       # no softmax branch
+    p = _with_ws(_params(flags=R, dtype=0))
+    assert _call(p) == E.HWA_ERR_UNSUPPORTED                       # fp32
+    p = _params(flags=R)
+    p.struct_size = hwa.Params.route_tau.offset                    # struct ends before tau
+    assert _call(p) == E.HWA_ERR_INVALID_ARG
+    p = _with_ws(_params(flags=R, head_dim=128), F=40, S=30000)
+    assert _call(p, F=40, S=30000) == E.HWA_ERR_UNSUPPORTED        # window > 4096 tiles
+    # the routed layout needs more workspace than the dense one
+    pd, pr = _params(), _params(flags=R)
+    assert hwa.workspace_bytes(10, 16, 5, pr) > hwa.workspace_bytes(10, 16, 5, pd)
+    L = hwa.route_layout(10, 16, 5, pr)
+    assert L["tiles_per_chunk"] == 1 and L["stride"] == 160 // 128 + 2

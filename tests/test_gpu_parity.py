@@ -156,7 +156,7 @@ def test_bf16_d128_ragged(rule):
 
 def test_bf16_separate_rope_inputs():
     # q_rope / k_rope feed the softmax branch only; the linear branch keeps
-    # raw q, k (the library then runs its readout as a separate kernel)
+    # raw q, k (the softmax kernel's fused readout then reads the raw q rows itself)
     cfg = inputs.tiny_config(frames=8, text_tokens=16, head_dim=128, tokens_per_frame=100,
                              dtype="bf16", heads=2, seed=107, chunk=3)
     _say(f"case {cfg['name']} with q_rope/k_rope")
