@@ -152,6 +152,10 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
 hipError_t launch_inverse(const Geom& g, float c2, const float* A, float* M,
                           hipStream_t st);
 
+// fp32 update matrices M_f: (I + c2 A_f)^-1 (invert), else I - c2 A_f
+hipError_t launch_update_f32(const Geom& g, bool invert, float c2, const float* A, float* M,
+                             hipStream_t st);
+
 // bf16 calls: M_f = (I + c2 A_f)^-1 (invert) or M_f = I - c2 A_f (not invert),
 // as hi and lo bf16 matrices in the bf16 scan's operand order, [B*H*F][2][d*d]
 // (d = 64 or 128).
