@@ -524,7 +524,6 @@ hwa_status hwa_linear_bwd(const void* q, const void* k, const void* v, const flo
   Geom g;
   if (!make_geom(frames, tokens_per_frame, chunk, radius, p, g)) return HWA_ERR_INVALID_ARG;
   if (rule < HWA_RULE_VDN_SOLVE || rule > HWA_RULE_VDN_SCALED) return HWA_ERR_INVALID_ARG;
-  if (rule == HWA_RULE_SANA_SCALED) return HWA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !beta || !alpha || !gate || !d_o || !p->conv_k || !p->conv_v ||
       !dq || !dk || !dv || !dbeta || !dalpha || !dgate || !dconv_k || !dconv_v)
     return HWA_ERR_INVALID_ARG;

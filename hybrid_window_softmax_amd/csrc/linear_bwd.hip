@@ -384,11 +384,21 @@ __global__ __launch_bounds__(256) void lin_adjoint_kernel(
 // ---------------------------------------------------------------- frame gradients
 // One workgroup per (frame, b*h): dB_f, dA_f (into the buffers A_f, B_f had)
 // and the scans' part of dalpha_f.
-template <int D>
+// vdn rules (S_f = X_f M_f, M_f = (I + cc A_f)^-1, X_f = S_{f-1} D_f + c1 B_f):
+//   dA_f = -cc (P_f^T dX^P_f + Q_f^T dX^Q_f), dB_f = c1 (dX^P_f + dX^Q_f).
+// SANA (S_f = X_f M_f + c2 B_f, M_f = I - cc A_f, X_f = S_{f-1} D_f): with
+// lam_f = dL/dS_f, dA_f = -cc D_f (P_{f-1}^T lam^P_f + Q_{f+1}^T lam^Q_f) and
+// dB_f = c2 (lam^P_f + lam^Q_f). lam_f is rebuilt as the adjoint scan formed
+// it: lam^P_f = dX^P_{f+1} D_{f+1} (+ the bank gradient when P_f is a bank
+// slot; lam^P_{F-1} is slot nch's alone), lam^Q_f = dX^Q_{f-1} D_{f-1} (+ the
+// bank gradient when Q_f is a slot; lam^Q_0 is slot 0's alone).
+// Both: dalpha_f = colsum(dX^P_f * P_{f-1} + dX^Q_f * Q_{f+1}).
+template <int D, bool SANA>
 __global__ __launch_bounds__(256) void lin_frame_grad_kernel(
     const float* __restrict__ Pst, const float* __restrict__ Qst,
-    const float* __restrict__ dXP, const float* __restrict__ dXQ, float cc, float c1,
-    float* __restrict__ dA, float* __restrict__ dB, float* __restrict__ dal, int F) {
+    const float* __restrict__ dXP, const float* __restrict__ dXQ, float cc, float cb,
+    const float* __restrict__ alpha, const float* __restrict__ dbank, int chunk, int nch,
+    int BH, float* __restrict__ dA, float* __restrict__ dB, float* __restrict__ dal, int F) {
   constexpr int BS = D / 16;
   constexpr int KR = 16;
   constexpr int RG = 256 / D, RPT = D / RG;
@@ -404,6 +414,25 @@ __global__ __launch_bounds__(256) void lin_frame_grad_kernel(
   const float* Q1 = Qst + so + (long long)(f + 1) * D * D;  // Q_{f+1}
   const float* xp = dXP + fo;
   const float* xq = dXQ + fo;
+  // SANA: lam^P_f and lam^Q_f at element ix = row * D + col
+  const float* xpn = dXP + fo + (long long)D * D;  // dX^P_{f+1} (read when f + 1 < F)
+  const float* xqp = dXQ + fo - (long long)D * D;  // dX^Q_{f-1} (read when f >= 1)
+  const float* apn = alpha + ((long long)bh * F + f + 1) * D;
+  const float* aqp = alpha + ((long long)bh * F + f - 1) * D;
+  const int slot_p = f == F - 1 ? nch : ((f + 1) % chunk == 0 ? (f + 1) / chunk : -1);
+  const int slot_q = f == 0 ? 0 : (f % chunk == 0 ? f / chunk : -1);
+  const float* bp = dbank + ((long long)bh * (nch + 1) + slot_p) * D * D;
+  const float* bq = dbank + (((long long)BH + bh) * (nch + 1) + slot_q) * D * D;
+  auto lam_p = [&](long long ix, int col) {
+    float x = f + 1 < F ? xpn[ix] * apn[col] : 0.0f;
+    if (slot_p >= 0) x += bp[ix];
+    return x;
+  };
+  auto lam_q = [&](long long ix, int col) {
+    float x = f >= 1 ? xqp[ix] * aqp[col] : 0.0f;
+    if (slot_q >= 0) x += bq[ix];
+    return x;
+  };
   {
     const int j = tid % D, rg = tid / D;
     float part = 0.0f;
@@ -411,7 +440,10 @@ __global__ __launch_bounds__(256) void lin_frame_grad_kernel(
     for (int k = 0; k < RPT; ++k) {
       const long long ix = (long long)(rg + RG * k) * D + j;
       const float a = xp[ix], b = xq[ix];
-      dB[fo + ix] = c1 * (a + b);
+      if constexpr (SANA)
+        dB[fo + ix] = cb * (lam_p(ix, j) + lam_q(ix, j));
+      else
+        dB[fo + ix] = cb * (a + b);
       part = fmaf(a, P0[ix], part);
       part = fmaf(b, Q1[ix], part);
     }
@@ -435,10 +467,17 @@ __global__ __launch_bounds__(256) void lin_frame_grad_kernel(
     for (int x = tid; x < KR * D; x += 256) {
       const int rr = x / D, col = x % D;
       const long long ix = (long long)(i0 + rr) * D + col;
-      sp[rr][col] = P1[ix];
-      sxp[rr][col] = xp[ix];
-      sq[rr][col] = Q0[ix];
-      sxq[rr][col] = xq[ix];
+      if constexpr (SANA) {
+        sp[rr][col] = P0[ix];
+        sxp[rr][col] = lam_p(ix, col);
+        sq[rr][col] = Q1[ix];
+        sxq[rr][col] = lam_q(ix, col);
+      } else {
+        sp[rr][col] = P1[ix];
+        sxp[rr][col] = xp[ix];
+        sq[rr][col] = Q0[ix];
+        sxq[rr][col] = xq[ix];
+      }
     }
     __syncthreads();
 #pragma unroll 4
@@ -457,10 +496,13 @@ __global__ __launch_bounds__(256) void lin_frame_grad_kernel(
         for (int b = 0; b < BS; ++b) acc[a][b] = fmaf(pa[a], xa[b], fmaf(qa[a], ya[b], acc[a][b]));
     }
   }
+  const float* af = alpha + ((long long)bh * F + f) * D;
 #pragma unroll
-  for (int a = 0; a < BS; ++a)
+  for (int a = 0; a < BS; ++a) {
+    const float ra = SANA ? -cc * af[ib + 16 * a] : -cc;
 #pragma unroll
-    for (int b = 0; b < BS; ++b) dA[fo + (long long)(ib + 16 * a) * D + jb + 16 * b] = -cc * acc[a][b];
+    for (int b = 0; b < BS; ++b) dA[fo + (long long)(ib + 16 * a) * D + jb + 16 * b] = ra * acc[a][b];
+  }
 }
 
 // ---------------------------------------------------------------- statistics
@@ -1250,15 +1292,17 @@ __global__ __launch_bounds__(256) void lin_param_grad_kernel(
 hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdArgs& a,
                              hipStream_t st) {
   const int BH = g.B * g.H;
-  const float cc = a.rule == HWA_RULE_VDN_SCALED ? a.c * a.c : 1.0f;
-  const float c1 = a.rule == HWA_RULE_VDN_SCALED ? a.c : 1.0f;
+  const bool sana = a.rule == HWA_RULE_SANA_SCALED;
+  const float cc = a.rule == HWA_RULE_VDN_SOLVE ? 1.0f : a.c * a.c;
+  // dB_f's factor: c1 of X_f = S D + c1 B_f (vdn rules), c2 of + c2 B_f (SANA)
+  const float cb = a.rule == HWA_RULE_VDN_SOLVE ? 1.0f : a.c;
   const bool bf = dtype == HWA_BF16;
   hipError_t e = hipSuccess;
   switch (stage) {
     case 0: {  // recompute: statistics, inverses, every frame's states
       e = launch_stats(g, dtype, a.k, a.v, a.beta, a.conv_k, a.conv_v, true, a.A, a.Bm, st);
       if (e != hipSuccess) return e;
-      e = launch_inverse(g, cc, a.A, a.M, st);
+      e = launch_update_f32(g, !sana, cc, a.A, a.M, st);
       if (e != hipSuccess) return e;
       Geom g1 = g;
       g1.chunk = 1;
@@ -1330,9 +1374,15 @@ hipError_t launch_linear_bwd(const Geom& g, int dtype, int stage, const LinBwdAr
       if ((e = hipGetLastError()) != hipSuccess) return e;
       {
         dim3 grid(g.F, BH);
-#define FG(DD)                                                                          \
-  hipLaunchKernelGGL(lin_frame_grad_kernel<DD>, grid, dim3(256), 0, st, a.Pst, a.Qst,    \
-                     a.dXP, a.dXQ, cc, c1, a.A, a.Bm, a.dal, g.F);
+#define FG(DD)                                                                            \
+  if (sana)                                                                                \
+    hipLaunchKernelGGL((lin_frame_grad_kernel<DD, true>), grid, dim3(256), 0, st, a.Pst,     \
+                       a.Qst, a.dXP, a.dXQ, cc, cb, a.alpha, a.dbank, g.chunk, g.nch, BH,  \
+                       a.A, a.Bm, a.dal, g.F);                                              \
+  else                                                                                     \
+    hipLaunchKernelGGL((lin_frame_grad_kernel<DD, false>), grid, dim3(256), 0, st, a.Pst,    \
+                       a.Qst, a.dXP, a.dXQ, cc, cb, a.alpha, a.dbank, g.chunk, g.nch, BH,  \
+                       a.A, a.Bm, a.dal, g.F);
         LB_SWITCH_D(FG)
 #undef FG
       }

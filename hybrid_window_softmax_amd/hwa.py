@@ -450,8 +450,9 @@ def hybrid_attention(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v, fra
                      tokens_per_frame: int, chunk: int = 5, radius: int = 1,
                      rule="vdn_solve", c: float = 0.5, text_scale: float = 0.5,
                      rms_eps: float = 1e-6, rms_weight=None):
-    """out = o_sm + y, differentiable in every tensor input (the update rules
-    vdn_solve and vdn_scaled; no q_rope / k_rope)."""
+    """out = o_sm + y, differentiable in every tensor input (all three update
+    rules, sana_scaled within the range hwa_linear_bwd states; no q_rope /
+    k_rope)."""
     return HybridAttention.apply(q, k, v, beta, alpha, gate, text_state, conv_k, conv_v,
                                  rms_weight, frames, tokens_per_frame, chunk, radius, rule, c,
                                  text_scale, rms_eps)

@@ -354,9 +354,9 @@ size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
  *                                          the branch never reads q_rope)
  *   beta [B, H, N], alpha [B, H, F, d], text_state [B, H, d, d] or NULL
  *                                          fp32, as for hybrid_attn_fwd
- *   frames .. rule                         as for hybrid_attn_fwd; rule
- *                                          HWA_RULE_SANA_SCALED returns
- *                                          HWA_ERR_UNSUPPORTED
+ *   frames .. rule                         as for hybrid_attn_fwd (all
+ *                                          three rules; see sana_scaled
+ *                                          below)
  *   dq, dk, dv, dgate [B, H, N, d] dtype   written (bf16: rounded from fp32)
  *   dbeta [B, H, N], dalpha [B, H, F, d]   fp32, written
  *   dtext_state [B, H, d, d] fp32 or NULL  dL/dtext_state (with a NULL
@@ -377,6 +377,12 @@ size_t hwa_softmax_bwd_workspace_bytes(int32_t frames, int32_t tokens_per_frame,
  * Outputs must not overlap each other, an input or the workspace. All
  * arithmetic is fp32, except that bf16 calls recompute the scan states with
  * the forward's split-bf16 MFMA scan (about 16 significant bits per product).
+ * sana_scaled: the backward carries no power-of-two exponents; it is exact
+ * (to fp32 rounding) while every recomputed state P_f, Q_f, every adjoint and
+ * every gathered state's gradient stays inside fp32's normal range (about
+ * 2^-126 .. 2^127). The states grow by up to ||I - c^2 A_f|| per frame (about
+ * 28 for the 1,560-token frames of the clip workloads, so about 20 frames
+ * there); past that the outputs are not finite.
  * Returns HWA_OK, or an error status before anything is enqueued.
  */
 #define HWA_NUM_LIN_BWD_STAGE_EVENTS 6

@@ -304,7 +304,6 @@ def test_linear_bwd_validation():
             continue
         assert _lin_call(p, **{name: None}) == E.HWA_ERR_INVALID_ARG, name
     assert _lin_call(_lin_ws(_params(conv_k=None))) == E.HWA_ERR_INVALID_ARG
-    assert _lin_call(p, rule=1) == E.HWA_ERR_UNSUPPORTED                 # sana_scaled
     assert _lin_call(p, rule=3) == E.HWA_ERR_INVALID_ARG
     assert _lin_call(p, F=0) == E.HWA_ERR_INVALID_ARG
     assert _lin_call(p, radius=-1) == E.HWA_ERR_INVALID_ARG

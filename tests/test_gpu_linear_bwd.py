@@ -147,11 +147,23 @@ def test_repeat_bit_exact():
         assert np.array_equal(a[n], b[n]), n
 
 
-def test_sana_scaled_unsupported():
-    inp = inputs.make("tiny-f32")
-    with pytest.raises(hwa.HwaError) as e:
-        _gpu_grads(inp, "sana_scaled", None, inputs.grad_output(inp.cfg))
-    assert e.value.code == hwa.HWA_ERR_UNSUPPORTED
+@pytest.mark.parametrize("kw,text", [
+    # the far field on both sides of every window (chunks of 2, radius 0)
+    (dict(frames=12, head_dim=32, tokens_per_frame=8, chunk=2, radius=0), True),
+    (dict(frames=9, head_dim=64, tokens_per_frame=20, batch=2, heads=2), False),
+    (dict(frames=14, head_dim=128, tokens_per_frame=24, chunk=3), True),
+])
+def test_sana_scaled_fp32(kw, text):
+    # sana_scaled: S_f = (S_{f-1} D_f)(I - c^2 A_f) + c B_f; at these sizes the
+    # states stay well inside fp32's range (the backward carries no exponents)
+    check(inputs.make(inputs.tiny_config(text_tokens=0, seed=403, **kw),
+                      random_rms_weight=True), "sana_scaled", text)
+
+
+def test_sana_scaled_bf16():
+    check(inputs.make(inputs.tiny_config(frames=11, head_dim=128, tokens_per_frame=45, heads=2,
+                                         text_tokens=0, dtype="bf16", seed=404)),
+          "sana_scaled")
 
 
 def test_long_clip_132600tok_one_head():
@@ -185,6 +197,8 @@ def test_long_clip_132600tok_one_head():
     ("small-bf16-text", "vdn_solve"),
     (inputs.tiny_config(frames=17, head_dim=32, tokens_per_frame=37, text_tokens=0, seed=402),
      "vdn_scaled"),
+    (inputs.tiny_config(frames=10, head_dim=64, tokens_per_frame=16, text_tokens=0, seed=405),
+     "sana_scaled"),
 ])
 def test_hybrid_autograd(cfg, rule):
     # hwa.hybrid_attention through torch autograd: out.backward(g) runs
