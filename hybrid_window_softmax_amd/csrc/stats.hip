@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void stats_kernel(
 //  - four consumer waves run the MFMAs of the previous tile from the other
 //    buffer; each owns a quarter of the 32 x 32 output blocks (A, then B).
 // One barrier per tile; both roles pass the same number of barriers.
-constexpr int SX_TT = 64;  // tokens per tile (8 groups of 8 per LDS row)
+constexpr int SX_TT = 64;  // tokens per tile
 // producer waves: d / 16 (4 channels x 4 tokens per thread over a 64-token tile)
 __host__ __device__ constexpr int sx_pw(int d) { return d / 16; }
 
@@ -188,14 +188,6 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
   static_assert(TPG == 4, "token group");
   static_assert(CG == 32 || CG == 16, "channel groups span a 32- or 16-lane group");
   typedef __bf16 bf16xT_t __attribute__((ext_vector_type(TPG)));
-  // element (channel c, token t) of a stage: the 8-token groups of channel
-  // row c are rotated by c / 8. Unrotated, the producers' 8-byte stores (the
-  // lanes of a half wave on rows 4 apart, 576 bytes) fell on two bank
-  // positions; rotated, both they and the consumers' 16-byte reads (rows 1
-  // apart) spread over every bank (measured about 1 % faster).
-  auto sx_at = [](int c, int t) {
-    return c * TP + ((((t >> 3) + (c >> 3)) & 7) << 3) + (t & 7);
-  };
   // [stage][k hi, k lo, v hi, v lo][channel][token]
   __shared__ __attribute__((aligned(16))) bf16_t buf[2][4][D * TP];
 
@@ -271,7 +263,7 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
         hv[u] = hb;
         lv[u] = lb;
       }
-      const int o = sx_at(c0 + i, tg * TPG);
+      const int o = (c0 + i) * TP + tg * TPG;
       *(bf16xT_t*)&buf[st][arr][o] = hv;
       *(bf16xT_t*)&buf[st][arr + 1][o] = lv;
     };
@@ -335,8 +327,8 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
           const int blk = cw * BPW + b;
           const int isB = blk / (NB * NB);
           const int ib = (blk / NB) % NB, jb = blk % NB;
-          const int ra = sx_at(ib * 32 + col, to);
-          const int rb = sx_at(jb * 32 + col, to);
+          const int ra = (ib * 32 + col) * TP + to;
+          const int rb = (jb * 32 + col) * TP + to;
           const bf16x8_t ah = *(const bf16x8_t*)&buf[st][isB ? 2 : 0][ra];
           const bf16x8_t al = *(const bf16x8_t*)&buf[st][isB ? 3 : 1][ra];
           const bf16x8_t bh8 = *(const bf16x8_t*)&buf[st][0][rb];
