@@ -156,3 +156,78 @@ def test_linear_bwd_graph_replay_bit_exact(name):
         _say(f"  replay {rep}: {mism} elements differ from the eager call")
         assert mism == 0
     del graph
+
+
+def _graph_check(label, call, ref):
+    """Capture `call` (which writes into its preallocated output and returns
+    it) in a graph, replay it three times with eager work in between, and
+    compare every replay with `ref` bit for bit."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one warm call on the capture stream
+        out = call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = call()
+    for r in range(3):
+        out.fill_(0)               # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        mism = int((out.view(torch.int16) != ref.view(torch.int16)).sum())
+        _say(f"  {label} replay {r}: {mism} elements differ from the eager call")
+        assert mism == 0
+    del graph
+
+
+def test_routed_forward_graph_replay_bit_exact():
+    # the routing kernels write every block mean, count and list entry the
+    # softmax kernel reads: no memset, no atomics
+    from hybrid_window_softmax_amd import hwa
+    cfg = inputs.WORKLOADS["small-bf16-text"]
+    _say("case small-bf16-text: routed forward (tau 0.5), eager calls, then a graph replayed")
+    case = GpuCase(inputs.make(cfg))
+    t = case.t
+
+    def call(out=None, ws=None):
+        return hwa.hybrid_attn_fwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["gate"],
+                                   case.text_state, t["conv_k"], t["conv_v"], cfg["frames"],
+                                   cfg["tokens_per_frame"], cfg["chunk"], cfg["radius"],
+                                   "vdn_solve", cfg["c"], 0.5, 1e-6, t["rms_weight"], out=out,
+                                   workspace=ws, route_tau=0.5)
+
+    ref, ws = call()
+    again, _ = call(ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), again.view(torch.int16))
+    out = torch.empty_like(ref)
+    _graph_check("routed", lambda: call(out, ws)[0], ref)
+
+
+def test_block_graph_replay_bit_exact():
+    # the block's GEMMs and the attention enqueue only kernels
+    from hybrid_window_softmax_amd import hwa
+    from harness import to_dev
+    cfg = inputs.tiny_config(head_dim=64, tokens_per_frame=64, frames=10, heads=2,
+                             text_tokens=0, dtype="bf16", seed=170)
+    _say("case block: eager calls, then a graph replayed")
+    inp = inputs.make(cfg)
+    xb, wqb, wob = inputs.block_inputs(cfg)
+    t = {n: to_dev(getattr(inp, n), True) for n in
+         ("beta", "alpha", "gate", "conv_k", "conv_v", "rms_weight")}
+    x, wq, wo = (to_dev(a, True) for a in (xb, wqb, wob))
+
+    def call(y=None, ws=None):
+        return hwa.block_fwd(x, wq, wo, t["beta"], t["alpha"], t["gate"], None, t["conv_k"],
+                             t["conv_v"], cfg["heads"], cfg["frames"], cfg["tokens_per_frame"],
+                             8, 10000.0, cfg["chunk"], cfg["radius"], "vdn_solve", cfg["c"],
+                             0.5, 1e-6, t["rms_weight"], y=y, workspace=ws)
+
+    ref, ws = call()
+    again, _ = call(ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), again.view(torch.int16))
+    y = torch.empty_like(ref)
+    _graph_check("block", lambda: call(y, ws)[0], ref)
