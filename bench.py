@@ -869,8 +869,6 @@ def time_routed(cfg, inp, rule, tau, steps, up, dense_ms):
     time per call, the kept fraction of the window's key blocks, and the
     routed o_sm's relative Frobenius error against the dense o_sm (both from
     softmax-only calls, every head)."""
-    import math
-
     import torch
     from hybrid_window_softmax_amd import hwa
     t = {n: up(getattr(inp, n)) for n in ("q", "k", "v", "gate", "beta", "alpha", "conv_k",

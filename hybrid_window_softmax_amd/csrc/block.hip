@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(GemmArgs g) {
   // per-lane byte offsets of the 4 direct-load slots of each tile: slot
   // s = (wave + 4 j) * 64 + lane lands at LDS byte 16 s = row 128 + chunk 16
   // and holds logical chunk pc ^ swz(row)
-  int a_off[4], w_off[4];
+  int w_off[4];
   long long a_row_base[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -98,7 +98,6 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(GemmArgs g) {
       const int b = m / g.T, tok = m % g.T;
       a_row_base[j] = ((long long)b * g.H * g.T + tok) * g.d + lc * 8;  // + h T d + c0
     }
-    a_off[j] = 0;
   }
   const long long a_elems = (long long)(AMODE == GA_ROWMAJOR ? (long long)g.M * g.K
                                                              : (long long)g.M * g.H * g.d);

@@ -9,7 +9,6 @@ it from the work queues, so repeated calls and replays must agree bit for bit.
 
 import sys
 
-import numpy as np
 import pytest
 import torch
 

@@ -10,7 +10,6 @@ comparisons of the forward. fp32 and bf16 (fused readout) calls, with the
 softmax branch's lse and output requested on one of them.
 """
 
-import numpy as np
 import pytest
 import torch
 
