@@ -140,3 +140,15 @@ def test_routed_full_size_guarded():
     # oracle
     _check(inputs.WORKLOADS["long-clip-832x480-85f"], 1.5, heads_full=[(0, 0), (0, 23)],
            guard=True)
+
+
+@pytest.mark.parametrize("kw,tau", [
+    (dict(head_dim=128, tokens_per_frame=100, frames=1), 1.0),                 # one frame
+    (dict(head_dim=64, tokens_per_frame=1, frames=23, chunk=4), 0.5),          # one token a frame
+    (dict(head_dim=128, tokens_per_frame=300, frames=8, radius=0), 1.5),       # no neighbours
+    (dict(head_dim=64, tokens_per_frame=130, frames=11, chunk=1), 10.0),       # best block only
+    (dict(head_dim=128, tokens_per_frame=77, frames=9, batch=2, heads=2), -0.5),
+])
+def test_routed_edge_shapes(kw, tau):
+    cfg = inputs.tiny_config(text_tokens=0, dtype="bf16", seed=152, **kw)
+    _check(cfg, tau)
