@@ -284,23 +284,31 @@ __global__ __launch_bounds__(2 * D) void scan_mfma_kernel(
     for (int r = 0; r < 16; ++r) sv[r] = acc[r] + (acc1[r] + acc2[r]);
     __syncthreads();  // M and this X buffer are read: free for the next frame
     if (SANA) {
-      // row max |S| over all columns: 32 lanes of a half, then the waves
+      // rows are renormalised only when some entry passed 2^64 (every dozen
+      // frames or so at 1,560 tokens per frame): the row maxima are gathered
+      // only then
+      bool big = false;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float m = fabsf(sv[r]);
+      for (int r = 0; r < 16; ++r) big |= fabsf(sv[r]) > 0x1p64f;
+      if (__syncthreads_or(big)) {
+        // row max |S| over all columns: 32 lanes of a half, then the waves
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if (col == 0) atomicMax(&rmax[buf][rowof(r)], __float_as_uint(m));
-      }
-      __syncthreads();
+        for (int r = 0; r < 16; ++r) {
+          float m = fabsf(sv[r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float m = __uint_as_float(rmax[buf][rowof(r)]);
-        if (m > 0x1p64f) {
-          int ex;
-          frexpf(m, &ex);
-          sv[r] = ldexpf(sv[r], -ex);
-          e[r] += ex;
+          for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+          if (col == 0) atomicMax(&rmax[buf][rowof(r)], __float_as_uint(m));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float m = __uint_as_float(rmax[buf][rowof(r)]);
+          if (m > 0x1p64f) {
+            int ex;
+            frexpf(m, &ex);
+            sv[r] = ldexpf(sv[r], -ex);
+            e[r] += ex;
+          }
         }
       }
       if (tid < 32) rmax[buf ^ 1][tid] = 0u;  // cleared for the next frame
@@ -437,23 +445,31 @@ __global__ __launch_bounds__(2 * D) void scan_packed_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) sv[r] = acc[r] + (acc1[r] + acc2[r]);
     if (SANA) {
-      // row max |S| over all columns: 32 lanes of a half, then the waves
+      // rows are renormalised only when some entry passed 2^64 (every dozen
+      // frames or so at 1,560 tokens per frame): the row maxima are gathered
+      // only then
+      bool big = false;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float m = fabsf(sv[r]);
+      for (int r = 0; r < 16; ++r) big |= fabsf(sv[r]) > 0x1p64f;
+      if (__syncthreads_or(big)) {
+        // row max |S| over all columns: 32 lanes of a half, then the waves
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if (col == 0) atomicMax(&rmax[buf][rowof(r)], __float_as_uint(m));
-      }
-      __syncthreads();
+        for (int r = 0; r < 16; ++r) {
+          float m = fabsf(sv[r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float m = __uint_as_float(rmax[buf][rowof(r)]);
-        if (m > 0x1p64f) {
-          int ex;
-          frexpf(m, &ex);
-          sv[r] = ldexpf(sv[r], -ex);
-          e[r] += ex;
+          for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+          if (col == 0) atomicMax(&rmax[buf][rowof(r)], __float_as_uint(m));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float m = __uint_as_float(rmax[buf][rowof(r)]);
+          if (m > 0x1p64f) {
+            int ex;
+            frexpf(m, &ex);
+            sv[r] = ldexpf(sv[r], -ex);
+            e[r] += ex;
+          }
         }
       }
       if (tid < 32) rmax[buf ^ 1][tid] = 0u;  // cleared for the next frame
