@@ -301,8 +301,11 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
   if (mark(0) != hipSuccess) return HWA_ERR_HIP;
   if (hwa::launch_window_table(g, lohi, st, sched) != hipSuccess) return HWA_ERR_HIP;
   if (mark(1) != hipSuccess) return HWA_ERR_HIP;
-  if (do_lin && hwa::launch_stats(g, p->dtype, k, v, beta, p->conv_k,
-                                  p->conv_v, true, A, Bm, st) != hipSuccess)
+  // on bf16 calls whose frames hold a multiple of 4 tokens the statistics
+  // kernel also writes the softmax's transposed v
+  const bool vt_fused = do_lin && do_sm && p->dtype == HWA_BF16 && g.S % 4 == 0;
+  if (do_lin && hwa::launch_stats(g, p->dtype, k, v, beta, p->conv_k, p->conv_v, true, A, Bm,
+                                  st, vt_fused ? v_t : nullptr) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(2) != hipSuccess) return HWA_ERR_HIP;
   const bool bf = p->dtype == HWA_BF16;
@@ -335,7 +338,7 @@ hwa_status hybrid_attn_fwd(const void* q, const void* k, const void* v,
                         st) != hipSuccess)
     return HWA_ERR_HIP;
   if (mark(5) != hipSuccess) return HWA_ERR_HIP;
-  if (do_sm && p->dtype == HWA_BF16 &&
+  if (do_sm && p->dtype == HWA_BF16 && !vt_fused &&
       hwa::launch_vtranspose(g, (const bf16_t*)v, v_t, st) != hipSuccess)
     return HWA_ERR_HIP;
   hwa::RouteArgs rt{(const int*)(ws + X.rcount), (const uint16_t*)(ws + X.rlist),

@@ -143,10 +143,13 @@ hipError_t launch_vtranspose(const Geom& g, const bf16_t* v, bf16_t* v_t,
                              hipStream_t st);
 
 // A_f, B_f of every (b, h, f). conv == false: text mode (no conv on k, raw v).
+// v_t (bf16 calls with S % 4 == 0 only, else null): also writes the raw v
+// transposed, [B*H][d][round_up64(N)] with zeros past N, as launch_vtranspose
+// does.
 hipError_t launch_stats(const Geom& g, int dtype, const void* k,
                         const void* v, const float* beta, const float* conv_k,
                         const float* conv_v, bool conv, float* A, float* Bm,
-                        hipStream_t st);
+                        hipStream_t st, bf16_t* v_t = nullptr);
 
 // M_f = (I + c2 A_f)^-1 for every (b, h, f) (Gauss-Jordan sweep, fp32).
 hipError_t launch_inverse(const Geom& g, float c2, const float* A, float* M,

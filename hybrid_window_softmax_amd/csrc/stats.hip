@@ -149,6 +149,11 @@ __global__ __launch_bounds__(256) void stats_kernel(
 //  - four consumer waves run the MFMAs of the previous tile from the other
 //    buffer; each owns a quarter of the 32 x 32 output blocks (A, then B).
 // One barrier per tile; both roles pass the same number of barriers.
+// With vt set, the producers also write the raw v rows they hold transposed
+// into vt ([d][Np] per (b, h), the softmax's V^T operand), which spares a
+// separate transpose pass over v; this needs S % 4 == 0, so that every thread's
+// 4 tokens lie inside the frame or outside it and its 8-byte stores are
+// aligned.
 constexpr int SX_TT = 64;  // tokens per tile
 // producer waves: d / 16 (4 channels x 4 tokens per thread over a 64-token tile)
 __host__ __device__ constexpr int sx_pw(int d) { return d / 16; }
@@ -176,7 +181,8 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ conv_k,
     const float* __restrict__ conv_v, int conv, float* __restrict__ A,
-    float* __restrict__ Bm, int F, int S, int H, long long N) {
+    float* __restrict__ Bm, int F, int S, int H, long long N, bf16_t* __restrict__ vt,
+    long long Np) {
   constexpr int NPW = sx_pw(D);      // producer waves
   constexpr int NP = 64 * NPW;       // producer threads
   constexpr int CG = D / 4;          // channel groups of 4
@@ -275,6 +281,19 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
       float kf[TPG][4], vf[TPG][4];
       conv4(kraw, wk, kf);
       conv4(vraw, wv, vf);
+      if (vt && s0 + tg * TPG < S) {
+        // raw v of this thread's tokens, channel by channel: rows 3..6 of
+        // vraw hold tokens sb..sb+3, channels c0..c0+3 as two bf16 pairs
+        bf16_t* dst = vt + ((long long)bh * D + c0) * Np + n0 + s0 + tg * TPG;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t w0 = i < 2 ? vraw[3].x : vraw[3].y, w1 = i < 2 ? vraw[4].x : vraw[4].y;
+          const uint32_t w2 = i < 2 ? vraw[5].x : vraw[5].y, w3 = i < 2 ? vraw[6].x : vraw[6].y;
+          *(uint2*)(dst + (long long)i * Np) =
+              make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
+        }
+      }
       if (s0 + SX_TT < S) fetch(s0 + SX_TT);
       // k' = sqrt(beta) L2(SiLU(conv_k(k)))
       float ss[TPG];
@@ -300,6 +319,11 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
         store(st, 2, i, y);
       }
     };
+    if (vt && f == F - 1) {  // keys past N of the transposed v read as zeros
+      const int pad = (int)(Np - N);
+      for (int x = tid; x < D * pad; x += NP)
+        vt[((long long)bh * D + x / pad) * Np + N + x % pad] = (bf16_t)0;
+    }
     fetch(0);
     make(0, 0);
     __syncthreads();  // tile 0 is in stage 0
@@ -358,7 +382,7 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
 hipError_t launch_stats(const Geom& g, int dtype, const void* k,
                         const void* v, const float* beta, const float* conv_k,
                         const float* conv_v, bool conv, float* A, float* Bm,
-                        hipStream_t st) {
+                        hipStream_t st, bf16_t* v_t) {
   dim3 grid(g.F, g.B * g.H);
 #define STATS_LAUNCH(TT, DD)                                                  \
   hipLaunchKernelGGL((stats_kernel<TT, DD>), grid, dim3(256), 0, st,          \
@@ -372,10 +396,12 @@ hipError_t launch_stats(const Geom& g, int dtype, const void* k,
     default: STATS_LAUNCH(TT, 128); break; \
   }
   if (dtype == HWA_BF16) {
+    if (v_t && g.S % 4 != 0) return hipErrorInvalidValue;
+    const long long Np = (g.N + 63) / 64 * 64;
 #define SX_LAUNCH(DD)                                                        \
   hipLaunchKernelGGL(stats_mfma_kernel<DD>, grid, dim3(64 * (sx_pw(DD) + 4)), 0, st, \
                      (const bf16_t*)k, (const bf16_t*)v, beta, conv_k,       \
-                     conv_v, (int)conv, A, Bm, g.F, g.S, g.H, g.N)
+                     conv_v, (int)conv, A, Bm, g.F, g.S, g.H, g.N, v_t, Np)
     if (g.d == 128) SX_LAUNCH(128);
     else SX_LAUNCH(64);
 #undef SX_LAUNCH

@@ -110,7 +110,11 @@ typedef struct {
                          /* timing: [0] start, then after [1] window table,   */
                          /* [2] statistics, [3] inverses, [4] scan, [5] decay */
                          /* products and (bf16) S_t of every frame, [6] V    */
-                         /* transpose (and the routing of HWA_FLAG_ROUTED),   */
+                         /* transpose (a separate pass only where the         */
+                         /* statistics kernel does not write it: frames of a  */
+                         /* token count that is not a multiple of 4, or       */
+                         /* HWA_FLAG_SOFTMAX_ONLY) and the routing of         */
+                         /* HWA_FLAG_ROUTED,                                  */
                          /* [7] softmax (with the                             */
                          /* linear-branch readout fused in, on bf16 calls     */
                          /* that run both branches), [8]                      */
