@@ -226,18 +226,29 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
     // overlap the feature work
     uint2 kraw[TPG + 3], vraw[TPG + 3];
     float braw[TPG];
+    // the frame's rows through buffer descriptors sized to the frame: a row
+    // before its start (a negative offset, past num_records as unsigned) or
+    // past its end reads zeros, with no branch per row
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kp + n0 * D), 0, S * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vp + n0 * D), 0, S * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t brs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(bp + n0), 0, S * 4, 0x00020000);
     auto fetch = [&](int s0) {
       const int sb = s0 + tg * TPG;
 #pragma unroll
-      for (int u = 0; u < TPG; ++u) braw[u] = sb + u < S ? bp[n0 + sb + u] : 0.0f;
+      for (int u = 0; u < TPG; ++u) {
+        int off = (sb + u) * 4;
+        asm volatile("" : "+v"(off));  // the whole offset stays in the range check
+        braw[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, off, 0, 0));
+      }
 #pragma unroll
       for (int x = 0; x < TPG + 3; ++x) {
-        const int s = sb - 3 + x;
-        kraw[x] = vraw[x] = make_uint2(0u, 0u);
-        if (s >= 0 && s < S) {
-          kraw[x] = *(const uint2*)(kp + (n0 + s) * D + c0);
-          vraw[x] = *(const uint2*)(vp + (n0 + s) * D + c0);
-        }
+        int off = ((sb - 3 + x) * D + c0) * 2;
+        asm volatile("" : "+v"(off));
+        kraw[x] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(krs, off, 0, 0));
+        vraw[x] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, 0));
       }
     };
     // causal width-4 conv of TPG tokens x 4 channels
