@@ -155,6 +155,7 @@ __global__ __launch_bounds__(256) void stats_kernel(
 // 4 tokens lie inside the frame or outside it and its 8-byte stores are
 // aligned.
 constexpr int SX_TT = 64;  // tokens per tile
+typedef unsigned v2u32_t __attribute__((ext_vector_type(2)));
 // producer waves: d / 16 (4 channels x 4 tokens per thread over a 64-token tile)
 __host__ __device__ constexpr int sx_pw(int d) { return d / 16; }
 
@@ -235,6 +236,10 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
         __builtin_amdgcn_make_buffer_rsrc((void*)(vp + n0 * D), 0, S * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t brs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(bp + n0), 0, S * 4, 0x00020000);
+    // this (b, h)'s transposed v, [d][Np] (fewer than 2^31 bytes, as the
+    // softmax requires of it)
+    const __amdgpu_buffer_rsrc_t vts = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vt + (long long)bh * D * Np), 0, (int)(D * Np * 2), 0x00020000);
     auto fetch = [&](int s0) {
       const int sb = s0 + tg * TPG;
 #pragma unroll
@@ -292,20 +297,27 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
       float kf[TPG][4], vf[TPG][4];
       conv4(kraw, wk, kf);
       conv4(vraw, wv, vf);
-      if (vt && s0 + tg * TPG < S) {
+      if (vt) {
         // raw v of this thread's tokens, channel by channel: rows 3..6 of
-        // vraw hold tokens sb..sb+3, channels c0..c0+3 as two bf16 pairs
-        bf16_t* dst = vt + ((long long)bh * D + c0) * Np + n0 + s0 + tg * TPG;
+        // vraw hold tokens sb..sb+3, channels c0..c0+3 as two bf16 pairs;
+        // a thread whose tokens lie past the frame stores out of range
+        // (dropped)
+        const int sb = s0 + tg * TPG;
+        int off = sb < S ? (c0 * (int)Np + (int)n0 + sb) * 2 : (int)0x80000000;
+        const int step = sb < S ? (int)Np * 2 : 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
           const uint32_t w0 = i < 2 ? vraw[3].x : vraw[3].y, w1 = i < 2 ? vraw[4].x : vraw[4].y;
           const uint32_t w2 = i < 2 ? vraw[5].x : vraw[5].y, w3 = i < 2 ? vraw[6].x : vraw[6].y;
-          *(uint2*)(dst + (long long)i * Np) =
-              make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
+          const uint2 val = make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, val), vts, off, 0, 0);
+          off += step;
         }
       }
-      if (s0 + SX_TT < S) fetch(s0 + SX_TT);
+      // the next tile's rows (rows past the frame read zeros, so the last
+      // tile fetches too)
+      fetch(s0 + SX_TT);
       // k' = sqrt(beta) L2(SiLU(conv_k(k)))
       float ss[TPG];
 #pragma unroll
