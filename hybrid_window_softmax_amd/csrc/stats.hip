@@ -237,9 +237,10 @@ __global__ __launch_bounds__(64 * (sx_pw(D) + 4)) void stats_mfma_kernel(
     const __amdgpu_buffer_rsrc_t brs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(bp + n0), 0, S * 4, 0x00020000);
     // this (b, h)'s transposed v, [d][Np] (fewer than 2^31 bytes, as the
-    // softmax requires of it)
+    // softmax requires of it); unused without vt
     const __amdgpu_buffer_rsrc_t vts = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vt + (long long)bh * D * Np), 0, (int)(D * Np * 2), 0x00020000);
+        vt ? (void*)(vt + (long long)bh * D * Np) : nullptr, 0, vt ? (int)(D * Np * 2) : 0,
+        0x00020000);
     auto fetch = [&](int s0) {
       const int sb = s0 + tg * TPG;
 #pragma unroll
